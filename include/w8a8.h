@@ -1,0 +1,153 @@
+/*
+ * w8a8.h — guarded W8A8 linear layer for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libw8a8.so.  The method is TurboT2VA's W8A8 linear (page "音视频
+ * 生成提速54倍！浙大等团队开源联合蒸馏方案TurboT2VA", 智猩猩, section 01.3
+ * "量化策略"): weights quantised statically to INT8 per output channel,
+ * activations dynamically to INT8 per row, the product accumulated in INT32,
+ * scale and bias applied once after the whole accumulation, and shapes the
+ * INT8 kernel cannot serve falling back to native BF16.  Padded-row compaction
+ * follows the closing paragraph of that section and the paperlayer.ai summary
+ * (section "C. Fused Multimodal Transformer Operations"): padded text
+ * positions are removed with the shared mask, every valid row kept unchanged.
+ *
+ * Conventions for every call:
+ *   - Tensors are device pointers on the current HIP device, dense row-major.
+ *     bf16 values are passed as uint16_t bit patterns.  The caller owns all
+ *     memory; nothing is allocated, freed or synchronised inside the library.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *     asynchronously; device faults surface at the caller's next sync.
+ *   - Outputs must not alias inputs.  Inputs must be finite.
+ *   - All argument checks run on the host before anything is launched; a
+ *     failed check returns W8A8_EINVAL and launches nothing.
+ *   - Zero-sized work (rows == 0, M == 0, ...) is a valid no-op returning W8A8_OK,
+ *     except compact_padded_rows, which still writes *count = 0.
+ */
+#ifndef W8A8_H
+#define W8A8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__)
+#define W8A8_API __attribute__((visibility("default")))
+#else
+#define W8A8_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    W8A8_OK = 0,
+    W8A8_EINVAL = -1,       /* bad argument: NULL, negative size, misalignment, combo */
+    W8A8_EUNSUPPORTED = -2, /* shape the INT8 GEMM does not serve (see w8a8_guard)     */
+    W8A8_EHIP = -3          /* a HIP launch failed                                     */
+} w8a8_status;
+
+typedef enum { W8A8_OUT_BF16 = 0, W8A8_OUT_I32 = 1 } w8a8_out;
+typedef enum { W8A8_ACT_NONE = 0, W8A8_ACT_GELU_TANH = 1 } w8a8_act;
+typedef enum { W8A8_PATH_INT8 = 0, W8A8_PATH_BF16 = 1 } w8a8_path;
+
+/* Largest K the INT8 path admits: |acc| <= 127*127*K stays below 2^31. */
+#define W8A8_MAX_K 131072
+
+/*
+ * Per-row symmetric INT8 quantisation (section 01.3: weights per output
+ * channel — the rows of W[N x K] — statically, activations per token row
+ * dynamically; the same routine serves both).
+ *
+ *   x     [rows x cols] bf16 input
+ *   q     [rows x cols] int8 codes out
+ *   scale [rows]        fp32 scale out
+ *
+ * For each row: a = max|x|; if a < 2^-100 then scale = 0 and every code is 0;
+ * else scale = RN32(a/127), inv = RN32(127/a), q = RNE(RN32(x*inv)) clamped to
+ * [-127, 127].  Dequantisation is q*scale.
+ * Alignment: 2-byte for x, 1-byte for q, 4-byte for scale; 16-byte x and
+ * 8-byte q with cols % 8 == 0 take the vector path.
+ */
+W8A8_API int w8a8_quantize_rows(const uint16_t* x, int64_t rows, int64_t cols, int8_t* q, float* scale,
+                       void* stream);
+
+/*
+ * INT8 GEMM with INT32 accumulation and the epilogue after full accumulation
+ * (section 01.3).
+ *
+ *   qa [M x K] int8, sa [M] fp32    quantised activations and their row scales
+ *   qw [N x K] int8, sw [N] fp32    quantised weights and their channel scales
+ *   bias [N] bf16 or NULL
+ *   out [M x N]: out_kind == W8A8_OUT_BF16 -> bf16
+ *                  y = bf16_RNE(fma(float(acc), RN32(sa[i]*sw[j]), bias[j]))
+ *                  (no bias: bf16_RNE(float(acc) * RN32(sa[i]*sw[j])));
+ *                  act == W8A8_ACT_GELU_TANH then applies
+ *                  g(z) = z/2 (1 + tanh(sqrt(2/pi)(z + 0.044715 z^3))) to the bf16 y
+ *                  and rounds to bf16 again.
+ *                out_kind == W8A8_OUT_I32 -> the raw int32 accumulator
+ *                  acc[i][j] = sum_k qa[i][k]*qw[j][k] (act must be NONE; sa, sw,
+ *                  bias are ignored and may be NULL).
+ * Shapes: w8a8_guard(N, K) must hold, else W8A8_EUNSUPPORTED (never a silent
+ * fallback).  M is unrestricted.  qa, qw, out must be 16-byte aligned.
+ */
+W8A8_API int w8a8_gemm(const int8_t* qa, const float* sa, int64_t M, const int8_t* qw, const float* sw,
+              int64_t N, int64_t K, const uint16_t* bias, int act, int out_kind, void* out,
+              void* stream);
+
+/*
+ * The guarded W8A8 linear y = X W^T + b (section 01.3; paperlayer.ai section C,
+ * "guarded acceleration according to architectural role and shape").
+ *
+ *   x [M x K] bf16, y [M x N] bf16, bias [N] bf16 or NULL
+ *   If w8a8_guard(N, K): INT8 path.  qw [N x K] int8 and sw [N] fp32 (the
+ *     weight prepared once with w8a8_quantize_rows) are required; x is
+ *     quantised per row into the workspace, then w8a8_gemm runs.  The
+ *     workspace needs w8a8_linear_workspace_bytes(M, K) bytes, 256-byte aligned.
+ *   Else: BF16 path (w8a8_linear_bf16); w [N x K] bf16 is required and the
+ *     workspace is unused (may be NULL).
+ *   path_taken (host pointer, may be NULL) receives W8A8_PATH_INT8 or _BF16.
+ */
+W8A8_API int w8a8_linear(const uint16_t* x, int64_t M, int64_t K, int64_t N, const int8_t* qw,
+                const float* sw, const uint16_t* w, const uint16_t* bias, int act, uint16_t* y,
+                void* workspace, size_t workspace_bytes, int* path_taken, void* stream);
+
+/*
+ * Native BF16 linear, the fallback of the guarded layer (section 01.3: branches
+ * the optimised operator cannot serve run in native BF16):
+ *   y = bf16_RNE(sum_k x[i][k] w[j][k] + b[j]) with fp32 accumulation, optional
+ *   GELU-tanh as in w8a8_gemm.  Any M, N, K >= 0; x, w, y need 4-byte alignment
+ *   only (rows of odd-multiple-of-2 K such as 2050 are allowed).
+ */
+W8A8_API int w8a8_linear_bf16(const uint16_t* x, int64_t M, int64_t K, const uint16_t* w, int64_t N,
+                     const uint16_t* bias, int act, uint16_t* y, void* stream);
+
+/*
+ * Padded-row compaction (section 01.3 closing paragraph; paperlayer.ai section C:
+ * only invalid prompt positions are removed, every valid token kept unchanged).
+ *
+ *   x    [B x L x D] bf16, mask [B x L] uint8 (nonzero = valid; any pattern)
+ *   out  [capacity B*L x D] bf16: the valid rows, in (b, t) order, copied bit-exactly
+ *   src_row [capacity B*L] int32: src_row[m] = b*L + t of output row m
+ *   count   [1] int32, device memory: number of valid rows (always written)
+ * The caller synchronises if it needs the count on the host.  B*L < 2^31.
+ */
+W8A8_API int compact_padded_rows(const uint16_t* x, const uint8_t* mask, int64_t B, int64_t L, int64_t D,
+                        uint16_t* out, int32_t* src_row, int32_t* count, void* stream);
+
+/* ---- host-only helpers: no GPU is touched ---- */
+
+/* 1 if the INT8 GEMM serves (N, K): K % 128 == 0, 128 <= K <= W8A8_MAX_K,
+ * N % 64 == 0, N >= 64.  0 otherwise (the linear then takes the BF16 path). */
+W8A8_API int w8a8_guard(int64_t N, int64_t K);
+
+/* Workspace bytes w8a8_linear needs on the INT8 path: M*K int8 codes rounded
+ * up to 256 bytes, then M fp32 scales.  0 for M <= 0 or K <= 0. */
+W8A8_API size_t w8a8_linear_workspace_bytes(int64_t M, int64_t K);
+
+/* Static string for a status code. */
+W8A8_API const char* w8a8_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* W8A8_H */

@@ -1,0 +1,256 @@
+"""Guarded W8A8 linear layer for AMD Instinct MI355X (gfx950).
+
+Thin Python binding over ``libw8a8.so`` (C ABI in ``include/w8a8.h``).  Every
+step of the path runs in the library's HIP kernels; this module only checks
+tensor shapes/dtypes, allocates outputs with torch (device memory) and passes
+pointers plus torch's current HIP stream.  There is no CPU fallback: if the
+native library is missing, every call raises.
+
+Method: TurboT2VA's W8A8 linear (智猩猩 article, section 01.3 "量化策略") and
+padded-text compaction (same section, closing paragraph; paperlayer.ai
+summary, section "C. Fused Multimodal Transformer Operations").
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libw8a8.so")
+
+OK, EINVAL, EUNSUPPORTED, EHIP = 0, -1, -2, -3
+OUT_BF16, OUT_I32 = 0, 1
+ACT_NONE, ACT_GELU_TANH = 0, 1
+PATH_INT8, PATH_BF16 = 0, 1
+MAX_K = 131072
+
+EXPORTS = ("w8a8_quantize_rows", "w8a8_gemm", "w8a8_linear", "w8a8_linear_bf16",
+           "compact_padded_rows", "w8a8_guard", "w8a8_linear_workspace_bytes",
+           "w8a8_status_str")
+
+_lib = None
+
+
+class W8A8Error(RuntimeError):
+    def __init__(self, fn, status):
+        super().__init__(f"{fn}: {status_str(status)} ({status})")
+        self.status = status
+
+
+def lib():
+    """The loaded native library (ctypes.CDLL).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"native library {LIB_PATH} is missing; build it with "
+                           "`python -m int8_w8a8_gemm_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I64, I, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+    L.w8a8_quantize_rows.argtypes = [P, I64, I64, P, P, P]
+    L.w8a8_gemm.argtypes = [P, P, I64, P, P, I64, I64, P, I, I, P, P]
+    L.w8a8_linear.argtypes = [P, I64, I64, I64, P, P, P, P, I, P, P, SZ, P, P]
+    L.w8a8_linear_bf16.argtypes = [P, I64, I64, P, I64, P, I, P, P]
+    L.compact_padded_rows.argtypes = [P, P, I64, I64, I64, P, P, P, P]
+    L.w8a8_guard.argtypes = [I64, I64]
+    L.w8a8_linear_workspace_bytes.argtypes = [I64, I64]
+    L.w8a8_linear_workspace_bytes.restype = SZ
+    L.w8a8_status_str.argtypes = [I]
+    L.w8a8_status_str.restype = ctypes.c_char_p
+    for name in ("w8a8_quantize_rows", "w8a8_gemm", "w8a8_linear", "w8a8_linear_bf16",
+                 "compact_padded_rows", "w8a8_guard"):
+        getattr(L, name).restype = I
+    _lib = L
+    return L
+
+
+# ---------------------------------------------------------------------------
+# host-only helpers
+# ---------------------------------------------------------------------------
+
+def guard(N: int, K: int) -> bool:
+    """True if the INT8 GEMM serves (N, K); otherwise the linear runs in BF16."""
+    return bool(lib().w8a8_guard(int(N), int(K)))
+
+
+def linear_workspace_bytes(M: int, K: int) -> int:
+    return int(lib().w8a8_linear_workspace_bytes(int(M), int(K)))
+
+
+def status_str(status: int) -> str:
+    return lib().w8a8_status_str(int(status)).decode()
+
+
+# ---------------------------------------------------------------------------
+# marshalling
+# ---------------------------------------------------------------------------
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _p(t: Optional[torch.Tensor]):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _need(t, name, dtype, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
+def _check(fn, status):
+    if status != OK:
+        raise W8A8Error(fn, status)
+
+
+# ---------------------------------------------------------------------------
+# the four calls of the path (+ the BF16 fallback on its own)
+# ---------------------------------------------------------------------------
+
+def quantize_rows(x: torch.Tensor, q: Optional[torch.Tensor] = None,
+                  scale: Optional[torch.Tensor] = None, stream=None):
+    """Per-row symmetric INT8 quantisation: x bf16 [R, C] -> (q int8 [R, C], scale fp32 [R])."""
+    _need(x, "x", torch.bfloat16)
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D")
+    R, C = x.shape
+    q = q if q is not None else torch.empty((R, C), dtype=torch.int8, device=x.device)
+    scale = scale if scale is not None else torch.empty((R,), dtype=torch.float32, device=x.device)
+    _need(q, "q", torch.int8, (R, C))
+    _need(scale, "scale", torch.float32, (R,))
+    _check("w8a8_quantize_rows",
+           lib().w8a8_quantize_rows(_p(x), R, C, _p(q), _p(scale), _stream(stream)))
+    return q, scale
+
+
+def gemm(qa, sa, qw, sw, bias=None, act=ACT_NONE, out_kind=OUT_BF16, out=None, stream=None):
+    """INT8 GEMM, INT32 accumulation, epilogue once after accumulation.
+    qa int8 [M, K], sa fp32 [M], qw int8 [N, K], sw fp32 [N], bias bf16 [N] or None.
+    Returns bf16 [M, N] (OUT_BF16) or int32 [M, N] (OUT_I32)."""
+    _need(qa, "qa", torch.int8)
+    _need(qw, "qw", torch.int8)
+    M, K = qa.shape
+    N = qw.shape[0]
+    if qw.shape[1] != K:
+        raise ValueError("qa and qw disagree on K")
+    if out_kind == OUT_BF16:
+        _need(sa, "sa", torch.float32, (M,))
+        _need(sw, "sw", torch.float32, (N,))
+    if bias is not None:
+        _need(bias, "bias", torch.bfloat16, (N,))
+    odt = torch.int32 if out_kind == OUT_I32 else torch.bfloat16
+    out = out if out is not None else torch.empty((M, N), dtype=odt, device=qa.device)
+    _need(out, "out", odt, (M, N))
+    _check("w8a8_gemm", lib().w8a8_gemm(_p(qa), _p(sa), M, _p(qw), _p(sw), N, K, _p(bias),
+                                        int(act), int(out_kind), _p(out), _stream(stream)))
+    return out
+
+
+def linear_bf16(x, w, bias=None, act=ACT_NONE, y=None, stream=None):
+    """Native BF16 linear (the fallback path): y = bf16(x w^T + b), fp32 accumulation."""
+    _need(x, "x", torch.bfloat16)
+    _need(w, "w", torch.bfloat16)
+    M, K = x.shape
+    N = w.shape[0]
+    if w.shape[1] != K:
+        raise ValueError("x and w disagree on K")
+    if bias is not None:
+        _need(bias, "bias", torch.bfloat16, (N,))
+    y = y if y is not None else torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _need(y, "y", torch.bfloat16, (M, N))
+    _check("w8a8_linear_bf16", lib().w8a8_linear_bf16(_p(x), M, K, _p(w), N, _p(bias), int(act),
+                                                      _p(y), _stream(stream)))
+    return y
+
+
+def linear(x, N, qw=None, sw=None, w=None, bias=None, act=ACT_NONE, y=None, workspace=None,
+           stream=None):
+    """The guarded W8A8 linear.  Returns (y bf16 [M, N], path) with path PATH_INT8 or PATH_BF16.
+    The INT8 path needs (qw, sw) prepared with quantize_rows(W); the BF16 path needs w."""
+    _need(x, "x", torch.bfloat16)
+    M, K = x.shape
+    if qw is not None:
+        _need(qw, "qw", torch.int8, (N, K))
+    if sw is not None:
+        _need(sw, "sw", torch.float32, (N,))
+    if w is not None:
+        _need(w, "w", torch.bfloat16, (N, K))
+    if bias is not None:
+        _need(bias, "bias", torch.bfloat16, (N,))
+    y = y if y is not None else torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _need(y, "y", torch.bfloat16, (M, N))
+    ws_bytes = linear_workspace_bytes(M, K) if guard(N, K) else 0
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty((ws_bytes,), dtype=torch.uint8, device=x.device)
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8)
+    path = ctypes.c_int(-1)
+    _check("w8a8_linear", lib().w8a8_linear(
+        _p(x), M, K, N, _p(qw), _p(sw), _p(w), _p(bias), int(act), _p(y), _p(workspace),
+        workspace.numel() if workspace is not None else 0, ctypes.byref(path), _stream(stream)))
+    return y, path.value
+
+
+def compact_padded_rows(x, mask, out=None, src_row=None, count=None, stream=None):
+    """Padded-row compaction: x bf16 [B, L, D], mask uint8 [B, L] ->
+    (out bf16 [B*L, D] with the first count rows valid, src_row int32 [B*L], count int32 [1]).
+    count stays on the device; read it with count.item() (a sync) when needed."""
+    _need(x, "x", torch.bfloat16)
+    _need(mask, "mask", torch.uint8)
+    B, L, D = x.shape
+    if tuple(mask.shape) != (B, L):
+        raise ValueError("mask must be [B, L]")
+    dev = x.device
+    out = out if out is not None else torch.empty((B * L, D), dtype=torch.bfloat16, device=dev)
+    src_row = src_row if src_row is not None else torch.empty((B * L,), dtype=torch.int32, device=dev)
+    count = count if count is not None else torch.empty((1,), dtype=torch.int32, device=dev)
+    _need(out, "out", torch.bfloat16, (B * L, D))
+    _need(src_row, "src_row", torch.int32, (B * L,))
+    _need(count, "count", torch.int32, (1,))
+    _check("compact_padded_rows", lib().compact_padded_rows(
+        _p(x), _p(mask), B, L, D, _p(out), _p(src_row), _p(count), _stream(stream)))
+    return out, src_row, count
+
+
+@dataclass
+class W8A8Linear:
+    """A linear layer prepared once: the INT8 weight and its per-channel scales when
+    the guard admits the shape (static weight quantisation), else the bf16 weight."""
+    N: int
+    K: int
+    qw: Optional[torch.Tensor]
+    sw: Optional[torch.Tensor]
+    w: Optional[torch.Tensor]
+    bias: Optional[torch.Tensor]
+    act: int = ACT_NONE
+
+    @classmethod
+    def prepare(cls, w: torch.Tensor, bias: Optional[torch.Tensor] = None, act: int = ACT_NONE,
+                keep_bf16: bool = False):
+        N, K = w.shape
+        if guard(N, K):
+            qw, sw = quantize_rows(w)
+            return cls(N, K, qw, sw, w if keep_bf16 else None, bias, act)
+        return cls(N, K, None, None, w, bias, act)
+
+    @property
+    def path(self) -> int:
+        return PATH_INT8 if self.qw is not None else PATH_BF16
+
+    def __call__(self, x: torch.Tensor, y=None, workspace=None, stream=None):
+        return linear(x, self.N, self.qw, self.sw, self.w, self.bias, self.act, y, workspace,
+                      stream)[0]

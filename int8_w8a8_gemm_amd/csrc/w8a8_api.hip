@@ -1,0 +1,134 @@
+// C ABI of libw8a8: argument checks, the shape guard and routing.
+//
+// Every check runs on the host before any launch; a failed check returns
+// W8A8_EINVAL and enqueues nothing.  Work goes onto the caller's stream; the
+// library allocates, frees and synchronises nothing.
+#include "../../include/w8a8.h"
+#include "common.h"
+
+namespace {
+
+constexpr int64_t kMaxRows = (int64_t)1 << 31;  // grid limits of the row-wise kernels
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+bool act_ok(int act) { return act == W8A8_ACT_NONE || act == W8A8_ACT_GELU_TANH; }
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+int launched(int rc) { return rc == 0 ? W8A8_OK : W8A8_EHIP; }
+
+}  // namespace
+
+extern "C" {
+
+int w8a8_guard(int64_t N, int64_t K) {
+    // INT8 kernel requirements: whole 128-byte K steps (no K tail), N in
+    // multiples of 64, and K small enough that |acc| <= 127*127*K < 2^31.
+    return (K >= 128 && K <= W8A8_MAX_K && K % 128 == 0 && N >= 64 && N % 64 == 0) ? 1 : 0;
+}
+
+size_t w8a8_linear_workspace_bytes(int64_t M, int64_t K) {
+    if (M <= 0 || K <= 0) return 0;
+    const size_t codes = ((size_t)M * (size_t)K + 255) & ~(size_t)255;
+    return codes + (size_t)M * sizeof(float);
+}
+
+const char* w8a8_status_str(int status) {
+    switch (status) {
+        case W8A8_OK: return "ok";
+        case W8A8_EINVAL: return "invalid argument";
+        case W8A8_EUNSUPPORTED: return "shape not supported by the INT8 GEMM";
+        case W8A8_EHIP: return "HIP launch failed";
+        default: return "unknown status";
+    }
+}
+
+int w8a8_quantize_rows(const uint16_t* x, int64_t rows, int64_t cols, int8_t* q, float* scale,
+                       void* stream) {
+    if (rows < 0 || cols < 0 || rows >= kMaxRows) return W8A8_EINVAL;
+    if (rows == 0) return W8A8_OK;
+    if (!scale || !aligned(scale, 4)) return W8A8_EINVAL;
+    if (cols > 0 && (!x || !q || !aligned(x, 2))) return W8A8_EINVAL;
+    return launched(w8a8::launch_quantize_rows(x, rows, cols, q, scale, as_stream(stream)));
+}
+
+int w8a8_gemm(const int8_t* qa, const float* sa, int64_t M, const int8_t* qw, const float* sw,
+              int64_t N, int64_t K, const uint16_t* bias, int act, int out_kind, void* out,
+              void* stream) {
+    if (M < 0 || N < 0 || K < 0) return W8A8_EINVAL;
+    if (!act_ok(act)) return W8A8_EINVAL;
+    if (out_kind != W8A8_OUT_BF16 && out_kind != W8A8_OUT_I32) return W8A8_EINVAL;
+    if (out_kind == W8A8_OUT_I32 && act != W8A8_ACT_NONE) return W8A8_EINVAL;
+    if (!w8a8_guard(N, K)) return W8A8_EUNSUPPORTED;
+    if (M >= kMaxRows) return W8A8_EINVAL;
+    if (M == 0) return W8A8_OK;
+    if (!qa || !qw || !out) return W8A8_EINVAL;
+    if (!aligned(qa, 16) || !aligned(qw, 16) || !aligned(out, 16)) return W8A8_EINVAL;
+    if (out_kind == W8A8_OUT_BF16) {
+        if (!sa || !sw || !aligned(sa, 4) || !aligned(sw, 4)) return W8A8_EINVAL;
+        if (bias && !aligned(bias, 2)) return W8A8_EINVAL;
+    }
+    return launched(w8a8::launch_gemm_i8(qa, sa, M, qw, sw, N, K, bias, act, out_kind, out,
+                                         as_stream(stream)));
+}
+
+int w8a8_linear_bf16(const uint16_t* x, int64_t M, int64_t K, const uint16_t* w, int64_t N,
+                     const uint16_t* bias, int act, uint16_t* y, void* stream) {
+    if (M < 0 || N < 0 || K < 0 || M >= kMaxRows || N >= kMaxRows) return W8A8_EINVAL;
+    if (!act_ok(act)) return W8A8_EINVAL;
+    if (M == 0 || N == 0) return W8A8_OK;
+    if (!y || !aligned(y, 2)) return W8A8_EINVAL;
+    if (K > 0 && (!x || !w || !aligned(x, 2) || !aligned(w, 2))) return W8A8_EINVAL;
+    if (bias && !aligned(bias, 2)) return W8A8_EINVAL;
+    return launched(w8a8::launch_gemm_bf16(x, M, K, w, N, bias, act, y, as_stream(stream)));
+}
+
+int w8a8_linear(const uint16_t* x, int64_t M, int64_t K, int64_t N, const int8_t* qw,
+                const float* sw, const uint16_t* w, const uint16_t* bias, int act, uint16_t* y,
+                void* workspace, size_t workspace_bytes, int* path_taken, void* stream) {
+    if (M < 0 || N < 0 || K < 0 || M >= kMaxRows) return W8A8_EINVAL;
+    if (!act_ok(act)) return W8A8_EINVAL;
+    const bool int8 = w8a8_guard(N, K) != 0;
+    if (int8) {
+        if (!qw || !sw) return W8A8_EINVAL;
+        if (M > 0) {
+            if (!x || !y || !aligned(x, 2) || !aligned(y, 16)) return W8A8_EINVAL;
+            if (!aligned(qw, 16) || !aligned(sw, 4) || (bias && !aligned(bias, 2)))
+                return W8A8_EINVAL;
+            if (!workspace || !aligned(workspace, 256) ||
+                workspace_bytes < w8a8_linear_workspace_bytes(M, K))
+                return W8A8_EINVAL;
+        }
+        if (path_taken) *path_taken = W8A8_PATH_INT8;
+        if (M == 0) return W8A8_OK;
+        int8_t* qx = static_cast<int8_t*>(workspace);
+        float* sx = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                             (w8a8_linear_workspace_bytes(M, K) - M * sizeof(float)));
+        hipStream_t s = as_stream(stream);
+        if (w8a8::launch_quantize_rows(x, M, K, qx, sx, s) != 0) return W8A8_EHIP;
+        return launched(w8a8::launch_gemm_i8(qx, sx, M, qw, sw, N, K, bias, act, W8A8_OUT_BF16, y, s));
+    }
+    if (!w && M > 0 && N > 0 && K > 0) return W8A8_EINVAL;
+    if (M > 0 && N > 0) {
+        if (!y || !aligned(y, 2)) return W8A8_EINVAL;
+        if (K > 0 && (!x || !aligned(x, 2) || !aligned(w, 2))) return W8A8_EINVAL;
+        if (bias && !aligned(bias, 2)) return W8A8_EINVAL;
+        if (N >= kMaxRows) return W8A8_EINVAL;
+    }
+    if (path_taken) *path_taken = W8A8_PATH_BF16;
+    if (M == 0 || N == 0) return W8A8_OK;
+    return launched(w8a8::launch_gemm_bf16(x, M, K, w, N, bias, act, y, as_stream(stream)));
+}
+
+int compact_padded_rows(const uint16_t* x, const uint8_t* mask, int64_t B, int64_t L, int64_t D,
+                        uint16_t* out, int32_t* src_row, int32_t* count, void* stream) {
+    if (B < 0 || L < 0 || D < 0) return W8A8_EINVAL;
+    if (L > 0 && B > (kMaxRows - 1) / L) return W8A8_EINVAL;
+    if (!count || !aligned(count, 4)) return W8A8_EINVAL;
+    const int64_t R = B * L;
+    if (R > 0) {
+        if (!mask || !src_row || !aligned(src_row, 4)) return W8A8_EINVAL;
+        if (D > 0 && (!x || !out || !aligned(x, 2) || !aligned(out, 2))) return W8A8_EINVAL;
+    }
+    return launched(w8a8::launch_compact_rows(x, mask, R, D, out, src_row, count, as_stream(stream)));
+}
+
+}  // extern "C"

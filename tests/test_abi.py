@@ -1,0 +1,157 @@
+"""C-ABI checks that need no GPU: the library loads, exports what the header
+declares, and every argument check returns before anything is launched."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import int8_w8a8_gemm_amd as w8
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w8a8.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    return re.findall(r"W8A8_API\s+[\w\s\*]+?\b(\w+)\s*\(", src)
+
+
+def test_header_declares_the_four_calls_and_helpers():
+    names = set(_declared())
+    for n in ("w8a8_quantize_rows", "w8a8_gemm", "w8a8_linear", "compact_padded_rows",
+              "w8a8_linear_bf16", "w8a8_guard", "w8a8_linear_workspace_bytes", "w8a8_status_str"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = w8.lib()
+    for n in _declared():
+        assert hasattr(lib, n), n
+    assert set(_declared()) == set(w8.EXPORTS)
+
+
+def test_guard_truth_table():
+    for N in (64, 128, 2048, 4096, 16384):
+        for K in (128, 256, 2048, 4096, 16384, 131072):
+            assert w8.guard(N, K), (N, K)
+    for N, K in [(4100, 4096), (2048, 2050), (32, 4096), (0, 4096), (4096, 0), (4096, 64),
+                 (4096, 131072 + 128), (100, 256), (128, 200), (-64, 256), (64, -128)]:
+        assert not w8.guard(N, K), (N, K)
+
+
+def test_workspace_bytes():
+    assert w8.linear_workspace_bytes(0, 4096) == 0
+    assert w8.linear_workspace_bytes(4, 0) == 0
+    assert w8.linear_workspace_bytes(1, 128) == 256 + 4
+    assert w8.linear_workspace_bytes(3, 100) == 512 + 12
+    M, K = 24576, 4096
+    assert w8.linear_workspace_bytes(M, K) == M * K + 4 * M
+
+
+def test_status_strings():
+    assert w8.status_str(0) == "ok"
+    assert "invalid" in w8.status_str(-1)
+    assert "not supported" in w8.status_str(-2)
+    assert "HIP" in w8.status_str(-3)
+    assert w8.status_str(123) == "unknown status"
+
+
+# Fake, never-dereferenced device addresses: every call below must be rejected
+# (or be a no-op) on the host before any HIP call is made.
+A16 = ctypes.c_void_p(0x10000)
+A16b = ctypes.c_void_p(0x20000)
+A16c = ctypes.c_void_p(0x30000)
+MIS = ctypes.c_void_p(0x10001)
+NULL = None
+
+
+def test_quantize_rows_rejects_bad_arguments():
+    L = w8.lib()
+    assert L.w8a8_quantize_rows(A16, -1, 8, A16b, A16c, NULL) == w8.EINVAL
+    assert L.w8a8_quantize_rows(A16, 4, -8, A16b, A16c, NULL) == w8.EINVAL
+    assert L.w8a8_quantize_rows(NULL, 4, 8, A16b, A16c, NULL) == w8.EINVAL
+    assert L.w8a8_quantize_rows(A16, 4, 8, NULL, A16c, NULL) == w8.EINVAL
+    assert L.w8a8_quantize_rows(A16, 4, 8, A16b, NULL, NULL) == w8.EINVAL
+    assert L.w8a8_quantize_rows(MIS, 4, 8, A16b, A16c, NULL) == w8.EINVAL
+    assert L.w8a8_quantize_rows(A16, 4, 8, A16b, MIS, NULL) == w8.EINVAL
+    assert L.w8a8_quantize_rows(A16, 1 << 31, 8, A16b, A16c, NULL) == w8.EINVAL
+    assert L.w8a8_quantize_rows(NULL, 0, 8, NULL, NULL, NULL) == w8.OK  # empty: no-op
+
+
+def test_gemm_rejects_bad_arguments_and_unsupported_shapes():
+    L = w8.lib()
+    g = lambda qa, sa, M, qw, sw, N, K, b, act, kind, out: L.w8a8_gemm(
+        qa, sa, M, qw, sw, N, K, b, act, kind, out, NULL)
+    assert g(A16, A16, -1, A16, A16, 64, 128, NULL, 0, 0, A16) == w8.EINVAL
+    assert g(A16, A16, 4, A16, A16, 64, 128, NULL, 2, 0, A16) == w8.EINVAL   # bad act
+    assert g(A16, A16, 4, A16, A16, 64, 128, NULL, 0, 5, A16) == w8.EINVAL   # bad out kind
+    assert g(A16, A16, 4, A16, A16, 64, 128, NULL, 1, 1, A16) == w8.EINVAL   # GELU on int32
+    assert g(A16, A16, 4, A16, A16, 4100, 4096, NULL, 0, 0, A16) == w8.EUNSUPPORTED
+    assert g(A16, A16, 4, A16, A16, 2048, 2050, NULL, 0, 0, A16) == w8.EUNSUPPORTED
+    assert g(A16, A16, 4, A16, A16, 64, 131072 + 128, NULL, 0, 0, A16) == w8.EUNSUPPORTED
+    assert g(NULL, A16, 4, A16, A16, 64, 128, NULL, 0, 0, A16) == w8.EINVAL
+    assert g(A16, A16, 4, NULL, A16, 64, 128, NULL, 0, 0, A16) == w8.EINVAL
+    assert g(A16, A16, 4, A16, A16, 64, 128, NULL, 0, 0, NULL) == w8.EINVAL
+    assert g(A16, NULL, 4, A16, A16, 64, 128, NULL, 0, 0, A16) == w8.EINVAL  # bf16 needs scales
+    assert g(MIS, A16, 4, A16, A16, 64, 128, NULL, 0, 0, A16) == w8.EINVAL
+    assert g(A16, A16, 4, MIS, A16, 64, 128, NULL, 0, 0, A16) == w8.EINVAL
+    assert g(A16, A16, 4, A16, A16, 64, 128, NULL, 0, 0, MIS) == w8.EINVAL
+    assert g(A16, A16, 4, A16, A16, 64, 128, MIS, 0, 0, A16) == w8.EINVAL   # odd bias address
+    assert g(NULL, NULL, 0, NULL, NULL, 64, 128, NULL, 0, 0, NULL) == w8.OK  # M == 0
+
+
+def test_linear_rejects_bad_arguments():
+    L = w8.lib()
+    path = ctypes.c_int(-7)
+    ws = w8.linear_workspace_bytes(4, 128)
+
+    def lin(x, M, K, N, qw, sw, w, b, act, y, wsp, wsb):
+        return L.w8a8_linear(x, M, K, N, qw, sw, w, b, act, y, wsp, wsb, ctypes.byref(path), NULL)
+
+    assert lin(A16, -1, 128, 64, A16, A16, NULL, NULL, 0, A16, A16, ws) == w8.EINVAL
+    assert lin(A16, 4, 128, 64, A16, A16, NULL, NULL, 3, A16, A16, ws) == w8.EINVAL
+    # INT8 path: needs qw, sw, a big enough 256-byte-aligned workspace
+    assert lin(A16, 4, 128, 64, NULL, A16, A16, NULL, 0, A16, A16, ws) == w8.EINVAL
+    assert lin(A16, 4, 128, 64, A16, NULL, A16, NULL, 0, A16, A16, ws) == w8.EINVAL
+    assert lin(A16, 4, 128, 64, A16, A16, NULL, NULL, 0, A16, NULL, ws) == w8.EINVAL
+    assert lin(A16, 4, 128, 64, A16, A16, NULL, NULL, 0, A16, A16, ws - 1) == w8.EINVAL
+    assert lin(A16, 4, 128, 64, A16, A16, NULL, NULL, 0, A16, ctypes.c_void_p(0x10010), ws) == w8.EINVAL
+    assert lin(A16, 4, 128, 64, A16, A16, NULL, NULL, 0, MIS, A16, ws) == w8.EINVAL
+    # BF16 path: needs w
+    assert lin(A16, 4, 130, 64, NULL, NULL, NULL, NULL, 0, A16, NULL, 0) == w8.EINVAL
+    assert lin(A16, 4, 128, 68, A16, A16, NULL, NULL, 0, A16, NULL, 0) == w8.EINVAL
+    # empty work reports the path and launches nothing
+    path.value = -7
+    assert lin(NULL, 0, 128, 64, A16, A16, NULL, NULL, 0, NULL, NULL, 0) == w8.OK
+    assert path.value == w8.PATH_INT8
+    path.value = -7
+    assert lin(NULL, 0, 130, 64, NULL, NULL, NULL, NULL, 0, NULL, NULL, 0) == w8.OK
+    assert path.value == w8.PATH_BF16
+
+
+def test_linear_bf16_and_compaction_reject_bad_arguments():
+    L = w8.lib()
+    assert L.w8a8_linear_bf16(A16, -2, 8, A16, 8, NULL, 0, A16, NULL) == w8.EINVAL
+    assert L.w8a8_linear_bf16(A16, 2, 8, A16, 8, NULL, 9, A16, NULL) == w8.EINVAL
+    assert L.w8a8_linear_bf16(NULL, 2, 8, A16, 8, NULL, 0, A16, NULL) == w8.EINVAL
+    assert L.w8a8_linear_bf16(A16, 2, 8, A16, 8, NULL, 0, NULL, NULL) == w8.EINVAL
+    assert L.w8a8_linear_bf16(MIS, 2, 8, A16, 8, NULL, 0, A16, NULL) == w8.EINVAL
+    assert L.w8a8_linear_bf16(NULL, 0, 8, NULL, 8, NULL, 0, NULL, NULL) == w8.OK
+    c = lambda x, m, B, Lq, D, o, s, n: L.compact_padded_rows(x, m, B, Lq, D, o, s, n, NULL)
+    assert c(A16, A16, -1, 4, 8, A16, A16, A16) == w8.EINVAL
+    assert c(A16, A16, 2, 4, 8, A16, A16, NULL) == w8.EINVAL          # count is required
+    assert c(A16, NULL, 2, 4, 8, A16, A16, A16) == w8.EINVAL
+    assert c(A16, A16, 2, 4, 8, A16, NULL, A16) == w8.EINVAL
+    assert c(A16, A16, 2, 4, 8, NULL, A16, A16) == w8.EINVAL
+    assert c(A16, A16, 2, 4, 8, A16, A16, MIS) == w8.EINVAL
+    assert c(A16, A16, 1 << 20, 1 << 12, 8, A16, A16, A16) == w8.EINVAL  # B*L >= 2^31
+
+
+def test_python_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros((4, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        w8.quantize_rows(x)
