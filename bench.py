@@ -1,0 +1,329 @@
+#!/usr/bin/env python3
+"""Benchmark of the guarded W8A8 linear on one MI355X.
+
+Workload (one step): the video FFN pair, all through the INT8 path —
+    X [24576 x 4096] bf16 --quantise--> qX, sX
+    H = GELU-tanh(W8A8(qX, W1 [16384 x 4096]) + b1)       bf16 [24576 x 16384]
+    H --quantise--> qH, sH
+    Y = W8A8(qH, W2 [4096 x 16384]) + b2                   bf16 [24576 x 4096]
+The weights are quantised once before timing (static, per output channel).
+Inputs are seeded synthetic tensors of the workload's shapes and value
+distributions, resident in HBM before the timed region.
+
+Prints ONE JSON line on stdout.  `value` is whole-step throughput in INT8
+tera-ops per second: 2 * (2*M*N*K) ops of the two GEMMs divided by the step
+time (quantisation and GELU included in the time).  `roofline` describes the
+dominant kernel (the INT8 GEMM), timed with HIP events around its launches on
+the stream it runs on.  `cpu_baseline` is the CPU oracle on a bounded row
+sample of the same step.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_INT8_TOPS = 5000.0   # MI355X dense INT8 MFMA, 5.0 POP/s
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense BF16 MFMA
+PEAK_HBM_GBS = 8000.0     # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_i8_video_ffn.json")
+GEMM_SOURCE = os.path.join(ROOT, "int8_w8a8_gemm_amd", "csrc", "gemm_i8.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--M", type=int, default=24576)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-rows", type=int, default=0,
+                   help="rows of the oracle sample (0: sized to ~15 s)")
+    p.add_argument("--no-extra", action="store_true", help="skip the secondary kernel benches")
+    return p.parse_args()
+
+
+def source_hash(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def stored_traffic():
+    """HBM bytes per GEMM launch from the committed rocprofv3 counter runs, if they
+    were taken on the current kernel source."""
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256_16") != source_hash(GEMM_SOURCE):
+        return None
+    return t
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: this path has no multi-GPU mode "
+              "(it would shard rows or output channels with no exchange); use --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import int8_w8a8_gemm_amd as w8
+    import workloads as wl
+
+    assert torch.cuda.is_available(), "bench needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w8.lib()
+
+    M, D, F = args.M, 4096, 16384
+    log(f"generating inputs M={M} D={D} F={F}")
+    ffn = wl.video_ffn(M=M)
+
+    def d(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    x = d(ffn.x)
+    w1, b1, w2, b2 = d(ffn.w1), d(ffn.b1), d(ffn.w2), d(ffn.b2)
+    qw1, sw1 = w8.quantize_rows(w1)   # static weight quantisation, untimed
+    qw2, sw2 = w8.quantize_rows(w2)
+    qx = torch.empty((M, D), dtype=torch.int8, device=dev)
+    sx = torch.empty((M,), dtype=torch.float32, device=dev)
+    h = torch.empty((M, F), dtype=torch.bfloat16, device=dev)
+    qh = torch.empty((M, F), dtype=torch.int8, device=dev)
+    sh = torch.empty((M,), dtype=torch.float32, device=dev)
+    y = torch.empty((M, D), dtype=torch.bfloat16, device=dev)
+    assert w8.guard(F, D) and w8.guard(D, F)
+    stream = torch.cuda.current_stream()
+
+    nev = 5
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)]
+              for _ in range(args.steps)]
+
+    def step(ev=None):
+        # the same two C-ABI calls w8a8_linear makes (quantise into a workspace,
+        # then the GEMM), issued separately so each kernel can be timed
+        if ev: ev[0].record(stream)
+        w8.quantize_rows(x, qx, sx)
+        if ev: ev[1].record(stream)
+        w8.gemm(qx, sx, qw1, sw1, b1, act=w8.ACT_GELU_TANH, out=h)
+        if ev: ev[2].record(stream)
+        w8.quantize_rows(h, qh, sh)
+        if ev: ev[3].record(stream)
+        w8.gemm(qh, sh, qw2, sw2, b2, act=w8.ACT_NONE, out=y)
+        if ev: ev[4].record(stream)
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    ops_gemm = 2.0 * M * F * D  # each of the two GEMMs
+    value = 2 * ops_gemm / (ms_per_step * 1e-3) / 1e12
+
+    def avg(a, b):
+        return float(np.mean([events[i][a].elapsed_time(events[i][b]) for i in range(args.steps)]))
+
+    t_qx, t_up, t_qh, t_down = avg(0, 1), avg(1, 2), avg(2, 3), avg(3, 4)
+    tops_up = ops_gemm / (t_up * 1e-3) / 1e12
+    tops_down = ops_gemm / (t_down * 1e-3) / 1e12
+    bytes_qx = 3.0 * M * D + 4.0 * M
+    bytes_qh = 3.0 * M * F + 4.0 * M
+    log(f"step {ms_per_step:.3f} ms: quant X {t_qx*1e3:.1f} us, GEMM up {t_up:.3f} ms "
+        f"({tops_up:.0f} TOPS), quant H {t_qh*1e3:.1f} us, GEMM down {t_down:.3f} ms "
+        f"({tops_down:.0f} TOPS)")
+
+    # dominant kernel: the longer of the two GEMM instantiations
+    dom_name, dom_t = ("gemm_i8 up (+GELU epilogue)", t_up) if t_up >= t_down else \
+        ("gemm_i8 down", t_down)
+    achieved = ops_gemm / (dom_t * 1e-3) / 1e12
+    traffic = None
+    st = stored_traffic()
+    if st is not None:
+        key = "up" if t_up >= t_down else "down"
+        traffic = st.get(key, {}).get("hbm_bytes_per_launch")
+    roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_INT8_TOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_INT8_TOPS, 4),
+                "traffic": traffic, "kernel": dom_name,
+                "algorithmic_per_launch": f"2*M*N*K = {ops_gemm:.4e} int8 ops"}
+
+    result = {
+        "metric": "INT8 W8A8 GEMM TOPS + % of MI355X INT8 MFMA peak (video FFN shape)",
+        "value": round(value, 1),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": "video FFN pair, guarded W8A8 linear x2: "
+                               f"X[{M}x{D}] . W1[{F}x{D}]^T +b1, GELU-tanh, . W2[{D}x{F}]^T +b2",
+                   "M": M, "D": D, "F": F, "act_up": "gelu_tanh", "parallelism": "single GPU"},
+        "roofline": roofline,
+        "kernels": {
+            "quantize_x": {"us": round(t_qx * 1e3, 2),
+                           "GB/s": round(bytes_qx / (t_qx * 1e-3) / 1e9, 1),
+                           "frac_hbm": round(bytes_qx / (t_qx * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+            "gemm_up_gelu": {"ms": round(t_up, 4), "TOPS": round(tops_up, 1),
+                             "frac_peak": round(tops_up / PEAK_INT8_TOPS, 4)},
+            "quantize_h": {"us": round(t_qh * 1e3, 2),
+                           "GB/s": round(bytes_qh / (t_qh * 1e-3) / 1e9, 1),
+                           "frac_hbm": round(bytes_qh / (t_qh * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+            "gemm_down": {"ms": round(t_down, 4), "TOPS": round(tops_down, 1),
+                          "frac_peak": round(tops_down / PEAK_INT8_TOPS, 4)},
+        },
+    }
+
+    if not args.no_extra:
+        result["extra"] = extra_benches(w8, wl, np, torch, dev, d, log)
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(ffn, args.cpu_rows, np, log)
+
+    print(json.dumps(result), flush=True)
+
+
+def _time(fn, iters, torch):
+    """Average ms per call over `iters` calls, timed with events on the current stream."""
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    fn()
+    torch.cuda.synchronize()
+    s.record()
+    for _ in range(iters):
+        fn()
+    e.record()
+    e.synchronize()
+    return s.elapsed_time(e) / iters
+
+
+def extra_benches(w8, wl, np, torch, dev, d, log):
+    """Secondary kernels: the quantiser on rotating buffers (so the 256 MB
+    Infinity Cache cannot hold the input), compaction, and the BF16 fallback."""
+    out = {}
+    # quantise X [24576 x 4096] rotating over 4 distinct inputs (4 x 201 MB)
+    M, K = 24576, 4096
+    gen = torch.Generator(device=dev).manual_seed(0)
+    xs = [torch.randn((M, K), device=dev, generator=gen).to(torch.bfloat16) for _ in range(4)]
+    qs = [torch.empty((M, K), dtype=torch.int8, device=dev) for _ in range(4)]
+    ss = [torch.empty((M,), dtype=torch.float32, device=dev) for _ in range(4)]
+    it = [0]
+
+    def q():
+        i = it[0] % 4
+        it[0] += 1
+        w8.quantize_rows(xs[i], qs[i], ss[i])
+
+    t = _time(q, 40, torch)
+    gbs = (3.0 * M * K + 4.0 * M) / (t * 1e-3) / 1e9
+    out["quantize_24576x4096_rotating"] = {"us": round(t * 1e3, 2), "GB/s": round(gbs, 1),
+                                           "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+    del xs, qs, ss
+    # compaction of the text rows [8 x 512 x 4096]
+    g = wl.guarded_mixed()
+    B, L, Dm = g.x.shape
+    xd = d(g.x.reshape(B * L, Dm)).view(B, L, Dm)
+    md = torch.from_numpy(g.mask).to(dev)
+    buf = torch.empty((B * L, Dm), dtype=torch.bfloat16, device=dev)
+    src = torch.empty((B * L,), dtype=torch.int32, device=dev)
+    cnt = torch.empty((1,), dtype=torch.int32, device=dev)
+    t = _time(lambda: w8.compact_padded_rows(xd, md, buf, src, cnt), 50, torch)
+    mc = int(cnt.item())
+    nbytes = 4.0 * mc * Dm + B * L + 4.0 * mc + 4
+    out["compact_8x512x4096"] = {"us": round(t * 1e3, 2), "rows_kept": mc,
+                                 "GB/s": round(nbytes / (t * 1e-3) / 1e9, 1),
+                                 "frac_hbm": round(nbytes / (t * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    # conforming text projection on the compacted rows, and the two fallbacks
+    xc = buf[:mc]
+    lw = w8.W8A8Linear.prepare(d(g.w), d(g.b))
+    yc = torch.empty((mc, 4096), dtype=torch.bfloat16, device=dev)
+    t = _time(lambda: lw(xc, y=yc), 20, torch)
+    out["linear_int8_text_Mc_x4096x4096"] = {"us": round(t * 1e3, 2),
+                                             "TOPS": round(2.0 * mc * 4096 * 4096 / (t * 1e-3) / 1e12, 1)}
+    wa = d(g.w_a)
+    ba = d(g.b_a)
+    ya = torch.empty((mc, 4100), dtype=torch.bfloat16, device=dev)
+    t = _time(lambda: w8.linear_bf16(xc, wa, ba, y=ya), 10, torch)
+    out["fallback_bf16_N4100"] = {"us": round(t * 1e3, 2),
+                                  "TFLOP/s": round(2.0 * mc * 4100 * 4096 / (t * 1e-3) / 1e12, 1)}
+    xb, wb, bb = d(g.x_b), d(g.w_b), d(g.b_b)
+    yb = torch.empty((2048, 2048), dtype=torch.bfloat16, device=dev)
+    t = _time(lambda: w8.linear_bf16(xb, wb, bb, y=yb), 10, torch)
+    out["fallback_bf16_K2050"] = {"us": round(t * 1e3, 2),
+                                  "TFLOP/s": round(2.0 * 2048 * 2048 * 2050 / (t * 1e-3) / 1e12, 1)}
+    # audio 2048^3 and attention projection 24576x4096x4096 GEMM alone
+    for name, (Mg, Ng, Kg) in {"gemm_audio_2048^3": (2048, 2048, 2048),
+                               "gemm_attn_proj_24576x4096x4096": (24576, 4096, 4096)}.items():
+        qa = torch.randint(-127, 128, (Mg, Kg), dtype=torch.int8, device=dev)
+        qb = torch.randint(-127, 128, (Ng, Kg), dtype=torch.int8, device=dev)
+        sa = torch.rand((Mg,), device=dev) * 0.01
+        sb = torch.rand((Ng,), device=dev) * 0.01
+        bias = torch.zeros((Ng,), dtype=torch.bfloat16, device=dev)
+        yo = torch.empty((Mg, Ng), dtype=torch.bfloat16, device=dev)
+        t = _time(lambda: w8.gemm(qa, sa, qb, sb, bias, out=yo), 20, torch)
+        tops = 2.0 * Mg * Ng * Kg / (t * 1e-3) / 1e12
+        out[name] = {"us": round(t * 1e3, 2), "TOPS": round(tops, 1),
+                     "frac_peak": round(tops / PEAK_INT8_TOPS, 4)}
+    log("extra: " + json.dumps(out))
+    return out
+
+
+def cpu_baseline(ffn, rows, np, log):
+    """The CPU oracle, as it stands, on a bounded row sample of the same step
+    (quantise X rows, INT32 product with W1, epilogue + GELU, quantise H rows,
+    INT32 product with W2, epilogue), weights quantised beforehand."""
+    import oracle
+
+    threads = oracle.default_threads()
+    qw1, sw1 = oracle.quantize_rows(ffn.w1, nthreads=threads)
+    qw2, sw2 = oracle.quantize_rows(ffn.w2, nthreads=threads)
+
+    def run(n):
+        xs = np.ascontiguousarray(ffn.x[:n])
+        t0 = time.perf_counter()
+        qx, sx = oracle.quantize_rows(xs, nthreads=threads)
+        hh = oracle.epilogue(oracle.gemm_i32(qx, qw1, nthreads=threads), sx, sw1, ffn.b1,
+                             act=oracle.ACT_GELU_TANH, nthreads=threads)
+        qh, sh = oracle.quantize_rows(hh, nthreads=threads)
+        oracle.epilogue(oracle.gemm_i32(qh, qw2, nthreads=threads), sh, sw2, ffn.b2,
+                        nthreads=threads)
+        return time.perf_counter() - t0
+
+    if rows <= 0:
+        probe = max(threads, 16)
+        tp = run(probe)
+        rows = int(min(ffn.x.shape[0], max(probe, probe * 15.0 / max(tp, 1e-3))))
+        rows = max(threads, rows - rows % threads)
+    log(f"cpu baseline: oracle on {rows} rows with {threads} threads")
+    t = run(rows)
+    ops = 2 * (2.0 * rows * ffn.w1.shape[0] * ffn.w1.shape[1])
+    return {"value": round(ops / t / 1e12, 6), "unit": "TOPS", "cores": threads, "kind": "oracle",
+            "seconds": round(t, 2),
+            "sample": f"first {rows} of {ffn.x.shape[0]} rows of the video FFN pair step "
+                      f"(quantise, INT32 GEMM, epilogue+GELU, quantise, INT32 GEMM, epilogue)"}
+
+
+if __name__ == "__main__":
+    main()

@@ -35,17 +35,12 @@ __device__ __forceinline__ float gelu_tanh(float z) {
     return __fdiv_rn(z, __fadd_rn(1.0f, e));
 }
 
-// The epilogue applied once per output after the whole INT32 accumulation.
-// ACT: 0 none, 1 GELU-tanh on the bf16-rounded value.
-template <int ACT>
-__device__ __forceinline__ uint32_t epilogue_bf16(int32_t acc, float sa, float sw, float b,
-                                                  bool has_bias) {
-    float t = (float)acc;  // v_cvt_f32_i32: round to nearest even
-    float u = __fmul_rn(sa, sw);
-    float v = has_bias ? __builtin_fmaf(t, u, b) : __fmul_rn(t, u);
-    uint32_t h = float_to_bf16_bits(v);
-    if (ACT == 1) h = float_to_bf16_bits(gelu_tanh(bf16_bits_to_float(h)));
-    return h;
+// Two binary32 values -> two bf16 (round to nearest even) packed low/high in a
+// dword; gfx950 does this in one v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    bf16x2 v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
 }
 
 }  // namespace w8a8

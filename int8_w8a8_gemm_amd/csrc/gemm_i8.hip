@@ -16,111 +16,421 @@ namespace w8a8 {
 namespace {
 
 // ---------------------------------------------------------------------------
-// Simple tiled kernel: 128x128 macro tile, BK = 64, 4 waves each 64x64, single
-// LDS buffer.  v_mfma_i32_16x16x64_i8; used for every shape the guard admits.
+// Tiled MFMA kernel.  A workgroup of 4 waves owns a BM x 256 output tile; the
+// waves form a 2 x 2 grid, each owning (BM/2) x 128 outputs, i.e. MI x 4 tiles
+// of v_mfma_i32_32x32x32_i8 (MI = BM/64) held as int32 accumulators in AGPRs.
+// With BM = 128 each wave needs 128 accumulators, so two workgroups share a
+// CU (two waves per SIMD from different workgroups): one's barrier waits,
+// load issue and epilogue overlap the other's MFMAs.  K is staged BK bytes at
+// a time through an NST-deep ring of LDS buffers.
+//
+// * Operands go global -> LDS directly (buffer_load_dwordx4 ... lds): a wave
+//   instruction moves 1 KB (64 lanes x 16 bytes); lane l lands at LDS offset
+//   16*l of that KB and is given the global chunk that belongs there under the
+//   swizzle below.  Lane offsets are fixed per tile and the stage's K position
+//   is a scalar offset, so the loads of a stage need no address arithmetic.
+// * An LDS row r (BK bytes = BK/16 chunks) stores logical K-chunk c at physical
+//   chunk c ^ f(r).  A fragment read has lane l on row l % 32 at logical chunk
+//   l / 32; with f(r) = (r ^ (r >> 3)) & 7 for 128-byte rows and (r >> 2) & 3
+//   for 64-byte rows these reads are free of LDS bank conflicts on gfx950
+//   (measured with the SQ_LDS_BANK_CONFLICT counter; LDS serves 256 bytes per
+//   clock, so a conflict-free ds_read_b128 takes 4 clocks).
+// * MFMA roles are transposed (A-operand = weight rows, B-operand = activation
+//   rows) so the accumulator holds D[n][m]: each lane ends with 4 consecutive
+//   output columns of one row and writes them as one 8-byte store.
+// * One barrier per K stage; the MFMAs of the stage's last K sub-step are
+//   issued after it, interleaved with the next stage's first fragment reads and
+//   the loads that refill the buffer just released.  The order of MFMAs, LDS
+//   reads and loads within a sub-step is fixed with sched_barrier.
+// * The tile's row scales, column scales and bias are staged into LDS during
+//   the prologue, so the epilogue reads them with LDS latency only.
+// * Tile order is XCD-aware: workgroup b runs on XCD b % 8, so each XCD is
+//   given a contiguous range of tiles, walked in groups of 1024 rows.
 // ---------------------------------------------------------------------------
-constexpr int S_BM = 128, S_BN = 128, S_BK = 64, S_PITCH = S_BK + 16;
+constexpr int L_BN = 256;
+constexpr int NUM_XCD = 8;
+constexpr int GROUP_ROWS = 1024;
 
-template <int OUT_I32, int ACT>
-__global__ __launch_bounds__(256) void gemm_i8_simple(const int8_t* __restrict__ qa,
-                                                      const float* __restrict__ sa, int64_t M,
-                                                      const int8_t* __restrict__ qw,
-                                                      const float* __restrict__ sw, int64_t N,
-                                                      int64_t K, const uint16_t* __restrict__ bias,
-                                                      void* __restrict__ out) {
-    __shared__ __attribute__((aligned(16))) int8_t As[S_BM * S_PITCH];
-    __shared__ __attribute__((aligned(16))) int8_t Bs[S_BN * S_PITCH];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
-    const int64_t ntn = (N + S_BN - 1) / S_BN;
-    const int64_t m0 = ((int64_t)blockIdx.x / ntn) * S_BM, n0 = ((int64_t)blockIdx.x % ntn) * S_BN;
+typedef __attribute__((address_space(3))) void lds_void;
 
-    v4i acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = (v4i){0, 0, 0, 0};
+template <int BM, int BK>
+struct Geo {
+    static constexpr int MI = BM / 64;                 // 32-row MFMA tiles per wave along M
+    static constexpr int NI = 4;                       // 32-col MFMA tiles per wave along N
+    static constexpr int NQ = MI + NI;                 // fragments per sub-step
+    static constexpr int NMFMA = MI * NI;              // MFMAs per sub-step
+    static constexpr int CPR = BK / 16;                // 16-byte chunks per LDS row
+    static constexpr int RPI = 64 / CPR;               // rows one 1-KB wave instruction fills
+    static constexpr int STAGE = (BM + L_BN) * BK;     // bytes per stage (A tile then B tile)
+    static constexpr int SUB = BK / 32;                // 32-deep MFMA sub-steps per stage
+    static constexpr int LPW_A = BM / 4 / RPI;         // A load instructions per wave per stage
+    static constexpr int LPW_B = L_BN / 4 / RPI;       // B load instructions per wave per stage
+    static constexpr int NLOAD = LPW_A + LPW_B;
+    static constexpr int WAVES_PER_SIMD = BM == 128 ? 2 : 1;
+};
 
-    // each thread moves 2 chunks of 16 bytes of A and of B per K step
-    int lrow[2], lcol[2];
-    const int8_t* ga[2];
-    const int8_t* gb[2];
+template <int BK>
+__device__ __forceinline__ int swz(int r, int c) {
+    if (BK == 128) return c ^ ((r ^ (r >> 3)) & 7);
+    return c ^ ((r >> 2) & 3);
+}
+
+// s_waitcnt immediate for gfx9: vmcnt(v) lgkmcnt(0), expcnt left free.
+template <int V>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+    static_assert(V >= 0 && V < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((V & 15) | ((V >> 4) << 14) | (7 << 4));
+}
+
+// The buffer-resource type exists only when compiling for the GPU; the host
+// pass sees a placeholder of the same size (kernels never run on the host).
+#if defined(__HIP_DEVICE_COMPILE__)
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+#else
+struct rsrc_t { int w[4]; };
+#endif
+
+#if defined(__HIP_DEVICE_COMPILE__)
+constexpr int kRawBufferWord3 = 0x00020000;  // untyped 32-bit buffer access
+#endif
+
+// Per-tile addressing.  Each operand is read through a buffer resource based
+// at the tile's first row and sized to the rows that exist, so rows past M
+// (or N) read as zero.  Every lane keeps fixed byte offsets for its loads; the
+// K position of a stage goes in the scalar offset, so issuing a stage's loads
+// writes no vector registers.
+template <int BM, int BK>
+struct Ctx {
+    rsrc_t rsrc[2];  // 0: activation panel, 1: weight panel
+    uint32_t voff_a[Geo<BM, BK>::LPW_A];
+    uint32_t voff_b[Geo<BM, BK>::LPW_B];
+    int wave, lane, wm, wn;
+};
+
+template <int BM, int BK>
+__device__ __forceinline__ void make_ctx(Ctx<BM, BK>& c, const int8_t* qa, const int8_t* qw,
+                                         int64_t M, int64_t N, int64_t K, int64_t m0, int64_t n0,
+                                         int wave, int lane) {
+    typedef Geo<BM, BK> G;
+#if defined(__HIP_DEVICE_COMPILE__)
+    const int64_t rows_a = (M - m0) < BM ? (M - m0) : BM;
+    const int64_t rows_w = (N - n0) < L_BN ? (N - n0) : L_BN;
+    c.rsrc[0] = __builtin_amdgcn_make_buffer_rsrc((void*)(qa + m0 * K), (short)0,
+                                                  (int)(rows_a * K), kRawBufferWord3);
+    c.rsrc[1] = __builtin_amdgcn_make_buffer_rsrc((void*)(qw + n0 * K), (short)0,
+                                                  (int)(rows_w * K), kRawBufferWord3);
+#endif
+    const int rsub = lane / G::CPR, pc = lane % G::CPR;
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-        const int chunk = tid + c * 256;
-        lrow[c] = chunk >> 2;
-        lcol[c] = (chunk & 3) * 16;
-        int64_t gm = m0 + lrow[c];
-        if (gm > M - 1) gm = M - 1;
-        int64_t gn = n0 + lrow[c];
-        if (gn > N - 1) gn = N - 1;
-        ga[c] = qa + gm * K + lcol[c];
-        gb[c] = qw + gn * K + lcol[c];
+    for (int i = 0; i < G::LPW_A; ++i) {
+        const int r = wave * (BM / 4) + i * G::RPI + rsub;  // tile-local A row
+        c.voff_a[i] = (uint32_t)r * (uint32_t)K + 16u * (uint32_t)swz<BK>(r, pc);
     }
-
-    for (int64_t k0 = 0; k0 < K; k0 += S_BK) {
-        v4i ra[2], rb[2];
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            ra[c] = *reinterpret_cast<const v4i*>(ga[c] + k0);
-            rb[c] = *reinterpret_cast<const v4i*>(gb[c] + k0);
-        }
-        __syncthreads();
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            *reinterpret_cast<v4i*>(As + lrow[c] * S_PITCH + lcol[c]) = ra[c];
-            *reinterpret_cast<v4i*>(Bs + lrow[c] * S_PITCH + lcol[c]) = rb[c];
-        }
-        __syncthreads();
-        v4i fa[4], fb[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            fa[i] = *reinterpret_cast<const v4i*>(As + (wm * 64 + i * 16 + (lane & 15)) * S_PITCH +
-                                                  (lane >> 4) * 16);
-            fb[i] = *reinterpret_cast<const v4i*>(Bs + (wn * 64 + i * 16 + (lane & 15)) * S_PITCH +
-                                                  (lane >> 4) * 16);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    for (int i = 0; i < G::LPW_B; ++i) {
+        const int r = wave * (L_BN / 4) + i * G::RPI + rsub;  // tile-local B row
+        c.voff_b[i] = (uint32_t)r * (uint32_t)K + 16u * (uint32_t)swz<BK>(r, pc);
     }
+    c.wave = wave;
+    c.lane = lane;
+    c.wm = wave >> 1;
+    c.wn = wave & 1;
+}
 
-    // C layout of a 16x16 MFMA tile: lane l holds column (l & 15), rows 4*(l >> 4) + r.
+// Load j (0 .. NLOAD-1) of one wave's share of a K stage: j < LPW_A loads A
+// rows, the rest B rows.  Lane l lands at LDS byte 16*l of the load's 1 KB.
+template <int BM, int BK>
+__device__ __forceinline__ void stage_load_one(const Ctx<BM, BK>& c, int k0, char* lds_stage,
+                                               int j) {
+    typedef Geo<BM, BK> G;
+    const bool is_a = j < G::LPW_A;
+    const int i = is_a ? j : j - G::LPW_A;
+    char* dst = is_a ? lds_stage + (c.wave * (BM / 4) + i * G::RPI) * BK
+                     : lds_stage + BM * BK + (c.wave * (L_BN / 4) + i * G::RPI) * BK;
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rsrc[is_a ? 0 : 1], (lds_void*)dst, 16,
+                                             is_a ? c.voff_a[i] : c.voff_b[i], k0, 0, 0);
+#else
+    (void)dst;
+#endif
+}
+
+template <int BM, int BK>
+__device__ __forceinline__ void stage_load(const Ctx<BM, BK>& c, int k0, char* lds_stage) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < Geo<BM, BK>::NLOAD; ++j) stage_load_one<BM, BK>(c, k0, lds_stage, j);
+}
+
+template <int MI>
+struct Frags {
+    v4i a[MI];  // activation rows (MFMA B-operand), m sub-tiles
+    v4i w[4];   // weight rows (MFMA A-operand), n sub-tiles
+};
+
+// Fragment q of sub-step ks: q < MI -> activation sub-tile q, else weight
+// sub-tile q - MI.  Lane l reads row l % 32 of the sub-tile at K-chunk 2*ks + l/32.
+template <int BM, int BK>
+__device__ __forceinline__ void read_frag(const char* lds_stage, const Ctx<BM, BK>& c, int ks,
+                                          int q, Frags<BM / 64>& f) {
+    constexpr int MI = BM / 64;
+    const int ch = 2 * ks + (c.lane >> 5);
+    if (q < MI) {
+        const int ra = c.wm * (BM / 2) + q * 32 + (c.lane & 31);
+        f.a[q] = *reinterpret_cast<const v4i*>(lds_stage + ra * BK + 16 * swz<BK>(ra, ch));
+    } else {
+        const int rw = c.wn * 128 + (q - MI) * 32 + (c.lane & 31);
+        f.w[q - MI] =
+            *reinterpret_cast<const v4i*>(lds_stage + BM * BK + rw * BK + 16 * swz<BK>(rw, ch));
+    }
+}
+
+template <int MI>
+__device__ __forceinline__ void mfma_one(v16i (&acc)[4][MI], const Frags<MI>& f, int j) {
+    const int ni = j / MI, mi = j % MI;
+    acc[ni][mi] = __builtin_amdgcn_mfma_i32_32x32x32_i8(f.w[ni], f.a[mi], acc[ni][mi], 0, 0, 0);
+}
+
+// One K stage, held in ring buffer kt % NST.
+// LOAD: stage kt+NST exists and is loaded into this buffer after the barrier.
+// NEXT: stage kt+1 exists.  STEADY: exactly NST-2 newer stages are in flight.
+// Each sub-step issues its MFMAs in a fixed order with the next fragment reads
+// (one after each of the first NQ MFMAs) and the refill loads (spread evenly)
+// placed between them; sched_barrier pins that order.
+template <int BM, int BK, int NST, bool LOAD, bool NEXT, bool STEADY>
+__device__ __forceinline__ void k_stage(const Ctx<BM, BK>& c, char* smem, int kt,
+                                        v16i (&acc)[4][BM / 64], Frags<BM / 64>& cur) {
+    typedef Geo<BM, BK> G;
+    char* buf = smem + (kt % NST) * G::STAGE;
+    Frags<G::MI> nxt;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int64_t col = n0 + wn * 64 + j * 16 + (lane & 15);
-            if (col >= N) continue;
-            float swj = 0.f, bj = 0.f;
-            if (!OUT_I32) {
-                swj = sw[col];
-                bj = bias ? bf16_bits_to_float(bias[col]) : 0.f;
+    for (int ks = 0; ks + 1 < G::SUB; ++ks) {
+#pragma unroll
+        for (int j = 0; j < G::NMFMA; ++j) {
+            mfma_one<G::MI>(acc, cur, j);
+            if (j < G::NQ) read_frag<BM, BK>(buf, c, ks + 1, j, nxt);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        cur = nxt;
+    }
+    char* next_buf = smem + ((kt + 1) % NST) * G::STAGE;
+    if (NEXT) {
+        // my loads of stage kt+1 have landed and my reads of stage kt are done ...
+        if (STEADY) wait_vm_lgkm0<G::NLOAD * (NST - 2)>();
+        else wait_vm_lgkm0<0>();
+        __syncthreads();  // ... and everyone's: stage kt+1 visible, buffer kt % NST free
+        __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int j = 0; j < G::NMFMA; ++j) {
+        mfma_one<G::MI>(acc, cur, j);
+        if (NEXT && j < G::NQ) read_frag<BM, BK>(next_buf, c, 0, j, nxt);
+        if (LOAD) {
+            // loads (j * NLOAD / NMFMA) .. ((j+1) * NLOAD / NMFMA) - 1 go after MFMA j
+#pragma unroll
+            for (int l = (j * G::NLOAD) / G::NMFMA; l < ((j + 1) * G::NLOAD) / G::NMFMA; ++l)
+                stage_load_one<BM, BK>(c, (kt + NST) * BK, buf, l);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    if (NEXT) cur = nxt;
+}
+
+// Workgroup id -> (tile row, tile col), XCD-aware.
+template <int BM>
+__device__ __forceinline__ void tile_of(int64_t bid, int64_t tm, int64_t tn, int64_t& tile_m,
+                                        int64_t& tile_n) {
+    constexpr int GROUP_M = GROUP_ROWS / BM;
+    const int64_t total = tm * tn;
+    int64_t t = bid;
+    if (total % NUM_XCD == 0) {
+        // XCD x (= bid % 8) takes tiles [x * total/8, (x+1) * total/8) in dispatch order
+        t = (bid % NUM_XCD) * (total / NUM_XCD) + bid / NUM_XCD;
+    }
+    // grouped raster: walk GROUP_M tile-rows at a time, column by column
+    const int64_t per_group = GROUP_M * tn;
+    const int64_t g = t / per_group;
+    const int64_t first_m = g * GROUP_M;
+    const int64_t gm = (tm - first_m) < GROUP_M ? (tm - first_m) : GROUP_M;
+    const int64_t r = t % per_group;
+    tile_m = first_m + r % gm;
+    tile_n = r / gm;
+}
+
+// Epilogue.  acc[ni][mi][i] holds D[n][m] for m = m0 + wm*(BM/2) + mi*32 +
+// (lane & 31) and n = n0 + wn*128 + ni*32 + 8*(i/4) + 4*(lane >> 5) + (i & 3):
+// four consecutive columns per group of four registers, written as one store.
+// Interior tiles skip the bounds checks.
+template <int BM, int ACT, bool HAS_BIAS>
+__device__ __forceinline__ void store_bf16(const v16i (&acc)[4][BM / 64], uint16_t* __restrict__ y,
+                                           int64_t M, int64_t N, int64_t m0, int64_t n0, int wm,
+                                           int wn, int lane, const float* sa_l, const float* sw_l,
+                                           const uint16_t* b_l) {
+    constexpr int MI = BM / 64;
+    const bool interior = (m0 + BM <= M) && (n0 + L_BN <= N);
+    const int ncol = wn * 128 + 4 * (lane >> 5);  // tile-local column of this lane's first group
+    float sam[MI];
+    uint16_t* rowp[MI];
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+        const int ml = wm * (BM / 2) + mi * 32 + (lane & 31);
+        sam[mi] = sa_l[ml];
+        rowp[mi] = y + (m0 + ml) * N + n0 + ncol;
+    }
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int cl = ncol + ni * 32 + 8 * g;
+            const v4f swv = *reinterpret_cast<const v4f*>(sw_l + cl);
+            float bv[4] = {0.f, 0.f, 0.f, 0.f};
+            if (HAS_BIAS) {
+                const uint2 bb = *reinterpret_cast<const uint2*>(b_l + cl);
+                bv[0] = bf16_bits_to_float(bb.x & 0xffffu);
+                bv[1] = bf16_bits_to_float(bb.x >> 16);
+                bv[2] = bf16_bits_to_float(bb.y & 0xffffu);
+                bv[3] = bf16_bits_to_float(bb.y >> 16);
             }
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int64_t row = m0 + wm * 64 + i * 16 + (lane >> 4) * 4 + r;
-                if (row >= M) continue;
-                if (OUT_I32) {
-                    reinterpret_cast<int32_t*>(out)[row * N + col] = acc[i][j][r];
+            for (int mi = 0; mi < MI; ++mi) {
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float t = (float)acc[ni][mi][4 * g + e];  // nearest even
+                    const float u = __fmul_rn(sam[mi], swv[e]);
+                    v[e] = HAS_BIAS ? __builtin_fmaf(t, u, bv[e]) : __fmul_rn(t, u);
+                }
+                uint2 o = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+                if (ACT == 1) {
+                    // GELU-tanh on the bf16-rounded value, rounded to bf16 again
+                    o = make_uint2(pack_bf16x2(gelu_tanh(bf16_bits_to_float(o.x & 0xffffu)),
+                                               gelu_tanh(bf16_bits_to_float(o.x >> 16))),
+                                   pack_bf16x2(gelu_tanh(bf16_bits_to_float(o.y & 0xffffu)),
+                                               gelu_tanh(bf16_bits_to_float(o.y >> 16))));
+                }
+                uint16_t* p = rowp[mi] + ni * 32 + 8 * g;
+                if (interior) {
+                    *reinterpret_cast<uint2*>(p) = o;
                 } else {
-                    reinterpret_cast<uint16_t*>(out)[row * N + col] =
-                        (uint16_t)epilogue_bf16<ACT>(acc[i][j][r], sa[row], swj, bj, bias != nullptr);
+                    const int ml = wm * (BM / 2) + mi * 32 + (lane & 31);
+                    if (m0 + ml < M && n0 + cl < N) *reinterpret_cast<uint2*>(p) = o;
                 }
             }
         }
     }
 }
 
+template <int BM>
+__device__ __forceinline__ void store_i32(const v16i (&acc)[4][BM / 64], int32_t* __restrict__ out,
+                                          int64_t M, int64_t N, int64_t m0, int64_t n0, int wm,
+                                          int wn, int lane) {
+    constexpr int MI = BM / 64;
+    const int ncol = wn * 128 + 4 * (lane >> 5);
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+        const int ml = wm * (BM / 2) + mi * 32 + (lane & 31);
+        if (m0 + ml >= M) continue;
+        int32_t* rowp = out + (m0 + ml) * N + n0 + ncol;
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                if (n0 + ncol + ni * 32 + 8 * g >= N) continue;
+                v4i v = {acc[ni][mi][4 * g], acc[ni][mi][4 * g + 1], acc[ni][mi][4 * g + 2],
+                         acc[ni][mi][4 * g + 3]};
+                *reinterpret_cast<v4i*>(rowp + ni * 32 + 8 * g) = v;
+            }
+    }
+}
+
+template <int BM, int BK, int NST, int OUT_I32, int ACT>
+__global__ __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(Geo<BM, BK>::WAVES_PER_SIMD, Geo<BM, BK>::WAVES_PER_SIMD)))
+void gemm_i8_tiled(const int8_t* __restrict__ qa, const float* __restrict__ sa, int64_t M,
+                   const int8_t* __restrict__ qw, const float* __restrict__ sw, int64_t N, int64_t K,
+                   const uint16_t* __restrict__ bias, void* __restrict__ out) {
+    typedef Geo<BM, BK> G;
+    constexpr int MI = G::MI;
+    // K ring, then the tile's row scales, column scales and bias for the epilogue
+    __shared__ __attribute__((aligned(1024))) char smem[NST * G::STAGE + BM * 4 + L_BN * (4 + 2)];
+    float* sa_l = reinterpret_cast<float*>(smem + NST * G::STAGE);
+    float* sw_l = sa_l + BM;
+    uint16_t* b_l = reinterpret_cast<uint16_t*>(sw_l + L_BN);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int64_t tm = (M + BM - 1) / BM, tn = (N + L_BN - 1) / L_BN;
+    int64_t tile_m, tile_n;
+    tile_of<BM>(blockIdx.x, tm, tn, tile_m, tile_n);
+    const int64_t m0 = tile_m * BM, n0 = tile_n * L_BN;
+    const int KT = (int)(K / BK);
+    Ctx<BM, BK> c;
+    make_ctx<BM, BK>(c, qa, qw, M, N, K, m0, n0, wave, lane);
+
+    v16i acc[4][MI];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < MI; ++j) acc[i][j] = (v16i){};
+
+    // prologue: fill the ring, stage the epilogue operands, wait for stage 0
+    for (int s = 0; s < NST; ++s)
+        if (s < KT) stage_load<BM, BK>(c, s * BK, smem + s * G::STAGE);
+    if (!OUT_I32) {
+        const int64_t n = n0 + tid;
+        if (tid < BM) {
+            const int64_t m = m0 + tid;
+            sa_l[tid] = sa[m < M ? m : M - 1];
+        }
+        sw_l[tid] = sw[n < N ? n : N - 1];
+        b_l[tid] = bias ? bias[n < N ? n : N - 1] : (uint16_t)0;
+    }
+    if (KT >= NST) wait_vm_lgkm0<G::NLOAD * (NST - 1)>();
+    else wait_vm_lgkm0<0>();
+    __syncthreads();
+    Frags<MI> cur;
+#pragma unroll
+    for (int q = 0; q < G::NQ; ++q) read_frag<BM, BK>(smem, c, 0, q, cur);
+
+    int kt = 0;
+    for (; kt + NST < KT; ++kt) k_stage<BM, BK, NST, true, true, true>(c, smem, kt, acc, cur);
+    if (kt == KT - NST && kt + 1 < KT) {
+        k_stage<BM, BK, NST, false, true, true>(c, smem, kt, acc, cur);
+        ++kt;
+    }
+    for (; kt + 1 < KT; ++kt) k_stage<BM, BK, NST, false, true, false>(c, smem, kt, acc, cur);
+    k_stage<BM, BK, NST, false, false, false>(c, smem, kt, acc, cur);
+
+    if (OUT_I32) {
+        store_i32<BM>(acc, reinterpret_cast<int32_t*>(out), M, N, m0, n0, wm, wn, lane);
+    } else if (bias) {
+        store_bf16<BM, ACT, true>(acc, reinterpret_cast<uint16_t*>(out), M, N, m0, n0, wm, wn, lane,
+                                  sa_l, sw_l, b_l);
+    } else {
+        store_bf16<BM, ACT, false>(acc, reinterpret_cast<uint16_t*>(out), M, N, m0, n0, wm, wn,
+                                   lane, sa_l, sw_l, b_l);
+    }
+}
+
+// 256 x 256 tiles, 64-byte K stages, 4-deep ring: the configuration with the
+// least data movement per MFMA, which is what sets the clock under the power cap.
+#ifndef W8A8_BM
+#define W8A8_BM 256
+#endif
+#ifndef W8A8_BK
+#define W8A8_BK 64
+#endif
+#ifndef W8A8_NST
+#define W8A8_NST 4
+#endif
+
 template <int OUT_I32, int ACT>
-hipError_t launch_simple(const int8_t* qa, const float* sa, int64_t M, const int8_t* qw,
-                         const float* sw, int64_t N, int64_t K, const uint16_t* bias, void* out,
-                         hipStream_t stream) {
-    const int64_t tiles = ((N + S_BN - 1) / S_BN) * ((M + S_BM - 1) / S_BM);
-    hipLaunchKernelGGL((gemm_i8_simple<OUT_I32, ACT>), dim3((unsigned)tiles), dim3(256), 0, stream, qa, sa, M, qw,
-                       sw, N, K, bias, out);
+hipError_t launch_large(const int8_t* qa, const float* sa, int64_t M, const int8_t* qw,
+                        const float* sw, int64_t N, int64_t K, const uint16_t* bias, void* out,
+                        hipStream_t stream) {
+    const int64_t tiles = ((N + L_BN - 1) / L_BN) * ((M + W8A8_BM - 1) / W8A8_BM);
+    hipLaunchKernelGGL((gemm_i8_tiled<W8A8_BM, W8A8_BK, W8A8_NST, OUT_I32, ACT>),
+                       dim3((unsigned)tiles), dim3(256), 0, stream, qa, sa, M, qw, sw, N, K, bias,
+                       out);
     return hipGetLastError();
 }
 
@@ -131,9 +441,9 @@ int launch_gemm_i8(const int8_t* qa, const float* sa, int64_t M, const int8_t* q
                    int out_kind, void* out, hipStream_t stream) {
     if (M == 0 || N == 0) return 0;
     hipError_t e;
-    if (out_kind == 1) e = launch_simple<1, 0>(qa, sa, M, qw, sw, N, K, bias, out, stream);
-    else if (act == 1) e = launch_simple<0, 1>(qa, sa, M, qw, sw, N, K, bias, out, stream);
-    else e = launch_simple<0, 0>(qa, sa, M, qw, sw, N, K, bias, out, stream);
+    if (out_kind == 1) e = launch_large<1, 0>(qa, sa, M, qw, sw, N, K, bias, out, stream);
+    else if (act == 1) e = launch_large<0, 1>(qa, sa, M, qw, sw, N, K, bias, out, stream);
+    else e = launch_large<0, 0>(qa, sa, M, qw, sw, N, K, bias, out, stream);
     return e == hipSuccess ? 0 : -1;
 }
 
