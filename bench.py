@@ -3,8 +3,8 @@
 
 Workload (one step): the video FFN pair, all through the INT8 path —
     X [24576 x 4096] bf16 --quantise--> qX, sX
-    H = GELU-tanh(W8A8(qX, W1 [16384 x 4096]) + b1)       bf16 [24576 x 16384]
-    H --quantise--> qH, sH
+    U = W8A8(qX, W1 [16384 x 4096]) + b1                   bf16 [24576 x 16384]
+    U --GELU-tanh + quantise (fused)--> qH, sH            (H = GELU(U) never stored)
     Y = W8A8(qH, W2 [4096 x 16384]) + b2                   bf16 [24576 x 4096]
 The weights are quantised once before timing (static, per output channel).
 Inputs are seeded synthetic tensors of the workload's shapes and value
@@ -50,6 +50,15 @@ def parse():
     p.add_argument("--cpu-rows", type=int, default=0,
                    help="rows of the oracle sample (0: sized to ~15 s)")
     p.add_argument("--no-extra", action="store_true", help="skip the secondary kernel benches")
+    p.add_argument("--probe-traffic", action="store_true",
+                   help="run a known-size copy and the step's kernels a few times, for "
+                        "rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs, then exit")
+    p.add_argument("--ceiling", action="store_true",
+                   help="measure the INT8 MFMA rate and clock for several kinds of operand "
+                        "data (the power-capped ceiling any INT8 GEMM faces), print JSON, exit")
+    p.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                   help="turn the two rocprofv3 counter outputs of --probe-traffic into "
+                        + TRAFFIC_FILE + " and exit (no GPU needed)")
     return p.parse_args()
 
 
@@ -69,8 +78,98 @@ def stored_traffic():
     return t
 
 
+COPY_BYTES = 1 << 30  # the calibration copy reads and writes 1 GiB
+
+
+def traffic_from(fetch_dir, write_dir):
+    """Per-launch HBM bytes of the GEMM from two rocprofv3 --pmc runs of
+    --probe-traffic, each counter scaled by what it reads for a plain copy of
+    known size (COPY_BYTES read, COPY_BYTES written)."""
+    import csv
+    import glob
+
+    def per_kernel(d, counter):
+        vals = {}
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                if r["Counter_Name"] != counter:
+                    continue
+                vals.setdefault(r["Kernel_Name"], {}).setdefault(r["Dispatch_Id"], 0.0)
+                vals[r["Kernel_Name"]][r["Dispatch_Id"]] += float(r["Counter_Value"])
+        return {k: sum(v.values()) / len(v) for k, v in vals.items()}
+
+    fetch = per_kernel(fetch_dir, "FETCH_SIZE")
+    write = per_kernel(write_dir, "WRITE_SIZE")
+    copy_f = [v for k, v in fetch.items() if "neg_kernel" in k or "neg" in k]
+    copy_w = [v for k, v in write.items() if "neg_kernel" in k or "neg" in k]
+    gemm_f = [v for k, v in fetch.items() if "gemm_i8_tiled" in k]
+    gemm_w = [v for k, v in write.items() if "gemm_i8_tiled" in k]
+    assert copy_f and copy_w and gemm_f and gemm_w, "counter runs lack the copy or the GEMM"
+    kf = COPY_BYTES / (copy_f[0] * 1024.0)   # true bytes per counted byte
+    kw = COPY_BYTES / (copy_w[0] * 1024.0)
+    rd = gemm_f[0] * 1024.0 * kf
+    wr = gemm_w[0] * 1024.0 * kw
+    out = {"kernel": "gemm_i8_tiled (video FFN up and down launches, averaged)",
+           "kernel_source_sha256_16": source_hash(GEMM_SOURCE),
+           "copy_scale_fetch": kf, "copy_scale_write": kw,
+           "read_bytes_per_launch": rd, "write_bytes_per_launch": wr,
+           "hbm_bytes_per_launch": rd + wr,
+           "command": "rocprofv3 --pmc FETCH_SIZE -d <FETCH_DIR> -f csv -- python3 bench.py "
+                      "--probe-traffic ; rocprofv3 --pmc WRITE_SIZE -d <WRITE_DIR> -f csv -- "
+                      "python3 bench.py --probe-traffic ; python3 bench.py --traffic-from "
+                      "<FETCH_DIR> <WRITE_DIR>"}
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
+
+
+def ceiling():
+    """INT8 MFMA throughput and shader clock for zero, constant, uniform-random and
+    Gaussian (sigma 32, like quantised N(0,1) rows) int8 operands."""
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    lib = ctypes.CDLL(os.path.join(ROOT, "int8_w8a8_gemm_amd", "libw8a8_probe.so"))
+    P = ctypes.c_void_p
+    lib.w8a8_probe_mfma.argtypes = [P, P, P, ctypes.c_int, ctypes.POINTER(ctypes.c_float), P]
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(0)
+    kinds = {
+        "zero": np.zeros(4096 * 16, np.int8),
+        "constant": np.tile(np.arange(1, 17, dtype=np.int8), 4096),
+        "uniform_random": rng.integers(-128, 128, 4096 * 16).astype(np.int8),
+        "gaussian_sigma32": np.clip(np.rint(rng.standard_normal(4096 * 16) * 32), -127, 127).astype(np.int8),
+    }
+    sink = torch.empty(1024 * 256, dtype=torch.int32, device=dev)
+    clk = torch.zeros(2, dtype=torch.int64, device=dev)
+    iters = 4000
+    out = {}
+    for name, ops in kinds.items():
+        t = torch.from_numpy(ops).to(dev)
+        ms = ctypes.c_float(0)
+        rc = lib.w8a8_probe_mfma(P(t.data_ptr()), P(sink.data_ptr()), P(clk.data_ptr()), iters,
+                                 ctypes.byref(ms), P(torch.cuda.current_stream().cuda_stream))
+        assert rc == 0, rc
+        c = clk.cpu().tolist()
+        tops = 1024 * 4 * iters * 8 * 65536.0 / (ms.value * 1e-3) / 1e12
+        out[name] = {"TOPS": round(tops, 1), "frac_of_5000": round(tops / PEAK_INT8_TOPS, 4),
+                     "clock_GHz": round(c[0] / (c[1] / 100e6) / 1e9, 3),
+                     "cycles_per_mfma": round(c[0] / (iters * 8), 2)}
+    print(json.dumps({"probe": "v_mfma_i32_32x32x32_i8 loop, 1 wave/SIMD, 8 accumulators",
+                      "results": out}))
+
+
 def main():
     args = parse()
+    if args.traffic_from:
+        traffic_from(*args.traffic_from)
+        return
+    if args.ceiling:
+        ceiling()
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: this path has no multi-GPU mode "
               "(it would shard rows or output channels with no exchange); use --gpus 1",
@@ -99,9 +198,10 @@ def main():
     w1, b1, w2, b2 = d(ffn.w1), d(ffn.b1), d(ffn.w2), d(ffn.b2)
     qw1, sw1 = w8.quantize_rows(w1)   # static weight quantisation, untimed
     qw2, sw2 = w8.quantize_rows(w2)
+    del w1, w2
     qx = torch.empty((M, D), dtype=torch.int8, device=dev)
     sx = torch.empty((M,), dtype=torch.float32, device=dev)
-    h = torch.empty((M, F), dtype=torch.bfloat16, device=dev)
+    u = torch.empty((M, F), dtype=torch.bfloat16, device=dev)
     qh = torch.empty((M, F), dtype=torch.int8, device=dev)
     sh = torch.empty((M,), dtype=torch.float32, device=dev)
     y = torch.empty((M, D), dtype=torch.bfloat16, device=dev)
@@ -113,17 +213,28 @@ def main():
               for _ in range(args.steps)]
 
     def step(ev=None):
-        # the same two C-ABI calls w8a8_linear makes (quantise into a workspace,
-        # then the GEMM), issued separately so each kernel can be timed
+        # quantise X, up GEMM, fused GELU + quantise of its output, down GEMM;
+        # each C-ABI call separately so each kernel can be timed
         if ev: ev[0].record(stream)
         w8.quantize_rows(x, qx, sx)
         if ev: ev[1].record(stream)
-        w8.gemm(qx, sx, qw1, sw1, b1, act=w8.ACT_GELU_TANH, out=h)
+        w8.gemm(qx, sx, qw1, sw1, b1, act=w8.ACT_NONE, out=u)
         if ev: ev[2].record(stream)
-        w8.quantize_rows(h, qh, sh)
+        w8.gelu_quantize_rows(u, qh, sh)
         if ev: ev[3].record(stream)
         w8.gemm(qh, sh, qw2, sw2, b2, act=w8.ACT_NONE, out=y)
         if ev: ev[4].record(stream)
+
+    if args.probe_traffic:
+        src = torch.zeros((COPY_BYTES // 2,), dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)   # reads and writes COPY_BYTES each
+        for _ in range(3):
+            step()
+        torch.cuda.synchronize()
+        log("traffic probe done")
+        return
 
     log(f"warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -149,18 +260,18 @@ def main():
     bytes_qx = 3.0 * M * D + 4.0 * M
     bytes_qh = 3.0 * M * F + 4.0 * M
     log(f"step {ms_per_step:.3f} ms: quant X {t_qx*1e3:.1f} us, GEMM up {t_up:.3f} ms "
-        f"({tops_up:.0f} TOPS), quant H {t_qh*1e3:.1f} us, GEMM down {t_down:.3f} ms "
+        f"({tops_up:.0f} TOPS), GELU+quant U {t_qh*1e3:.1f} us, GEMM down {t_down:.3f} ms "
         f"({tops_down:.0f} TOPS)")
 
-    # dominant kernel: the longer of the two GEMM instantiations
-    dom_name, dom_t = ("gemm_i8 up (+GELU epilogue)", t_up) if t_up >= t_down else \
-        ("gemm_i8 down", t_down)
+    # dominant kernel: the INT8 GEMM (one kernel, launched for the up and the
+    # down projection with the same op count): average launch duration
+    dom_name = "gemm_i8_tiled (video FFN up and down, averaged)"
+    dom_t = 0.5 * (t_up + t_down)
     achieved = ops_gemm / (dom_t * 1e-3) / 1e12
     traffic = None
     st = stored_traffic()
     if st is not None:
-        key = "up" if t_up >= t_down else "down"
-        traffic = st.get(key, {}).get("hbm_bytes_per_launch")
+        traffic = st.get("hbm_bytes_per_launch")
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_INT8_TOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_INT8_TOPS, 4),
                 "traffic": traffic, "kernel": dom_name,
@@ -180,16 +291,17 @@ def main():
         "dtype": "int8",
         "data": "synthetic",
         "config": {"workload": "video FFN pair, guarded W8A8 linear x2: "
-                               f"X[{M}x{D}] . W1[{F}x{D}]^T +b1, GELU-tanh, . W2[{D}x{F}]^T +b2",
+                               f"X[{M}x{D}] . W1[{F}x{D}]^T +b1, GELU-tanh (fused into the "
+                               f"down projection's quantisation), . W2[{D}x{F}]^T +b2",
                    "M": M, "D": D, "F": F, "act_up": "gelu_tanh", "parallelism": "single GPU"},
         "roofline": roofline,
         "kernels": {
             "quantize_x": {"us": round(t_qx * 1e3, 2),
                            "GB/s": round(bytes_qx / (t_qx * 1e-3) / 1e9, 1),
                            "frac_hbm": round(bytes_qx / (t_qx * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
-            "gemm_up_gelu": {"ms": round(t_up, 4), "TOPS": round(tops_up, 1),
-                             "frac_peak": round(tops_up / PEAK_INT8_TOPS, 4)},
-            "quantize_h": {"us": round(t_qh * 1e3, 2),
+            "gemm_up": {"ms": round(t_up, 4), "TOPS": round(tops_up, 1),
+                        "frac_peak": round(tops_up / PEAK_INT8_TOPS, 4)},
+            "gelu_quantize_u": {"us": round(t_qh * 1e3, 2),
                            "GB/s": round(bytes_qh / (t_qh * 1e-3) / 1e9, 1),
                            "frac_hbm": round(bytes_qh / (t_qh * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
             "gemm_down": {"ms": round(t_down, 4), "TOPS": round(tops_down, 1),
@@ -304,9 +416,9 @@ def cpu_baseline(ffn, rows, np, log):
         xs = np.ascontiguousarray(ffn.x[:n])
         t0 = time.perf_counter()
         qx, sx = oracle.quantize_rows(xs, nthreads=threads)
-        hh = oracle.epilogue(oracle.gemm_i32(qx, qw1, nthreads=threads), sx, sw1, ffn.b1,
-                             act=oracle.ACT_GELU_TANH, nthreads=threads)
-        qh, sh = oracle.quantize_rows(hh, nthreads=threads)
+        uu = oracle.epilogue(oracle.gemm_i32(qx, qw1, nthreads=threads), sx, sw1, ffn.b1,
+                             nthreads=threads)
+        qh, sh = oracle.gelu_quantize_rows(uu, nthreads=threads)
         oracle.epilogue(oracle.gemm_i32(qh, qw2, nthreads=threads), sh, sw2, ffn.b2,
                         nthreads=threads)
         return time.perf_counter() - t0
@@ -322,7 +434,7 @@ def cpu_baseline(ffn, rows, np, log):
     return {"value": round(ops / t / 1e12, 6), "unit": "TOPS", "cores": threads, "kind": "oracle",
             "seconds": round(t, 2),
             "sample": f"first {rows} of {ffn.x.shape[0]} rows of the video FFN pair step "
-                      f"(quantise, INT32 GEMM, epilogue+GELU, quantise, INT32 GEMM, epilogue)"}
+                      f"(quantise, INT32 GEMM, epilogue, GELU + quantise, INT32 GEMM, epilogue)"}
 
 
 if __name__ == "__main__":

@@ -72,6 +72,22 @@ W8A8_API int w8a8_quantize_rows(const uint16_t* x, int64_t rows, int64_t cols, i
                        void* stream);
 
 /*
+ * Fused GELU + per-row INT8 quantisation: the input of a linear that follows a
+ * GELU-tanh (the FFN down projection, whose input is the up projection's
+ * output passed through GELU; the quantisation is the per-row dynamic
+ * activation quantisation of section 01.3).
+ *
+ *   y     [rows x cols] bf16 pre-activation
+ *   q     [rows x cols] int8 codes of h, scale [rows] fp32
+ *
+ * h = GELU-tanh(y) correctly rounded to bf16 (the same value w8a8_gemm's
+ * W8A8_ACT_GELU_TANH epilogue produces), then exactly w8a8_quantize_rows(h).
+ * h itself is not written.  Same alignment rules as w8a8_quantize_rows.
+ */
+W8A8_API int w8a8_gelu_quantize_rows(const uint16_t* y, int64_t rows, int64_t cols, int8_t* q,
+                                     float* scale, void* stream);
+
+/*
  * INT8 GEMM with INT32 accumulation and the epilogue after full accumulation
  * (section 01.3).
  *
@@ -83,7 +99,8 @@ W8A8_API int w8a8_quantize_rows(const uint16_t* x, int64_t rows, int64_t cols, i
  *                  (no bias: bf16_RNE(float(acc) * RN32(sa[i]*sw[j])));
  *                  act == W8A8_ACT_GELU_TANH then applies
  *                  g(z) = z/2 (1 + tanh(sqrt(2/pi)(z + 0.044715 z^3))) to the bf16 y
- *                  and rounds to bf16 again.
+ *                  and rounds g(y) correctly to bf16 (round to nearest even of the
+ *                  exact value).
  *                out_kind == W8A8_OUT_I32 -> the raw int32 accumulator
  *                  acc[i][j] = sum_k qa[i][k]*qw[j][k] (act must be NONE; sa, sw,
  *                  bias are ignored and may be NULL).

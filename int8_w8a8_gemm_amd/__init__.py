@@ -28,7 +28,7 @@ ACT_NONE, ACT_GELU_TANH = 0, 1
 PATH_INT8, PATH_BF16 = 0, 1
 MAX_K = 131072
 
-EXPORTS = ("w8a8_quantize_rows", "w8a8_gemm", "w8a8_linear", "w8a8_linear_bf16",
+EXPORTS = ("w8a8_quantize_rows", "w8a8_gelu_quantize_rows", "w8a8_gemm", "w8a8_linear", "w8a8_linear_bf16",
            "compact_padded_rows", "w8a8_guard", "w8a8_linear_workspace_bytes",
            "w8a8_status_str")
 
@@ -52,6 +52,7 @@ def lib():
     L = ctypes.CDLL(LIB_PATH)
     P, I64, I, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
     L.w8a8_quantize_rows.argtypes = [P, I64, I64, P, P, P]
+    L.w8a8_gelu_quantize_rows.argtypes = [P, I64, I64, P, P, P]
     L.w8a8_gemm.argtypes = [P, P, I64, P, P, I64, I64, P, I, I, P, P]
     L.w8a8_linear.argtypes = [P, I64, I64, I64, P, P, P, P, I, P, P, SZ, P, P]
     L.w8a8_linear_bf16.argtypes = [P, I64, I64, P, I64, P, I, P, P]
@@ -61,7 +62,7 @@ def lib():
     L.w8a8_linear_workspace_bytes.restype = SZ
     L.w8a8_status_str.argtypes = [I]
     L.w8a8_status_str.restype = ctypes.c_char_p
-    for name in ("w8a8_quantize_rows", "w8a8_gemm", "w8a8_linear", "w8a8_linear_bf16",
+    for name in ("w8a8_quantize_rows", "w8a8_gelu_quantize_rows", "w8a8_gemm", "w8a8_linear", "w8a8_linear_bf16",
                  "compact_padded_rows", "w8a8_guard"):
         getattr(L, name).restype = I
     _lib = L
@@ -134,6 +135,23 @@ def quantize_rows(x: torch.Tensor, q: Optional[torch.Tensor] = None,
     _need(scale, "scale", torch.float32, (R,))
     _check("w8a8_quantize_rows",
            lib().w8a8_quantize_rows(_p(x), R, C, _p(q), _p(scale), _stream(stream)))
+    return q, scale
+
+
+def gelu_quantize_rows(y: torch.Tensor, q: Optional[torch.Tensor] = None,
+                       scale: Optional[torch.Tensor] = None, stream=None):
+    """h = GELU-tanh(y) (correctly rounded to bf16), then per-row INT8 quantisation of h:
+    y bf16 [R, C] -> (q int8 [R, C], scale fp32 [R]).  h is not materialised."""
+    _need(y, "y", torch.bfloat16)
+    if y.dim() != 2:
+        raise ValueError("y must be 2-D")
+    R, C = y.shape
+    q = q if q is not None else torch.empty((R, C), dtype=torch.int8, device=y.device)
+    scale = scale if scale is not None else torch.empty((R,), dtype=torch.float32, device=y.device)
+    _need(q, "q", torch.int8, (R, C))
+    _need(scale, "scale", torch.float32, (R,))
+    _check("w8a8_gelu_quantize_rows",
+           lib().w8a8_gelu_quantize_rows(_p(y), R, C, _p(q), _p(scale), _stream(stream)))
     return q, scale
 
 

@@ -21,6 +21,9 @@ LIB = os.path.join(HERE, "libw8a8.so")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 
 SOURCES = ["quantize_rows.hip", "compact_rows.hip", "gemm_i8.hip", "gemm_bf16.hip", "w8a8_api.hip"]
+# measurement probe, a library of its own (not part of libw8a8's ABI)
+PROBE_SOURCES = ["probe_mfma.hip"]
+PROBE_LIB = os.path.join(HERE, "libw8a8_probe.so")
 ARCH = "gfx950"
 FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-ffp-contract=off",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -56,10 +59,12 @@ def build(verbose: bool = False, jobs: int = 5) -> str:
         return obj
 
     with ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(compile_one, SOURCES))
-    tmp = LIB + ".tmp"
-    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
-    os.replace(tmp, LIB)
+        objs = list(ex.map(compile_one, SOURCES + PROBE_SOURCES))
+    for lib, n in ((LIB, len(SOURCES)), (PROBE_LIB, None)):
+        part = objs[:n] if n is not None else objs[len(SOURCES):]
+        tmp = lib + ".tmp"
+        _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *part, "-o", tmp])
+        os.replace(tmp, lib)
     return LIB
 
 

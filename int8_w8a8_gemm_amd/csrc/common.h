@@ -24,15 +24,57 @@ __device__ __forceinline__ uint32_t float_to_bf16_bits(float f) {
     return ((u & 0x7fffffffu) > 0x7f800000u) ? ((u >> 16) | 0x40u) : r;
 }
 
-// GELU, tanh approximation, on a binary32 input; returns binary32.
-// 1 + tanh(t) is evaluated as 2 / (1 + exp(-2t)) so large negative inputs keep
-// their relative accuracy.
-__device__ __forceinline__ float gelu_tanh(float z) {
-    const float c = 0.7978845608028654f;  // sqrt(2/pi)
-    float z3 = __fmul_rn(__fmul_rn(z, z), z);
-    float t = __fmul_rn(c, __fadd_rn(z, __fmul_rn(0.044715f, z3)));
-    float e = expf(-2.0f * t);
-    return __fdiv_rn(z, __fadd_rn(1.0f, e));
+// GELU, tanh approximation, g(z) = z/2 (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3))),
+// evaluated on a bf16 input and correctly rounded to bf16.
+//
+// 1 + tanh(u) = 2 / (1 + exp(-2u)), so g(z) = z / (1 + 2^w) with
+// w = -2 log2(e) sqrt(2/pi) (z + 0.044715 z^3), which keeps relative accuracy
+// for z << 0.  Fast path in binary32: w from z^2 and two constants, 2^w with
+// v_exp_f32 and the reciprocal with v_rcp_f32 (1 ulp each).  Its error is at
+// most 2.8|w| + 3 binary32 ulps of g; when the low 16 bits of the binary32
+// result are within 16 + 4|w| ulps of the bf16 rounding midpoint (0x8000),
+// or w > 100 (results near the bottom of the exponent range), the value is
+// recomputed in binary64 and rounded directly to bf16.
+__device__ __forceinline__ uint32_t f64_to_bf16_bits(double v) {
+    const uint64_t u = __double_as_longlong(v);
+    const uint32_t sign = (uint32_t)(u >> 48) & 0x8000u;
+    const double a = fabs(v);
+    if (!(a < 3.4e38)) return sign | (a == a ? 0x7f80u : 0x7fc0u);  // inf / NaN
+    if (a >= 0x1p-126) {
+        // keep 8 significant bits: round the binary64 mantissa at bit 45, ties to even
+        uint64_t m = u & 0x7fffffffffffffffull;
+        m += ((1ull << 44) - 1) + ((m >> 45) & 1);
+        m &= ~((1ull << 45) - 1);
+        const float f = (float)__longlong_as_double((long long)m);  // exact
+        const uint32_t fb = __float_as_uint(f);
+        return sign | ((fb >> 16) & 0x7fffu);  // 0x7f80 if it rounded past the max
+    }
+    // bf16 subnormal: spacing 2^-133; the integer multiple is the encoding
+    const double r = rint(a * 0x1p133);
+    return sign | (uint32_t)r;
+}
+
+__device__ __forceinline__ uint32_t gelu_bf16_rn(uint32_t hbits) {
+    const float z = __uint_as_float(hbits << 16);
+    // -2 log2(e) sqrt(2/pi) * {1, 0.044715}
+    const float B = -2.3022082f, A = -0.10294324f;
+    const float t = __fmul_rn(z, z);
+    const float p = __builtin_fmaf(t, A, B);
+    const float w = __fmul_rn(p, z);
+    const float e = __builtin_amdgcn_exp2f(w);
+    const float r = __builtin_amdgcn_rcpf(__fadd_rn(1.0f, e));
+    const float g = __fmul_rn(z, r);
+    const uint32_t gb = __float_as_uint(g);
+    const int dist = abs((int)(gb & 0xffffu) - 0x8000);
+    const float margin = 16.0f + 4.0f * fabsf(w);
+    if (w > 100.0f || !((float)dist > margin)) {
+        const double zd = (double)z;
+        const double u = 0.79788456080286535588 * (zd + 0.044715 * zd * zd * zd);
+        return f64_to_bf16_bits(zd / (1.0 + exp(-2.0 * u)));
+    }
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    bf16x2 v = {(__bf16)g, (__bf16)0.0f};
+    return __builtin_bit_cast(uint32_t, v) & 0xffffu;
 }
 
 // Two binary32 values -> two bf16 (round to nearest even) packed low/high in a
@@ -48,7 +90,7 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // Host-side launchers (defined in the .hip files, called by the C-ABI layer).
 namespace w8a8 {
 int launch_quantize_rows(const uint16_t* x, int64_t rows, int64_t cols, int8_t* q, float* scale,
-                         hipStream_t stream);
+                         hipStream_t stream, bool gelu = false);
 int launch_compact_rows(const uint16_t* x, const uint8_t* mask, int64_t R, int64_t D,
                         uint16_t* out, int32_t* src_row, int32_t* count, hipStream_t stream);
 int launch_gemm_i8(const int8_t* qa, const float* sa, int64_t M, const int8_t* qw,

@@ -96,7 +96,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const uint16_t* __restri
                 const int64_t row = m0 + wm * 64 + i * 16 + (lane >> 4) * 4 + r;
                 if (row >= M) continue;
                 uint32_t h = float_to_bf16_bits(__fadd_rn(acc[i][j][r], bj));
-                if (ACT == 1) h = float_to_bf16_bits(gelu_tanh(bf16_bits_to_float(h)));
+                if (ACT == 1) h = gelu_bf16_rn(h);
                 y[row * N + col] = (uint16_t)h;
             }
         }

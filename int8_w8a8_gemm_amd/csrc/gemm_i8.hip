@@ -301,11 +301,9 @@ __device__ __forceinline__ void store_bf16(const v16i (&acc)[4][BM / 64], uint16
                 }
                 uint2 o = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
                 if (ACT == 1) {
-                    // GELU-tanh on the bf16-rounded value, rounded to bf16 again
-                    o = make_uint2(pack_bf16x2(gelu_tanh(bf16_bits_to_float(o.x & 0xffffu)),
-                                               gelu_tanh(bf16_bits_to_float(o.x >> 16))),
-                                   pack_bf16x2(gelu_tanh(bf16_bits_to_float(o.y & 0xffffu)),
-                                               gelu_tanh(bf16_bits_to_float(o.y >> 16))));
+                    // GELU-tanh on the bf16-rounded value, correctly rounded to bf16
+                    o = make_uint2(gelu_bf16_rn(o.x & 0xffffu) | (gelu_bf16_rn(o.x >> 16) << 16),
+                                   gelu_bf16_rn(o.y & 0xffffu) | (gelu_bf16_rn(o.y >> 16) << 16));
                 }
                 uint16_t* p = rowp[mi] + ni * 32 + 8 * g;
                 if (interior) {

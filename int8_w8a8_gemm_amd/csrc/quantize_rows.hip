@@ -7,6 +7,10 @@
 //     q = RNE(RN32(x * inv)) clamped to [-127, 127],
 // and rows with a < 2^-100 get scale 0 and all-zero codes.
 //
+// The GELU variant quantises h = GELU-tanh(x) (correctly rounded to bf16) in
+// the same pass: the input of an FFN down projection, straight from the
+// up projection's bf16 output, without writing h to memory.
+//
 // The kernel is HBM-bound (2 bytes read + 1 byte written per element).  The
 // vector path keeps a whole row in registers so each element is read from HBM
 // once: 16-byte loads (8 bf16 per lane per chunk, a wave moves 1 KB per
@@ -63,9 +67,18 @@ __device__ __forceinline__ uint2 quant8(u32x4 v, float inv) {
     return make_uint2(o[0], o[1]);
 }
 
+// GELU applied to the 8 bf16 of one chunk.
+__device__ __forceinline__ u32x4 gelu8(u32x4 v) {
+    u32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        o[i] = gelu_bf16_rn(v[i] & 0xffffu) | (gelu_bf16_rn(v[i] >> 16) << 16);
+    return o;
+}
+
 // WPR waves cooperate on one row; each lane holds CPL 16-byte chunks.  Serves
 // rows of up to WPR*64*CPL*8 elements with cols % 8 == 0.
-template <int WPR, int CPL>
+template <int WPR, int CPL, bool GELU>
 __global__ __launch_bounds__(kBlock) void quantize_rows_vec(const uint16_t* __restrict__ x,
                                                             int64_t rows, int64_t cols,
                                                             int8_t* __restrict__ q,
@@ -86,6 +99,7 @@ __global__ __launch_bounds__(kBlock) void quantize_rows_vec(const uint16_t* __re
         const int64_t ch = (int64_t)(c * WPR + wr) * 64 + lane;
         if (live && ch < nchunk) {
             v[c] = __builtin_nontemporal_load(xr + ch);
+            if (GELU) v[c] = gelu8(v[c]);
         } else {
             v[c] = (u32x4){0u, 0u, 0u, 0u};
         }
@@ -126,6 +140,7 @@ __global__ __launch_bounds__(kBlock) void quantize_rows_vec(const uint16_t* __re
 }
 
 // Any cols, any alignment: one block per row, two passes over the row.
+template <bool GELU>
 __global__ __launch_bounds__(kBlock) void quantize_rows_generic(const uint16_t* __restrict__ x,
                                                                 int64_t rows, int64_t cols,
                                                                 int8_t* __restrict__ q,
@@ -136,7 +151,10 @@ __global__ __launch_bounds__(kBlock) void quantize_rows_generic(const uint16_t* 
     const uint16_t* xr = x + row * cols;
     int8_t* qr = q + row * cols;
     uint32_t amax = 0;
-    for (int64_t k = threadIdx.x; k < cols; k += kBlock) amax = max(amax, (uint32_t)(xr[k] & 0x7fffu));
+    for (int64_t k = threadIdx.x; k < cols; k += kBlock) {
+        const uint32_t h = GELU ? gelu_bf16_rn(xr[k]) : (uint32_t)xr[k];
+        amax = max(amax, h & 0x7fffu);
+    }
     amax = wave_max_u32(amax);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
     __syncthreads();
@@ -149,39 +167,49 @@ __global__ __launch_bounds__(kBlock) void quantize_rows_generic(const uint16_t* 
     }
     const float inv = __fdiv_rn(127.0f, a);
     if (threadIdx.x == 0) scale[row] = __fdiv_rn(a, 127.0f);
-    for (int64_t k = threadIdx.x; k < cols; k += kBlock)
-        qr[k] = (int8_t)quant1(__uint_as_float((uint32_t)xr[k] << 16), inv);
+    for (int64_t k = threadIdx.x; k < cols; k += kBlock) {
+        const uint32_t h = GELU ? gelu_bf16_rn(xr[k]) : (uint32_t)xr[k];
+        qr[k] = (int8_t)quant1(__uint_as_float(h << 16), inv);
+    }
 }
 
 template <int WPR, int CPL>
 hipError_t launch_vec(const uint16_t* x, int64_t rows, int64_t cols, int8_t* q, float* scale,
-                      hipStream_t stream) {
+                      hipStream_t stream, bool gelu) {
     constexpr int RPB = (kBlock / 64) / WPR;
     const int64_t blocks = (rows + RPB - 1) / RPB;
-    hipLaunchKernelGGL((quantize_rows_vec<WPR, CPL>), dim3((unsigned)blocks), dim3(kBlock), 0,
-                       stream, x, rows, cols, q, scale);
+    if (gelu)
+        hipLaunchKernelGGL((quantize_rows_vec<WPR, CPL, true>), dim3((unsigned)blocks), dim3(kBlock),
+                           0, stream, x, rows, cols, q, scale);
+    else
+        hipLaunchKernelGGL((quantize_rows_vec<WPR, CPL, false>), dim3((unsigned)blocks),
+                           dim3(kBlock), 0, stream, x, rows, cols, q, scale);
     return hipGetLastError();
 }
 
 }  // namespace
 
 int launch_quantize_rows(const uint16_t* x, int64_t rows, int64_t cols, int8_t* q, float* scale,
-                         hipStream_t stream) {
+                         hipStream_t stream, bool gelu) {
     if (rows == 0) return 0;
     const bool vec = (cols % 8 == 0) && (reinterpret_cast<uintptr_t>(x) % 16 == 0) &&
                      (reinterpret_cast<uintptr_t>(q) % 8 == 0) && cols > 0;
     const int64_t nchunk = cols / 8;
     hipError_t e;
-    if (vec && nchunk <= 64) e = launch_vec<1, 1>(x, rows, cols, q, scale, stream);
-    else if (vec && nchunk <= 128) e = launch_vec<1, 2>(x, rows, cols, q, scale, stream);
-    else if (vec && nchunk <= 256) e = launch_vec<1, 4>(x, rows, cols, q, scale, stream);
-    else if (vec && nchunk <= 512) e = launch_vec<1, 8>(x, rows, cols, q, scale, stream);
-    else if (vec && nchunk <= 1024) e = launch_vec<2, 8>(x, rows, cols, q, scale, stream);
-    else if (vec && nchunk <= 2048) e = launch_vec<4, 8>(x, rows, cols, q, scale, stream);
-    else if (vec && nchunk <= 4096) e = launch_vec<4, 16>(x, rows, cols, q, scale, stream);
+    if (vec && nchunk <= 64) e = launch_vec<1, 1>(x, rows, cols, q, scale, stream, gelu);
+    else if (vec && nchunk <= 128) e = launch_vec<1, 2>(x, rows, cols, q, scale, stream, gelu);
+    else if (vec && nchunk <= 256) e = launch_vec<1, 4>(x, rows, cols, q, scale, stream, gelu);
+    else if (vec && nchunk <= 512) e = launch_vec<1, 8>(x, rows, cols, q, scale, stream, gelu);
+    else if (vec && nchunk <= 1024) e = launch_vec<2, 8>(x, rows, cols, q, scale, stream, gelu);
+    else if (vec && nchunk <= 2048) e = launch_vec<4, 8>(x, rows, cols, q, scale, stream, gelu);
+    else if (vec && nchunk <= 4096) e = launch_vec<4, 16>(x, rows, cols, q, scale, stream, gelu);
     else {
-        hipLaunchKernelGGL(quantize_rows_generic, dim3((unsigned)rows), dim3(kBlock), 0, stream, x,
-                           rows, cols, q, scale);
+        if (gelu)
+            hipLaunchKernelGGL(quantize_rows_generic<true>, dim3((unsigned)rows), dim3(kBlock), 0,
+                               stream, x, rows, cols, q, scale);
+        else
+            hipLaunchKernelGGL(quantize_rows_generic<false>, dim3((unsigned)rows), dim3(kBlock), 0,
+                               stream, x, rows, cols, q, scale);
         e = hipGetLastError();
     }
     return e == hipSuccess ? 0 : -1;

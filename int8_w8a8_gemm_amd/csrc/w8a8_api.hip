@@ -50,6 +50,15 @@ int w8a8_quantize_rows(const uint16_t* x, int64_t rows, int64_t cols, int8_t* q,
     return launched(w8a8::launch_quantize_rows(x, rows, cols, q, scale, as_stream(stream)));
 }
 
+int w8a8_gelu_quantize_rows(const uint16_t* y, int64_t rows, int64_t cols, int8_t* q,
+                            float* scale, void* stream) {
+    if (rows < 0 || cols < 0 || rows >= kMaxRows) return W8A8_EINVAL;
+    if (rows == 0) return W8A8_OK;
+    if (!scale || !aligned(scale, 4)) return W8A8_EINVAL;
+    if (cols > 0 && (!y || !q || !aligned(y, 2))) return W8A8_EINVAL;
+    return launched(w8a8::launch_quantize_rows(y, rows, cols, q, scale, as_stream(stream), true));
+}
+
 int w8a8_gemm(const int8_t* qa, const float* sa, int64_t M, const int8_t* qw, const float* sw,
               int64_t N, int64_t K, const uint16_t* bias, int act, int out_kind, void* out,
               void* stream) {

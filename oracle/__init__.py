@@ -66,6 +66,7 @@ def _load():
     lib.oracle_f64_to_bf16.restype = ctypes.c_uint16
     lib.oracle_gelu_tanh_f64.argtypes = [ctypes.c_double]
     lib.oracle_gelu_tanh_f64.restype = ctypes.c_double
+    lib.oracle_gelu_rows.argtypes = [P, I64, P, I]
     lib.oracle_gelu_bf16.argtypes = [ctypes.c_uint16]
     lib.oracle_gelu_bf16.restype = ctypes.c_uint16
     _lib = lib
@@ -173,6 +174,20 @@ def w8a8_linear(x, w, bias=None, act=ACT_NONE, nthreads=None):
     rc = _check(_load().oracle_w8a8_linear(_ptr(x), M, K, _ptr(w), N, _ptr(b), int(act), _ptr(y),
                                            _threads(nthreads)), "oracle_w8a8_linear")
     return y, rc
+
+
+def gelu_rows(y, nthreads=None):
+    """GELU-tanh of every bf16 element, each rounded once to bf16 (the activation
+    between the FFN halves; float64 evaluation)."""
+    y = _c(y, np.uint16)
+    h = np.empty_like(y)
+    _check(_load().oracle_gelu_rows(_ptr(y), y.size, _ptr(h), _threads(nthreads)), "oracle_gelu_rows")
+    return h
+
+
+def gelu_quantize_rows(y, nthreads=None):
+    """Per-row INT8 quantisation of GELU-tanh(y): the down projection's input."""
+    return quantize_rows(gelu_rows(y, nthreads), nthreads)
 
 
 def guard(N: int, K: int) -> bool:

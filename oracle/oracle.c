@@ -16,7 +16,7 @@
  * "C. Fused Multimodal Transformer Operations"), describe removing padded text
  * positions with the shared text mask while keeping every valid token.
  *
- * Readings where the pages are silent (each also listed in the design doc):
+ * Readings where the pages are silent:
  *   Q  symmetric per-row scale s = absmax/127 in fp32, codes rne(x * (127/absmax))
  *      clamped to [-127,127]; rows with absmax < 2^-100 get s = 0, q = 0.
  *   E  epilogue in fp32: v = fma(float(acc), fl(sa*sw), float(bias)); y = bf16_rne(v).
@@ -206,6 +206,21 @@ double oracle_gelu_tanh_f64(double z) {
 
 uint16_t oracle_gelu_bf16(uint16_t y) {
     return f64_to_bf16(oracle_gelu_tanh_f64((double)bf16_to_f32(y)));
+}
+
+/* Elementwise GELU over an array of bf16 values (h[i] = oracle_gelu_bf16(y[i])). */
+typedef struct { const uint16_t* y; uint16_t* h; } gelu_ctx;
+
+static void gelu_range(void* p, int64_t i0, int64_t i1) {
+    gelu_ctx* c = (gelu_ctx*)p;
+    for (int64_t i = i0; i < i1; ++i) c->h[i] = oracle_gelu_bf16(c->y[i]);
+}
+
+int oracle_gelu_rows(const uint16_t* y, int64_t n, uint16_t* h, int nthreads) {
+    if (n < 0) return -1;
+    gelu_ctx c = {y, h};
+    parallel_rows(gelu_range, &c, n, nthreads);
+    return 0;
 }
 
 /* ---------------------------------------------------------------------- */
