@@ -49,13 +49,23 @@ namespace {
 // ---------------------------------------------------------------------------
 constexpr int L_BN = 256;
 constexpr int NUM_XCD = 8;
-constexpr int GROUP_ROWS = 1024;
+#ifndef W8A8_GROUP_ROWS
+#define W8A8_GROUP_ROWS 1024
+#endif
+constexpr int GROUP_ROWS = W8A8_GROUP_ROWS;
 
 typedef __attribute__((address_space(3))) void lds_void;
 
+#ifndef W8A8_WAVES
+#define W8A8_WAVES 8
+#endif
+constexpr int WAVES = W8A8_WAVES;          // waves per workgroup: 2 x (WAVES/2) grid
+constexpr int WM = WAVES / 2;              // waves along M
+constexpr int THREADS = WAVES * 64;
+
 template <int BM, int BK>
 struct Geo {
-    static constexpr int MI = BM / 64;                 // 32-row MFMA tiles per wave along M
+    static constexpr int MI = BM / WM / 32;            // 32-row MFMA tiles per wave along M
     static constexpr int NI = 4;                       // 32-col MFMA tiles per wave along N
     static constexpr int NQ = MI + NI;                 // fragments per sub-step
     static constexpr int NMFMA = MI * NI;              // MFMAs per sub-step
@@ -63,10 +73,10 @@ struct Geo {
     static constexpr int RPI = 64 / CPR;               // rows one 1-KB wave instruction fills
     static constexpr int STAGE = (BM + L_BN) * BK;     // bytes per stage (A tile then B tile)
     static constexpr int SUB = BK / 32;                // 32-deep MFMA sub-steps per stage
-    static constexpr int LPW_A = BM / 4 / RPI;         // A load instructions per wave per stage
-    static constexpr int LPW_B = L_BN / 4 / RPI;       // B load instructions per wave per stage
+    static constexpr int LPW_A = BM / WAVES / RPI;     // A load instructions per wave per stage
+    static constexpr int LPW_B = L_BN / WAVES / RPI;   // B load instructions per wave per stage
     static constexpr int NLOAD = LPW_A + LPW_B;
-    static constexpr int WAVES_PER_SIMD = BM == 128 ? 2 : 1;
+    static constexpr int WAVES_PER_SIMD = MI * 4 > 8 ? WAVES / 4 : 2;
 };
 
 template <int BK>
@@ -123,18 +133,18 @@ __device__ __forceinline__ void make_ctx(Ctx<BM, BK>& c, const int8_t* qa, const
     const int rsub = lane / G::CPR, pc = lane % G::CPR;
 #pragma unroll
     for (int i = 0; i < G::LPW_A; ++i) {
-        const int r = wave * (BM / 4) + i * G::RPI + rsub;  // tile-local A row
+        const int r = wave * (BM / WAVES) + i * G::RPI + rsub;  // tile-local A row
         c.voff_a[i] = (uint32_t)r * (uint32_t)K + 16u * (uint32_t)swz<BK>(r, pc);
     }
 #pragma unroll
     for (int i = 0; i < G::LPW_B; ++i) {
-        const int r = wave * (L_BN / 4) + i * G::RPI + rsub;  // tile-local B row
+        const int r = wave * (L_BN / WAVES) + i * G::RPI + rsub;  // tile-local B row
         c.voff_b[i] = (uint32_t)r * (uint32_t)K + 16u * (uint32_t)swz<BK>(r, pc);
     }
     c.wave = wave;
     c.lane = lane;
-    c.wm = wave >> 1;
-    c.wn = wave & 1;
+    c.wm = wave % WM;
+    c.wn = wave / WM;
 }
 
 // Load j (0 .. NLOAD-1) of one wave's share of a K stage: j < LPW_A loads A
@@ -145,8 +155,8 @@ __device__ __forceinline__ void stage_load_one(const Ctx<BM, BK>& c, int k0, cha
     typedef Geo<BM, BK> G;
     const bool is_a = j < G::LPW_A;
     const int i = is_a ? j : j - G::LPW_A;
-    char* dst = is_a ? lds_stage + (c.wave * (BM / 4) + i * G::RPI) * BK
-                     : lds_stage + BM * BK + (c.wave * (L_BN / 4) + i * G::RPI) * BK;
+    char* dst = is_a ? lds_stage + (c.wave * (BM / WAVES) + i * G::RPI) * BK
+                     : lds_stage + BM * BK + (c.wave * (L_BN / WAVES) + i * G::RPI) * BK;
 #if defined(__HIP_DEVICE_COMPILE__)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rsrc[is_a ? 0 : 1], (lds_void*)dst, 16,
                                              is_a ? c.voff_a[i] : c.voff_b[i], k0, 0, 0);
@@ -171,11 +181,11 @@ struct Frags {
 // sub-tile q - MI.  Lane l reads row l % 32 of the sub-tile at K-chunk 2*ks + l/32.
 template <int BM, int BK>
 __device__ __forceinline__ void read_frag(const char* lds_stage, const Ctx<BM, BK>& c, int ks,
-                                          int q, Frags<BM / 64>& f) {
-    constexpr int MI = BM / 64;
+                                          int q, Frags<BM / WM / 32>& f) {
+    constexpr int MI = BM / WM / 32;
     const int ch = 2 * ks + (c.lane >> 5);
     if (q < MI) {
-        const int ra = c.wm * (BM / 2) + q * 32 + (c.lane & 31);
+        const int ra = c.wm * (BM / WM) + q * 32 + (c.lane & 31);
         f.a[q] = *reinterpret_cast<const v4i*>(lds_stage + ra * BK + 16 * swz<BK>(ra, ch));
     } else {
         const int rw = c.wn * 128 + (q - MI) * 32 + (c.lane & 31);
@@ -198,7 +208,7 @@ __device__ __forceinline__ void mfma_one(v16i (&acc)[4][MI], const Frags<MI>& f,
 // placed between them; sched_barrier pins that order.
 template <int BM, int BK, int NST, bool LOAD, bool NEXT, bool STEADY>
 __device__ __forceinline__ void k_stage(const Ctx<BM, BK>& c, char* smem, int kt,
-                                        v16i (&acc)[4][BM / 64], Frags<BM / 64>& cur) {
+                                        v16i (&acc)[4][BM / WM / 32], Frags<BM / WM / 32>& cur) {
     typedef Geo<BM, BK> G;
     char* buf = smem + (kt % NST) * G::STAGE;
     Frags<G::MI> nxt;
@@ -261,18 +271,18 @@ __device__ __forceinline__ void tile_of(int64_t bid, int64_t tm, int64_t tn, int
 // four consecutive columns per group of four registers, written as one store.
 // Interior tiles skip the bounds checks.
 template <int BM, int ACT, bool HAS_BIAS>
-__device__ __forceinline__ void store_bf16(const v16i (&acc)[4][BM / 64], uint16_t* __restrict__ y,
+__device__ __forceinline__ void store_bf16(const v16i (&acc)[4][BM / WM / 32], uint16_t* __restrict__ y,
                                            int64_t M, int64_t N, int64_t m0, int64_t n0, int wm,
                                            int wn, int lane, const float* sa_l, const float* sw_l,
                                            const uint16_t* b_l) {
-    constexpr int MI = BM / 64;
+    constexpr int MI = BM / WM / 32;
     const bool interior = (m0 + BM <= M) && (n0 + L_BN <= N);
     const int ncol = wn * 128 + 4 * (lane >> 5);  // tile-local column of this lane's first group
     float sam[MI];
     uint16_t* rowp[MI];
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
-        const int ml = wm * (BM / 2) + mi * 32 + (lane & 31);
+        const int ml = wm * (BM / WM) + mi * 32 + (lane & 31);
         sam[mi] = sa_l[ml];
         rowp[mi] = y + (m0 + ml) * N + n0 + ncol;
     }
@@ -309,7 +319,7 @@ __device__ __forceinline__ void store_bf16(const v16i (&acc)[4][BM / 64], uint16
                 if (interior) {
                     *reinterpret_cast<uint2*>(p) = o;
                 } else {
-                    const int ml = wm * (BM / 2) + mi * 32 + (lane & 31);
+                    const int ml = wm * (BM / WM) + mi * 32 + (lane & 31);
                     if (m0 + ml < M && n0 + cl < N) *reinterpret_cast<uint2*>(p) = o;
                 }
             }
@@ -318,14 +328,14 @@ __device__ __forceinline__ void store_bf16(const v16i (&acc)[4][BM / 64], uint16
 }
 
 template <int BM>
-__device__ __forceinline__ void store_i32(const v16i (&acc)[4][BM / 64], int32_t* __restrict__ out,
+__device__ __forceinline__ void store_i32(const v16i (&acc)[4][BM / WM / 32], int32_t* __restrict__ out,
                                           int64_t M, int64_t N, int64_t m0, int64_t n0, int wm,
                                           int wn, int lane) {
-    constexpr int MI = BM / 64;
+    constexpr int MI = BM / WM / 32;
     const int ncol = wn * 128 + 4 * (lane >> 5);
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
-        const int ml = wm * (BM / 2) + mi * 32 + (lane & 31);
+        const int ml = wm * (BM / WM) + mi * 32 + (lane & 31);
         if (m0 + ml >= M) continue;
         int32_t* rowp = out + (m0 + ml) * N + n0 + ncol;
 #pragma unroll
@@ -341,7 +351,7 @@ __device__ __forceinline__ void store_i32(const v16i (&acc)[4][BM / 64], int32_t
 }
 
 template <int BM, int BK, int NST, int OUT_I32, int ACT>
-__global__ __launch_bounds__(256)
+__global__ __launch_bounds__(THREADS)
 __attribute__((amdgpu_waves_per_eu(Geo<BM, BK>::WAVES_PER_SIMD, Geo<BM, BK>::WAVES_PER_SIMD)))
 void gemm_i8_tiled(const int8_t* __restrict__ qa, const float* __restrict__ sa, int64_t M,
                    const int8_t* __restrict__ qw, const float* __restrict__ sw, int64_t N, int64_t K,
@@ -355,7 +365,7 @@ void gemm_i8_tiled(const int8_t* __restrict__ qa, const float* __restrict__ sa, 
     uint16_t* b_l = reinterpret_cast<uint16_t*>(sw_l + L_BN);
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave % WM, wn = wave / WM;
     const int64_t tm = (M + BM - 1) / BM, tn = (N + L_BN - 1) / L_BN;
     int64_t tile_m, tile_n;
     tile_of<BM>(blockIdx.x, tm, tn, tile_m, tile_n);
@@ -373,7 +383,7 @@ void gemm_i8_tiled(const int8_t* __restrict__ qa, const float* __restrict__ sa, 
     // prologue: fill the ring, stage the epilogue operands, wait for stage 0
     for (int s = 0; s < NST; ++s)
         if (s < KT) stage_load<BM, BK>(c, s * BK, smem + s * G::STAGE);
-    if (!OUT_I32) {
+    if (!OUT_I32 && tid < 256) {
         const int64_t n = n0 + tid;
         if (tid < BM) {
             const int64_t m = m0 + tid;
@@ -409,16 +419,17 @@ void gemm_i8_tiled(const int8_t* __restrict__ qa, const float* __restrict__ sa, 
     }
 }
 
-// 256 x 256 tiles, 64-byte K stages, 4-deep ring: the configuration with the
-// least data movement per MFMA, which is what sets the clock under the power cap.
+// 256 x 256 tiles (the least data movement per MFMA, which is what sets the
+// clock under the power cap), 8 waves (two per SIMD, so one wave's load issue
+// and LDS waits overlap the other's MFMAs), 128-byte K stages, 2-deep ring.
 #ifndef W8A8_BM
 #define W8A8_BM 256
 #endif
 #ifndef W8A8_BK
-#define W8A8_BK 64
+#define W8A8_BK 128
 #endif
 #ifndef W8A8_NST
-#define W8A8_NST 4
+#define W8A8_NST 2
 #endif
 
 template <int OUT_I32, int ACT>
@@ -427,7 +438,7 @@ hipError_t launch_large(const int8_t* qa, const float* sa, int64_t M, const int8
                         hipStream_t stream) {
     const int64_t tiles = ((N + L_BN - 1) / L_BN) * ((M + W8A8_BM - 1) / W8A8_BM);
     hipLaunchKernelGGL((gemm_i8_tiled<W8A8_BM, W8A8_BK, W8A8_NST, OUT_I32, ACT>),
-                       dim3((unsigned)tiles), dim3(256), 0, stream, qa, sa, M, qw, sw, N, K, bias,
+                       dim3((unsigned)tiles), dim3(THREADS), 0, stream, qa, sa, M, qw, sw, N, K, bias,
                        out);
     return hipGetLastError();
 }
