@@ -266,48 +266,51 @@ __device__ __forceinline__ void tile_of(int64_t bid, int64_t tm, int64_t tn, int
     tile_n = r / gm;
 }
 
-// Epilogue.  acc[ni][mi][i] holds D[n][m] for m = m0 + wm*(BM/2) + mi*32 +
+// Epilogue.  acc[ni][mi][i] holds D[n][m] for m = m0 + wm*(BM/WM) + mi*32 +
 // (lane & 31) and n = n0 + wn*128 + ni*32 + 8*(i/4) + 4*(lane >> 5) + (i & 3):
-// four consecutive columns per group of four registers, written as one store.
-// Interior tiles skip the bounds checks.
+// four consecutive columns per group of four registers.
+//
+// Stored straight from the accumulator layout, one wave instruction would
+// touch 32 rows with 16 bytes each.  Instead the bf16 tile is first written to
+// LDS (the K ring is free by then), then copied out so that each wave
+// instruction writes two whole 512-byte tile rows.  Staged rows are padded to
+// 528 bytes: every LDS address is then a per-lane base plus a compile-time
+// offset, and the 16-byte row reads are free of bank conflicts.
+constexpr int OUT_ROW = L_BN * 2 + 16;  // bytes per staged output row
+
 template <int BM, int ACT, bool HAS_BIAS>
 __device__ __forceinline__ void store_bf16(const v16i (&acc)[4][BM / WM / 32], uint16_t* __restrict__ y,
-                                           int64_t M, int64_t N, int64_t m0, int64_t n0, int wm,
-                                           int wn, int lane, const float* sa_l, const float* sw_l,
-                                           const uint16_t* b_l) {
+                                           int64_t M, int64_t N, int64_t m0, int64_t n0, int wave,
+                                           int wm, int wn, int lane, const float* sa_l,
+                                           const float* sw_l, const float* b_l, char* stage) {
     constexpr int MI = BM / WM / 32;
-    const bool interior = (m0 + BM <= M) && (n0 + L_BN <= N);
-    const int ncol = wn * 128 + 4 * (lane >> 5);  // tile-local column of this lane's first group
+    const int half = lane >> 5;
+    const int ncol = wn * 128 + 4 * half;  // tile-local column of this lane's first group
     float sam[MI];
-    uint16_t* rowp[MI];
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi) {
-        const int ml = wm * (BM / WM) + mi * 32 + (lane & 31);
-        sam[mi] = sa_l[ml];
-        rowp[mi] = y + (m0 + ml) * N + n0 + ncol;
-    }
+    for (int mi = 0; mi < MI; ++mi) sam[mi] = sa_l[wm * (BM / WM) + mi * 32 + (lane & 31)];
+    // this lane's staged position for (mi, ni, g) = 0: row wm*(BM/WM) + (lane & 31)
+    char* wbase = stage + (wm * (BM / WM) + (lane & 31)) * OUT_ROW + ncol * 2;
+    __syncthreads();  // every wave is done reading the K ring
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni) {
+        v4f swv[4], bv[4];
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             const int cl = ncol + ni * 32 + 8 * g;
-            const v4f swv = *reinterpret_cast<const v4f*>(sw_l + cl);
-            float bv[4] = {0.f, 0.f, 0.f, 0.f};
-            if (HAS_BIAS) {
-                const uint2 bb = *reinterpret_cast<const uint2*>(b_l + cl);
-                bv[0] = bf16_bits_to_float(bb.x & 0xffffu);
-                bv[1] = bf16_bits_to_float(bb.x >> 16);
-                bv[2] = bf16_bits_to_float(bb.y & 0xffffu);
-                bv[3] = bf16_bits_to_float(bb.y >> 16);
-            }
+            swv[g] = *reinterpret_cast<const v4f*>(sw_l + cl);
+            if (HAS_BIAS) bv[g] = *reinterpret_cast<const v4f*>(b_l + cl);
+        }
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
 #pragma unroll
             for (int mi = 0; mi < MI; ++mi) {
                 float v[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const float t = (float)acc[ni][mi][4 * g + e];  // nearest even
-                    const float u = __fmul_rn(sam[mi], swv[e]);
-                    v[e] = HAS_BIAS ? __builtin_fmaf(t, u, bv[e]) : __fmul_rn(t, u);
+                    const float u = __fmul_rn(sam[mi], swv[g][e]);
+                    v[e] = HAS_BIAS ? __builtin_fmaf(t, u, bv[g][e]) : __fmul_rn(t, u);
                 }
                 uint2 o = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
                 if (ACT == 1) {
@@ -315,15 +318,29 @@ __device__ __forceinline__ void store_bf16(const v16i (&acc)[4][BM / WM / 32], u
                     o = make_uint2(gelu_bf16_rn(o.x & 0xffffu) | (gelu_bf16_rn(o.x >> 16) << 16),
                                    gelu_bf16_rn(o.y & 0xffffu) | (gelu_bf16_rn(o.y >> 16) << 16));
                 }
-                uint16_t* p = rowp[mi] + ni * 32 + 8 * g;
-                if (interior) {
-                    *reinterpret_cast<uint2*>(p) = o;
-                } else {
-                    const int ml = wm * (BM / WM) + mi * 32 + (lane & 31);
-                    if (m0 + ml < M && n0 + cl < N) *reinterpret_cast<uint2*>(p) = o;
-                }
+                *reinterpret_cast<uint2*>(wbase + mi * 32 * OUT_ROW + (ni * 32 + 8 * g) * 2) = o;
             }
         }
+    }
+    __syncthreads();
+    // copy-out: wave w owns tile rows [w*BM/WAVES, (w+1)*BM/WAVES), two rows per instruction
+    constexpr int RPW = BM / WAVES;
+    const bool interior = (m0 + BM <= M) && (n0 + L_BN <= N);
+    const int c8 = lane & 31;
+    const int r0 = wave * RPW + half;
+    const char* rbase = stage + r0 * OUT_ROW + c8 * 16;
+    v4i d[RPW / 2];
+#pragma unroll
+    for (int i = 0; i < RPW / 2; ++i) d[i] = *reinterpret_cast<const v4i*>(rbase + 2 * i * OUT_ROW);
+    uint16_t* gbase = y + (m0 + r0) * N + n0 + 8 * c8;
+    if (interior) {
+#pragma unroll
+        for (int i = 0; i < RPW / 2; ++i) *reinterpret_cast<v4i*>(gbase + 2 * i * N) = d[i];
+    } else {
+#pragma unroll
+        for (int i = 0; i < RPW / 2; ++i)
+            if (m0 + r0 + 2 * i < M && n0 + 8 * c8 < N)
+                *reinterpret_cast<v4i*>(gbase + 2 * i * N) = d[i];
     }
 }
 
@@ -358,11 +375,15 @@ void gemm_i8_tiled(const int8_t* __restrict__ qa, const float* __restrict__ sa, 
                    const uint16_t* __restrict__ bias, void* __restrict__ out) {
     typedef Geo<BM, BK> G;
     constexpr int MI = G::MI;
-    // K ring, then the tile's row scales, column scales and bias for the epilogue
-    __shared__ __attribute__((aligned(1024))) char smem[NST * G::STAGE + BM * 4 + L_BN * (4 + 2)];
-    float* sa_l = reinterpret_cast<float*>(smem + NST * G::STAGE);
+    // K ring (reused to stage the bf16 output tile), then the tile's row scales,
+    // column scales and bias (as binary32) for the epilogue.  All of it is one
+    // LDS object: with several, the compiler can no longer tell the fragment
+    // reads from the in-flight direct-to-LDS loads and waits for every load.
+    constexpr int RING = NST * G::STAGE > BM * OUT_ROW ? NST * G::STAGE : BM * OUT_ROW;
+    __shared__ __attribute__((aligned(1024))) char smem[RING + (BM + 2 * L_BN) * 4];
+    float* sa_l = reinterpret_cast<float*>(smem + RING);
     float* sw_l = sa_l + BM;
-    uint16_t* b_l = reinterpret_cast<uint16_t*>(sw_l + L_BN);
+    float* b_l = sw_l + L_BN;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave % WM, wn = wave / WM;
@@ -390,7 +411,7 @@ void gemm_i8_tiled(const int8_t* __restrict__ qa, const float* __restrict__ sa, 
             sa_l[tid] = sa[m < M ? m : M - 1];
         }
         sw_l[tid] = sw[n < N ? n : N - 1];
-        b_l[tid] = bias ? bias[n < N ? n : N - 1] : (uint16_t)0;
+        b_l[tid] = bias ? bf16_bits_to_float(bias[n < N ? n : N - 1]) : 0.0f;
     }
     if (KT >= NST) wait_vm_lgkm0<G::NLOAD * (NST - 1)>();
     else wait_vm_lgkm0<0>();
@@ -411,11 +432,11 @@ void gemm_i8_tiled(const int8_t* __restrict__ qa, const float* __restrict__ sa, 
     if (OUT_I32) {
         store_i32<BM>(acc, reinterpret_cast<int32_t*>(out), M, N, m0, n0, wm, wn, lane);
     } else if (bias) {
-        store_bf16<BM, ACT, true>(acc, reinterpret_cast<uint16_t*>(out), M, N, m0, n0, wm, wn, lane,
-                                  sa_l, sw_l, b_l);
+        store_bf16<BM, ACT, true>(acc, reinterpret_cast<uint16_t*>(out), M, N, m0, n0, wave, wm,
+                                  wn, lane, sa_l, sw_l, b_l, smem);
     } else {
-        store_bf16<BM, ACT, false>(acc, reinterpret_cast<uint16_t*>(out), M, N, m0, n0, wm, wn,
-                                   lane, sa_l, sw_l, b_l);
+        store_bf16<BM, ACT, false>(acc, reinterpret_cast<uint16_t*>(out), M, N, m0, n0, wave, wm,
+                                   wn, lane, sa_l, sw_l, b_l, smem);
     }
 }
 
