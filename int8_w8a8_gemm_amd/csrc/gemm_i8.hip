@@ -11,18 +11,19 @@
 // A/B operands want: every lane feeds 16 consecutive K bytes of one row.
 #include "common.h"
 
+#include <atomic>
+
 namespace w8a8 {
 
 namespace {
 
 // ---------------------------------------------------------------------------
-// Tiled MFMA kernel.  A workgroup of 4 waves owns a BM x 256 output tile; the
-// waves form a 2 x 2 grid, each owning (BM/2) x 128 outputs, i.e. MI x 4 tiles
-// of v_mfma_i32_32x32x32_i8 (MI = BM/64) held as int32 accumulators in AGPRs.
-// With BM = 128 each wave needs 128 accumulators, so two workgroups share a
-// CU (two waves per SIMD from different workgroups): one's barrier waits,
-// load issue and epilogue overlap the other's MFMAs.  K is staged BK bytes at
-// a time through an NST-deep ring of LDS buffers.
+// Tiled MFMA kernel.  A workgroup of WAVES = 8 waves owns a BM x 256 output
+// tile; the waves form a (WAVES/2) x 2 grid, each owning (BM/4) x 128 outputs,
+// i.e. MI x 4 tiles of v_mfma_i32_32x32x32_i8 (MI = BM/128) held as int32
+// accumulators.  Two waves share each SIMD, so one wave's load issue, LDS waits
+// and barrier arrival overlap the other's MFMAs.  K is staged BK bytes at a
+// time through an NST-deep ring of LDS buffers.
 //
 // * Operands go global -> LDS directly (buffer_load_dwordx4 ... lds): a wave
 //   instruction moves 1 KB (64 lanes x 16 bytes); lane l lands at LDS offset
@@ -85,6 +86,19 @@ __device__ __forceinline__ int swz(int r, int c) {
     return c ^ ((r >> 2) & 3);
 }
 
+// Workgroup barrier for the wave's own LDS reads and writes (ds_*) only.
+// __syncthreads() also waits for every global load and store in flight, and
+// any LDS fence waits for the direct-to-LDS loads; this one leaves both in
+// flight (the next tile's prefetch, the output stores), so it must not be
+// used where those loads' data is about to be read.  The empty asm statements
+// keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt, expcnt left free
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // s_waitcnt immediate for gfx9: vmcnt(v) lgkmcnt(0), expcnt left free.
 template <int V>
 __device__ __forceinline__ void wait_vm_lgkm0() {
@@ -117,11 +131,11 @@ struct Ctx {
     int wave, lane, wm, wn;
 };
 
+// Points the context's buffer resources at the operand panels of the tile
+// whose first output row is m0 and first output column n0.
 template <int BM, int BK>
-__device__ __forceinline__ void make_ctx(Ctx<BM, BK>& c, const int8_t* qa, const int8_t* qw,
-                                         int64_t M, int64_t N, int64_t K, int64_t m0, int64_t n0,
-                                         int wave, int lane) {
-    typedef Geo<BM, BK> G;
+__device__ __forceinline__ void set_tile(Ctx<BM, BK>& c, const int8_t* qa, const int8_t* qw,
+                                         int64_t M, int64_t N, int64_t K, int64_t m0, int64_t n0) {
 #if defined(__HIP_DEVICE_COMPILE__)
     const int64_t rows_a = (M - m0) < BM ? (M - m0) : BM;
     const int64_t rows_w = (N - n0) < L_BN ? (N - n0) : L_BN;
@@ -130,6 +144,12 @@ __device__ __forceinline__ void make_ctx(Ctx<BM, BK>& c, const int8_t* qa, const
     c.rsrc[1] = __builtin_amdgcn_make_buffer_rsrc((void*)(qw + n0 * K), (short)0,
                                                   (int)(rows_w * K), kRawBufferWord3);
 #endif
+}
+
+// Lane offsets are tile-local, so they are set once per workgroup.
+template <int BM, int BK>
+__device__ __forceinline__ void make_ctx(Ctx<BM, BK>& c, int64_t K, int wave, int lane) {
+    typedef Geo<BM, BK> G;
     const int rsub = lane / G::CPR, pc = lane % G::CPR;
 #pragma unroll
     for (int i = 0; i < G::LPW_A; ++i) {
@@ -271,45 +291,58 @@ __device__ __forceinline__ void tile_of(int64_t bid, int64_t tm, int64_t tn, int
 // four consecutive columns per group of four registers.
 //
 // Stored straight from the accumulator layout, one wave instruction would
-// touch 32 rows with 16 bytes each.  Instead the bf16 tile is first written to
-// LDS (the K ring is free by then), then copied out so that each wave
-// instruction writes two whole 512-byte tile rows.  Staged rows are padded to
-// 528 bytes: every LDS address is then a per-lane base plus a compile-time
-// offset, and the 16-byte row reads are free of bank conflicts.
+// touch 32 rows with 16 bytes each.  Instead the bf16 tile goes through LDS,
+// in MI passes of BM/MI rows (pass p holds the rows of MFMA sub-tile mi = p),
+// and is copied out so that each wave instruction writes two whole 512-byte
+// tile rows.  Staged rows are padded to 528 bytes: every LDS address is a
+// per-lane base plus a compile-time offset, and the 16-byte row reads are free
+// of bank conflicts.  `stage` must not overlap the K buffer that the next
+// tile's first stage is being loaded into.
 constexpr int OUT_ROW = L_BN * 2 + 16;  // bytes per staged output row
+
+template <int BM>
+struct Epi {
+    static constexpr int MI = BM / WM / 32;
+    static constexpr int SROWS = BM / MI;        // staged rows per pass (= WM * 32)
+    static constexpr int RPW = SROWS / WAVES;    // staged rows each wave copies out per pass
+    static constexpr int BYTES = SROWS * OUT_ROW;
+    static_assert(32 % RPW == 0 && RPW % 2 == 0, "copy-out rows per wave");
+};
 
 template <int BM, int ACT, bool HAS_BIAS>
 __device__ __forceinline__ void store_bf16(const v16i (&acc)[4][BM / WM / 32], uint16_t* __restrict__ y,
                                            int64_t M, int64_t N, int64_t m0, int64_t n0, int wave,
                                            int wm, int wn, int lane, const float* sa_l,
                                            const float* sw_l, const float* b_l, char* stage) {
-    constexpr int MI = BM / WM / 32;
+    typedef Epi<BM> E;
     const int half = lane >> 5;
     const int ncol = wn * 128 + 4 * half;  // tile-local column of this lane's first group
-    float sam[MI];
+    char* wbase = stage + (wm * 32 + (lane & 31)) * OUT_ROW + ncol * 2;
+    const bool interior = (m0 + BM <= M) && (n0 + L_BN <= N);
+    const int c8 = lane & 31;
+    // copy-out: staged row s = wave*RPW + 2i + half is tile row (s/32)*(BM/WM) + p*32 + s%32
+    const int s0 = wave * E::RPW + half;
+    const char* rbase = stage + s0 * OUT_ROW + c8 * 16;
+    const int trow0 = (s0 / 32) * (BM / WM) + (s0 % 32);
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi) sam[mi] = sa_l[wm * (BM / WM) + mi * 32 + (lane & 31)];
-    // this lane's staged position for (mi, ni, g) = 0: row wm*(BM/WM) + (lane & 31)
-    char* wbase = stage + (wm * (BM / WM) + (lane & 31)) * OUT_ROW + ncol * 2;
-    __syncthreads();  // every wave is done reading the K ring
+    for (int p = 0; p < E::MI; ++p) {
+        const float sam = sa_l[wm * (BM / WM) + p * 32 + (lane & 31)];
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni) {
-        v4f swv[4], bv[4];
+        for (int ni = 0; ni < 4; ++ni) {
+            v4f swv[4], bv[4];
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const int cl = ncol + ni * 32 + 8 * g;
-            swv[g] = *reinterpret_cast<const v4f*>(sw_l + cl);
-            if (HAS_BIAS) bv[g] = *reinterpret_cast<const v4f*>(b_l + cl);
-        }
+            for (int g = 0; g < 4; ++g) {
+                const int cl = ncol + ni * 32 + 8 * g;
+                swv[g] = *reinterpret_cast<const v4f*>(sw_l + cl);
+                if (HAS_BIAS) bv[g] = *reinterpret_cast<const v4f*>(b_l + cl);
+            }
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-#pragma unroll
-            for (int mi = 0; mi < MI; ++mi) {
+            for (int g = 0; g < 4; ++g) {
                 float v[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const float t = (float)acc[ni][mi][4 * g + e];  // nearest even
-                    const float u = __fmul_rn(sam[mi], swv[g][e]);
+                    const float t = (float)acc[ni][p][4 * g + e];  // nearest even
+                    const float u = __fmul_rn(sam, swv[g][e]);
                     v[e] = HAS_BIAS ? __builtin_fmaf(t, u, bv[g][e]) : __fmul_rn(t, u);
                 }
                 uint2 o = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
@@ -318,29 +351,26 @@ __device__ __forceinline__ void store_bf16(const v16i (&acc)[4][BM / WM / 32], u
                     o = make_uint2(gelu_bf16_rn(o.x & 0xffffu) | (gelu_bf16_rn(o.x >> 16) << 16),
                                    gelu_bf16_rn(o.y & 0xffffu) | (gelu_bf16_rn(o.y >> 16) << 16));
                 }
-                *reinterpret_cast<uint2*>(wbase + mi * 32 * OUT_ROW + (ni * 32 + 8 * g) * 2) = o;
+                *reinterpret_cast<uint2*>(wbase + (ni * 32 + 8 * g) * 2) = o;
             }
         }
-    }
-    __syncthreads();
-    // copy-out: wave w owns tile rows [w*BM/WAVES, (w+1)*BM/WAVES), two rows per instruction
-    constexpr int RPW = BM / WAVES;
-    const bool interior = (m0 + BM <= M) && (n0 + L_BN <= N);
-    const int c8 = lane & 31;
-    const int r0 = wave * RPW + half;
-    const char* rbase = stage + r0 * OUT_ROW + c8 * 16;
-    v4i d[RPW / 2];
+        lds_barrier();
+        v4i d[E::RPW / 2];
 #pragma unroll
-    for (int i = 0; i < RPW / 2; ++i) d[i] = *reinterpret_cast<const v4i*>(rbase + 2 * i * OUT_ROW);
-    uint16_t* gbase = y + (m0 + r0) * N + n0 + 8 * c8;
-    if (interior) {
+        for (int i = 0; i < E::RPW / 2; ++i)
+            d[i] = *reinterpret_cast<const v4i*>(rbase + 2 * i * OUT_ROW);
+        const int64_t row = m0 + trow0 + p * 32;
+        uint16_t* gbase = y + row * N + n0 + 8 * c8;
+        if (interior) {
 #pragma unroll
-        for (int i = 0; i < RPW / 2; ++i) *reinterpret_cast<v4i*>(gbase + 2 * i * N) = d[i];
-    } else {
+            for (int i = 0; i < E::RPW / 2; ++i) *reinterpret_cast<v4i*>(gbase + 2 * i * N) = d[i];
+        } else {
 #pragma unroll
-        for (int i = 0; i < RPW / 2; ++i)
-            if (m0 + r0 + 2 * i < M && n0 + 8 * c8 < N)
-                *reinterpret_cast<v4i*>(gbase + 2 * i * N) = d[i];
+            for (int i = 0; i < E::RPW / 2; ++i)
+                if (row + 2 * i < M && n0 + 8 * c8 < N)
+                    *reinterpret_cast<v4i*>(gbase + 2 * i * N) = d[i];
+        }
+        lds_barrier();  // the staging area is free again
     }
 }
 
@@ -367,7 +397,14 @@ __device__ __forceinline__ void store_i32(const v16i (&acc)[4][BM / WM / 32], in
     }
 }
 
-template <int BM, int BK, int NST, int OUT_I32, int ACT>
+// Persistent kernel (PERSIST): the grid holds one workgroup per CU (or one per
+// tile if there are fewer tiles), and workgroup b walks tiles b, b + grid, ...
+// While a tile's epilogue runs, the next tile's first K stage is already
+// loading into ring buffer 0 and its scales into registers; the output is
+// staged in the LDS above buffer 0.  Without PERSIST each workgroup does one
+// tile (the GELU epilogue's binary64 slow path needs the registers that the
+// tile loop's live state would take).
+template <int BM, int BK, int NST, int OUT_I32, int ACT, bool PERSIST>
 __global__ __launch_bounds__(THREADS)
 __attribute__((amdgpu_waves_per_eu(Geo<BM, BK>::WAVES_PER_SIMD, Geo<BM, BK>::WAVES_PER_SIMD)))
 void gemm_i8_tiled(const int8_t* __restrict__ qa, const float* __restrict__ sa, int64_t M,
@@ -375,11 +412,13 @@ void gemm_i8_tiled(const int8_t* __restrict__ qa, const float* __restrict__ sa, 
                    const uint16_t* __restrict__ bias, void* __restrict__ out) {
     typedef Geo<BM, BK> G;
     constexpr int MI = G::MI;
-    // K ring (reused to stage the bf16 output tile), then the tile's row scales,
-    // column scales and bias (as binary32) for the epilogue.  All of it is one
-    // LDS object: with several, the compiler can no longer tell the fragment
-    // reads from the in-flight direct-to-LDS loads and waits for every load.
-    constexpr int RING = NST * G::STAGE > BM * OUT_ROW ? NST * G::STAGE : BM * OUT_ROW;
+    // K ring (from byte STAGE on, also the output staging area), then the
+    // tile's row scales, column scales and bias (as binary32).  All of it is
+    // one LDS object: with several, the compiler can no longer tell the
+    // fragment reads from the in-flight direct-to-LDS loads and waits for
+    // every load.
+    constexpr int RING = NST * G::STAGE > G::STAGE + Epi<BM>::BYTES ? NST * G::STAGE
+                                                                    : G::STAGE + Epi<BM>::BYTES;
     __shared__ __attribute__((aligned(1024))) char smem[RING + (BM + 2 * L_BN) * 4];
     float* sa_l = reinterpret_cast<float*>(smem + RING);
     float* sw_l = sa_l + BM;
@@ -387,56 +426,100 @@ void gemm_i8_tiled(const int8_t* __restrict__ qa, const float* __restrict__ sa, 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave % WM, wn = wave / WM;
-    const int64_t tm = (M + BM - 1) / BM, tn = (N + L_BN - 1) / L_BN;
-    int64_t tile_m, tile_n;
-    tile_of<BM>(blockIdx.x, tm, tn, tile_m, tile_n);
-    const int64_t m0 = tile_m * BM, n0 = tile_n * L_BN;
+    const int64_t tm = (M + BM - 1) / BM, tn = (N + L_BN - 1) / L_BN, total = tm * tn;
     const int KT = (int)(K / BK);
+    int64_t t = blockIdx.x, tile_m, tile_n;
+    tile_of<BM>(t, tm, tn, tile_m, tile_n);
+    int64_t m0 = tile_m * BM, n0 = tile_n * L_BN;
     Ctx<BM, BK> c;
-    make_ctx<BM, BK>(c, qa, qw, M, N, K, m0, n0, wave, lane);
+    make_ctx<BM, BK>(c, K, wave, lane);
+    set_tile<BM, BK>(c, qa, qw, M, N, K, m0, n0);
 
-    v16i acc[4][MI];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < MI; ++j) acc[i][j] = (v16i){};
-
-    // prologue: fill the ring, stage the epilogue operands, wait for stage 0
+    // first tile: epilogue operands, then fill the ring and wait for stage 0
+    // (the bias stays in bf16 bits until it is written: converting it at once
+    // would make the wave wait for the load)
+    float nsa = 0.f, nsw = 0.f;
+    uint32_t nb = 0;
+    if (!OUT_I32 && tid < L_BN) {
+        const int64_t n = n0 + tid < N ? n0 + tid : N - 1;
+        if (tid < BM) nsa = sa[m0 + tid < M ? m0 + tid : M - 1];
+        nsw = sw[n];
+        if (bias) nb = bias[n];
+    }
     for (int s = 0; s < NST; ++s)
         if (s < KT) stage_load<BM, BK>(c, s * BK, smem + s * G::STAGE);
-    if (!OUT_I32 && tid < 256) {
-        const int64_t n = n0 + tid;
-        if (tid < BM) {
-            const int64_t m = m0 + tid;
-            sa_l[tid] = sa[m < M ? m : M - 1];
-        }
-        sw_l[tid] = sw[n < N ? n : N - 1];
-        b_l[tid] = bias ? bf16_bits_to_float(bias[n < N ? n : N - 1]) : 0.0f;
+    if (!OUT_I32 && tid < L_BN) {
+        if (tid < BM) sa_l[tid] = nsa;
+        sw_l[tid] = nsw;
+        b_l[tid] = bf16_bits_to_float(nb);
     }
     if (KT >= NST) wait_vm_lgkm0<G::NLOAD * (NST - 1)>();
     else wait_vm_lgkm0<0>();
     __syncthreads();
-    Frags<MI> cur;
+
+    for (;;) {
+        v16i acc[4][MI];
 #pragma unroll
-    for (int q = 0; q < G::NQ; ++q) read_frag<BM, BK>(smem, c, 0, q, cur);
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < MI; ++j) acc[i][j] = (v16i){};
+        Frags<MI> cur;
+#pragma unroll
+        for (int q = 0; q < G::NQ; ++q) read_frag<BM, BK>(smem, c, 0, q, cur);
 
-    int kt = 0;
-    for (; kt + NST < KT; ++kt) k_stage<BM, BK, NST, true, true, true>(c, smem, kt, acc, cur);
-    if (kt == KT - NST && kt + 1 < KT) {
-        k_stage<BM, BK, NST, false, true, true>(c, smem, kt, acc, cur);
-        ++kt;
-    }
-    for (; kt + 1 < KT; ++kt) k_stage<BM, BK, NST, false, true, false>(c, smem, kt, acc, cur);
-    k_stage<BM, BK, NST, false, false, false>(c, smem, kt, acc, cur);
+        int kt = 0;
+        for (; kt + NST < KT; ++kt) k_stage<BM, BK, NST, true, true, true>(c, smem, kt, acc, cur);
+        if (kt == KT - NST && kt + 1 < KT) {
+            k_stage<BM, BK, NST, false, true, true>(c, smem, kt, acc, cur);
+            ++kt;
+        }
+        for (; kt + 1 < KT; ++kt) k_stage<BM, BK, NST, false, true, false>(c, smem, kt, acc, cur);
+        k_stage<BM, BK, NST, false, false, false>(c, smem, kt, acc, cur);
 
-    if (OUT_I32) {
-        store_i32<BM>(acc, reinterpret_cast<int32_t*>(out), M, N, m0, n0, wm, wn, lane);
-    } else if (bias) {
-        store_bf16<BM, ACT, true>(acc, reinterpret_cast<uint16_t*>(out), M, N, m0, n0, wave, wm,
-                                  wn, lane, sa_l, sw_l, b_l, smem);
-    } else {
-        store_bf16<BM, ACT, false>(acc, reinterpret_cast<uint16_t*>(out), M, N, m0, n0, wave, wm,
-                                   wn, lane, sa_l, sw_l, b_l, smem);
+        const int64_t t_next = t + gridDim.x;
+        const bool has_next = PERSIST && t_next < total;
+        int64_t m0n = 0, n0n = 0;
+        lds_barrier();  // every wave is done reading the K ring
+        if (has_next) {
+            tile_of<BM>(t_next, tm, tn, tile_m, tile_n);
+            m0n = tile_m * BM;
+            n0n = tile_n * L_BN;
+            if (!OUT_I32 && tid < L_BN) {
+                const int64_t n = n0n + tid < N ? n0n + tid : N - 1;
+                if (tid < BM) nsa = sa[m0n + tid < M ? m0n + tid : M - 1];
+                nsw = sw[n];
+                if (bias) nb = bias[n];
+            }
+            set_tile<BM, BK>(c, qa, qw, M, N, K, m0n, n0n);
+            stage_load<BM, BK>(c, 0, smem);  // next tile's stage 0 -> buffer 0
+        }
+        // The epilogue's lane addresses depend only on the lane, and hoisted out
+        // of the tile loop they would stay live across the K loop; an opaque
+        // copy of the lane index keeps them local to the epilogue.
+        int elane = lane;
+        asm volatile("" : "+v"(elane));
+        if (OUT_I32) {
+            store_i32<BM>(acc, reinterpret_cast<int32_t*>(out), M, N, m0, n0, wm, wn, elane);
+        } else if (bias) {
+            store_bf16<BM, ACT, true>(acc, reinterpret_cast<uint16_t*>(out), M, N, m0, n0, wave,
+                                      wm, wn, elane, sa_l, sw_l, b_l, smem + G::STAGE);
+        } else {
+            store_bf16<BM, ACT, false>(acc, reinterpret_cast<uint16_t*>(out), M, N, m0, n0, wave,
+                                       wm, wn, elane, sa_l, sw_l, b_l, smem + G::STAGE);
+        }
+        if (!has_next) break;
+        if (!OUT_I32 && tid < L_BN) {  // this tile's epilogue is done with the old values
+            if (tid < BM) sa_l[tid] = nsa;
+            sw_l[tid] = nsw;
+            b_l[tid] = bf16_bits_to_float(nb);
+        }
+        wait_vm_lgkm0<0>();  // the next tile's stage 0 (and this tile's stores) are done ...
+        __syncthreads();     // ... for every wave, and the staging area is free
+        for (int s = 1; s < NST; ++s)
+            if (s < KT) stage_load<BM, BK>(c, s * BK, smem + s * G::STAGE);
+        t = t_next;
+        m0 = m0n;
+        n0 = n0n;
     }
 }
 
@@ -453,13 +536,38 @@ void gemm_i8_tiled(const int8_t* __restrict__ qa, const float* __restrict__ sa, 
 #define W8A8_NST 2
 #endif
 
+// Compute units of the current device, queried once per device.
+int cu_count() {
+    constexpr int kMaxDevices = 64;
+    static std::atomic<int> cached[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return -1;
+    if (dev < kMaxDevices) {
+        const int v = cached[dev].load(std::memory_order_relaxed);
+        if (v > 0) return v;
+    }
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+        return -1;
+    if (dev < kMaxDevices) cached[dev].store(cus, std::memory_order_relaxed);
+    return cus;
+}
+
 template <int OUT_I32, int ACT>
 hipError_t launch_large(const int8_t* qa, const float* sa, int64_t M, const int8_t* qw,
                         const float* sw, int64_t N, int64_t K, const uint16_t* bias, void* out,
                         hipStream_t stream) {
     const int64_t tiles = ((N + L_BN - 1) / L_BN) * ((M + W8A8_BM - 1) / W8A8_BM);
-    hipLaunchKernelGGL((gemm_i8_tiled<W8A8_BM, W8A8_BK, W8A8_NST, OUT_I32, ACT>),
-                       dim3((unsigned)tiles), dim3(THREADS), 0, stream, qa, sa, M, qw, sw, N, K, bias,
+    constexpr bool persist = ACT == 0;
+    int64_t grid = tiles;
+    if (persist) {
+        const int cus = cu_count();
+        if (cus <= 0) return hipErrorInvalidDevice;
+        grid = tiles < cus ? tiles : cus;
+    }
+    hipLaunchKernelGGL((gemm_i8_tiled<W8A8_BM, W8A8_BK, W8A8_NST, OUT_I32, ACT, persist>),
+                       dim3((unsigned)grid), dim3(THREADS), 0, stream, qa, sa, M, qw, sw, N, K, bias,
                        out);
     return hipGetLastError();
 }
