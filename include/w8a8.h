@@ -80,12 +80,23 @@ W8A8_API int w8a8_quantize_rows(const uint16_t* x, int64_t rows, int64_t cols, i
  *   y     [rows x cols] bf16 pre-activation
  *   q     [rows x cols] int8 codes of h, scale [rows] fp32
  *
- * h = GELU-tanh(y) correctly rounded to bf16 (the same value w8a8_gemm's
+ * h = GELU-tanh(y) rounded to bf16 (the same value w8a8_gemm's
  * W8A8_ACT_GELU_TANH epilogue produces), then exactly w8a8_quantize_rows(h).
  * h itself is not written.  Same alignment rules as w8a8_quantize_rows.
  */
 W8A8_API int w8a8_gelu_quantize_rows(const uint16_t* y, int64_t rows, int64_t cols, int8_t* q,
                                      float* scale, void* stream);
+
+/*
+ * Elementwise GELU-tanh on bf16 values: the activation between the halves of
+ * an FFN, on its own.
+ *
+ *   x [n] bf16 in, y [n] bf16 out (2-byte aligned, not overlapping)
+ *
+ * y[i] = g(x[i]) rounded to bf16 exactly as the W8A8_ACT_GELU_TANH epilogue of
+ * w8a8_gemm does (one table lookup per element).
+ */
+W8A8_API int w8a8_gelu_bf16(const uint16_t* x, int64_t n, uint16_t* y, void* stream);
 
 /*
  * INT8 GEMM with INT32 accumulation and the epilogue after full accumulation
@@ -99,8 +110,10 @@ W8A8_API int w8a8_gelu_quantize_rows(const uint16_t* y, int64_t rows, int64_t co
  *                  (no bias: bf16_RNE(float(acc) * RN32(sa[i]*sw[j])));
  *                  act == W8A8_ACT_GELU_TANH then applies
  *                  g(z) = z/2 (1 + tanh(sqrt(2/pi)(z + 0.044715 z^3))) to the bf16 y
- *                  and rounds g(y) correctly to bf16 (round to nearest even of the
- *                  exact value).
+ *                  and rounds g(y) once to bf16 from its binary64 value (round to
+ *                  nearest even).  That is the correctly rounded value except for
+ *                  |y| < 2^-125, where the binary64 value is the exact midpoint
+ *                  y/2 and goes to the even neighbour.
  *                out_kind == W8A8_OUT_I32 -> the raw int32 accumulator
  *                  acc[i][j] = sum_k qa[i][k]*qw[j][k] (act must be NONE; sa, sw,
  *                  bias are ignored and may be NULL).
@@ -132,8 +145,8 @@ W8A8_API int w8a8_linear(const uint16_t* x, int64_t M, int64_t K, int64_t N, con
  * Native BF16 linear, the fallback of the guarded layer (section 01.3: branches
  * the optimised operator cannot serve run in native BF16):
  *   y = bf16_RNE(sum_k x[i][k] w[j][k] + b[j]) with fp32 accumulation, optional
- *   GELU-tanh as in w8a8_gemm.  Any M, N, K >= 0; x, w, y need 4-byte alignment
- *   only (rows of odd-multiple-of-2 K such as 2050 are allowed).
+ *   GELU-tanh as in w8a8_gemm.  Any M, N, K >= 0; x, w, y, bias need 2-byte
+ *   alignment only (rows of any K, e.g. 2050, are allowed).
  */
 W8A8_API int w8a8_linear_bf16(const uint16_t* x, int64_t M, int64_t K, const uint16_t* w, int64_t N,
                      const uint16_t* bias, int act, uint16_t* y, void* stream);

@@ -28,7 +28,7 @@ ACT_NONE, ACT_GELU_TANH = 0, 1
 PATH_INT8, PATH_BF16 = 0, 1
 MAX_K = 131072
 
-EXPORTS = ("w8a8_quantize_rows", "w8a8_gelu_quantize_rows", "w8a8_gemm", "w8a8_linear", "w8a8_linear_bf16",
+EXPORTS = ("w8a8_quantize_rows", "w8a8_gelu_quantize_rows", "w8a8_gelu_bf16", "w8a8_gemm", "w8a8_linear", "w8a8_linear_bf16",
            "compact_padded_rows", "w8a8_guard", "w8a8_linear_workspace_bytes",
            "w8a8_status_str")
 
@@ -53,6 +53,7 @@ def lib():
     P, I64, I, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
     L.w8a8_quantize_rows.argtypes = [P, I64, I64, P, P, P]
     L.w8a8_gelu_quantize_rows.argtypes = [P, I64, I64, P, P, P]
+    L.w8a8_gelu_bf16.argtypes = [P, I64, P, P]
     L.w8a8_gemm.argtypes = [P, P, I64, P, P, I64, I64, P, I, I, P, P]
     L.w8a8_linear.argtypes = [P, I64, I64, I64, P, P, P, P, I, P, P, SZ, P, P]
     L.w8a8_linear_bf16.argtypes = [P, I64, I64, P, I64, P, I, P, P]
@@ -140,7 +141,7 @@ def quantize_rows(x: torch.Tensor, q: Optional[torch.Tensor] = None,
 
 def gelu_quantize_rows(y: torch.Tensor, q: Optional[torch.Tensor] = None,
                        scale: Optional[torch.Tensor] = None, stream=None):
-    """h = GELU-tanh(y) (correctly rounded to bf16), then per-row INT8 quantisation of h:
+    """h = GELU-tanh(y) (rounded to bf16 as the GELU epilogue), then per-row INT8 quantisation of h:
     y bf16 [R, C] -> (q int8 [R, C], scale fp32 [R]).  h is not materialised."""
     _need(y, "y", torch.bfloat16)
     if y.dim() != 2:
@@ -153,6 +154,15 @@ def gelu_quantize_rows(y: torch.Tensor, q: Optional[torch.Tensor] = None,
     _check("w8a8_gelu_quantize_rows",
            lib().w8a8_gelu_quantize_rows(_p(y), R, C, _p(q), _p(scale), _stream(stream)))
     return q, scale
+
+
+def gelu_bf16(x: torch.Tensor, y: Optional[torch.Tensor] = None, stream=None):
+    """Elementwise GELU-tanh on bf16: y = g(x) rounded to bf16, as the GELU epilogue."""
+    _need(x, "x", torch.bfloat16)
+    y = y if y is not None else torch.empty_like(x)
+    _need(y, "y", torch.bfloat16, tuple(x.shape))
+    _check("w8a8_gelu_bf16", lib().w8a8_gelu_bf16(_p(x), x.numel(), _p(y), _stream(stream)))
+    return y
 
 
 def gemm(qa, sa, qw, sw, bias=None, act=ACT_NONE, out_kind=OUT_BF16, out=None, stream=None):

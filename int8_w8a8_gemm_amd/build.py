@@ -3,7 +3,8 @@
     python -m int8_w8a8_gemm_amd.build
 
 Each source compiles to its own object under ``_build/``; the shared library
-is linked into this package directory.  Flags: gfx950 only, -O3, no floating
+is linked into this package directory.  The GELU lookup table is generated
+first, by a host program (csrc/gen_gelu_table.c, gcc + libquadmath).  Flags: gfx950 only, -O3, no floating
 point contraction (the epilogue spells out its one fma), and packed-fp32
 instructions disabled.
 """
@@ -27,7 +28,7 @@ PROBE_LIB = os.path.join(HERE, "libw8a8_probe.so")
 ARCH = "gfx950"
 FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-ffp-contract=off",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-         "-Wall", "-Wno-unused-command-line-argument", f"-I{INCLUDE}"]
+         "-Wall", "-Wno-unused-command-line-argument", f"-I{INCLUDE}", f"-I{BUILD}"]
 
 
 def _hipcc():
@@ -47,9 +48,19 @@ def _run(cmd):
     return err
 
 
+def _gelu_table():
+    """Generates _build/gelu_table.inc (the bf16 GELU table) with the host
+    compiler; the generator fails if any entry's rounding is not certain."""
+    gen = os.path.join(BUILD, "gen_gelu_table")
+    _run(["gcc", "-O2", "-std=c11", "-Wall", os.path.join(CSRC, "gen_gelu_table.c"), "-o", gen,
+          "-lquadmath", "-lm"])
+    _run([gen, os.path.join(BUILD, "gelu_table.inc")])
+
+
 def build(verbose: bool = False, jobs: int = 5) -> str:
     os.makedirs(BUILD, exist_ok=True)
     hipcc = _hipcc()
+    _gelu_table()
 
     def compile_one(src):
         obj = os.path.join(BUILD, src.replace(".hip", ".o"))

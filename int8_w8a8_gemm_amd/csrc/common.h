@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace w8a8 {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
@@ -25,7 +27,9 @@ __device__ __forceinline__ uint32_t float_to_bf16_bits(float f) {
 }
 
 // GELU, tanh approximation, g(z) = z/2 (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3))),
-// evaluated on a bf16 input and correctly rounded to bf16.
+// evaluated on a bf16 input and rounded once to bf16 from its binary64 value:
+// the correctly rounded result, except for |z| < 2^-125, where the binary64
+// value is the exact midpoint z/2 and the tie goes to even.
 //
 // 1 + tanh(u) = 2 / (1 + exp(-2u)), so g(z) = z / (1 + 2^w) with
 // w = -2 log2(e) sqrt(2/pi) (z + 0.044715 z^3), which keeps relative accuracy
@@ -89,6 +93,24 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 // Host-side launchers (defined in the .hip files, called by the C-ABI layer).
 namespace w8a8 {
+// Compute units of the current device, queried once per device (-1 on error).
+inline int cu_count() {
+    constexpr int kMaxDevices = 64;
+    static std::atomic<int> cached[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return -1;
+    if (dev < kMaxDevices) {
+        const int v = cached[dev].load(std::memory_order_relaxed);
+        if (v > 0) return v;
+    }
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+        return -1;
+    if (dev < kMaxDevices) cached[dev].store(cus, std::memory_order_relaxed);
+    return cus;
+}
+int launch_gelu_bf16(const uint16_t* x, int64_t n, uint16_t* y, hipStream_t stream);
 int launch_quantize_rows(const uint16_t* x, int64_t rows, int64_t cols, int8_t* q, float* scale,
                          hipStream_t stream, bool gelu = false);
 int launch_compact_rows(const uint16_t* x, const uint8_t* mask, int64_t R, int64_t D,

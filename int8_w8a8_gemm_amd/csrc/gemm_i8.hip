@@ -11,8 +11,6 @@
 // A/B operands want: every lane feeds 16 consecutive K bytes of one row.
 #include "common.h"
 
-#include <atomic>
-
 namespace w8a8 {
 
 namespace {
@@ -347,7 +345,7 @@ __device__ __forceinline__ void store_bf16(const v16i (&acc)[4][BM / WM / 32], u
                 }
                 uint2 o = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
                 if (ACT == 1) {
-                    // GELU-tanh on the bf16-rounded value, correctly rounded to bf16
+                    // GELU-tanh of the bf16-rounded value, rounded to bf16 (gelu_bf16_rn)
                     o = make_uint2(gelu_bf16_rn(o.x & 0xffffu) | (gelu_bf16_rn(o.x >> 16) << 16),
                                    gelu_bf16_rn(o.y & 0xffffu) | (gelu_bf16_rn(o.y >> 16) << 16));
                 }
@@ -535,24 +533,6 @@ void gemm_i8_tiled(const int8_t* __restrict__ qa, const float* __restrict__ sa, 
 #ifndef W8A8_NST
 #define W8A8_NST 2
 #endif
-
-// Compute units of the current device, queried once per device.
-int cu_count() {
-    constexpr int kMaxDevices = 64;
-    static std::atomic<int> cached[kMaxDevices];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return -1;
-    if (dev < kMaxDevices) {
-        const int v = cached[dev].load(std::memory_order_relaxed);
-        if (v > 0) return v;
-    }
-    int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        cus <= 0)
-        return -1;
-    if (dev < kMaxDevices) cached[dev].store(cus, std::memory_order_relaxed);
-    return cus;
-}
 
 template <int OUT_I32, int ACT>
 hipError_t launch_large(const int8_t* qa, const float* sa, int64_t M, const int8_t* qw,

@@ -7,9 +7,13 @@
 //     q = RNE(RN32(x * inv)) clamped to [-127, 127],
 // and rows with a < 2^-100 get scale 0 and all-zero codes.
 //
-// The GELU variant quantises h = GELU-tanh(x) (correctly rounded to bf16) in
-// the same pass: the input of an FFN down projection, straight from the
-// up projection's bf16 output, without writing h to memory.
+// The GELU variant quantises h = GELU-tanh(x) (rounded once to bf16 from its
+// binary64 value) in the same pass: the input of an FFN down projection,
+// straight from the up projection's bf16 output, without writing h to memory.
+// Large inputs take a table-driven kernel: GELU of a bf16 input has only 65536
+// possible values, so a 128 KB table (built with the library, see
+// gen_gelu_table.c) sits in each CU's LDS and GELU becomes one LDS lookup per
+// element instead of ~20 VALU instructions; that kernel is HBM-bound.
 //
 // The kernel is HBM-bound (2 bytes read + 1 byte written per element).  The
 // vector path keeps a whole row in registers so each element is read from HBM
@@ -25,6 +29,12 @@ namespace {
 
 constexpr int kBlock = 256;  // 4 waves
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// GELU-tanh of every bf16 bit pattern, as bf16 bits (generated at build time).
+__device__ __attribute__((aligned(16))) const uint16_t kGeluTable[65536] = {
+#include "gelu_table.inc"
+};
 
 __device__ __forceinline__ uint32_t absmax_bits(u32x4 v) {
     // Each dword holds two bf16; clear both sign bits and take the packed
@@ -74,6 +84,51 @@ __device__ __forceinline__ u32x4 gelu8(u32x4 v) {
     for (int i = 0; i < 4; ++i)
         o[i] = gelu_bf16_rn(v[i] & 0xffffu) | (gelu_bf16_rn(v[i] >> 16) << 16);
     return o;
+}
+
+// 8 bf16 (one chunk) -> 8 int8, without the clamp of quant1: for |x| <= a,
+// |x * RN(127/a)| <= 127 (1 + 2^-24) rounds to at most 127, so the clamp never
+// acts.  rint(x * inv) + 128 lies in [1, 255] and v_cvt_pk_u8_f32 packs it
+// exactly; flipping bit 7 of each byte gives the two's complement code.
+__device__ __forceinline__ uint2 quant8_pk(u32x4 v, float inv) {
+    uint32_t o[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const uint32_t w0 = v[2 * h], w1 = v[2 * h + 1];
+        uint32_t r = __builtin_amdgcn_cvt_pk_u8_f32(
+            __builtin_rintf(__fmul_rn(__uint_as_float(w0 << 16), inv)) + 128.0f, 0, 0);
+        r = __builtin_amdgcn_cvt_pk_u8_f32(
+            __builtin_rintf(__fmul_rn(__uint_as_float(w0 & 0xffff0000u), inv)) + 128.0f, 1, r);
+        r = __builtin_amdgcn_cvt_pk_u8_f32(
+            __builtin_rintf(__fmul_rn(__uint_as_float(w1 << 16), inv)) + 128.0f, 2, r);
+        r = __builtin_amdgcn_cvt_pk_u8_f32(
+            __builtin_rintf(__fmul_rn(__uint_as_float(w1 & 0xffff0000u), inv)) + 128.0f, 3, r);
+        o[h] = r ^ 0x80808080u;
+    }
+    return make_uint2(o[0], o[1]);
+}
+
+// GELU of the 8 bf16 of one chunk by table lookup (lut: the table in LDS).
+__device__ __forceinline__ u32x4 gelu8_lut(u32x4 v, const uint16_t* lut) {
+    u32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        u16x2 p;
+        p.x = lut[v[i] & 0xffffu];
+        p.y = lut[v[i] >> 16];
+        o[i] = __builtin_bit_cast(uint32_t, p);
+    }
+    return o;
+}
+
+// Workgroup barrier for LDS only: global loads in flight (the next rows'
+// prefetch) stay in flight.  The empty asm statements keep the compiler from
+// moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt, expcnt left free
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 }
 
 // WPR waves cooperate on one row; each lane holds CPL 16-byte chunks.  Serves
@@ -173,6 +228,110 @@ __global__ __launch_bounds__(kBlock) void quantize_rows_generic(const uint16_t* 
     }
 }
 
+// Table-driven GELU + quantise.  One 16-wave workgroup per CU copies the GELU
+// table into LDS once and then walks row groups (16/WPR rows at a time, WPR
+// waves per row as in quantize_rows_vec); the chunks of the next row group
+// are loaded while the current one is processed.  Same constraints as
+// quantize_rows_vec.
+constexpr int kLutBlock = 1024;
+constexpr int kLutWaves = kLutBlock / 64;
+
+template <int WPR, int CPL>
+__global__ __launch_bounds__(kLutBlock) void gelu_quantize_rows_lut(const uint16_t* __restrict__ x,
+                                                                   int64_t rows, int64_t cols,
+                                                                   int8_t* __restrict__ q,
+                                                                   float* __restrict__ scale) {
+    constexpr int RPB = kLutWaves / WPR;  // rows per workgroup per step
+    __shared__ __attribute__((aligned(16))) uint16_t lut[65536];
+    __shared__ uint32_t red[2][kLutWaves];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wr = wave % WPR, w0 = wave - wr;
+    const int64_t nchunk = cols >> 3;
+    const int64_t step = (int64_t)gridDim.x * RPB;
+
+    auto load_row = [&](int64_t row, u32x4 (&v)[CPL]) {
+        const bool live = row < rows;
+        const u32x4* xr = reinterpret_cast<const u32x4*>(x + (live ? row : 0) * cols);
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            const int64_t ch = (int64_t)(c * WPR + wr) * 64 + lane;
+            v[c] = (live && ch < nchunk) ? __builtin_nontemporal_load(xr + ch)
+                                          : (u32x4){0u, 0u, 0u, 0u};
+        }
+    };
+
+    int64_t row = (int64_t)blockIdx.x * RPB + wave / WPR;
+    u32x4 v[CPL];
+    load_row(row, v);
+    {
+        const u32x4* src = reinterpret_cast<const u32x4*>(kGeluTable);
+        u32x4* dst = reinterpret_cast<u32x4*>(lut);
+        for (int i = threadIdx.x; i < 65536 / 8; i += kLutBlock) dst[i] = src[i];
+    }
+    __syncthreads();
+
+    int it = 0;
+    for (int64_t base = (int64_t)blockIdx.x * RPB; base < rows; base += step, ++it) {
+        u32x4 nv[CPL];
+        load_row(row + step, nv);
+        uint32_t amax = 0;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            v[c] = gelu8_lut(v[c], lut);
+            amax = max(amax, absmax_bits(v[c]));
+        }
+        amax = wave_max_u32(amax);
+        if (WPR > 1) {
+            // red[it & 1]: a wave rewrites its slot two steps later, after the
+            // barrier of the step in between, so no reader is still using it
+            if (lane == 0) red[it & 1][wave] = amax;
+            lds_barrier();
+#pragma unroll
+            for (int i = 0; i < WPR; ++i) amax = max(amax, red[it & 1][w0 + i]);
+        }
+        if (row < rows) {
+            const float a = __uint_as_float(amax << 16);
+            int8_t* qr = q + row * cols;
+            const bool zero = !(a >= 0x1p-100f);
+            const float inv = zero ? 0.0f : __fdiv_rn(127.0f, a);
+            if (wr == 0 && lane == 0) scale[row] = zero ? 0.0f : __fdiv_rn(a, 127.0f);
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) {
+                const int64_t ch = (int64_t)(c * WPR + wr) * 64 + lane;
+                if (ch < nchunk) {
+                    const uint2 o = zero ? make_uint2(0, 0) : quant8_pk(v[c], inv);
+                    __builtin_nontemporal_store(o.x, reinterpret_cast<uint32_t*>(qr) + 2 * ch);
+                    __builtin_nontemporal_store(o.y, reinterpret_cast<uint32_t*>(qr) + 2 * ch + 1);
+                }
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) v[c] = nv[c];
+        row += step;
+    }
+}
+
+// Elementwise GELU by table lookup (the table is read through the caches).
+__global__ __launch_bounds__(kBlock) void gelu_bf16_kernel(const uint16_t* __restrict__ x, int64_t n,
+                                                           uint16_t* __restrict__ y) {
+    const int64_t stride = (int64_t)gridDim.x * kBlock;
+    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n; i += stride)
+        y[i] = kGeluTable[x[i]];
+}
+
+template <int WPR, int CPL>
+hipError_t launch_lut(const uint16_t* x, int64_t rows, int64_t cols, int8_t* q, float* scale,
+                      hipStream_t stream) {
+    constexpr int RPB = kLutWaves / WPR;
+    const int cus = cu_count();
+    if (cus <= 0) return hipErrorInvalidDevice;
+    const int64_t groups = (rows + RPB - 1) / RPB;
+    const int64_t grid = groups < cus ? groups : cus;
+    hipLaunchKernelGGL((gelu_quantize_rows_lut<WPR, CPL>), dim3((unsigned)grid), dim3(kLutBlock), 0,
+                       stream, x, rows, cols, q, scale);
+    return hipGetLastError();
+}
+
 template <int WPR, int CPL>
 hipError_t launch_vec(const uint16_t* x, int64_t rows, int64_t cols, int8_t* q, float* scale,
                       hipStream_t stream, bool gelu) {
@@ -196,6 +355,15 @@ int launch_quantize_rows(const uint16_t* x, int64_t rows, int64_t cols, int8_t* 
                      (reinterpret_cast<uintptr_t>(q) % 8 == 0) && cols > 0;
     const int64_t nchunk = cols / 8;
     hipError_t e;
+    // the table kernel pays a 128 KB table copy per CU: worth it from about
+    // 2^24 elements on
+    if (gelu && vec && rows * cols >= ((int64_t)1 << 24) && nchunk <= 4096) {
+        if (nchunk <= 512) e = launch_lut<1, 8>(x, rows, cols, q, scale, stream);
+        else if (nchunk <= 1024) e = launch_lut<2, 8>(x, rows, cols, q, scale, stream);
+        else if (nchunk <= 2048) e = launch_lut<4, 8>(x, rows, cols, q, scale, stream);
+        else e = launch_lut<8, 8>(x, rows, cols, q, scale, stream);
+        return e == hipSuccess ? 0 : -1;
+    }
     if (vec && nchunk <= 64) e = launch_vec<1, 1>(x, rows, cols, q, scale, stream, gelu);
     else if (vec && nchunk <= 128) e = launch_vec<1, 2>(x, rows, cols, q, scale, stream, gelu);
     else if (vec && nchunk <= 256) e = launch_vec<1, 4>(x, rows, cols, q, scale, stream, gelu);
@@ -213,6 +381,14 @@ int launch_quantize_rows(const uint16_t* x, int64_t rows, int64_t cols, int8_t* 
         e = hipGetLastError();
     }
     return e == hipSuccess ? 0 : -1;
+}
+
+int launch_gelu_bf16(const uint16_t* x, int64_t n, uint16_t* y, hipStream_t stream) {
+    if (n == 0) return 0;
+    const int64_t blocks = (n + kBlock - 1) / kBlock;
+    const int64_t grid = blocks < 65536 ? blocks : 65536;
+    hipLaunchKernelGGL(gelu_bf16_kernel, dim3((unsigned)grid), dim3(kBlock), 0, stream, x, n, y);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 }  // namespace w8a8

@@ -59,6 +59,13 @@ int w8a8_gelu_quantize_rows(const uint16_t* y, int64_t rows, int64_t cols, int8_
     return launched(w8a8::launch_quantize_rows(y, rows, cols, q, scale, as_stream(stream), true));
 }
 
+int w8a8_gelu_bf16(const uint16_t* x, int64_t n, uint16_t* y, void* stream) {
+    if (n < 0) return W8A8_EINVAL;
+    if (n == 0) return W8A8_OK;
+    if (!x || !y || !aligned(x, 2) || !aligned(y, 2)) return W8A8_EINVAL;
+    return launched(w8a8::launch_gelu_bf16(x, n, y, as_stream(stream)));
+}
+
 int w8a8_gemm(const int8_t* qa, const float* sa, int64_t M, const int8_t* qw, const float* sw,
               int64_t N, int64_t K, const uint16_t* bias, int act, int out_kind, void* out,
               void* stream) {

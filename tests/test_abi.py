@@ -81,6 +81,16 @@ def test_quantize_rows_rejects_bad_arguments():
     assert L.w8a8_quantize_rows(NULL, 0, 8, NULL, NULL, NULL) == w8.OK  # empty: no-op
 
 
+def test_gelu_bf16_rejects_bad_arguments():
+    L = w8.lib()
+    assert L.w8a8_gelu_bf16(A16, -1, A16b, NULL) == w8.EINVAL
+    assert L.w8a8_gelu_bf16(NULL, 8, A16b, NULL) == w8.EINVAL
+    assert L.w8a8_gelu_bf16(A16, 8, NULL, NULL) == w8.EINVAL
+    assert L.w8a8_gelu_bf16(MIS, 8, A16b, NULL) == w8.EINVAL
+    assert L.w8a8_gelu_bf16(A16, 8, MIS, NULL) == w8.EINVAL
+    assert L.w8a8_gelu_bf16(NULL, 0, NULL, NULL) == w8.OK  # empty: no-op
+
+
 def test_gemm_rejects_bad_arguments_and_unsupported_shapes():
     L = w8.lib()
     g = lambda qa, sa, M, qw, sw, N, K, b, act, kind, out: L.w8a8_gemm(
