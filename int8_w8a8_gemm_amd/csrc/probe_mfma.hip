@@ -31,9 +31,11 @@ __global__ __launch_bounds__(256) void mfma_loop(const v4i* __restrict__ ops, in
     const long long t0 = __builtin_readcyclecounter();
     const long long r0 = __builtin_amdgcn_s_memrealtime();
     for (int it = 0; it < iters; ++it) {
+        // operand registers chosen at compile time: consecutive MFMAs see
+        // different data, and no instruction between them rewrites an operand
 #pragma unroll
         for (int j = 0; j < 8; ++j)
-            c[j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[j & 3], b[(j + it) & 3], c[j], 0, 0, 0);
+            c[j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[j & 3], b[(j >> 1) & 3], c[j], 0, 0, 0);
     }
     const long long t1 = __builtin_readcyclecounter();
     const long long r1 = __builtin_amdgcn_s_memrealtime();
