@@ -127,8 +127,16 @@ def test_quantize_empty_rows_is_noop():
 # INT8 GEMM: int32 accumulator and bf16 epilogue
 # ---------------------------------------------------------------------------
 
+# On a 256-CU MI355X the launcher takes 256 x 256 tiles when there are at
+# least 128 of them, else 128 x 128 tiles when there are at least 128 of those,
+# else 64 x 64 tiles; a persistent 256 x 256 workgroup takes several tiles when
+# there are more than 256.  Covered here: 64 x 64 tiles (the first seven shapes),
+# 128 x 128 tiles (2048^3 and 2000 x 1984, ragged), 256 x 256 tiles with ragged
+# M, with ragged N, and with both (4100 x 4096, 4096 x 4160, 3900 x 3776; the
+# first two with workgroups taking two tiles).
 GEMM_SHAPES = [(1, 64, 128), (64, 128, 256), (129, 192, 384), (300, 320, 1024), (257, 64, 4096),
-               (1000, 448, 2048), (33, 256, 16384), (2048, 2048, 2048)]
+               (1000, 448, 2048), (33, 256, 16384), (2048, 2048, 2048), (2000, 1984, 512),
+               (4100, 4096, 256), (4096, 4160, 128), (3900, 3776, 128)]
 
 
 @pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
@@ -152,7 +160,8 @@ def test_gemm_int32_extremes_and_max_k():
     assert np.all(acc[0::2] == 16129 * K) and np.all(acc[1::2] == -16129 * K)
 
 
-@pytest.mark.parametrize("M,N,K", [(64, 128, 256), (129, 192, 384), (2048, 2048, 2048)])
+@pytest.mark.parametrize("M,N,K", [(64, 128, 256), (129, 192, 384), (2048, 2048, 2048),
+                                   (2000, 1984, 512), (4100, 4160, 128), (3900, 3776, 128)])
 @pytest.mark.parametrize("act", [w8.ACT_NONE, w8.ACT_GELU_TANH])
 @pytest.mark.parametrize("with_bias", [True, False])
 def test_gemm_epilogue_matches_oracle(M, N, K, act, with_bias):
