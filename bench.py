@@ -33,7 +33,7 @@ PEAK_INT8_TOPS = 5000.0   # MI355X dense INT8 MFMA, 5.0 POP/s
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense BF16 MFMA
 PEAK_HBM_GBS = 8000.0     # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_i8_video_ffn.json")
-GEMM_SOURCE = os.path.join(ROOT, "int8_w8a8_gemm_amd", "csrc", "gemm_i8.hip")
+GEMM_SOURCE = os.path.join(ROOT, "int8_w8a8_gemm_amd", "csrc", "gemm_tiled.hip")
 
 
 def log(*a):

@@ -21,7 +21,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libw8a8.so")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 
-SOURCES = ["quantize_rows.hip", "compact_rows.hip", "gemm_i8.hip", "gemm_bf16.hip", "w8a8_api.hip"]
+SOURCES = ["quantize_rows.hip", "compact_rows.hip", "gemm_tiled.hip", "gemm_bf16.hip", "w8a8_api.hip"]
 # measurement probe, a library of its own (not part of libw8a8's ABI)
 PROBE_SOURCES = ["probe_mfma.hip"]
 PROBE_LIB = os.path.join(HERE, "libw8a8_probe.so")

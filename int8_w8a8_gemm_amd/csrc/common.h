@@ -120,4 +120,8 @@ int launch_gemm_i8(const int8_t* qa, const float* sa, int64_t M, const int8_t* q
                    int out_kind, void* out, hipStream_t stream);
 int launch_gemm_bf16(const uint16_t* x, int64_t M, int64_t K, const uint16_t* w, int64_t N,
                      const uint16_t* bias, int act, uint16_t* y, hipStream_t stream);
+// The tiled MFMA path for BF16 operands (gemm_tiled.hip) and the shapes it serves.
+bool gemm_bf16_tiled_ok(const uint16_t* x, int64_t K, const uint16_t* w);
+int launch_gemm_bf16_tiled(const uint16_t* x, int64_t M, int64_t K, const uint16_t* w, int64_t N,
+                           const uint16_t* bias, int act, uint16_t* y, hipStream_t stream);
 }  // namespace w8a8

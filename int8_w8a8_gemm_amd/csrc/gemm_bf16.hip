@@ -3,9 +3,12 @@
 // TurboT2VA (智猩猩 article, section 01.3 "量化策略"): branches whose matrix
 // shapes the optimised INT8 operator cannot serve run in native BF16.
 //     y[i][j] = bf16_RNE(sum_k x[i][k] * w[j][k] + b[j])
-// with fp32 accumulation on v_mfma_f32_16x16x32_bf16 and an optional
-// GELU-tanh on the bf16 result.  Every edge is masked: any M, N, K, and rows
-// that are only 4-byte aligned (K = 2050) are read with 4-byte loads.
+// with fp32 accumulation and an optional GELU-tanh on the bf16 result.
+// Operands with K % 64 == 0 and 16-byte aligned rows take the tiled MFMA
+// kernel shared with the INT8 path (gemm_tiled.hip, any M and N).  Everything
+// else takes the kernel below: v_mfma_f32_16x16x32_bf16 on 128 x 128 tiles
+// with every edge masked (any M, N, K), rows that are only 4-byte aligned
+// (K = 2050) read with 4-byte loads and 2-byte aligned ones element by element.
 #include "common.h"
 
 namespace w8a8 {
@@ -117,6 +120,7 @@ hipError_t launch(const uint16_t* x, int64_t M, int64_t K, const uint16_t* w, in
 int launch_gemm_bf16(const uint16_t* x, int64_t M, int64_t K, const uint16_t* w, int64_t N,
                      const uint16_t* bias, int act, uint16_t* y, hipStream_t stream) {
     if (M == 0 || N == 0) return 0;
+    if (gemm_bf16_tiled_ok(x, K, w)) return launch_gemm_bf16_tiled(x, M, K, w, N, bias, act, y, stream);
     const bool pairs = (K % 2 == 0) && (reinterpret_cast<uintptr_t>(x) % 4 == 0) &&
                        (reinterpret_cast<uintptr_t>(w) % 4 == 0);
     hipError_t e;

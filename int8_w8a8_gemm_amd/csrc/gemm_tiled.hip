@@ -1,14 +1,22 @@
-// INT8 x INT8 -> INT32 GEMM with the once-after-accumulation epilogue, gfx950.
+// Tiled MFMA GEMM for gfx950: the INT8 W8A8 product and the native BF16
+// fallback of the guarded layer share one kernel.
 //
 // TurboT2VA (智猩猩 article, section 01.3 "量化策略"): the W8A8 product is
 // accumulated in INT32 and the scales and bias are applied once, after the
-// whole accumulation, never per K block.  Here
+// whole accumulation, never per K block; branches the INT8 operator cannot
+// serve run in native BF16.  Here, for INT8 operands
 //     acc[i][j] = sum_k qa[i][k] * qw[j][k]              (exact int32)
 //     y[i][j]   = bf16_RNE(fma(float(acc), RN32(sa[i]*sw[j]), bias[j]))
-// with an optional GELU-tanh on the bf16 y, or the raw acc in int32 mode.
+// (or the raw acc in int32 mode), and for BF16 operands
+//     acc[i][j] = sum_k x[i][k] * w[j][k]                (fp32 accumulation)
+//     y[i][j]   = bf16_RNE(acc + bias[j])
+// each with an optional GELU-tanh on the bf16 y.
 //
-// Both operands are K-contiguous (qa [M x K], qw [N x K]), the layout the MFMA
+// Both operands are K-contiguous ([M x K] and [N x K]), the layout the MFMA
 // A/B operands want: every lane feeds 16 consecutive K bytes of one row.
+// v_mfma_i32_32x32x32_i8 (32 int8 of K per row) and v_mfma_f32_32x32x16_bf16
+// (16 bf16) take their operands in the same byte layout and issue in the same
+// 32 cycles, so the whole data path is shared and counts K in bytes.
 #include "common.h"
 
 namespace w8a8 {
@@ -16,10 +24,10 @@ namespace w8a8 {
 namespace {
 
 // ---------------------------------------------------------------------------
-// Tiled MFMA kernel.  A workgroup of WM x WN waves owns a BM x BN output tile;
-// wave (wm, wn) owns (BM/WM) x (BN/WN) outputs, i.e. MI x NI tiles of
-// v_mfma_i32_32x32x32_i8 held as int32 accumulators.  K is staged BK bytes at
-// a time through an NST-deep ring of LDS buffers.  Three configurations:
+// A workgroup of WM x WN waves owns a BM x BN output tile; wave (wm, wn) owns
+// (BM/WM) x (BN/WN) outputs, i.e. MI x NI tiles of 32 x 32 MFMA accumulators.
+// K is staged BK bytes at a time through an NST-deep ring of LDS buffers.
+// Three configurations:
 //   large: 256 x 256 tile, 4 x 2 waves (two per SIMD, so one wave's load issue,
 //          LDS waits and barrier arrival overlap the other's MFMAs), each wave
 //          64 x 128; the least operand traffic per MFMA.
@@ -58,6 +66,25 @@ constexpr int GROUP_ROWS = W8A8_GROUP_ROWS;
 
 typedef __attribute__((address_space(3))) void lds_void;
 
+// Operand element types.  mfma() takes 16 bytes of weight row (A operand) and
+// activation row (B operand) per lane and accumulates a 32 x 32 tile.
+struct ElemI8 {
+    static constexpr int BYTES = 1;
+    typedef v16i acc_t;
+    static __device__ __forceinline__ acc_t mfma(v4i w, v4i a, acc_t c) {
+        return __builtin_amdgcn_mfma_i32_32x32x32_i8(w, a, c, 0, 0, 0);
+    }
+};
+
+struct ElemBF16 {
+    static constexpr int BYTES = 2;
+    typedef v16f acc_t;
+    static __device__ __forceinline__ acc_t mfma(v4i w, v4i a, acc_t c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, w),
+                                                       __builtin_bit_cast(v8bf, a), c, 0, 0, 0);
+    }
+};
+
 template <int BM_, int BN_, int WM_, int WN_, int BK_, int NST_>
 struct Cfg {
     static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_, NST = NST_;
@@ -71,7 +98,7 @@ struct Cfg {
     static constexpr int CPR = BK / 16;                // 16-byte chunks per LDS row
     static constexpr int RPI = 64 / CPR;               // rows one 1-KB wave instruction fills
     static constexpr int STAGE = (BM + BN) * BK;       // bytes per stage (A tile then B tile)
-    static constexpr int SUB = BK / 32;                // 32-deep MFMA sub-steps per stage
+    static constexpr int SUB = BK / 32;                // 32-byte MFMA sub-steps per stage
     static constexpr int LPW_A = BM / WAVES / RPI;     // A load instructions per wave per stage
     static constexpr int LPW_B = BN / WAVES / RPI;     // B load instructions per wave per stage
     static constexpr int NLOAD = LPW_A + LPW_B;
@@ -138,7 +165,7 @@ constexpr int kRawBufferWord3 = 0x00020000;  // untyped 32-bit buffer access
 // at the tile's first row and sized to the rows that exist, so rows past M
 // (or N) read as zero.  Every lane keeps fixed byte offsets for its loads; the
 // K position of a stage goes in the scalar offset, so issuing a stage's loads
-// writes no vector registers.
+// writes no vector registers.  KB is the row length in bytes.
 template <class C>
 struct Ctx {
     rsrc_t rsrc[2];  // 0: activation panel, 1: weight panel
@@ -150,31 +177,31 @@ struct Ctx {
 // Points the context's buffer resources at the operand panels of the tile
 // whose first output row is m0 and first output column n0.
 template <class C>
-__device__ __forceinline__ void set_tile(Ctx<C>& c, const int8_t* qa, const int8_t* qw, int64_t M,
-                                         int64_t N, int64_t K, int64_t m0, int64_t n0) {
+__device__ __forceinline__ void set_tile(Ctx<C>& c, const char* a, const char* w, int64_t M,
+                                         int64_t N, int64_t KB, int64_t m0, int64_t n0) {
 #if defined(__HIP_DEVICE_COMPILE__)
     const int64_t rows_a = (M - m0) < C::BM ? (M - m0) : C::BM;
     const int64_t rows_w = (N - n0) < C::BN ? (N - n0) : C::BN;
-    c.rsrc[0] = __builtin_amdgcn_make_buffer_rsrc((void*)(qa + m0 * K), (short)0,
-                                                  (int)(rows_a * K), kRawBufferWord3);
-    c.rsrc[1] = __builtin_amdgcn_make_buffer_rsrc((void*)(qw + n0 * K), (short)0,
-                                                  (int)(rows_w * K), kRawBufferWord3);
+    c.rsrc[0] = __builtin_amdgcn_make_buffer_rsrc((void*)(a + m0 * KB), (short)0,
+                                                  (int)(rows_a * KB), kRawBufferWord3);
+    c.rsrc[1] = __builtin_amdgcn_make_buffer_rsrc((void*)(w + n0 * KB), (short)0,
+                                                  (int)(rows_w * KB), kRawBufferWord3);
 #endif
 }
 
 // Lane offsets are tile-local, so they are set once per workgroup.
 template <class C>
-__device__ __forceinline__ void make_ctx(Ctx<C>& c, int64_t K, int wave, int lane) {
+__device__ __forceinline__ void make_ctx(Ctx<C>& c, int64_t KB, int wave, int lane) {
     const int rsub = lane / C::CPR, pc = lane % C::CPR;
 #pragma unroll
     for (int i = 0; i < C::LPW_A; ++i) {
         const int r = wave * (C::BM / C::WAVES) + i * C::RPI + rsub;  // tile-local A row
-        c.voff_a[i] = (uint32_t)r * (uint32_t)K + 16u * (uint32_t)swz<C::BK>(r, pc);
+        c.voff_a[i] = (uint32_t)r * (uint32_t)KB + 16u * (uint32_t)swz<C::BK>(r, pc);
     }
 #pragma unroll
     for (int i = 0; i < C::LPW_B; ++i) {
         const int r = wave * (C::BN / C::WAVES) + i * C::RPI + rsub;  // tile-local B row
-        c.voff_b[i] = (uint32_t)r * (uint32_t)K + 16u * (uint32_t)swz<C::BK>(r, pc);
+        c.voff_b[i] = (uint32_t)r * (uint32_t)KB + 16u * (uint32_t)swz<C::BK>(r, pc);
     }
     c.wave = wave;
     c.lane = lane;
@@ -210,8 +237,8 @@ struct Frags {
     v4i w[C::NI];  // weight rows (MFMA A-operand), n sub-tiles
 };
 
-template <class C>
-using Acc = v16i[C::NI][C::MI];
+template <class C, class E>
+using Acc = typename E::acc_t[C::NI][C::MI];
 
 // Fragment q of sub-step ks: q < MI -> activation sub-tile q, else weight
 // sub-tile q - MI.  Lane l reads row l % 32 of the sub-tile at K-chunk 2*ks + l/32.
@@ -229,10 +256,10 @@ __device__ __forceinline__ void read_frag(const char* lds_stage, const Ctx<C>& c
     }
 }
 
-template <class C>
-__device__ __forceinline__ void mfma_one(Acc<C>& acc, const Frags<C>& f, int j) {
+template <class C, class E>
+__device__ __forceinline__ void mfma_one(Acc<C, E>& acc, const Frags<C>& f, int j) {
     const int ni = j / C::MI, mi = j % C::MI;
-    acc[ni][mi] = __builtin_amdgcn_mfma_i32_32x32x32_i8(f.w[ni], f.a[mi], acc[ni][mi], 0, 0, 0);
+    acc[ni][mi] = E::mfma(f.w[ni], f.a[mi], acc[ni][mi]);
 }
 
 // One K stage, held in ring buffer kt % NST.
@@ -242,8 +269,8 @@ __device__ __forceinline__ void mfma_one(Acc<C>& acc, const Frags<C>& f, int j) 
 // (one after each of the first NQ MFMAs; any left over after the last) and the
 // refill loads (spread evenly) placed between them; sched_barrier pins that
 // order.
-template <class C, bool LOAD, bool NEXT, bool STEADY>
-__device__ __forceinline__ void k_stage(const Ctx<C>& c, char* smem, int kt, Acc<C>& acc,
+template <class C, class E, bool LOAD, bool NEXT, bool STEADY>
+__device__ __forceinline__ void k_stage(const Ctx<C>& c, char* smem, int kt, Acc<C, E>& acc,
                                         Frags<C>& cur) {
     char* buf = smem + (kt % C::NST) * C::STAGE;
     Frags<C> nxt;
@@ -251,7 +278,7 @@ __device__ __forceinline__ void k_stage(const Ctx<C>& c, char* smem, int kt, Acc
     for (int ks = 0; ks + 1 < C::SUB; ++ks) {
 #pragma unroll
         for (int j = 0; j < C::NMFMA; ++j) {
-            mfma_one<C>(acc, cur, j);
+            mfma_one<C, E>(acc, cur, j);
             if (j < C::NQ) read_frag<C>(buf, c, ks + 1, j, nxt);
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -269,7 +296,7 @@ __device__ __forceinline__ void k_stage(const Ctx<C>& c, char* smem, int kt, Acc
     }
 #pragma unroll
     for (int j = 0; j < C::NMFMA; ++j) {
-        mfma_one<C>(acc, cur, j);
+        mfma_one<C, E>(acc, cur, j);
         if (NEXT && j < C::NQ) read_frag<C>(next_buf, c, 0, j, nxt);
         if (LOAD) {
             // loads (j * NLOAD / NMFMA) .. ((j+1) * NLOAD / NMFMA) - 1 go after MFMA j
@@ -318,9 +345,11 @@ __device__ __forceinline__ void tile_of(int64_t bid, int64_t tm, int64_t tn, int
 // (64 lanes x 16 bytes).  Staged rows are padded by 16 bytes: every LDS address
 // is a per-lane base plus a compile-time offset, and the 16-byte row reads are
 // free of bank conflicts.  `stage` must not overlap the K buffer that the next
-// tile's first stage is being loaded into.
-template <class C, int ACT, bool HAS_BIAS>
-__device__ __forceinline__ void store_bf16(const Acc<C>& acc, uint16_t* __restrict__ y, int64_t M,
+// tile's first stage is being loaded into.  VEC_OUT: y rows are 16-byte
+// aligned and N % 8 == 0, so every 16-byte chunk is stored whole; otherwise
+// chunks are stored element by element.
+template <class C, class E, int ACT, bool HAS_BIAS, bool VEC_OUT>
+__device__ __forceinline__ void store_bf16(const Acc<C, E>& acc, uint16_t* __restrict__ y, int64_t M,
                                            int64_t N, int64_t m0, int64_t n0, int wave, int wm,
                                            int wn, int lane, const float* sa_l, const float* sw_l,
                                            const float* b_l, char* stage) {
@@ -336,14 +365,15 @@ __device__ __forceinline__ void store_bf16(const Acc<C>& acc, uint16_t* __restri
     const int trow0 = (s0 / 32) * C::TM + (s0 % 32);
 #pragma unroll
     for (int p = 0; p < C::MI; ++p) {
-        const float sam = sa_l[wm * C::TM + p * 32 + (lane & 31)];
+        float sam = 0.f;
+        if constexpr (E::BYTES == 1) sam = sa_l[wm * C::TM + p * 32 + (lane & 31)];
 #pragma unroll
         for (int ni = 0; ni < C::NI; ++ni) {
             v4f swv[4], bv[4];
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int cl = ncol + ni * 32 + 8 * g;
-                swv[g] = *reinterpret_cast<const v4f*>(sw_l + cl);
+                if constexpr (E::BYTES == 1) swv[g] = *reinterpret_cast<const v4f*>(sw_l + cl);
                 if (HAS_BIAS) bv[g] = *reinterpret_cast<const v4f*>(b_l + cl);
             }
 #pragma unroll
@@ -351,9 +381,14 @@ __device__ __forceinline__ void store_bf16(const Acc<C>& acc, uint16_t* __restri
                 float v[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const float t = (float)acc[ni][p][4 * g + e];  // nearest even
-                    const float u = __fmul_rn(sam, swv[g][e]);
-                    v[e] = HAS_BIAS ? __builtin_fmaf(t, u, bv[g][e]) : __fmul_rn(t, u);
+                    if constexpr (E::BYTES == 1) {
+                        const float t = (float)acc[ni][p][4 * g + e];  // nearest even
+                        const float u = __fmul_rn(sam, swv[g][e]);
+                        v[e] = HAS_BIAS ? __builtin_fmaf(t, u, bv[g][e]) : __fmul_rn(t, u);
+                    } else {
+                        const float t = acc[ni][p][4 * g + e];
+                        v[e] = HAS_BIAS ? __fadd_rn(t, bv[g][e]) : t;
+                    }
                 }
                 uint2 o = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
                 if (ACT == 1) {
@@ -372,24 +407,34 @@ __device__ __forceinline__ void store_bf16(const Acc<C>& acc, uint16_t* __restri
             d[i] = *reinterpret_cast<const v4i*>(rbase + i * C::RPINS * C::OUT_ROW);
         const int64_t row = m0 + trow0 + p * 32;
         uint16_t* gbase = y + row * N + n0 + 8 * cc;
-        if (interior) {
+        if (VEC_OUT && interior) {
 #pragma unroll
             for (int i = 0; i < NI_OUT; ++i)
                 *reinterpret_cast<v4i*>(gbase + i * C::RPINS * N) = d[i];
-        } else {
+        } else if (VEC_OUT) {
 #pragma unroll
             for (int i = 0; i < NI_OUT; ++i)
                 if (row + i * C::RPINS < M && n0 + 8 * cc < N)
                     *reinterpret_cast<v4i*>(gbase + i * C::RPINS * N) = d[i];
+        } else {
+#pragma unroll
+            for (int i = 0; i < NI_OUT; ++i) {
+                if (row + i * C::RPINS >= M) continue;
+                uint16_t* pr = gbase + i * C::RPINS * N;
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (n0 + 8 * cc + e < N)
+                        pr[e] = (uint16_t)(((uint32_t)d[i][e >> 1] >> (16 * (e & 1))) & 0xffffu);
+            }
         }
         lds_barrier();  // the staging area is free again
     }
 }
 
 template <class C>
-__device__ __forceinline__ void store_i32(const Acc<C>& acc, int32_t* __restrict__ out, int64_t M,
-                                          int64_t N, int64_t m0, int64_t n0, int wm, int wn,
-                                          int lane) {
+__device__ __forceinline__ void store_i32(const Acc<C, ElemI8>& acc, int32_t* __restrict__ out,
+                                          int64_t M, int64_t N, int64_t m0, int64_t n0, int wm,
+                                          int wn, int lane) {
     const int ncol = wn * C::TN + 4 * (lane >> 5);
 #pragma unroll
     for (int mi = 0; mi < C::MI; ++mi) {
@@ -415,13 +460,16 @@ __device__ __forceinline__ void store_i32(const Acc<C>& acc, int32_t* __restrict
 // registers; the output is staged in the LDS above buffer 0.  Without PERSIST
 // each workgroup does one tile (the GELU epilogue's binary64 slow path needs
 // the registers that the tile loop's live state would take).
-template <class C, int OUT_I32, int ACT, bool PERSIST>
+// a, w: [M x K] and [N x K] operands of E; sa, sw: INT8 row and column scales
+// (unused for BF16); K in elements.
+template <class C, class E, int OUT_I32, int ACT, bool PERSIST, bool VEC_OUT>
 __global__ __launch_bounds__(C::THREADS)
 __attribute__((amdgpu_waves_per_eu(C::WAVES_PER_SIMD, C::WAVES_PER_SIMD)))
-void gemm_i8_tiled(const int8_t* __restrict__ qa, const float* __restrict__ sa, int64_t M,
-                   const int8_t* __restrict__ qw, const float* __restrict__ sw, int64_t N, int64_t K,
-                   const uint16_t* __restrict__ bias, void* __restrict__ out) {
+void gemm_tiled(const void* __restrict__ a, const float* __restrict__ sa, int64_t M,
+                const void* __restrict__ w, const float* __restrict__ sw, int64_t N, int64_t K,
+                const uint16_t* __restrict__ bias, void* __restrict__ out) {
     constexpr int BM = C::BM, BN = C::BN, BK = C::BK, NST = C::NST, MI = C::MI;
+    constexpr bool SCALES = !OUT_I32 && E::BYTES == 1;
     // K ring (from byte STAGE on, also the output staging area), then the
     // tile's row scales, column scales and bias (as binary32).  All of it is
     // one LDS object: with several, the compiler can no longer tell the
@@ -431,34 +479,37 @@ void gemm_i8_tiled(const int8_t* __restrict__ qa, const float* __restrict__ sa, 
     float* sa_l = reinterpret_cast<float*>(smem + C::RING);
     float* sw_l = sa_l + BM;
     float* b_l = sw_l + BN;
+    const char* ab = static_cast<const char*>(a);
+    const char* wb = static_cast<const char*>(w);
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave % C::WM, wn = wave / C::WM;
     const int64_t tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN, total = tm * tn;
-    const int KT = (int)(K / BK);
+    const int64_t KB = K * E::BYTES;
+    const int KT = (int)(KB / BK);
     int64_t t = blockIdx.x, tile_m, tile_n;
     tile_of<C>(t, tm, tn, tile_m, tile_n);
     int64_t m0 = tile_m * BM, n0 = tile_n * BN;
     Ctx<C> c;
-    make_ctx<C>(c, K, wave, lane);
-    set_tile<C>(c, qa, qw, M, N, K, m0, n0);
+    make_ctx<C>(c, KB, wave, lane);
+    set_tile<C>(c, ab, wb, M, N, KB, m0, n0);
 
     // first tile: epilogue operands, then fill the ring and wait for stage 0
     // (the bias stays in bf16 bits until it is written: converting it at once
     // would make the wave wait for the load)
     float nsa = 0.f, nsw = 0.f;
     uint32_t nb = 0;
-    if (!OUT_I32 && tid < BM) nsa = sa[m0 + tid < M ? m0 + tid : M - 1];
+    if (SCALES && tid < BM) nsa = sa[m0 + tid < M ? m0 + tid : M - 1];
     if (!OUT_I32 && tid < BN) {
         const int64_t n = n0 + tid < N ? n0 + tid : N - 1;
-        nsw = sw[n];
+        if (SCALES) nsw = sw[n];
         if (bias) nb = bias[n];
     }
     for (int s = 0; s < NST; ++s)
         if (s < KT) stage_load<C>(c, s * BK, smem + s * C::STAGE);
-    if (!OUT_I32 && tid < BM) sa_l[tid] = nsa;
+    if (SCALES && tid < BM) sa_l[tid] = nsa;
     if (!OUT_I32 && tid < BN) {
-        sw_l[tid] = nsw;
+        if (SCALES) sw_l[tid] = nsw;
         b_l[tid] = bf16_bits_to_float(nb);
     }
     if (KT >= NST) wait_vm_lgkm0<C::NLOAD * (NST - 1)>();
@@ -466,23 +517,23 @@ void gemm_i8_tiled(const int8_t* __restrict__ qa, const float* __restrict__ sa, 
     __syncthreads();
 
     for (;;) {
-        Acc<C> acc;
+        Acc<C, E> acc;
 #pragma unroll
         for (int i = 0; i < C::NI; ++i)
 #pragma unroll
-            for (int j = 0; j < MI; ++j) acc[i][j] = (v16i){};
+            for (int j = 0; j < MI; ++j) acc[i][j] = (typename E::acc_t){};
         Frags<C> cur;
 #pragma unroll
         for (int q = 0; q < C::NQ; ++q) read_frag<C>(smem, c, 0, q, cur);
 
         int kt = 0;
-        for (; kt + NST < KT; ++kt) k_stage<C, true, true, true>(c, smem, kt, acc, cur);
+        for (; kt + NST < KT; ++kt) k_stage<C, E, true, true, true>(c, smem, kt, acc, cur);
         if (kt == KT - NST && kt + 1 < KT) {
-            k_stage<C, false, true, true>(c, smem, kt, acc, cur);
+            k_stage<C, E, false, true, true>(c, smem, kt, acc, cur);
             ++kt;
         }
-        for (; kt + 1 < KT; ++kt) k_stage<C, false, true, false>(c, smem, kt, acc, cur);
-        k_stage<C, false, false, false>(c, smem, kt, acc, cur);
+        for (; kt + 1 < KT; ++kt) k_stage<C, E, false, true, false>(c, smem, kt, acc, cur);
+        k_stage<C, E, false, false, false>(c, smem, kt, acc, cur);
 
         const int64_t t_next = t + gridDim.x;
         const bool has_next = PERSIST && t_next < total;
@@ -492,13 +543,13 @@ void gemm_i8_tiled(const int8_t* __restrict__ qa, const float* __restrict__ sa, 
             tile_of<C>(t_next, tm, tn, tile_m, tile_n);
             m0n = tile_m * BM;
             n0n = tile_n * BN;
-            if (!OUT_I32 && tid < BM) nsa = sa[m0n + tid < M ? m0n + tid : M - 1];
+            if (SCALES && tid < BM) nsa = sa[m0n + tid < M ? m0n + tid : M - 1];
             if (!OUT_I32 && tid < BN) {
                 const int64_t n = n0n + tid < N ? n0n + tid : N - 1;
-                nsw = sw[n];
+                if (SCALES) nsw = sw[n];
                 if (bias) nb = bias[n];
             }
-            set_tile<C>(c, qa, qw, M, N, K, m0n, n0n);
+            set_tile<C>(c, ab, wb, M, N, KB, m0n, n0n);
             stage_load<C>(c, 0, smem);  // next tile's stage 0 -> buffer 0
         }
         // The epilogue's lane addresses depend only on the lane, and hoisted out
@@ -506,20 +557,23 @@ void gemm_i8_tiled(const int8_t* __restrict__ qa, const float* __restrict__ sa, 
         // copy of the lane index keeps them local to the epilogue.
         int elane = lane;
         asm volatile("" : "+v"(elane));
-        if (OUT_I32) {
+        if constexpr (OUT_I32 != 0) {
             store_i32<C>(acc, reinterpret_cast<int32_t*>(out), M, N, m0, n0, wm, wn, elane);
-        } else if (bias) {
-            store_bf16<C, ACT, true>(acc, reinterpret_cast<uint16_t*>(out), M, N, m0, n0, wave, wm,
-                                     wn, elane, sa_l, sw_l, b_l, smem + C::STAGE);
         } else {
-            store_bf16<C, ACT, false>(acc, reinterpret_cast<uint16_t*>(out), M, N, m0, n0, wave,
-                                      wm, wn, elane, sa_l, sw_l, b_l, smem + C::STAGE);
+            if (bias)
+                store_bf16<C, E, ACT, true, VEC_OUT>(acc, reinterpret_cast<uint16_t*>(out), M, N,
+                                                     m0, n0, wave, wm, wn, elane, sa_l, sw_l, b_l,
+                                                     smem + C::STAGE);
+            else
+                store_bf16<C, E, ACT, false, VEC_OUT>(acc, reinterpret_cast<uint16_t*>(out), M,
+                                                      N, m0, n0, wave, wm, wn, elane, sa_l, sw_l,
+                                                      b_l, smem + C::STAGE);
         }
         if (!has_next) break;
         // this tile's epilogue is done with the old values
-        if (!OUT_I32 && tid < BM) sa_l[tid] = nsa;
+        if (SCALES && tid < BM) sa_l[tid] = nsa;
         if (!OUT_I32 && tid < BN) {
-            sw_l[tid] = nsw;
+            if (SCALES) sw_l[tid] = nsw;
             b_l[tid] = bf16_bits_to_float(nb);
         }
         wait_vm_lgkm0<0>();  // the next tile's stage 0 (and this tile's stores) are done ...
@@ -537,10 +591,10 @@ int64_t tile_count(int64_t M, int64_t N) {
     return ((N + C::BN - 1) / C::BN) * ((M + C::BM - 1) / C::BM);
 }
 
-template <class C, int OUT_I32, int ACT>
-hipError_t launch_cfg(const int8_t* qa, const float* sa, int64_t M, const int8_t* qw,
-                      const float* sw, int64_t N, int64_t K, const uint16_t* bias, void* out,
-                      int cus, hipStream_t stream) {
+template <class C, class E, int OUT_I32, int ACT, bool VEC_OUT>
+hipError_t launch_cfg(const void* a, const float* sa, int64_t M, const void* w, const float* sw,
+                      int64_t N, int64_t K, const uint16_t* bias, void* out, int cus,
+                      hipStream_t stream) {
     const int64_t tiles = tile_count<C>(M, N);
     constexpr bool persist = ACT == 0;
     // workgroups that fit on one CU at once (160 KB of LDS is the limit)
@@ -550,25 +604,28 @@ hipError_t launch_cfg(const int8_t* qa, const float* sa, int64_t M, const int8_t
         const int64_t slots = (int64_t)cus * per_cu;
         grid = tiles < slots ? tiles : slots;
     }
-    hipLaunchKernelGGL((gemm_i8_tiled<C, OUT_I32, ACT, persist>), dim3((unsigned)grid),
-                       dim3(C::THREADS), 0, stream, qa, sa, M, qw, sw, N, K, bias, out);
+    hipLaunchKernelGGL((gemm_tiled<C, E, OUT_I32, ACT, persist, VEC_OUT>), dim3((unsigned)grid),
+                       dim3(C::THREADS), 0, stream, a, sa, M, w, sw, N, K, bias, out);
     return hipGetLastError();
 }
 
 // The largest tile whose count covers at least half of the CUs: 256 x 256
 // tiles move the least data per MFMA (which is what sets the clock under the
 // power cap), smaller ones only pay off when the large ones leave most CUs idle.
-template <int OUT_I32, int ACT>
-hipError_t launch_tiles(const int8_t* qa, const float* sa, int64_t M, const int8_t* qw,
-                        const float* sw, int64_t N, int64_t K, const uint16_t* bias, void* out,
+template <class E, int OUT_I32, int ACT, bool VEC_OUT>
+hipError_t launch_tiles(const void* a, const float* sa, int64_t M, const void* w, const float* sw,
+                        int64_t N, int64_t K, const uint16_t* bias, void* out,
                         hipStream_t stream) {
     const int cus = cu_count();
     if (cus <= 0) return hipErrorInvalidDevice;
     if (2 * tile_count<CfgLarge>(M, N) >= cus)
-        return launch_cfg<CfgLarge, OUT_I32, ACT>(qa, sa, M, qw, sw, N, K, bias, out, cus, stream);
+        return launch_cfg<CfgLarge, E, OUT_I32, ACT, VEC_OUT>(a, sa, M, w, sw, N, K, bias, out, cus,
+                                                             stream);
     if (2 * tile_count<CfgSmall>(M, N) >= cus)
-        return launch_cfg<CfgSmall, OUT_I32, ACT>(qa, sa, M, qw, sw, N, K, bias, out, cus, stream);
-    return launch_cfg<CfgTiny, OUT_I32, ACT>(qa, sa, M, qw, sw, N, K, bias, out, cus, stream);
+        return launch_cfg<CfgSmall, E, OUT_I32, ACT, VEC_OUT>(a, sa, M, w, sw, N, K, bias, out, cus,
+                                                             stream);
+    return launch_cfg<CfgTiny, E, OUT_I32, ACT, VEC_OUT>(a, sa, M, w, sw, N, K, bias, out, cus,
+                                                        stream);
 }
 
 }  // namespace
@@ -578,9 +635,33 @@ int launch_gemm_i8(const int8_t* qa, const float* sa, int64_t M, const int8_t* q
                    int out_kind, void* out, hipStream_t stream) {
     if (M == 0 || N == 0) return 0;
     hipError_t e;
-    if (out_kind == 1) e = launch_tiles<1, 0>(qa, sa, M, qw, sw, N, K, bias, out, stream);
-    else if (act == 1) e = launch_tiles<0, 1>(qa, sa, M, qw, sw, N, K, bias, out, stream);
-    else e = launch_tiles<0, 0>(qa, sa, M, qw, sw, N, K, bias, out, stream);
+    if (out_kind == 1)
+        e = launch_tiles<ElemI8, 1, 0, true>(qa, sa, M, qw, sw, N, K, bias, out, stream);
+    else if (act == 1)
+        e = launch_tiles<ElemI8, 0, 1, true>(qa, sa, M, qw, sw, N, K, bias, out, stream);
+    else
+        e = launch_tiles<ElemI8, 0, 0, true>(qa, sa, M, qw, sw, N, K, bias, out, stream);
+    return e == hipSuccess ? 0 : -1;
+}
+
+bool gemm_bf16_tiled_ok(const uint16_t* x, int64_t K, const uint16_t* w) {
+    // whole 128-byte K stages, 16-byte aligned operand rows, and stage offsets
+    // and buffer sizes that fit the 32-bit buffer addressing
+    return K >= 64 && K % 64 == 0 && K <= (1 << 20) &&
+           reinterpret_cast<uintptr_t>(x) % 16 == 0 && reinterpret_cast<uintptr_t>(w) % 16 == 0;
+}
+
+int launch_gemm_bf16_tiled(const uint16_t* x, int64_t M, int64_t K, const uint16_t* w, int64_t N,
+                           const uint16_t* bias, int act, uint16_t* y, hipStream_t stream) {
+    if (M == 0 || N == 0) return 0;
+    const bool vec = N % 8 == 0 && reinterpret_cast<uintptr_t>(y) % 16 == 0;
+    hipError_t e;
+    if (act == 1)
+        e = vec ? launch_tiles<ElemBF16, 0, 1, true>(x, nullptr, M, w, nullptr, N, K, bias, y, stream)
+                : launch_tiles<ElemBF16, 0, 1, false>(x, nullptr, M, w, nullptr, N, K, bias, y, stream);
+    else
+        e = vec ? launch_tiles<ElemBF16, 0, 0, true>(x, nullptr, M, w, nullptr, N, K, bias, y, stream)
+                : launch_tiles<ElemBF16, 0, 0, false>(x, nullptr, M, w, nullptr, N, K, bias, y, stream);
     return e == hipSuccess ? 0 : -1;
 }
 

@@ -419,6 +419,8 @@ def test_guarded_mixed_batch():
 
 
 def _check_fallback(got, x, w, b, act=oracle.ACT_NONE):
+    if act != oracle.ACT_NONE:
+        return _check_fallback_gelu(got, x, w, b)
     ref = oracle.linear_bf16(x, w, b, act=act)
     d = ulp_dist_bf16(got, ref)
     ok1 = d <= 1
@@ -440,6 +442,44 @@ def _check_fallback(got, x, w, b, act=oracle.ACT_NONE):
     assert frac > 0.999
 
 
+def _gelu64(z):
+    """GELU-tanh in float64 (only for tolerance intervals)."""
+    return 0.5 * z * (1.0 + math.tanh(math.sqrt(2.0 / math.pi) * (z + 0.044715 * z**3)))
+
+
+def _check_fallback_gelu(got, x, w, b):
+    """GELU after the BF16 linear: the pre-activation may differ from the
+    oracle's within the summation bound (ulp + gamma_K * sum |x||w| + |b|), and
+    GELU is then applied to it.  Every output that is not bit-exact must lie in
+    GELU's image of that pre-activation interval (GELU falls to its minimum at
+    z = -0.7518 and rises after), widened by one output ulp for the rounding."""
+    lin = oracle.linear_bf16(x, w, b)
+    ref = oracle.gelu_rows(lin)
+    bad = np.argwhere(got != ref)
+    say(f"  fallback+GELU bit-exact: {1 - bad.shape[0] / got.size:.6f}")
+    assert bad.shape[0] <= max(10, got.size // 1000)
+    K = x.shape[1]
+    u = 2.0**-23
+    gamma = K * u / (1 - K * u)
+    xf = np.abs(wl.from_bf16_bits(x).astype(np.float64))
+    wf = np.abs(wl.from_bf16_bits(w).astype(np.float64))
+    zmin = -0.7517916
+
+    def ulp(v):
+        return math.ldexp(1.0, math.frexp(abs(v))[1] - 8) if v != 0 else 2.0**-133
+
+    for i, j in bad:
+        zf = float(wl.from_bf16_bits(lin[i:i + 1, j])[0])
+        mag = float(xf[i] @ wf[j]) + abs(float(wl.from_bf16_bits(b[j:j + 1])[0]))
+        r = ulp(zf) + gamma * mag
+        cand = [_gelu64(zf - r), _gelu64(zf + r)]
+        if zf - r < zmin < zf + r:
+            cand.append(_gelu64(zmin))
+        lo, hi = min(cand), max(cand)
+        gf = float(wl.from_bf16_bits(got[i:i + 1, j])[0])
+        assert lo - ulp(lo) <= gf <= hi + ulp(hi), (i, j, zf, r, gf, lo, hi)
+
+
 def test_fallback_on_conforming_shapes_and_gelu():
     say("fallback tiny/audio + gelu")
     lin = wl.tiny()
@@ -454,6 +494,43 @@ def test_fallback_on_conforming_shapes_and_gelu():
         b = wl.to_bf16_bits(rng.standard_normal(N).astype(np.float32) * np.float32(0.01))
         y = h_u16(w8.linear_bf16(d_bf16(x), d_bf16(w), d_bf16(b)))
         _check_fallback(y, x, w, b)
+
+
+# The tiled BF16 path (K % 64 == 0, 16-byte aligned operands) on each tile
+# configuration: 64 x 64 (first two), 128 x 128, 256 x 256 (last two, the
+# last with workgroups taking two tiles); N % 8 != 0 stores element by
+# element, K = 64 is a single stage.
+@pytest.mark.parametrize("M,N,K", [(300, 100, 64), (97, 256, 1024), (2000, 1992, 256),
+                                   (4100, 4100, 64), (4352, 4104, 192)])
+@pytest.mark.parametrize("act", [w8.ACT_NONE, w8.ACT_GELU_TANH])
+def test_fallback_tiled_path(M, N, K, act):
+    say(f"fallback tiled M={M} N={N} K={K} act={act}")
+    rng = np.random.default_rng(M + 3 * N + K + act)
+    x = wl.to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+    w = wl.to_bf16_bits(rng.standard_normal((N, K)).astype(np.float32) * np.float32(0.05))
+    b = wl.to_bf16_bits(rng.standard_normal(N).astype(np.float32) * np.float32(0.01))
+    y = h_u16(w8.linear_bf16(d_bf16(x), d_bf16(w), d_bf16(b), act=act))
+    _check_fallback(y, x, w, b, act=act)
+
+
+def test_fallback_tiled_and_generic_agree_on_offsets():
+    """The same product through the tiled kernel (aligned views) and the
+    generic one (views offset by one element, 2-byte aligned): both within the
+    fallback bar, output rows written exactly once."""
+    say("fallback tiled vs generic")
+    M, N, K = 257, 192, 128
+    rng = np.random.default_rng(11)
+    x = wl.to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+    w = wl.to_bf16_bits(rng.standard_normal((N, K)).astype(np.float32) * np.float32(0.05))
+    xg = torch.zeros(M * K + 1, dtype=torch.bfloat16, device=DEV)
+    wg = torch.zeros(N * K + 1, dtype=torch.bfloat16, device=DEV)
+    xg[1:] = d_bf16(x).view(-1)
+    wg[1:] = d_bf16(w).view(-1)
+    y_tiled = h_u16(w8.linear_bf16(d_bf16(x), d_bf16(w)))
+    y_generic = h_u16(w8.linear_bf16(xg[1:].view(M, K), wg[1:].view(N, K)))
+    zero_b = np.zeros(N, np.uint16)
+    _check_fallback(y_tiled, x, w, zero_b)
+    _check_fallback(y_generic, x, w, zero_b)
 
 
 # ---------------------------------------------------------------------------
