@@ -102,14 +102,17 @@ def traffic_from(fetch_dir, write_dir):
     write = per_kernel(write_dir, "WRITE_SIZE")
     copy_f = [v for k, v in fetch.items() if "neg_kernel" in k or "neg" in k]
     copy_w = [v for k, v in write.items() if "neg_kernel" in k or "neg" in k]
-    gemm_f = [v for k, v in fetch.items() if "gemm_i8_tiled" in k]
-    gemm_w = [v for k, v in write.items() if "gemm_i8_tiled" in k]
+    # the INT8 tiled GEMM's launches (the video FFN shapes run 256 x 256 tiles)
+    def is_gemm(k):
+        return "gemm_tiled" in k and "ElemI8" in k
+    gemm_f = [v for k, v in fetch.items() if is_gemm(k)]
+    gemm_w = [v for k, v in write.items() if is_gemm(k)]
     assert copy_f and copy_w and gemm_f and gemm_w, "counter runs lack the copy or the GEMM"
     kf = COPY_BYTES / (copy_f[0] * 1024.0)   # true bytes per counted byte
     kw = COPY_BYTES / (copy_w[0] * 1024.0)
     rd = gemm_f[0] * 1024.0 * kf
     wr = gemm_w[0] * 1024.0 * kw
-    out = {"kernel": "gemm_i8_tiled (video FFN up and down launches, averaged)",
+    out = {"kernel": "gemm_tiled<Cfg<256,256,...>, ElemI8> (video FFN up and down launches, averaged)",
            "kernel_source_sha256_16": source_hash(GEMM_SOURCE),
            "copy_scale_fetch": kf, "copy_scale_write": kw,
            "read_bytes_per_launch": rd, "write_bytes_per_launch": wr,
@@ -265,7 +268,7 @@ def main():
 
     # dominant kernel: the INT8 GEMM (one kernel, launched for the up and the
     # down projection with the same op count): average launch duration
-    dom_name = "gemm_i8_tiled (video FFN up and down, averaged)"
+    dom_name = "gemm_tiled, INT8, 256x256 tiles (video FFN up and down, averaged)"
     dom_t = 0.5 * (t_up + t_down)
     achieved = ops_gemm / (dom_t * 1e-3) / 1e12
     traffic = None

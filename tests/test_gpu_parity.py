@@ -574,6 +574,26 @@ def test_compaction_matches_oracle(B, L, D, kind):
     assert np.all(hb[:pad] == 0x1234) and np.all(hb[pad + n * D:] == 0x1234)
 
 
+def test_compaction_unaligned_mask_and_rows():
+    """Mask not 4-byte aligned (prefix counted byte by byte) and x rows not
+    16-byte aligned (copied element by element): same result as the oracle."""
+    say("compact unaligned mask / rows")
+    rng = np.random.default_rng(77)
+    B, L, D = 5, 203, 40
+    x = wl.to_bf16_bits(rng.standard_normal((B, L, D)).astype(np.float32))
+    mask = (rng.random((B, L)) < 0.6).astype(np.uint8)
+    mbuf = torch.zeros(B * L + 1, dtype=torch.uint8, device=DEV)
+    mbuf[1:] = torch.from_numpy(mask.ravel()).to(DEV)
+    xbuf = torch.zeros(B * L * D + 1, dtype=torch.bfloat16, device=DEV)
+    xbuf[1:] = d_bf16(x.reshape(-1))
+    out, src, cnt = w8.compact_padded_rows(xbuf[1:].view(B, L, D), mbuf[1:].view(B, L))
+    n = int(cnt.item())
+    o_out, o_src, o_n = oracle.compact_rows(x, mask)
+    assert n == o_n
+    assert np.array_equal(h(src)[:n], o_src)
+    assert np.array_equal(h_u16(out[:n]), o_out)
+
+
 def test_compaction_commutes_with_linear_on_gpu():
     say("compaction commutes with the linear")
     rng = np.random.default_rng(21)
