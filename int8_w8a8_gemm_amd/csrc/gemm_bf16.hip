@@ -4,11 +4,11 @@
 // shapes the optimised INT8 operator cannot serve run in native BF16.
 //     y[i][j] = bf16_RNE(sum_k x[i][k] * w[j][k] + b[j])
 // with fp32 accumulation and an optional GELU-tanh on the bf16 result.
-// Operands with K % 64 == 0 and 16-byte aligned rows take the tiled MFMA
-// kernel shared with the INT8 path (gemm_tiled.hip, any M and N).  Everything
-// else takes the kernel below: v_mfma_f32_16x16x32_bf16 on 128 x 128 tiles
-// with every edge masked (any M, N, K), rows that are only 4-byte aligned
-// (K = 2050) read with 4-byte loads and 2-byte aligned ones element by element.
+// Operands with K even and 4-byte aligned rows take the tiled MFMA kernel
+// shared with the INT8 path (gemm_tiled.hip, any M and N; the K tail of the
+// last stage is masked).  Everything else (K odd or 2-byte aligned operands)
+// takes the kernel below: v_mfma_f32_16x16x32_bf16 on 128 x 128 tiles with
+// every edge masked, operands read element by element.
 #include "common.h"
 
 namespace w8a8 {

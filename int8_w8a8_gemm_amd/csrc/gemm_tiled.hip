@@ -256,6 +256,28 @@ __device__ __forceinline__ void read_frag(const char* lds_stage, const Ctx<C>& c
     }
 }
 
+// Keeps the first `valid` bytes of a 16-byte fragment (0 <= valid, even), zero
+// beyond: the K tail of the last stage, whose loads ran on into the next row.
+__device__ __forceinline__ v4i keep_bytes(v4i v, int valid) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        const int keep = valid - 4 * d;
+        v[d] = keep >= 4 ? v[d] : keep >= 2 ? (v[d] & 0xffff) : 0;
+    }
+    return v;
+}
+
+// Masks the fragments of sub-step ks of the last stage to the row's `tail`
+// valid bytes of that stage.
+template <class C>
+__device__ __forceinline__ void mask_tail(Frags<C>& f, const Ctx<C>& c, int ks, int tail) {
+    const int valid = tail - (32 * ks + 16 * (c.lane >> 5));
+#pragma unroll
+    for (int q = 0; q < C::MI; ++q) f.a[q] = keep_bytes(f.a[q], valid);
+#pragma unroll
+    for (int q = 0; q < C::NI; ++q) f.w[q] = keep_bytes(f.w[q], valid);
+}
+
 template <class C, class E>
 __device__ __forceinline__ void mfma_one(Acc<C, E>& acc, const Frags<C>& f, int j) {
     const int ni = j / C::MI, mi = j % C::MI;
@@ -271,11 +293,15 @@ __device__ __forceinline__ void mfma_one(Acc<C, E>& acc, const Frags<C>& f, int 
 // order.
 template <class C, class E, bool LOAD, bool NEXT, bool STEADY>
 __device__ __forceinline__ void k_stage(const Ctx<C>& c, char* smem, int kt, Acc<C, E>& acc,
-                                        Frags<C>& cur) {
+                                        Frags<C>& cur, int tail = C::BK) {
+    // tail: valid bytes of each row in this stage, < BK only in a BF16 last
+    // stage (the INT8 path has whole stages)
+    constexpr bool MAYBE_TAIL = !NEXT && E::BYTES == 2;
     char* buf = smem + (kt % C::NST) * C::STAGE;
     Frags<C> nxt;
 #pragma unroll
     for (int ks = 0; ks + 1 < C::SUB; ++ks) {
+        if (MAYBE_TAIL && tail < C::BK) mask_tail<C>(cur, c, ks, tail);
 #pragma unroll
         for (int j = 0; j < C::NMFMA; ++j) {
             mfma_one<C, E>(acc, cur, j);
@@ -287,6 +313,7 @@ __device__ __forceinline__ void k_stage(const Ctx<C>& c, char* smem, int kt, Acc
         cur = nxt;
     }
     char* next_buf = smem + ((kt + 1) % C::NST) * C::STAGE;
+    if (MAYBE_TAIL && tail < C::BK) mask_tail<C>(cur, c, C::SUB - 1, tail);
     if (NEXT) {
         // my loads of stage kt+1 have landed and my reads of stage kt are done ...
         if (STEADY) wait_vm_lgkm0<C::NLOAD * (C::NST - 2)>();
@@ -486,7 +513,9 @@ void gemm_tiled(const void* __restrict__ a, const float* __restrict__ sa, int64_
     const int wm = wave % C::WM, wn = wave / C::WM;
     const int64_t tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN, total = tm * tn;
     const int64_t KB = K * E::BYTES;
-    const int KT = (int)(KB / BK);
+    // INT8 rows are whole stages; a BF16 row may end inside its last stage
+    const int KT = E::BYTES == 1 ? (int)(KB / BK) : (int)((KB + BK - 1) / BK);
+    const int tail = (int)(KB - (int64_t)(KT - 1) * BK);  // valid bytes in the last stage
     int64_t t = blockIdx.x, tile_m, tile_n;
     tile_of<C>(t, tm, tn, tile_m, tile_n);
     int64_t m0 = tile_m * BM, n0 = tile_n * BN;
@@ -533,7 +562,7 @@ void gemm_tiled(const void* __restrict__ a, const float* __restrict__ sa, int64_
             ++kt;
         }
         for (; kt + 1 < KT; ++kt) k_stage<C, E, false, true, false>(c, smem, kt, acc, cur);
-        k_stage<C, E, false, false, false>(c, smem, kt, acc, cur);
+        k_stage<C, E, false, false, false>(c, smem, kt, acc, cur, tail);
 
         const int64_t t_next = t + gridDim.x;
         const bool has_next = PERSIST && t_next < total;
@@ -645,10 +674,11 @@ int launch_gemm_i8(const int8_t* qa, const float* sa, int64_t M, const int8_t* q
 }
 
 bool gemm_bf16_tiled_ok(const uint16_t* x, int64_t K, const uint16_t* w) {
-    // whole 128-byte K stages, 16-byte aligned operand rows, and stage offsets
+    // rows of whole dwords (K even, 4-byte aligned operands: the 16-byte loads
+    // are dword aligned; the last stage's tail is masked), and stage offsets
     // and buffer sizes that fit the 32-bit buffer addressing
-    return K >= 64 && K % 64 == 0 && K <= (1 << 20) &&
-           reinterpret_cast<uintptr_t>(x) % 16 == 0 && reinterpret_cast<uintptr_t>(w) % 16 == 0;
+    return K >= 2 && K % 2 == 0 && K <= (1 << 20) &&
+           reinterpret_cast<uintptr_t>(x) % 4 == 0 && reinterpret_cast<uintptr_t>(w) % 4 == 0;
 }
 
 int launch_gemm_bf16_tiled(const uint16_t* x, int64_t M, int64_t K, const uint16_t* w, int64_t N,

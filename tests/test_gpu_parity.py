@@ -513,6 +513,22 @@ def test_fallback_tiled_path(M, N, K, act):
     _check_fallback(y, x, w, b, act=act)
 
 
+# The tiled BF16 path with a K tail (K even, K % 64 != 0, rows 4-byte aligned):
+# the last stage's loads run on into the next row and are masked.  K = 2 is a
+# single partial stage; 2048 x 2048 x 2050 is the fallback workload.
+@pytest.mark.parametrize("M,N,K", [(300, 100, 2), (97, 256, 66), (257, 192, 130),
+                                   (2048, 2048, 2050), (4100, 4100, 190)])
+@pytest.mark.parametrize("act", [w8.ACT_NONE, w8.ACT_GELU_TANH])
+def test_fallback_tiled_k_tail(M, N, K, act):
+    say(f"fallback tiled K tail M={M} N={N} K={K} act={act}")
+    rng = np.random.default_rng(M + 5 * N + K + act)
+    x = wl.to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+    w = wl.to_bf16_bits(rng.standard_normal((N, K)).astype(np.float32) * np.float32(0.05))
+    b = wl.to_bf16_bits(rng.standard_normal(N).astype(np.float32) * np.float32(0.01))
+    y = h_u16(w8.linear_bf16(d_bf16(x), d_bf16(w), d_bf16(b), act=act))
+    _check_fallback(y, x, w, b, act=act)
+
+
 def test_fallback_tiled_and_generic_agree_on_offsets():
     """The same product through the tiled kernel (aligned views) and the
     generic one (views offset by one element, 2-byte aligned): both within the
