@@ -370,13 +370,26 @@ def extra_benches(w8, wl, np, torch, dev, d, log):
     out["compact_8x512x4096"] = {"us": round(t * 1e3, 2), "rows_kept": mc,
                                  "GB/s": round(nbytes / (t * 1e-3) / 1e9, 1),
                                  "frac_hbm": round(nbytes / (t * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
-    # conforming text projection on the compacted rows, and the two fallbacks
+    # compaction fused with the per-row quantisation (reads the valid rows once,
+    # writes their int8 codes and scales)
+    qb = torch.empty((B * L, Dm), dtype=torch.int8, device=dev)
+    sb = torch.empty((B * L,), dtype=torch.float32, device=dev)
+    t = _time(lambda: w8.compact_quantize_rows(xd, md, qb, sb, src, cnt), 50, torch)
+    nbytes = 3.0 * mc * Dm + B * L + 8.0 * mc + 4
+    out["compact_quantize_8x512x4096"] = {"us": round(t * 1e3, 2), "rows_kept": mc,
+                                          "GB/s": round(nbytes / (t * 1e-3) / 1e9, 1),
+                                          "frac_hbm": round(nbytes / (t * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    # the text projection both ways: guarded linear on the compacted bf16 rows
+    # (quantise + GEMM), and the INT8 GEMM on the fused kernel's codes
     xc = buf[:mc]
     lw = w8.W8A8Linear.prepare(d(g.w), d(g.b))
     yc = torch.empty((mc, 4096), dtype=torch.bfloat16, device=dev)
     t = _time(lambda: lw(xc, y=yc), 20, torch)
     out["linear_int8_text_Mc_x4096x4096"] = {"us": round(t * 1e3, 2),
                                              "TOPS": round(2.0 * mc * 4096 * 4096 / (t * 1e-3) / 1e12, 1)}
+    t = _time(lambda: w8.gemm(qb[:mc], sb[:mc], lw.qw, lw.sw, lw.bias, out=yc), 20, torch)
+    out["gemm_int8_text_Mc_x4096x4096"] = {"us": round(t * 1e3, 2),
+                                           "TOPS": round(2.0 * mc * 4096 * 4096 / (t * 1e-3) / 1e12, 1)}
     wa = d(g.w_a)
     ba = d(g.b_a)
     ya = torch.empty((mc, 4100), dtype=torch.bfloat16, device=dev)

@@ -164,6 +164,27 @@ W8A8_API int w8a8_linear_bf16(const uint16_t* x, int64_t M, int64_t K, const uin
 W8A8_API int compact_padded_rows(const uint16_t* x, const uint8_t* mask, int64_t B, int64_t L, int64_t D,
                         uint16_t* out, int32_t* src_row, int32_t* count, void* stream);
 
+/*
+ * Compaction fused with the per-row activation quantisation (section 01.3:
+ * padded positions are dropped with the shared text mask, and activations are
+ * quantised to INT8 per row at run time): one pass over the valid rows, which
+ * are never written back in bf16.
+ *
+ *   x    [B x L x D] bf16, mask [B x L] uint8 (nonzero = valid; any pattern)
+ *   q    [capacity B*L x D] int8, scale [capacity B*L] fp32: the valid rows, in
+ *        (b, t) order, quantised exactly as w8a8_quantize_rows does
+ *   src_row [capacity B*L] int32, count [1] int32 (device): as compact_padded_rows
+ *
+ * Equal to compact_padded_rows followed by w8a8_quantize_rows on the first
+ * count rows.  Rows of q and scale past count are not written.  The INT8 GEMM
+ * then runs on them (w8a8_gemm with M = count, read after a synchronisation).
+ * Alignment: 2-byte x, 4-byte scale, src_row, count; 16-byte x with 8-byte q
+ * and D % 8 == 0 take the vector path.  B*L < 2^31.
+ */
+W8A8_API int w8a8_compact_quantize_rows(const uint16_t* x, const uint8_t* mask, int64_t B,
+                                        int64_t L, int64_t D, int8_t* q, float* scale,
+                                        int32_t* src_row, int32_t* count, void* stream);
+
 /* ---- host-only helpers: no GPU is touched ---- */
 
 /* 1 if the INT8 GEMM serves (N, K): K % 128 == 0, 128 <= K <= W8A8_MAX_K,

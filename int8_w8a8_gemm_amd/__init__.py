@@ -29,7 +29,7 @@ PATH_INT8, PATH_BF16 = 0, 1
 MAX_K = 131072
 
 EXPORTS = ("w8a8_quantize_rows", "w8a8_gelu_quantize_rows", "w8a8_gelu_bf16", "w8a8_gemm", "w8a8_linear", "w8a8_linear_bf16",
-           "compact_padded_rows", "w8a8_guard", "w8a8_linear_workspace_bytes",
+           "compact_padded_rows", "w8a8_compact_quantize_rows", "w8a8_guard", "w8a8_linear_workspace_bytes",
            "w8a8_status_str")
 
 _lib = None
@@ -58,6 +58,7 @@ def lib():
     L.w8a8_linear.argtypes = [P, I64, I64, I64, P, P, P, P, I, P, P, SZ, P, P]
     L.w8a8_linear_bf16.argtypes = [P, I64, I64, P, I64, P, I, P, P]
     L.compact_padded_rows.argtypes = [P, P, I64, I64, I64, P, P, P, P]
+    L.w8a8_compact_quantize_rows.argtypes = [P, P, I64, I64, I64, P, P, P, P, P]
     L.w8a8_guard.argtypes = [I64, I64]
     L.w8a8_linear_workspace_bytes.argtypes = [I64, I64]
     L.w8a8_linear_workspace_bytes.restype = SZ
@@ -252,6 +253,29 @@ def compact_padded_rows(x, mask, out=None, src_row=None, count=None, stream=None
     _check("compact_padded_rows", lib().compact_padded_rows(
         _p(x), _p(mask), B, L, D, _p(out), _p(src_row), _p(count), _stream(stream)))
     return out, src_row, count
+
+
+def compact_quantize_rows(x, mask, q=None, scale=None, src_row=None, count=None, stream=None):
+    """Compaction fused with per-row INT8 quantisation: x bf16 [B, L, D], mask uint8
+    [B, L] -> (q int8 [B*L, D], scale fp32 [B*L], src_row int32 [B*L], count int32 [1]),
+    the first count rows valid.  count stays on the device."""
+    _need(x, "x", torch.bfloat16)
+    _need(mask, "mask", torch.uint8)
+    B, L, D = x.shape
+    if tuple(mask.shape) != (B, L):
+        raise ValueError("mask must be [B, L]")
+    dev = x.device
+    q = q if q is not None else torch.empty((B * L, D), dtype=torch.int8, device=dev)
+    scale = scale if scale is not None else torch.empty((B * L,), dtype=torch.float32, device=dev)
+    src_row = src_row if src_row is not None else torch.empty((B * L,), dtype=torch.int32, device=dev)
+    count = count if count is not None else torch.empty((1,), dtype=torch.int32, device=dev)
+    _need(q, "q", torch.int8, (B * L, D))
+    _need(scale, "scale", torch.float32, (B * L,))
+    _need(src_row, "src_row", torch.int32, (B * L,))
+    _need(count, "count", torch.int32, (1,))
+    _check("w8a8_compact_quantize_rows", lib().w8a8_compact_quantize_rows(
+        _p(x), _p(mask), B, L, D, _p(q), _p(scale), _p(src_row), _p(count), _stream(stream)))
+    return q, scale, src_row, count
 
 
 @dataclass

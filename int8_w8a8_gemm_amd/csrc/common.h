@@ -115,6 +115,9 @@ int launch_quantize_rows(const uint16_t* x, int64_t rows, int64_t cols, int8_t* 
                          hipStream_t stream, bool gelu = false);
 int launch_compact_rows(const uint16_t* x, const uint8_t* mask, int64_t R, int64_t D,
                         uint16_t* out, int32_t* src_row, int32_t* count, hipStream_t stream);
+int launch_compact_quantize_rows(const uint16_t* x, const uint8_t* mask, int64_t R, int64_t D,
+                                 int8_t* q, float* scale, int32_t* src_row, int32_t* count,
+                                 hipStream_t stream);
 int launch_gemm_i8(const int8_t* qa, const float* sa, int64_t M, const int8_t* qw,
                    const float* sw, int64_t N, int64_t K, const uint16_t* bias, int act,
                    int out_kind, void* out, hipStream_t stream);

@@ -346,7 +346,159 @@ hipError_t launch_vec(const uint16_t* x, int64_t rows, int64_t cols, int8_t* q, 
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Compaction fused with the per-row quantisation: the valid rows of a padded
+// [B*L x D] batch (mask != 0) are quantised straight into dense rows of q, in
+// increasing source order, with src_row and the count as for compaction.  The
+// result equals compaction followed by quantize_rows; the compacted bf16 rows
+// are never written.  Block i owns source rows [8i, 8i+8), one wave each: the
+// block counts the valid mask bytes before its first row (four per load when
+// the mask is 4-byte aligned), ranks its rows with a ballot, and every wave
+// with a valid row quantises it as quantize_rows_vec does (row in registers).
+constexpr int kCqRows = 8;
+constexpr int kCqBlock = kCqRows * 64;
+
+// Nonzero bytes in a 32-bit word.
+__device__ __forceinline__ int nonzero_bytes(uint32_t w) {
+    const uint32_t hi = ((w & 0x7f7f7f7fu) + 0x7f7f7f7fu) | w;  // bit 7 of each byte: byte != 0
+    return __builtin_popcount(hi & 0x80808080u);
+}
+
+// Valid rows before r0, the rank of this wave's row among the block's valid
+// rows, and the block's count.  Every wave of the block calls it (it holds a
+// barrier).
+__device__ __forceinline__ void cq_rank(const uint8_t* __restrict__ mask, int64_t R, int64_t r0,
+                                        int mask_words, int* red, int& base, int& rank,
+                                        int& nvalid, bool& valid) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    int local = 0;
+    if (mask_words) {
+        const uint32_t* mw = reinterpret_cast<const uint32_t*>(mask);
+        for (int64_t i = threadIdx.x; i < r0 / 4; i += kCqBlock) local += nonzero_bytes(mw[i]);
+    } else {
+        for (int64_t i = threadIdx.x; i < r0; i += kCqBlock) local += (mask[i] != 0);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) local += __shfl_xor(local, off, 64);
+    if (lane == 0) red[wave] = local;
+    __syncthreads();
+    base = 0;
+#pragma unroll
+    for (int i = 0; i < kCqRows; ++i) base += red[i];
+    const int64_t rl = r0 + lane;
+    const uint64_t bal = __ballot(lane < kCqRows && rl < R && mask[rl] != 0);
+    valid = (bal >> wave) & 1;
+    rank = __builtin_popcountll(bal & ((1ull << wave) - 1));
+    nvalid = __builtin_popcountll(bal);
+}
+
+template <int CPL>
+__global__ __launch_bounds__(kCqBlock) void compact_quantize_rows_vec(
+    const uint16_t* __restrict__ x, const uint8_t* __restrict__ mask, int64_t R, int64_t D,
+    int8_t* __restrict__ q, float* __restrict__ scale, int32_t* __restrict__ src_row,
+    int32_t* __restrict__ count, int mask_words) {
+    __shared__ int red[kCqRows];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t r0 = (int64_t)blockIdx.x * kCqRows;
+    int base, rank, nvalid;
+    bool valid;
+    cq_rank(mask, R, r0, mask_words, red, base, rank, nvalid, valid);
+    if (blockIdx.x == gridDim.x - 1 && threadIdx.x == 0) *count = base + nvalid;
+    if (!valid) return;
+    const int64_t r = r0 + wave, m = base + rank;
+    if (lane == 0) src_row[m] = (int32_t)r;
+
+    const int64_t nchunk = D >> 3;
+    const u32x4* xr = reinterpret_cast<const u32x4*>(x + r * D);
+    u32x4 v[CPL];
+    uint32_t amax = 0;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+        const int64_t ch = (int64_t)c * 64 + lane;
+        v[c] = ch < nchunk ? __builtin_nontemporal_load(xr + ch) : (u32x4){0u, 0u, 0u, 0u};
+        amax = max(amax, absmax_bits(v[c]));
+    }
+    amax = wave_max_u32(amax);
+    const float a = __uint_as_float(amax << 16);
+    const bool zero = !(a >= 0x1p-100f);
+    const float inv = zero ? 0.0f : __fdiv_rn(127.0f, a);
+    if (lane == 0) scale[m] = zero ? 0.0f : __fdiv_rn(a, 127.0f);
+    int8_t* qr = q + m * D;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+        const int64_t ch = (int64_t)c * 64 + lane;
+        if (ch < nchunk) {
+            const uint2 o = zero ? make_uint2(0, 0) : quant8_pk(v[c], inv);
+            __builtin_nontemporal_store(o.x, reinterpret_cast<uint32_t*>(qr) + 2 * ch);
+            __builtin_nontemporal_store(o.y, reinterpret_cast<uint32_t*>(qr) + 2 * ch + 1);
+        }
+    }
+}
+
+// Any D and alignment: each wave reads its row twice, element by element.
+__global__ __launch_bounds__(kCqBlock) void compact_quantize_rows_generic(
+    const uint16_t* __restrict__ x, const uint8_t* __restrict__ mask, int64_t R, int64_t D,
+    int8_t* __restrict__ q, float* __restrict__ scale, int32_t* __restrict__ src_row,
+    int32_t* __restrict__ count, int mask_words) {
+    __shared__ int red[kCqRows];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t r0 = (int64_t)blockIdx.x * kCqRows;
+    int base, rank, nvalid;
+    bool valid;
+    cq_rank(mask, R, r0, mask_words, red, base, rank, nvalid, valid);
+    if (blockIdx.x == gridDim.x - 1 && threadIdx.x == 0) *count = base + nvalid;
+    if (!valid) return;
+    const int64_t r = r0 + wave, m = base + rank;
+    if (lane == 0) src_row[m] = (int32_t)r;
+    const uint16_t* xr = x + r * D;
+    int8_t* qr = q + m * D;
+    uint32_t amax = 0;
+    for (int64_t k = lane; k < D; k += 64) amax = max(amax, (uint32_t)xr[k] & 0x7fffu);
+    amax = wave_max_u32(amax);
+    const float a = __uint_as_float(amax << 16);
+    if (!(a >= 0x1p-100f)) {
+        if (lane == 0) scale[m] = 0.0f;
+        for (int64_t k = lane; k < D; k += 64) qr[k] = 0;
+        return;
+    }
+    const float inv = __fdiv_rn(127.0f, a);
+    if (lane == 0) scale[m] = __fdiv_rn(a, 127.0f);
+    for (int64_t k = lane; k < D; k += 64)
+        qr[k] = (int8_t)quant1(__uint_as_float((uint32_t)xr[k] << 16), inv);
+}
+
+template <int CPL>
+hipError_t launch_cq(const uint16_t* x, const uint8_t* mask, int64_t R, int64_t D, int8_t* q,
+                     float* scale, int32_t* src_row, int32_t* count, int mask_words,
+                     int64_t blocks, hipStream_t stream) {
+    hipLaunchKernelGGL(compact_quantize_rows_vec<CPL>, dim3((unsigned)blocks), dim3(kCqBlock), 0,
+                       stream, x, mask, R, D, q, scale, src_row, count, mask_words);
+    return hipGetLastError();
+}
+
 }  // namespace
+
+int launch_compact_quantize_rows(const uint16_t* x, const uint8_t* mask, int64_t R, int64_t D,
+                                 int8_t* q, float* scale, int32_t* src_row, int32_t* count,
+                                 hipStream_t stream) {
+    const int64_t blocks = R > 0 ? (R + kCqRows - 1) / kCqRows : 1;
+    const int mask_words = reinterpret_cast<uintptr_t>(mask) % 4 == 0 ? 1 : 0;
+    const bool vec = D > 0 && D % 8 == 0 && reinterpret_cast<uintptr_t>(x) % 16 == 0 &&
+                     reinterpret_cast<uintptr_t>(q) % 8 == 0;
+    const int64_t nchunk = D / 8;
+    hipError_t e;
+    if (vec && nchunk <= 64) e = launch_cq<1>(x, mask, R, D, q, scale, src_row, count, mask_words, blocks, stream);
+    else if (vec && nchunk <= 128) e = launch_cq<2>(x, mask, R, D, q, scale, src_row, count, mask_words, blocks, stream);
+    else if (vec && nchunk <= 256) e = launch_cq<4>(x, mask, R, D, q, scale, src_row, count, mask_words, blocks, stream);
+    else if (vec && nchunk <= 512) e = launch_cq<8>(x, mask, R, D, q, scale, src_row, count, mask_words, blocks, stream);
+    else if (vec && nchunk <= 1024) e = launch_cq<16>(x, mask, R, D, q, scale, src_row, count, mask_words, blocks, stream);
+    else {
+        hipLaunchKernelGGL(compact_quantize_rows_generic, dim3((unsigned)blocks), dim3(kCqBlock), 0,
+                           stream, x, mask, R, D, q, scale, src_row, count, mask_words);
+        e = hipGetLastError();
+    }
+    return e == hipSuccess ? 0 : -1;
+}
 
 int launch_quantize_rows(const uint16_t* x, int64_t rows, int64_t cols, int8_t* q, float* scale,
                          hipStream_t stream, bool gelu) {

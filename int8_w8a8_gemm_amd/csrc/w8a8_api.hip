@@ -147,4 +147,20 @@ int compact_padded_rows(const uint16_t* x, const uint8_t* mask, int64_t B, int64
     return launched(w8a8::launch_compact_rows(x, mask, R, D, out, src_row, count, as_stream(stream)));
 }
 
+int w8a8_compact_quantize_rows(const uint16_t* x, const uint8_t* mask, int64_t B, int64_t L,
+                               int64_t D, int8_t* q, float* scale, int32_t* src_row,
+                               int32_t* count, void* stream) {
+    if (B < 0 || L < 0 || D < 0) return W8A8_EINVAL;
+    if (L > 0 && B > (kMaxRows - 1) / L) return W8A8_EINVAL;
+    if (!count || !aligned(count, 4)) return W8A8_EINVAL;
+    const int64_t R = B * L;
+    if (R > 0) {
+        if (!mask || !src_row || !aligned(src_row, 4) || !scale || !aligned(scale, 4))
+            return W8A8_EINVAL;
+        if (D > 0 && (!x || !q || !aligned(x, 2))) return W8A8_EINVAL;
+    }
+    return launched(w8a8::launch_compact_quantize_rows(x, mask, R, D, q, scale, src_row, count,
+                                                       as_stream(stream)));
+}
+
 }  // extern "C"

@@ -160,6 +160,24 @@ def test_linear_bf16_and_compaction_reject_bad_arguments():
     assert c(A16, A16, 1 << 20, 1 << 12, 8, A16, A16, A16) == w8.EINVAL  # B*L >= 2^31
 
 
+def test_compact_quantize_rejects_bad_arguments():
+    L = w8.lib()
+    cq = lambda x, m, B, Lq, D, q, sc, s, n: L.w8a8_compact_quantize_rows(x, m, B, Lq, D, q, sc, s, n, NULL)
+    assert cq(A16, A16, -1, 4, 8, A16, A16, A16, A16) == w8.EINVAL
+    assert cq(A16, A16, 2, -4, 8, A16, A16, A16, A16) == w8.EINVAL
+    assert cq(A16, A16, 2, 4, -8, A16, A16, A16, A16) == w8.EINVAL
+    assert cq(A16, A16, 2, 4, 8, A16, A16, A16, NULL) == w8.EINVAL     # count is required
+    assert cq(A16, A16, 2, 4, 8, A16, A16, A16, MIS) == w8.EINVAL      # count misaligned
+    assert cq(A16, NULL, 2, 4, 8, A16, A16, A16, A16) == w8.EINVAL     # mask
+    assert cq(A16, A16, 2, 4, 8, A16, NULL, A16, A16) == w8.EINVAL     # scale
+    assert cq(A16, A16, 2, 4, 8, A16, MIS, A16, A16) == w8.EINVAL
+    assert cq(A16, A16, 2, 4, 8, A16, A16, NULL, A16) == w8.EINVAL     # src_row
+    assert cq(NULL, A16, 2, 4, 8, A16, A16, A16, A16) == w8.EINVAL     # x
+    assert cq(A16, A16, 2, 4, 8, NULL, A16, A16, A16) == w8.EINVAL     # q
+    assert cq(MIS, A16, 2, 4, 8, A16, A16, A16, A16) == w8.EINVAL      # x misaligned
+    assert cq(A16, A16, 1 << 20, 1 << 12, 8, A16, A16, A16, A16) == w8.EINVAL  # B*L >= 2^31
+
+
 def test_python_binding_refuses_cpu_tensors():
     import torch
     x = torch.zeros((4, 128), dtype=torch.bfloat16)

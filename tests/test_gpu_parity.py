@@ -610,6 +610,77 @@ def test_compaction_unaligned_mask_and_rows():
     assert np.array_equal(h_u16(out[:n]), o_out)
 
 
+# Compaction fused with quantisation against the oracle's compaction followed by
+# its quantisation: 16-byte path with 8 and 1 chunks per lane, 16 (D = 8192),
+# the element path (D % 8 != 0, D > 8192), empty / full masks, no rows at all.
+@pytest.mark.parametrize("B,L,D,kind", [(8, 512, 4096, "prefix"), (3, 50, 16, "random"),
+                                       (2, 33, 8192, "random"), (2, 40, 12, "random"),
+                                       (1, 21, 8200, "random"), (4, 33, 64, "none"),
+                                       (4, 33, 64, "all"), (0, 16, 64, "none")])
+def test_compact_quantize_matches_oracle(B, L, D, kind):
+    say(f"compact+quantise B={B} L={L} D={D} {kind}")
+    rng = np.random.default_rng(B * 100 + L + D)
+    xf = rng.standard_normal((B, L, D)).astype(np.float32)
+    if B * L > 3:
+        xf.reshape(-1, D)[1] = 0.0                      # a zero row: scale 0, codes 0
+        xf.reshape(-1, D)[2, :: 7] *= 40.0              # outliers
+    x = wl.to_bf16_bits(xf)
+    if kind == "prefix":
+        lengths = rng.integers(64, L, B, endpoint=True)
+        mask = (np.arange(L)[None, :] < lengths[:, None]).astype(np.uint8)
+    elif kind == "random":
+        mask = (rng.random((B, L)) < 0.55).astype(np.uint8) * rng.integers(1, 255, (B, L)).astype(np.uint8)
+        if B * L > 3:
+            mask.reshape(-1)[1:3] = 1                   # keep the zero and outlier rows
+    elif kind == "none":
+        mask = np.zeros((B, L), np.uint8)
+    else:
+        mask = np.ones((B, L), np.uint8)
+    xd = d_bf16(x.reshape(B * L, D)).view(B, L, D) if B * L > 0 else \
+        torch.empty((B, L, D), dtype=torch.bfloat16, device=DEV)
+    q, sc, src, cnt = w8.compact_quantize_rows(xd, torch.from_numpy(mask).to(DEV))
+    n = int(cnt.item())
+    o_out, o_src, o_n = oracle.compact_rows(x, mask)
+    assert n == o_n
+    assert np.array_equal(h(src)[:n], o_src)
+    if n:
+        qo, so = oracle.quantize_rows(o_out)
+        assert np.array_equal(h(sc)[:n].view(np.uint32), so.view(np.uint32))
+        assert np.array_equal(h(q)[:n], qo)
+
+
+def test_compact_quantize_unaligned_and_into_gemm():
+    """Unaligned mask and rows (word-free prefix, element path), then the text
+    path: fused compaction + quantisation, INT8 GEMM on the count rows, equal
+    to the guarded linear on the compacted bf16 rows."""
+    say("compact+quantise unaligned, then GEMM")
+    rng = np.random.default_rng(5)
+    B, L, D, N = 3, 70, 256, 128
+    x = wl.to_bf16_bits(rng.standard_normal((B, L, D)).astype(np.float32))
+    mask = (rng.random((B, L)) < 0.5).astype(np.uint8)
+    mbuf = torch.zeros(B * L + 1, dtype=torch.uint8, device=DEV)
+    mbuf[1:] = torch.from_numpy(mask.ravel()).to(DEV)
+    xbuf = torch.zeros(B * L * D + 1, dtype=torch.bfloat16, device=DEV)
+    xbuf[1:] = d_bf16(x.reshape(-1))
+    q, sc, src, cnt = w8.compact_quantize_rows(xbuf[1:].view(B, L, D), mbuf[1:].view(B, L))
+    n = int(cnt.item())
+    o_out, o_src, o_n = oracle.compact_rows(x, mask)
+    qo, so = oracle.quantize_rows(o_out)
+    assert n == o_n and np.array_equal(h(src)[:n], o_src)
+    assert np.array_equal(h(q)[:n], qo) and np.array_equal(h(sc)[:n].view(np.uint32), so.view(np.uint32))
+    # aligned input, into the INT8 GEMM
+    w = wl.to_bf16_bits(rng.standard_normal((N, D)).astype(np.float32) * np.float32(0.02))
+    b = wl.to_bf16_bits(rng.standard_normal(N).astype(np.float32) * np.float32(0.01))
+    qw, sw = oracle.quantize_rows(w)
+    q2, sc2, _, cnt2 = w8.compact_quantize_rows(d_bf16(x.reshape(B * L, D)).view(B, L, D),
+                                                torch.from_numpy(mask).to(DEV))
+    n2 = int(cnt2.item())
+    y = w8.gemm(q2[:n2], sc2[:n2], d_i8(qw), torch.from_numpy(sw).to(DEV), d_bf16(b))
+    ref, path = oracle.w8a8_linear(o_out, w, b)
+    assert path == 0                                     # the INT8 path
+    assert np.array_equal(h_u16(y), ref)
+
+
 def test_compaction_commutes_with_linear_on_gpu():
     say("compaction commutes with the linear")
     rng = np.random.default_rng(21)
