@@ -19,6 +19,8 @@
 // 32 cycles, so the whole data path is shared and counts K in bytes.
 #include "common.h"
 
+#include <type_traits>
+
 namespace w8a8 {
 
 namespace {
@@ -390,8 +392,11 @@ __device__ __forceinline__ void store_bf16(const Acc<C, E>& acc, uint16_t* __res
     const int s0 = wave * C::RPW + (int)((unsigned)lane / C::RCH);
     const char* rbase = stage + s0 * C::OUT_ROW + cc * 16;
     const int trow0 = (s0 / 32) * C::TM + (s0 % 32);
-#pragma unroll
-    for (int p = 0; p < C::MI; ++p) {
+    // one staging pass per MFMA row sub-tile, p a compile-time constant (a
+    // runtime pass loop left the accumulators dynamically indexed, in scratch,
+    // where the GELU body made the loop too large to unroll)
+    auto pass = [&](auto pc) {
+        constexpr int p = decltype(pc)::value;
         float sam = 0.f;
         if constexpr (E::BYTES == 1) sam = sa_l[wm * C::TM + p * 32 + (lane & 31)];
 #pragma unroll
@@ -455,7 +460,10 @@ __device__ __forceinline__ void store_bf16(const Acc<C, E>& acc, uint16_t* __res
             }
         }
         lds_barrier();  // the staging area is free again
-    }
+    };
+    static_assert(C::MI >= 1 && C::MI <= 2, "epilogue passes");
+    pass(std::integral_constant<int, 0>{});
+    if constexpr (C::MI > 1) pass(std::integral_constant<int, 1>{});
 }
 
 template <class C>

@@ -61,22 +61,6 @@ __device__ __forceinline__ int quant1(float x, float inv) {
     return (int)r;
 }
 
-// 8 bf16 -> 8 int8 packed in a uint2.
-__device__ __forceinline__ uint2 quant8(u32x4 v, float inv) {
-    uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    uint32_t o[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        int q0 = quant1(__uint_as_float(w[2 * h] << 16), inv);
-        int q1 = quant1(__uint_as_float(w[2 * h] & 0xffff0000u), inv);
-        int q2 = quant1(__uint_as_float(w[2 * h + 1] << 16), inv);
-        int q3 = quant1(__uint_as_float(w[2 * h + 1] & 0xffff0000u), inv);
-        o[h] = (uint32_t)(q0 & 0xff) | ((uint32_t)(q1 & 0xff) << 8) |
-               ((uint32_t)(q2 & 0xff) << 16) | ((uint32_t)(q3 & 0xff) << 24);
-    }
-    return make_uint2(o[0], o[1]);
-}
-
 // GELU applied to the 8 bf16 of one chunk.
 __device__ __forceinline__ u32x4 gelu8(u32x4 v) {
     u32x4 o;
@@ -187,7 +171,7 @@ __global__ __launch_bounds__(kBlock) void quantize_rows_vec(const uint16_t* __re
     for (int c = 0; c < CPL; ++c) {
         const int64_t ch = (int64_t)(c * WPR + wr) * 64 + lane;
         if (ch < nchunk) {
-            uint2 o = quant8(v[c], inv);
+            uint2 o = quant8_pk(v[c], inv);
             __builtin_nontemporal_store(o.x, reinterpret_cast<uint32_t*>(qr) + 2 * ch);
             __builtin_nontemporal_store(o.y, reinterpret_cast<uint32_t*>(qr) + 2 * ch + 1);
         }
