@@ -121,7 +121,10 @@ struct Cfg {
     static_assert(THREADS >= BM && THREADS >= BN, "scale staging");
 };
 
-typedef Cfg<256, 256, 4, 2, 128, 2> CfgLarge;
+#ifndef W8A8_LARGE_CFG
+#define W8A8_LARGE_CFG 256, 256, 4, 2, 128, 2
+#endif
+typedef Cfg<W8A8_LARGE_CFG> CfgLarge;
 typedef Cfg<128, 128, 2, 2, 128, 2> CfgSmall;
 typedef Cfg<64, 64, 2, 2, 128, 2> CfgTiny;
 
