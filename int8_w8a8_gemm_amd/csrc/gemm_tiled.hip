@@ -29,15 +29,22 @@ namespace {
 // A workgroup of WM x WN waves owns a BM x BN output tile; wave (wm, wn) owns
 // (BM/WM) x (BN/WN) outputs, i.e. MI x NI tiles of 32 x 32 MFMA accumulators.
 // K is staged BK bytes at a time through an NST-deep ring of LDS buffers.
-// Three configurations:
+// Four configurations:
+//   xl:    384 x 256 tile (INT8 without GELU only), 4 x 2 waves of 96 x 128:
+//          7 fragment reads per 12 MFMAs instead of 6 per 8, and 17% fewer
+//          operand bytes per MFMA.  Its two 80 KB K stages fill the LDS, so
+//          the tile's scales live in the ring once the K loop is done, and its
+//          192 accumulators leave no room for a second set of fragments.
 //   large: 256 x 256 tile, 4 x 2 waves (two per SIMD, so one wave's load issue,
 //          LDS waits and barrier arrival overlap the other's MFMAs), each wave
-//          64 x 128; the least operand traffic per MFMA.
+//          64 x 128.
 //   small: 128 x 128 tile, 2 x 2 waves of 64 x 64.
 //   tiny:  64 x 64 tile, 2 x 2 waves of 32 x 32.
-// The launcher takes the largest tile whose tile count covers at least half
-// of the CUs (a large tile on a CU still outruns four small ones; measured on
-// the 2378-row text projection, the 2048^3 audio GEMM and 1024 x 1024 x 4096).
+// The launcher takes the largest of large/small/tiny whose tile count covers
+// at least half of the CUs (a large tile on a CU still outruns four small
+// ones; measured on the 2378-row text projection, the 2048^3 audio GEMM and
+// 1024 x 1024 x 4096), and xl over large where it needs no more rounds of
+// tiles per CU and the tile loop is long (see launch_tiles).
 //
 // * Operands go global -> LDS directly (buffer_load_dwordx4 ... lds): a wave
 //   instruction moves 1 KB (64 lanes x 16 bytes); lane l lands at LDS offset
@@ -97,6 +104,11 @@ struct Cfg {
     static constexpr int NI = TN / 32;                 // 32-col MFMA tiles per wave along N
     static constexpr int NQ = MI + NI;                 // fragments per sub-step
     static constexpr int NMFMA = MI * NI;              // MFMAs per sub-step
+    // Fragment registers: with room to spare the next sub-step's fragments go
+    // to fresh registers early in the sub-step; where the accumulators leave
+    // no room (RECYCLE) each is read into the register of the fragment it
+    // replaces, right after that fragment's last MFMA.
+    static constexpr bool RECYCLE = NMFMA * 16 + 2 * NQ * 4 > 200;
     static constexpr int CPR = BK / 16;                // 16-byte chunks per LDS row
     static constexpr int RPI = 64 / CPR;               // rows one 1-KB wave instruction fills
     static constexpr int STAGE = (BM + BN) * BK;       // bytes per stage (A tile then B tile)
@@ -112,18 +124,29 @@ struct Cfg {
     static constexpr int RPINS = 64 / RCH;             // output rows per copy-out instruction
     static constexpr int RPW = SROWS / WAVES;          // staged rows each wave copies per pass
     static constexpr int EPI_BYTES = SROWS * OUT_ROW;
-    // LDS: K ring (from byte STAGE on also the staging area), then the scales
+    // LDS: K ring (from byte STAGE on also the staging area), then the tile's
+    // row scales, column scales and bias as binary32.  Where the ring fills the
+    // 160 KB of LDS, the scales go in the ring above the staging area instead:
+    // they are then written only once the K loop is done with the ring.
     static constexpr int RING = NST * STAGE > STAGE + EPI_BYTES ? NST * STAGE : STAGE + EPI_BYTES;
-    static constexpr int SMEM = RING + (BM + 2 * BN) * 4;
+    static constexpr int SCALE_BYTES = (BM + 2 * BN) * 4;
+    static constexpr bool SCALES_IN_RING = RING + SCALE_BYTES > 160 * 1024;
+    static constexpr int SCALE_OFF = SCALES_IN_RING ? STAGE + EPI_BYTES : RING;
+    static constexpr int SMEM = SCALES_IN_RING ? RING : RING + SCALE_BYTES;
+    static_assert(SMEM <= 160 * 1024 && SCALE_OFF + SCALE_BYTES <= SMEM, "LDS budget");
     static_assert(BM % (WAVES * RPI) == 0 && BN % (WAVES * RPI) == 0, "load split");
     static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile");
     static_assert(RPW % RPINS == 0 && 32 % RPW == 0, "copy-out rows per wave");
     static_assert(THREADS >= BM && THREADS >= BN, "scale staging");
 };
 
+#ifndef W8A8_XL_CFG
+#define W8A8_XL_CFG 384, 256, 4, 2, 128, 2
+#endif
 #ifndef W8A8_LARGE_CFG
 #define W8A8_LARGE_CFG 256, 256, 4, 2, 128, 2
 #endif
+typedef Cfg<W8A8_XL_CFG> CfgXL;
 typedef Cfg<W8A8_LARGE_CFG> CfgLarge;
 typedef Cfg<128, 128, 2, 2, 128, 2> CfgSmall;
 typedef Cfg<64, 64, 2, 2, 128, 2> CfgTiny;
@@ -176,6 +199,10 @@ struct Ctx {
     rsrc_t rsrc[2];  // 0: activation panel, 1: weight panel
     uint32_t voff_a[C::LPW_A];
     uint32_t voff_b[C::LPW_B];
+    // fragment reads: LDS byte offset of this lane's row in the wave's first
+    // activation / weight sub-tile, and 16 x the physical chunk of its K-chunk
+    // (lane >> 5) in that row; every other read adds compile-time constants
+    uint32_t fa, fw, ga, gw;
     int wave, lane, wm, wn;
 };
 
@@ -212,6 +239,12 @@ __device__ __forceinline__ void make_ctx(Ctx<C>& c, int64_t KB, int wave, int la
     c.lane = lane;
     c.wm = wave % C::WM;
     c.wn = wave / C::WM;
+    const int hi = lane >> 5;
+    const int ra = c.wm * C::TM + (lane & 31), rw = c.wn * C::TN + (lane & 31);
+    c.fa = (uint32_t)(ra * C::BK);
+    c.fw = (uint32_t)(C::BM * C::BK + rw * C::BK);
+    c.ga = 16u * (uint32_t)swz<C::BK>(ra, hi);
+    c.gw = 16u * (uint32_t)swz<C::BK>(rw, hi);
 }
 
 // Load j (0 .. NLOAD-1) of one wave's share of a K stage: j < LPW_A loads A
@@ -246,19 +279,22 @@ template <class C, class E>
 using Acc = typename E::acc_t[C::NI][C::MI];
 
 // Fragment q of sub-step ks: q < MI -> activation sub-tile q, else weight
-// sub-tile q - MI.  Lane l reads row l % 32 of the sub-tile at K-chunk 2*ks + l/32.
+// sub-tile q - MI.  Lane l reads row l % 32 of the sub-tile at K-chunk
+// ch = 2*ks + l/32, stored at physical chunk ch ^ f(row).  Sub-tile i starts
+// 32*i rows further on, where f changes by 4*(i & 1) for 128-byte rows and not
+// at all for 64-byte rows; so 16 * (ch ^ f(row)) = g ^ (32*ks) ^ (64*(i & 1))
+// (128-byte rows) with g = 16 * ((l/32) ^ f(first row)) from the context:
+// one XOR-add per read.  ga, gw are that g for the two operands.
 template <class C>
-__device__ __forceinline__ void read_frag(const char* lds_stage, const Ctx<C>& c, int ks, int q,
-                                          Frags<C>& f) {
-    const int ch = 2 * ks + (c.lane >> 5);
-    if (q < C::MI) {
-        const int ra = c.wm * C::TM + q * 32 + (c.lane & 31);
-        f.a[q] = *reinterpret_cast<const v4i*>(lds_stage + ra * C::BK + 16 * swz<C::BK>(ra, ch));
-    } else {
-        const int rw = c.wn * C::TN + (q - C::MI) * 32 + (c.lane & 31);
-        f.w[q - C::MI] = *reinterpret_cast<const v4i*>(lds_stage + C::BM * C::BK + rw * C::BK +
-                                                       16 * swz<C::BK>(rw, ch));
-    }
+__device__ __forceinline__ void read_frag(const char* lds_stage, const Ctx<C>& c, uint32_t ga,
+                                          uint32_t gw, int ks, int q, Frags<C>& f) {
+    const bool is_a = q < C::MI;
+    const int i = is_a ? q : q - C::MI;
+    const uint32_t k = (uint32_t)(32 * ks) ^ (C::BK == 128 ? 64u * (uint32_t)(i & 1) : 0u);
+    const uint32_t off = ((is_a ? ga : gw) ^ k) + (is_a ? c.fa : c.fw);
+    const v4i v = *reinterpret_cast<const v4i*>(lds_stage + off + i * 32 * C::BK);
+    if (is_a) f.a[i] = v;
+    else f.w[i] = v;
 }
 
 // Keeps the first `valid` bytes of a 16-byte fragment (0 <= valid, even), zero
@@ -289,13 +325,59 @@ __device__ __forceinline__ void mfma_one(Acc<C, E>& acc, const Frags<C>& f, int 
     acc[ni][mi] = E::mfma(f.w[ni], f.a[mi], acc[ni][mi]);
 }
 
+// The MFMAs of one sub-step, with (READ) the fragment reads of sub-step rks
+// of buffer rbuf and (LOAD) this wave's loads of stage kload into lbuf placed
+// between them (spread evenly); sched_barrier pins that order.  Without
+// RECYCLE the next fragments go to fresh registers, one read after each of the
+// first NQ MFMAs (any left over after the last); with it each fragment is read
+// into the register it replaces once its last MFMA has issued.  The fragment
+// XOR bases are passed through an empty asm statement so that their per-read
+// combinations are formed next to each read, not hoisted out of the K loop
+// into NQ x SUB registers.
+template <class C, class E, bool READ, bool LOAD>
+__device__ __forceinline__ void mfma_step(const Ctx<C>& c, Acc<C, E>& acc, Frags<C>& cur,
+                                          const char* rbuf, int rks, char* lbuf, int kload) {
+    uint32_t ga = c.ga, gw = c.gw;
+    asm volatile("" : "+v"(ga), "+v"(gw));
+    auto loads_after = [&](int j) {
+        if (LOAD) {
+            // loads (j * NLOAD / NMFMA) .. ((j+1) * NLOAD / NMFMA) - 1 go after MFMA j
+#pragma unroll
+            for (int l = (j * C::NLOAD) / C::NMFMA; l < ((j + 1) * C::NLOAD) / C::NMFMA; ++l)
+                stage_load_one<C>(c, kload, lbuf, l);
+        }
+    };
+    if constexpr (C::RECYCLE) {
+#pragma unroll
+        for (int j = 0; j < C::NMFMA; ++j) {
+            mfma_one<C, E>(acc, cur, j);  // MFMA j uses w[j / MI] and a[j % MI]
+            if (READ && j % C::MI == C::MI - 1)
+                read_frag<C>(rbuf, c, ga, gw, rks, C::MI + j / C::MI, cur);
+            if (READ && j >= (C::NI - 1) * C::MI)
+                read_frag<C>(rbuf, c, ga, gw, rks, j - (C::NI - 1) * C::MI, cur);
+            loads_after(j);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    } else {
+        Frags<C> nxt;
+#pragma unroll
+        for (int j = 0; j < C::NMFMA; ++j) {
+            mfma_one<C, E>(acc, cur, j);
+            if (READ && j < C::NQ) read_frag<C>(rbuf, c, ga, gw, rks, j, nxt);
+            loads_after(j);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (READ) {
+#pragma unroll
+            for (int j = C::NMFMA; j < C::NQ; ++j) read_frag<C>(rbuf, c, ga, gw, rks, j, nxt);
+            cur = nxt;
+        }
+    }
+}
+
 // One K stage, held in ring buffer kt % NST.
 // LOAD: stage kt+NST exists and is loaded into this buffer after the barrier.
 // NEXT: stage kt+1 exists.  STEADY: exactly NST-2 newer stages are in flight.
-// Each sub-step issues its MFMAs in a fixed order with the next fragment reads
-// (one after each of the first NQ MFMAs; any left over after the last) and the
-// refill loads (spread evenly) placed between them; sched_barrier pins that
-// order.
 template <class C, class E, bool LOAD, bool NEXT, bool STEADY>
 __device__ __forceinline__ void k_stage(const Ctx<C>& c, char* smem, int kt, Acc<C, E>& acc,
                                         Frags<C>& cur, int tail = C::BK) {
@@ -303,19 +385,10 @@ __device__ __forceinline__ void k_stage(const Ctx<C>& c, char* smem, int kt, Acc
     // stage (the INT8 path has whole stages)
     constexpr bool MAYBE_TAIL = !NEXT && E::BYTES == 2;
     char* buf = smem + (kt % C::NST) * C::STAGE;
-    Frags<C> nxt;
 #pragma unroll
     for (int ks = 0; ks + 1 < C::SUB; ++ks) {
         if (MAYBE_TAIL && tail < C::BK) mask_tail<C>(cur, c, ks, tail);
-#pragma unroll
-        for (int j = 0; j < C::NMFMA; ++j) {
-            mfma_one<C, E>(acc, cur, j);
-            if (j < C::NQ) read_frag<C>(buf, c, ks + 1, j, nxt);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-#pragma unroll
-        for (int j = C::NMFMA; j < C::NQ; ++j) read_frag<C>(buf, c, ks + 1, j, nxt);
-        cur = nxt;
+        mfma_step<C, E, true, false>(c, acc, cur, buf, ks + 1, nullptr, 0);
     }
     char* next_buf = smem + ((kt + 1) % C::NST) * C::STAGE;
     if (MAYBE_TAIL && tail < C::BK) mask_tail<C>(cur, c, C::SUB - 1, tail);
@@ -326,44 +399,31 @@ __device__ __forceinline__ void k_stage(const Ctx<C>& c, char* smem, int kt, Acc
         __syncthreads();  // ... and everyone's: stage kt+1 visible, buffer kt % NST free
         __builtin_amdgcn_sched_barrier(0);
     }
-#pragma unroll
-    for (int j = 0; j < C::NMFMA; ++j) {
-        mfma_one<C, E>(acc, cur, j);
-        if (NEXT && j < C::NQ) read_frag<C>(next_buf, c, 0, j, nxt);
-        if (LOAD) {
-            // loads (j * NLOAD / NMFMA) .. ((j+1) * NLOAD / NMFMA) - 1 go after MFMA j
-#pragma unroll
-            for (int l = (j * C::NLOAD) / C::NMFMA; l < ((j + 1) * C::NLOAD) / C::NMFMA; ++l)
-                stage_load_one<C>(c, (kt + C::NST) * C::BK, buf, l);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-    }
-    if (NEXT) {
-#pragma unroll
-        for (int j = C::NMFMA; j < C::NQ; ++j) read_frag<C>(next_buf, c, 0, j, nxt);
-        cur = nxt;
-    }
+    mfma_step<C, E, NEXT, LOAD>(c, acc, cur, next_buf, 0, buf, (kt + C::NST) * C::BK);
 }
 
-// Workgroup id -> (tile row, tile col), XCD-aware.
+// Workgroup id -> (tile row, tile col), XCD-aware.  Tile indices fit in 32
+// bits (the launcher checks), and 32-bit division is a short sequence where
+// the 64-bit one is a long scalar routine on every tile of a persistent loop.
 template <class C>
 __device__ __forceinline__ void tile_of(int64_t bid, int64_t tm, int64_t tn, int64_t& tile_m,
                                         int64_t& tile_n) {
-    constexpr int GROUP_M = GROUP_ROWS / C::BM;
-    const int64_t total = tm * tn;
-    int64_t t = bid;
+    constexpr uint32_t GROUP_M = GROUP_ROWS / C::BM;
+    const uint32_t tm32 = (uint32_t)tm, tn32 = (uint32_t)tn, total = tm32 * tn32;
+    uint32_t t = (uint32_t)bid;
     if (total % NUM_XCD == 0) {
         // XCD x (= bid % 8) takes tiles [x * total/8, (x+1) * total/8) in dispatch order
-        t = (bid % NUM_XCD) * (total / NUM_XCD) + bid / NUM_XCD;
+        t = (t % NUM_XCD) * (total / NUM_XCD) + t / NUM_XCD;
     }
     // grouped raster: walk GROUP_M tile-rows at a time, column by column
-    const int64_t per_group = GROUP_M * tn;
-    const int64_t g = t / per_group;
-    const int64_t first_m = g * GROUP_M;
-    const int64_t gm = (tm - first_m) < GROUP_M ? (tm - first_m) : GROUP_M;
-    const int64_t r = t % per_group;
-    tile_m = first_m + r % gm;
-    tile_n = r / gm;
+    const uint32_t per_group = GROUP_M * tn32;
+    const uint32_t g = t / per_group;
+    const uint32_t first_m = g * GROUP_M;
+    const uint32_t gm = (tm32 - first_m) < GROUP_M ? (tm32 - first_m) : GROUP_M;
+    const uint32_t r = t - g * per_group;
+    const uint32_t rn = r / gm;
+    tile_m = (int64_t)(first_m + (r - rn * gm));
+    tile_n = (int64_t)rn;
 }
 
 // Epilogue.  acc[ni][mi][i] holds D[n][m] for m = m0 + wm*TM + mi*32 +
@@ -433,6 +493,9 @@ __device__ __forceinline__ void store_bf16(const Acc<C, E>& acc, uint16_t* __res
                 }
                 *reinterpret_cast<uint2*>(wbase + (ni * 32 + 8 * g) * 2) = o;
             }
+            // register-tight tiles: keep the next column group's scale reads
+            // from being hoisted next to this one's (they would spill)
+            if constexpr (C::RECYCLE) __builtin_amdgcn_sched_barrier(0);
         }
         lds_barrier();
         constexpr int NI_OUT = C::RPW / C::RPINS;  // copy-out instructions per wave per pass
@@ -464,9 +527,11 @@ __device__ __forceinline__ void store_bf16(const Acc<C, E>& acc, uint16_t* __res
         }
         lds_barrier();  // the staging area is free again
     };
-    static_assert(C::MI >= 1 && C::MI <= 2, "epilogue passes");
+    static_assert(C::MI >= 1 && C::MI <= 4, "epilogue passes");
     pass(std::integral_constant<int, 0>{});
     if constexpr (C::MI > 1) pass(std::integral_constant<int, 1>{});
+    if constexpr (C::MI > 2) pass(std::integral_constant<int, 2>{});
+    if constexpr (C::MI > 3) pass(std::integral_constant<int, 3>{});
 }
 
 template <class C>
@@ -508,13 +573,13 @@ void gemm_tiled(const void* __restrict__ a, const float* __restrict__ sa, int64_
                 const uint16_t* __restrict__ bias, void* __restrict__ out) {
     constexpr int BM = C::BM, BN = C::BN, BK = C::BK, NST = C::NST, MI = C::MI;
     constexpr bool SCALES = !OUT_I32 && E::BYTES == 1;
-    // K ring (from byte STAGE on, also the output staging area), then the
+    // K ring (from byte STAGE on, also the output staging area) and the
     // tile's row scales, column scales and bias (as binary32).  All of it is
     // one LDS object: with several, the compiler can no longer tell the
     // fragment reads from the in-flight direct-to-LDS loads and waits for
     // every load.
     __shared__ __attribute__((aligned(1024))) char smem[C::SMEM];
-    float* sa_l = reinterpret_cast<float*>(smem + C::RING);
+    float* sa_l = reinterpret_cast<float*>(smem + C::SCALE_OFF);
     float* sw_l = sa_l + BM;
     float* b_l = sw_l + BN;
     const char* ab = static_cast<const char*>(a);
@@ -545,13 +610,18 @@ void gemm_tiled(const void* __restrict__ a, const float* __restrict__ sa, int64_
         if (SCALES) nsw = sw[n];
         if (bias) nb = bias[n];
     }
+    // the epilogue operands go to LDS now, or (scales in the ring) stay in
+    // registers until the K loop is done with the ring
+    auto put_scales = [&]() {
+        if (SCALES && tid < BM) sa_l[tid] = nsa;
+        if (!OUT_I32 && tid < BN) {
+            if (SCALES) sw_l[tid] = nsw;
+            b_l[tid] = bf16_bits_to_float(nb);
+        }
+    };
     for (int s = 0; s < NST; ++s)
         if (s < KT) stage_load<C>(c, s * BK, smem + s * C::STAGE);
-    if (SCALES && tid < BM) sa_l[tid] = nsa;
-    if (!OUT_I32 && tid < BN) {
-        if (SCALES) sw_l[tid] = nsw;
-        b_l[tid] = bf16_bits_to_float(nb);
-    }
+    if constexpr (!C::SCALES_IN_RING) put_scales();
     if (KT >= NST) wait_vm_lgkm0<C::NLOAD * (NST - 1)>();
     else wait_vm_lgkm0<0>();
     __syncthreads();
@@ -564,7 +634,7 @@ void gemm_tiled(const void* __restrict__ a, const float* __restrict__ sa, int64_
             for (int j = 0; j < MI; ++j) acc[i][j] = (typename E::acc_t){};
         Frags<C> cur;
 #pragma unroll
-        for (int q = 0; q < C::NQ; ++q) read_frag<C>(smem, c, 0, q, cur);
+        for (int q = 0; q < C::NQ; ++q) read_frag<C>(smem, c, c.ga, c.gw, 0, q, cur);
 
         int kt = 0;
         for (; kt + NST < KT; ++kt) k_stage<C, E, true, true, true>(c, smem, kt, acc, cur);
@@ -579,6 +649,10 @@ void gemm_tiled(const void* __restrict__ a, const float* __restrict__ sa, int64_
         const bool has_next = PERSIST && t_next < total;
         int64_t m0n = 0, n0n = 0;
         lds_barrier();  // every wave is done reading the K ring
+        if constexpr (C::SCALES_IN_RING) {
+            put_scales();
+            lds_barrier();
+        }
         if (has_next) {
             tile_of<C>(t_next, tm, tn, tile_m, tile_n);
             m0n = tile_m * BM;
@@ -611,11 +685,7 @@ void gemm_tiled(const void* __restrict__ a, const float* __restrict__ sa, int64_
         }
         if (!has_next) break;
         // this tile's epilogue is done with the old values
-        if (SCALES && tid < BM) sa_l[tid] = nsa;
-        if (!OUT_I32 && tid < BN) {
-            if (SCALES) sw_l[tid] = nsw;
-            b_l[tid] = bf16_bits_to_float(nb);
-        }
+        if constexpr (!C::SCALES_IN_RING) put_scales();
         wait_vm_lgkm0<0>();  // the next tile's stage 0 (and this tile's stores) are done ...
         __syncthreads();     // ... for every wave, and the staging area is free
         for (int s = 1; s < NST; ++s)
@@ -636,6 +706,7 @@ hipError_t launch_cfg(const void* a, const float* sa, int64_t M, const void* w, 
                       int64_t N, int64_t K, const uint16_t* bias, void* out, int cus,
                       hipStream_t stream) {
     const int64_t tiles = tile_count<C>(M, N);
+    if (tiles >= (int64_t(1) << 31)) return hipErrorInvalidValue;  // tile indices are 32-bit
     constexpr bool persist = ACT == 0;
     // workgroups that fit on one CU at once (160 KB of LDS is the limit)
     constexpr int per_cu = (160 * 1024) / C::SMEM < 1 ? 1 : (160 * 1024) / C::SMEM;
@@ -649,15 +720,27 @@ hipError_t launch_cfg(const void* a, const float* sa, int64_t M, const void* w, 
     return hipGetLastError();
 }
 
-// The largest tile whose count covers at least half of the CUs: 256 x 256
-// tiles move the least data per MFMA (which is what sets the clock under the
-// power cap), smaller ones only pay off when the large ones leave most CUs idle.
+// Tile choice.  Larger tiles move less data per MFMA, which is what sets the
+// clock under the power cap; smaller ones only pay off when the large ones
+// leave most CUs idle.  xl (1.5x the work of a large tile) is taken when it
+// needs no more rounds of persistent tiles than large does (rounds x 1.5 <=
+// large's rounds) and either K >= 8192 or there are at least 8 xl tiles per
+// CU: measured 2-3% faster on the FFN up (24576 x 16384 x 4096, 16 tiles per
+// CU) and down (K = 16384) projections, but 3-7% slower on 24576 x 4096 x 4096
+// (4 tiles per CU with a short K loop).
 template <class E, int OUT_I32, int ACT, bool VEC_OUT>
 hipError_t launch_tiles(const void* a, const float* sa, int64_t M, const void* w, const float* sw,
                         int64_t N, int64_t K, const uint16_t* bias, void* out,
                         hipStream_t stream) {
     const int cus = cu_count();
     if (cus <= 0) return hipErrorInvalidDevice;
+    if constexpr (E::BYTES == 1 && ACT == 0) {
+        const int64_t txl = tile_count<CfgXL>(M, N), tl = tile_count<CfgLarge>(M, N);
+        const int64_t rounds_xl = (txl + cus - 1) / cus, rounds_l = (tl + cus - 1) / cus;
+        if (2 * txl >= cus && 3 * rounds_xl <= 2 * rounds_l && (K >= 8192 || txl >= 8 * (int64_t)cus))
+            return launch_cfg<CfgXL, E, OUT_I32, ACT, VEC_OUT>(a, sa, M, w, sw, N, K, bias, out,
+                                                              cus, stream);
+    }
     if (2 * tile_count<CfgLarge>(M, N) >= cus)
         return launch_cfg<CfgLarge, E, OUT_I32, ACT, VEC_OUT>(a, sa, M, w, sw, N, K, bias, out, cus,
                                                              stream);

@@ -182,6 +182,39 @@ def test_gemm_epilogue_matches_oracle(M, N, K, act, with_bias):
         assert np.array_equal(got, ref)  # same binary32 sequence on both sides
 
 
+def _tile_edge_rows(M, tile, rng, extra=120):
+    """Rows on both sides of every tile boundary, the ragged last tile and a
+    seeded random sample."""
+    edges = [r for b in range(tile, M, tile) for r in (b - 1, b)]
+    tail = list(range(max(0, M - 70), M))
+    rnd = list(rng.choice(M, extra, replace=False))
+    return np.unique(np.array([0, 1] + edges + tail + rnd, dtype=np.int64))
+
+
+def test_gemm_xl_tiles_ragged_sampled():
+    """6100 x 4032 x 8192: K >= 8192 with 256 tiles of 384 x 256 rows x columns,
+    so on a 256-CU MI355X the 384 x 256 tile path runs (ragged in M and in N).
+    INT32 accumulators and the bf16 epilogue (with bias) compared on sampled
+    rows that include both sides of every 384-row tile boundary and the
+    ragged last tile; all columns."""
+    M, N, K = 6100, 4032, 8192
+    say(f"gemm xl tiles M={M} N={N} K={K}")
+    rng = np.random.default_rng(8192)
+    qa = rng.integers(-127, 128, (M, K), dtype=np.int8)
+    qw = rng.integers(-127, 128, (N, K), dtype=np.int8)
+    rows = _tile_edge_rows(M, 384, rng)
+    qa_d, qw_d = d_i8(qa), d_i8(qw)
+    acc = h(w8.gemm(qa_d, None, qw_d, None, out_kind=w8.OUT_I32))
+    acc_ref = oracle.gemm_i32(np.ascontiguousarray(qa[rows]), qw)
+    assert np.array_equal(acc[rows], acc_ref)
+    sa = (rng.random(M, dtype=np.float32) * np.float32(1e-4) + np.float32(1e-6)).astype(np.float32)
+    sw = (rng.random(N, dtype=np.float32) * np.float32(1e-3) + np.float32(1e-6)).astype(np.float32)
+    b = wl.to_bf16_bits(rng.standard_normal(N).astype(np.float32))
+    y = w8.gemm(qa_d, torch.from_numpy(sa).to(DEV), qw_d, torch.from_numpy(sw).to(DEV), d_bf16(b))
+    ref = oracle.epilogue(acc_ref, np.ascontiguousarray(sa[rows]), sw, b)
+    assert np.array_equal(h_u16(y)[rows], ref)
+
+
 def test_gemm_rejects_unsupported_shape_on_device():
     qa = torch.zeros((4, 2050), dtype=torch.int8, device=DEV)
     qw = torch.zeros((64, 2050), dtype=torch.int8, device=DEV)
