@@ -102,7 +102,7 @@ def traffic_from(fetch_dir, write_dir):
     write = per_kernel(write_dir, "WRITE_SIZE")
     copy_f = [v for k, v in fetch.items() if "neg_kernel" in k or "neg" in k]
     copy_w = [v for k, v in write.items() if "neg_kernel" in k or "neg" in k]
-    # the INT8 tiled GEMM's launches (the video FFN shapes run 256 x 256 tiles)
+    # the INT8 tiled GEMM's launches (the video FFN shapes run 384 x 256 tiles)
     def is_gemm(k):
         return "gemm_tiled" in k and "ElemI8" in k
     gemm_f = [v for k, v in fetch.items() if is_gemm(k)]
@@ -112,7 +112,7 @@ def traffic_from(fetch_dir, write_dir):
     kw = COPY_BYTES / (copy_w[0] * 1024.0)
     rd = gemm_f[0] * 1024.0 * kf
     wr = gemm_w[0] * 1024.0 * kw
-    out = {"kernel": "gemm_tiled<Cfg<256,256,...>, ElemI8> (video FFN up and down launches, averaged)",
+    out = {"kernel": "gemm_tiled<Cfg<384,256,...>, ElemI8> (video FFN up and down launches, averaged)",
            "kernel_source_sha256_16": source_hash(GEMM_SOURCE),
            "copy_scale_fetch": kf, "copy_scale_write": kw,
            "read_bytes_per_launch": rd, "write_bytes_per_launch": wr,
@@ -268,7 +268,7 @@ def main():
 
     # dominant kernel: the INT8 GEMM (one kernel, launched for the up and the
     # down projection with the same op count): average launch duration
-    dom_name = "gemm_tiled, INT8, 256x256 tiles (video FFN up and down, averaged)"
+    dom_name = "gemm_tiled, INT8, 384x256 tiles (video FFN up and down, averaged)"
     dom_t = 0.5 * (t_up + t_down)
     achieved = ops_gemm / (dom_t * 1e-3) / 1e12
     traffic = None
@@ -401,14 +401,18 @@ def extra_benches(w8, wl, np, torch, dev, d, log):
     t = _time(lambda: w8.linear_bf16(xb, wb, bb, y=yb), 10, torch)
     out["fallback_bf16_K2050"] = {"us": round(t * 1e3, 2),
                                   "TFLOP/s": round(2.0 * 2048 * 2048 * 2050 / (t * 1e-3) / 1e12, 1)}
-    # audio 2048^3 and attention projection 24576x4096x4096 GEMM alone
+    # audio 2048^3 and attention projection 24576x4096x4096 GEMM alone, on the
+    # codes and scales the quantiser gives for seeded N(0,1) activations and
+    # N(0, 0.02^2) weights (the value distribution the step's GEMMs see: under
+    # the power cap the clock, and so the rate, depends on the operand data)
     for name, (Mg, Ng, Kg) in {"gemm_audio_2048^3": (2048, 2048, 2048),
                                "gemm_attn_proj_24576x4096x4096": (24576, 4096, 4096)}.items():
-        qa = torch.randint(-127, 128, (Mg, Kg), dtype=torch.int8, device=dev)
-        qb = torch.randint(-127, 128, (Ng, Kg), dtype=torch.int8, device=dev)
-        sa = torch.rand((Mg,), device=dev) * 0.01
-        sb = torch.rand((Ng,), device=dev) * 0.01
-        bias = torch.zeros((Ng,), dtype=torch.bfloat16, device=dev)
+        xa = torch.randn((Mg, Kg), device=dev, generator=gen).to(torch.bfloat16)
+        wg = (torch.randn((Ng, Kg), device=dev, generator=gen) * 0.02).to(torch.bfloat16)
+        qa, sa = w8.quantize_rows(xa)
+        qb, sb = w8.quantize_rows(wg)
+        del xa, wg
+        bias = (torch.randn((Ng,), device=dev, generator=gen) * 0.01).to(torch.bfloat16)
         yo = torch.empty((Mg, Ng), dtype=torch.bfloat16, device=dev)
         t = _time(lambda: w8.gemm(qa, sa, qb, sb, bias, out=yo), 20, torch)
         tops = 2.0 * Mg * Ng * Kg / (t * 1e-3) / 1e12

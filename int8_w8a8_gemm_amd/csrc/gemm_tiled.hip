@@ -49,8 +49,9 @@ namespace {
 // * Operands go global -> LDS directly (buffer_load_dwordx4 ... lds): a wave
 //   instruction moves 1 KB (64 lanes x 16 bytes); lane l lands at LDS offset
 //   16*l of that KB and is given the global chunk that belongs there under the
-//   swizzle below.  Lane offsets are fixed per tile and the stage's K position
-//   is a scalar offset, so the loads of a stage need no address arithmetic.
+//   swizzle below.  A lane's offsets are fixed per tile and the stage's K
+//   position is a scalar offset; each load's lane offset is formed from two
+//   per-lane values and wave-uniform terms as it is issued (see load_voff).
 // * An LDS row r (BK bytes = BK/16 chunks) stores logical K-chunk c at physical
 //   chunk c ^ f(r).  A fragment read has lane l on row l % 32 at logical chunk
 //   l / 32; with f(r) = (r ^ (r >> 3)) & 7 for 128-byte rows and (r >> 2) & 3
@@ -191,14 +192,15 @@ constexpr int kRawBufferWord3 = 0x00020000;  // untyped 32-bit buffer access
 
 // Per-tile addressing.  Each operand is read through a buffer resource based
 // at the tile's first row and sized to the rows that exist, so rows past M
-// (or N) read as zero.  Every lane keeps fixed byte offsets for its loads; the
-// K position of a stage goes in the scalar offset, so issuing a stage's loads
-// writes no vector registers.  KB is the row length in bytes.
+// (or N) read as zero (the range check sees the lane offset, so the row part
+// of the address stays in it); the K position of a stage goes in the scalar
+// offset.  KB is the row length in bytes.
 template <class C>
 struct Ctx {
     rsrc_t rsrc[2];  // 0: activation panel, 1: weight panel
-    uint32_t voff_a[C::LPW_A];
-    uint32_t voff_b[C::LPW_B];
+    // loads: lrow = (lane / CPR) * KB; lx = 16 x this lane's chunk before the
+    // wave-uniform part of the swizzle (see load_voff)
+    uint32_t lrow, lx, kb;
     // fragment reads: LDS byte offset of this lane's row in the wave's first
     // activation / weight sub-tile, and 16 x the physical chunk of its K-chunk
     // (lane >> 5) in that row; every other read adds compile-time constants
@@ -221,25 +223,18 @@ __device__ __forceinline__ void set_tile(Ctx<C>& c, const char* a, const char* w
 #endif
 }
 
-// Lane offsets are tile-local, so they are set once per workgroup.
+// The per-lane values of the context: tile-local, so the same for every
+// tile.  The persistent loop recomputes them (a few VALU operations) from an
+// opaque copy of the lane index at the end of each tile rather than keeping
+// them live through the epilogue, where the accumulators fill the registers.
 template <class C>
-__device__ __forceinline__ void make_ctx(Ctx<C>& c, int64_t KB, int wave, int lane) {
-    const int rsub = lane / C::CPR, pc = lane % C::CPR;
-#pragma unroll
-    for (int i = 0; i < C::LPW_A; ++i) {
-        const int r = wave * (C::BM / C::WAVES) + i * C::RPI + rsub;  // tile-local A row
-        c.voff_a[i] = (uint32_t)r * (uint32_t)KB + 16u * (uint32_t)swz<C::BK>(r, pc);
-    }
-#pragma unroll
-    for (int i = 0; i < C::LPW_B; ++i) {
-        const int r = wave * (C::BN / C::WAVES) + i * C::RPI + rsub;  // tile-local B row
-        c.voff_b[i] = (uint32_t)r * (uint32_t)KB + 16u * (uint32_t)swz<C::BK>(r, pc);
-    }
-    c.wave = wave;
-    c.lane = lane;
-    c.wm = wave % C::WM;
-    c.wn = wave / C::WM;
-    const int hi = lane >> 5;
+__device__ __forceinline__ void lane_ctx(Ctx<C>& c, int lane) {
+    const int rsub = (int)((unsigned)lane / C::CPR), pc = (int)((unsigned)lane % C::CPR);
+    c.lrow = (uint32_t)rsub * c.kb;
+    // 128-byte rows: swz(r0 + rsub, pc) = pc ^ rsub ^ ((r0 >> 3) & 7) for r0 % 8 == 0;
+    // 64-byte rows: swz(r0 + rsub, pc) = pc ^ ((rsub >> 2) & 3) for r0 % 16 == 0
+    c.lx = C::BK == 128 ? 16u * (uint32_t)(pc ^ rsub) : 16u * (uint32_t)(pc ^ ((rsub >> 2) & 3));
+    const int hi = (int)((unsigned)lane >> 5);
     const int ra = c.wm * C::TM + (lane & 31), rw = c.wn * C::TN + (lane & 31);
     c.fa = (uint32_t)(ra * C::BK);
     c.fw = (uint32_t)(C::BM * C::BK + rw * C::BK);
@@ -247,26 +242,50 @@ __device__ __forceinline__ void make_ctx(Ctx<C>& c, int64_t KB, int wave, int la
     c.gw = 16u * (uint32_t)swz<C::BK>(rw, hi);
 }
 
-// Load j (0 .. NLOAD-1) of one wave's share of a K stage: j < LPW_A loads A
-// rows, the rest B rows.  Lane l lands at LDS byte 16*l of the load's 1 KB.
 template <class C>
-__device__ __forceinline__ void stage_load_one(const Ctx<C>& c, int k0, char* lds_stage, int j) {
+__device__ __forceinline__ void make_ctx(Ctx<C>& c, int64_t KB, int wave, int lane) {
+    c.kb = (uint32_t)KB;
+    c.wave = wave;
+    c.lane = lane;
+    c.wm = wave % C::WM;
+    c.wn = wave / C::WM;
+    lane_ctx<C>(c, lane);
+}
+
+// Load j (0 .. NLOAD-1) of one wave's share of a K stage: j < LPW_A loads A
+// rows, the rest B rows.  The load covers tile rows r0 .. r0 + RPI - 1 (r0
+// wave-uniform, a multiple of RPI); lane l takes row r0 + l / CPR, logical
+// chunk l % CPR, which lands at LDS byte 16*l of the load's 1 KB, the physical
+// chunk of the swizzle.  Its lane offset is row * KB + 16 * swz(row, chunk) =
+// lrow + r0 * KB + (lx ^ 16 * ((r0 >> 3) & 7)) for 128-byte rows (the XOR term
+// is 0 for 64-byte rows): two VALU operations per load instead of a register
+// per load held across the K loop.  lrow and lx are passed by the caller
+// through an empty asm statement so that the compiler forms each offset here.
+template <class C>
+__device__ __forceinline__ void stage_load_one(const Ctx<C>& c, uint32_t lrow, uint32_t lx, int k0,
+                                               char* lds_stage, int j) {
+    static_assert(C::BK == 128 || C::BK == 64, "swizzle");
     const bool is_a = j < C::LPW_A;
     const int i = is_a ? j : j - C::LPW_A;
-    char* dst = is_a ? lds_stage + (c.wave * (C::BM / C::WAVES) + i * C::RPI) * C::BK
-                     : lds_stage + C::BM * C::BK + (c.wave * (C::BN / C::WAVES) + i * C::RPI) * C::BK;
+    const uint32_t r0 = (uint32_t)(c.wave * ((is_a ? C::BM : C::BN) / C::WAVES) + i * C::RPI);
+    const uint32_t xr = C::BK == 128 ? 16u * ((r0 >> 3) & 7u) : 0u;
+    const uint32_t voff = lrow + r0 * c.kb + (lx ^ xr);
+    char* dst = lds_stage + (is_a ? 0 : C::BM * C::BK) + r0 * C::BK;
 #if defined(__HIP_DEVICE_COMPILE__)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rsrc[is_a ? 0 : 1], (lds_void*)dst, 16,
-                                             is_a ? c.voff_a[i] : c.voff_b[i], k0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rsrc[is_a ? 0 : 1], (lds_void*)dst, 16, voff, k0,
+                                             0, 0);
 #else
     (void)dst;
+    (void)voff;
 #endif
 }
 
 template <class C>
 __device__ __forceinline__ void stage_load(const Ctx<C>& c, int k0, char* lds_stage) {
+    uint32_t lrow = c.lrow, lx = c.lx;
+    asm volatile("" : "+v"(lrow), "+v"(lx));
 #pragma unroll
-    for (int j = 0; j < C::NLOAD; ++j) stage_load_one<C>(c, k0, lds_stage, j);
+    for (int j = 0; j < C::NLOAD; ++j) stage_load_one<C>(c, lrow, lx, k0, lds_stage, j);
 }
 
 template <class C>
@@ -285,13 +304,24 @@ using Acc = typename E::acc_t[C::NI][C::MI];
 // at all for 64-byte rows; so 16 * (ch ^ f(row)) = g ^ (32*ks) ^ (64*(i & 1))
 // (128-byte rows) with g = 16 * ((l/32) ^ f(first row)) from the context:
 // one XOR-add per read.  ga, gw are that g for the two operands.
+// The four per-lane fragment-read values of the context.
+struct FragBase {
+    uint32_t fa, fw, ga, gw;
+};
+
 template <class C>
-__device__ __forceinline__ void read_frag(const char* lds_stage, const Ctx<C>& c, uint32_t ga,
-                                          uint32_t gw, int ks, int q, Frags<C>& f) {
+__device__ __forceinline__ FragBase frag_base(const Ctx<C>& c) {
+    FragBase b{c.fa, c.fw, c.ga, c.gw};
+    return b;
+}
+
+template <class C>
+__device__ __forceinline__ void read_frag(const char* lds_stage, const FragBase& fb, int ks, int q,
+                                          Frags<C>& f) {
     const bool is_a = q < C::MI;
     const int i = is_a ? q : q - C::MI;
     const uint32_t k = (uint32_t)(32 * ks) ^ (C::BK == 128 ? 64u * (uint32_t)(i & 1) : 0u);
-    const uint32_t off = ((is_a ? ga : gw) ^ k) + (is_a ? c.fa : c.fw);
+    const uint32_t off = ((is_a ? fb.ga : fb.gw) ^ k) + (is_a ? fb.fa : fb.fw);
     const v4i v = *reinterpret_cast<const v4i*>(lds_stage + off + i * 32 * C::BK);
     if (is_a) f.a[i] = v;
     else f.w[i] = v;
@@ -331,20 +361,22 @@ __device__ __forceinline__ void mfma_one(Acc<C, E>& acc, const Frags<C>& f, int 
 // RECYCLE the next fragments go to fresh registers, one read after each of the
 // first NQ MFMAs (any left over after the last); with it each fragment is read
 // into the register it replaces once its last MFMA has issued.  The fragment
-// XOR bases are passed through an empty asm statement so that their per-read
-// combinations are formed next to each read, not hoisted out of the K loop
-// into NQ x SUB registers.
+// bases (and the load offsets' lane values) are passed through an empty asm
+// statement so that their per-read combinations are formed next to each read,
+// not hoisted out of the K loop into registers of their own.
 template <class C, class E, bool READ, bool LOAD>
 __device__ __forceinline__ void mfma_step(const Ctx<C>& c, Acc<C, E>& acc, Frags<C>& cur,
                                           const char* rbuf, int rks, char* lbuf, int kload) {
-    uint32_t ga = c.ga, gw = c.gw;
-    asm volatile("" : "+v"(ga), "+v"(gw));
+    FragBase fb = frag_base(c);
+    uint32_t lrow = c.lrow, lx = c.lx;
+    asm volatile("" : "+v"(fb.fa), "+v"(fb.fw), "+v"(fb.ga), "+v"(fb.gw));
+    if (LOAD) asm volatile("" : "+v"(lrow), "+v"(lx));
     auto loads_after = [&](int j) {
         if (LOAD) {
             // loads (j * NLOAD / NMFMA) .. ((j+1) * NLOAD / NMFMA) - 1 go after MFMA j
 #pragma unroll
             for (int l = (j * C::NLOAD) / C::NMFMA; l < ((j + 1) * C::NLOAD) / C::NMFMA; ++l)
-                stage_load_one<C>(c, kload, lbuf, l);
+                stage_load_one<C>(c, lrow, lx, kload, lbuf, l);
         }
     };
     if constexpr (C::RECYCLE) {
@@ -352,9 +384,9 @@ __device__ __forceinline__ void mfma_step(const Ctx<C>& c, Acc<C, E>& acc, Frags
         for (int j = 0; j < C::NMFMA; ++j) {
             mfma_one<C, E>(acc, cur, j);  // MFMA j uses w[j / MI] and a[j % MI]
             if (READ && j % C::MI == C::MI - 1)
-                read_frag<C>(rbuf, c, ga, gw, rks, C::MI + j / C::MI, cur);
+                read_frag<C>(rbuf, fb, rks, C::MI + j / C::MI, cur);
             if (READ && j >= (C::NI - 1) * C::MI)
-                read_frag<C>(rbuf, c, ga, gw, rks, j - (C::NI - 1) * C::MI, cur);
+                read_frag<C>(rbuf, fb, rks, j - (C::NI - 1) * C::MI, cur);
             loads_after(j);
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -363,13 +395,13 @@ __device__ __forceinline__ void mfma_step(const Ctx<C>& c, Acc<C, E>& acc, Frags
 #pragma unroll
         for (int j = 0; j < C::NMFMA; ++j) {
             mfma_one<C, E>(acc, cur, j);
-            if (READ && j < C::NQ) read_frag<C>(rbuf, c, ga, gw, rks, j, nxt);
+            if (READ && j < C::NQ) read_frag<C>(rbuf, fb, rks, j, nxt);
             loads_after(j);
             __builtin_amdgcn_sched_barrier(0);
         }
         if (READ) {
 #pragma unroll
-            for (int j = C::NMFMA; j < C::NQ; ++j) read_frag<C>(rbuf, c, ga, gw, rks, j, nxt);
+            for (int j = C::NMFMA; j < C::NQ; ++j) read_frag<C>(rbuf, fb, rks, j, nxt);
             cur = nxt;
         }
     }
@@ -599,24 +631,36 @@ void gemm_tiled(const void* __restrict__ a, const float* __restrict__ sa, int64_
     make_ctx<C>(c, KB, wave, lane);
     set_tile<C>(c, ab, wb, M, N, KB, m0, n0);
 
-    // first tile: epilogue operands, then fill the ring and wait for stage 0
-    // (the bias stays in bf16 bits until it is written: converting it at once
-    // would make the wave wait for the load)
+    // Epilogue operands of a tile: row scales, column scales and bias (the
+    // bias stays in bf16 bits until it is written: converting it at once
+    // would make the wave wait for the load).  They are loaded with the tile's
+    // first stages (or during the previous tile's epilogue) and written to LDS
+    // before its K loop; with the scales in the ring they are loaded during
+    // the tile's last K stage instead and written once the K loop is done
+    // with the ring, so no register holds them across the K loop.
+    // Every thread loads (clamped indices; only threads below BM / BN store),
+    // so that each load defines its register anew and nothing carries over
+    // from the previous tile.
     float nsa = 0.f, nsw = 0.f;
     uint32_t nb = 0;
-    if (SCALES && tid < BM) nsa = sa[m0 + tid < M ? m0 + tid : M - 1];
-    if (!OUT_I32 && tid < BN) {
-        const int64_t n = n0 + tid < N ? n0 + tid : N - 1;
-        if (SCALES) nsw = sw[n];
-        if (bias) nb = bias[n];
-    }
-    // the epilogue operands go to LDS now, or (scales in the ring) stay in
-    // registers until the K loop is done with the ring
+    auto load_scales = [&](int64_t m0_, int64_t n0_) {
+        if (SCALES) nsa = sa[m0_ + tid < M ? m0_ + tid : M - 1];
+        if (!OUT_I32) {
+            const int64_t n = n0_ + tid < N ? n0_ + tid : N - 1;
+            if (SCALES) nsw = sw[n];
+            nb = bias ? (uint32_t)bias[n] : 0u;
+        }
+    };
+    if constexpr (!C::SCALES_IN_RING) load_scales(m0, n0);
     auto put_scales = [&]() {
-        if (SCALES && tid < BM) sa_l[tid] = nsa;
-        if (!OUT_I32 && tid < BN) {
-            if (SCALES) sw_l[tid] = nsw;
-            b_l[tid] = bf16_bits_to_float(nb);
+        // an opaque copy of the thread index: the LDS addresses are formed
+        // here, not kept in registers across the K loop
+        int et = tid;
+        asm volatile("" : "+v"(et));
+        if (SCALES && et < BM) sa_l[et] = nsa;
+        if (!OUT_I32 && et < BN) {
+            if (SCALES) sw_l[et] = nsw;
+            b_l[et] = bf16_bits_to_float(nb);
         }
     };
     for (int s = 0; s < NST; ++s)
@@ -633,8 +677,9 @@ void gemm_tiled(const void* __restrict__ a, const float* __restrict__ sa, int64_
 #pragma unroll
             for (int j = 0; j < MI; ++j) acc[i][j] = (typename E::acc_t){};
         Frags<C> cur;
+        const FragBase fb0 = frag_base(c);
 #pragma unroll
-        for (int q = 0; q < C::NQ; ++q) read_frag<C>(smem, c, c.ga, c.gw, 0, q, cur);
+        for (int q = 0; q < C::NQ; ++q) read_frag<C>(smem, fb0, 0, q, cur);
 
         int kt = 0;
         for (; kt + NST < KT; ++kt) k_stage<C, E, true, true, true>(c, smem, kt, acc, cur);
@@ -643,6 +688,7 @@ void gemm_tiled(const void* __restrict__ a, const float* __restrict__ sa, int64_
             ++kt;
         }
         for (; kt + 1 < KT; ++kt) k_stage<C, E, false, true, false>(c, smem, kt, acc, cur);
+        if constexpr (C::SCALES_IN_RING) load_scales(m0, n0);
         k_stage<C, E, false, false, false>(c, smem, kt, acc, cur, tail);
 
         const int64_t t_next = t + gridDim.x;
@@ -657,12 +703,7 @@ void gemm_tiled(const void* __restrict__ a, const float* __restrict__ sa, int64_
             tile_of<C>(t_next, tm, tn, tile_m, tile_n);
             m0n = tile_m * BM;
             n0n = tile_n * BN;
-            if (SCALES && tid < BM) nsa = sa[m0n + tid < M ? m0n + tid : M - 1];
-            if (!OUT_I32 && tid < BN) {
-                const int64_t n = n0n + tid < N ? n0n + tid : N - 1;
-                if (SCALES) nsw = sw[n];
-                if (bias) nb = bias[n];
-            }
+            if constexpr (!C::SCALES_IN_RING) load_scales(m0n, n0n);
             set_tile<C>(c, ab, wb, M, N, KB, m0n, n0n);
             stage_load<C>(c, 0, smem);  // next tile's stage 0 -> buffer 0
         }
@@ -688,6 +729,7 @@ void gemm_tiled(const void* __restrict__ a, const float* __restrict__ sa, int64_
         if constexpr (!C::SCALES_IN_RING) put_scales();
         wait_vm_lgkm0<0>();  // the next tile's stage 0 (and this tile's stores) are done ...
         __syncthreads();     // ... for every wave, and the staging area is free
+        lane_ctx<C>(c, elane);
         for (int s = 1; s < NST; ++s)
             if (s < KT) stage_load<C>(c, s * BK, smem + s * C::STAGE);
         t = t_next;

@@ -133,7 +133,9 @@ def test_quantize_empty_rows_is_noop():
 # there are more than 256.  Covered here: 64 x 64 tiles (the first seven shapes),
 # 128 x 128 tiles (2048^3 and 2000 x 1984, ragged), 256 x 256 tiles with ragged
 # M, with ragged N, and with both (4100 x 4096, 4096 x 4160, 3900 x 3776; the
-# first two with workgroups taking two tiles).
+# first two with workgroups taking two tiles).  The 384 x 256 tiles (INT8
+# without GELU, long K loops or many tiles) are covered by
+# test_gemm_xl_tiles_ragged_sampled and by the full-size FFN tests.
 GEMM_SHAPES = [(1, 64, 128), (64, 128, 256), (129, 192, 384), (300, 320, 1024), (257, 64, 4096),
                (1000, 448, 2048), (33, 256, 16384), (2048, 2048, 2048), (2000, 1984, 512),
                (4100, 4096, 256), (4096, 4160, 128), (3900, 3776, 128)]
