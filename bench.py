@@ -44,7 +44,7 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--M", type=int, default=24576)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=0,
@@ -321,11 +321,20 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def _time(fn, iters, torch):
-    """Average ms per call over `iters` calls, timed with events on the current stream."""
+def _time(fn, iters, torch, warm_ms=20.0):
+    """Average ms per call over `iters` calls, timed with events on the current stream,
+    after at least `warm_ms` of untimed calls: the GPU's clocks take some tens of
+    milliseconds of steady work to settle (a 350 us GEMM measured ~15% slower over
+    its first 20 calls after other work)."""
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    import time
     fn()
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < warm_ms:
+        for _ in range(8):  # back to back, so that short kernels keep the GPU busy
+            fn()
+        torch.cuda.synchronize()
     s.record()
     for _ in range(iters):
         fn()

@@ -38,13 +38,17 @@ namespace {
 //   large: 256 x 256 tile, 4 x 2 waves (two per SIMD, so one wave's load issue,
 //          LDS waits and barrier arrival overlap the other's MFMAs), each wave
 //          64 x 128.
+//   mid:   192 x 256 tile, 2 x 4 waves of 96 x 64: three quarters of a large
+//          tile's work, for row counts where large tiles leave many CUs idle
+//          in their last round (the ~2300-row text projection: 160 large
+//          tiles or 208 mid ones on 256 CUs).
 //   small: 128 x 128 tile, 2 x 2 waves of 64 x 64.
 //   tiny:  64 x 64 tile, 2 x 2 waves of 32 x 32.
 // The launcher takes the largest of large/small/tiny whose tile count covers
 // at least half of the CUs (a large tile on a CU still outruns four small
 // ones; measured on the 2378-row text projection, the 2048^3 audio GEMM and
-// 1024 x 1024 x 4096), and xl over large where it needs no more rounds of
-// tiles per CU and the tile loop is long (see launch_tiles).
+// 1024 x 1024 x 4096), then xl or mid instead of large where their rounds of
+// tiles per CU cost less (see launch_tiles).
 //
 // * Operands go global -> LDS directly (buffer_load_dwordx4 ... lds): a wave
 //   instruction moves 1 KB (64 lanes x 16 bytes); lane l lands at LDS offset
@@ -147,8 +151,12 @@ struct Cfg {
 #ifndef W8A8_LARGE_CFG
 #define W8A8_LARGE_CFG 256, 256, 4, 2, 128, 2
 #endif
+#ifndef W8A8_MID_CFG
+#define W8A8_MID_CFG 192, 256, 2, 4, 128, 2
+#endif
 typedef Cfg<W8A8_XL_CFG> CfgXL;
 typedef Cfg<W8A8_LARGE_CFG> CfgLarge;
+typedef Cfg<W8A8_MID_CFG> CfgMid;
 typedef Cfg<128, 128, 2, 2, 128, 2> CfgSmall;
 typedef Cfg<64, 64, 2, 2, 128, 2> CfgTiny;
 
@@ -783,9 +791,17 @@ hipError_t launch_tiles(const void* a, const float* sa, int64_t M, const void* w
             return launch_cfg<CfgXL, E, OUT_I32, ACT, VEC_OUT>(a, sa, M, w, sw, N, K, bias, out,
                                                               cus, stream);
     }
-    if (2 * tile_count<CfgLarge>(M, N) >= cus)
+    if (2 * tile_count<CfgLarge>(M, N) >= cus) {
+        // mid when its rounds x 3/4 of a large tile's work, with 7% for its
+        // lower efficiency per MFMA, come to less than large's rounds
+        const int64_t tl = tile_count<CfgLarge>(M, N), tmid = tile_count<CfgMid>(M, N);
+        const int64_t rounds_l = (tl + cus - 1) / cus, rounds_mid = (tmid + cus - 1) / cus;
+        if (8025 * rounds_mid < 10000 * rounds_l)
+            return launch_cfg<CfgMid, E, OUT_I32, ACT, VEC_OUT>(a, sa, M, w, sw, N, K, bias, out,
+                                                               cus, stream);
         return launch_cfg<CfgLarge, E, OUT_I32, ACT, VEC_OUT>(a, sa, M, w, sw, N, K, bias, out, cus,
                                                              stream);
+    }
     if (2 * tile_count<CfgSmall>(M, N) >= cus)
         return launch_cfg<CfgSmall, E, OUT_I32, ACT, VEC_OUT>(a, sa, M, w, sw, N, K, bias, out, cus,
                                                              stream);

@@ -129,16 +129,19 @@ def test_quantize_empty_rows_is_noop():
 
 # On a 256-CU MI355X the launcher takes 256 x 256 tiles when there are at
 # least 128 of them, else 128 x 128 tiles when there are at least 128 of those,
-# else 64 x 64 tiles; a persistent 256 x 256 workgroup takes several tiles when
-# there are more than 256.  Covered here: 64 x 64 tiles (the first seven shapes),
-# 128 x 128 tiles (2048^3 and 2000 x 1984, ragged), 256 x 256 tiles with ragged
-# M, with ragged N, and with both (4100 x 4096, 4096 x 4160, 3900 x 3776; the
-# first two with workgroups taking two tiles).  The 384 x 256 tiles (INT8
-# without GELU, long K loops or many tiles) are covered by
-# test_gemm_xl_tiles_ragged_sampled and by the full-size FFN tests.
+# else 64 x 64 tiles; instead of 256 x 256 it takes 192 x 256 tiles where their
+# rounds of tiles per CU cost less, and 384 x 256 (INT8 without GELU, long K
+# loops or many tiles).  A persistent workgroup takes several tiles when there
+# are more than 256.  Covered here: 64 x 64 tiles (the first seven shapes),
+# 128 x 128 tiles (2048^3 and 2000 x 1984, ragged), 192 x 256 tiles with ragged
+# M, with ragged N (4100 x 4096, 4096 x 4160, both with workgroups taking two
+# tiles) and on a text-projection row count (2378 x 4096), 256 x 256 tiles
+# with ragged M and N (3900 x 3776, 3900 x 4032).  The 384 x 256 tiles are
+# covered by test_gemm_xl_tiles_ragged_sampled and by the full-size FFN tests.
 GEMM_SHAPES = [(1, 64, 128), (64, 128, 256), (129, 192, 384), (300, 320, 1024), (257, 64, 4096),
                (1000, 448, 2048), (33, 256, 16384), (2048, 2048, 2048), (2000, 1984, 512),
-               (4100, 4096, 256), (4096, 4160, 128), (3900, 3776, 128)]
+               (4100, 4096, 256), (4096, 4160, 128), (2378, 4096, 512), (3900, 3776, 128),
+               (3900, 4032, 128)]
 
 
 @pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
@@ -163,7 +166,8 @@ def test_gemm_int32_extremes_and_max_k():
 
 
 @pytest.mark.parametrize("M,N,K", [(64, 128, 256), (129, 192, 384), (2048, 2048, 2048),
-                                   (2000, 1984, 512), (4100, 4160, 128), (3900, 3776, 128)])
+                                   (2000, 1984, 512), (4100, 4160, 128), (2378, 4096, 256),
+                                   (3900, 3776, 128)])
 @pytest.mark.parametrize("act", [w8.ACT_NONE, w8.ACT_GELU_TANH])
 @pytest.mark.parametrize("with_bias", [True, False])
 def test_gemm_epilogue_matches_oracle(M, N, K, act, with_bias):
@@ -532,11 +536,11 @@ def test_fallback_on_conforming_shapes_and_gelu():
 
 
 # The tiled BF16 path (K % 64 == 0, 16-byte aligned operands) on each tile
-# configuration: 64 x 64 (first two), 128 x 128, 256 x 256 (last two, the
-# last with workgroups taking two tiles); N % 8 != 0 stores element by
-# element, K = 64 is a single stage.
+# configuration: 64 x 64 (first two), 128 x 128, 192 x 256 (4100 x 4100 and
+# 4352 x 4104, with workgroups taking two tiles), 256 x 256 (3900 x 3900);
+# N % 8 != 0 stores element by element, K = 64 is a single stage.
 @pytest.mark.parametrize("M,N,K", [(300, 100, 64), (97, 256, 1024), (2000, 1992, 256),
-                                   (4100, 4100, 64), (4352, 4104, 192)])
+                                   (4100, 4100, 64), (4352, 4104, 192), (3900, 3900, 64)])
 @pytest.mark.parametrize("act", [w8.ACT_NONE, w8.ACT_GELU_TANH])
 def test_fallback_tiled_path(M, N, K, act):
     say(f"fallback tiled M={M} N={N} K={K} act={act}")
@@ -550,9 +554,10 @@ def test_fallback_tiled_path(M, N, K, act):
 
 # The tiled BF16 path with a K tail (K even, K % 64 != 0, rows 4-byte aligned):
 # the last stage's loads run on into the next row and are masked.  K = 2 is a
-# single partial stage; 2048 x 2048 x 2050 is the fallback workload.
+# single partial stage; 2048 x 2048 x 2050 is the fallback workload; 4100 x
+# 4100 runs 192 x 256 tiles, 3900 x 4032 256 x 256 tiles.
 @pytest.mark.parametrize("M,N,K", [(300, 100, 2), (97, 256, 66), (257, 192, 130),
-                                   (2048, 2048, 2050), (4100, 4100, 190)])
+                                   (2048, 2048, 2050), (4100, 4100, 190), (3900, 4032, 130)])
 @pytest.mark.parametrize("act", [w8.ACT_NONE, w8.ACT_GELU_TANH])
 def test_fallback_tiled_k_tail(M, N, K, act):
     say(f"fallback tiled K tail M={M} N={N} K={K} act={act}")
