@@ -156,8 +156,11 @@ struct Cfg {
 #endif
 typedef Cfg<W8A8_XL_CFG> CfgXL;
 typedef Cfg<W8A8_LARGE_CFG> CfgLarge;
+#ifndef W8A8_SMALL_CFG
+#define W8A8_SMALL_CFG 128, 128, 2, 2, 128, 2
+#endif
 typedef Cfg<W8A8_MID_CFG> CfgMid;
-typedef Cfg<128, 128, 2, 2, 128, 2> CfgSmall;
+typedef Cfg<W8A8_SMALL_CFG> CfgSmall;
 typedef Cfg<64, 64, 2, 2, 128, 2> CfgTiny;
 
 template <int BK>

@@ -51,6 +51,7 @@ def _load():
     I64 = ctypes.c_int64
     I = ctypes.c_int
     lib.oracle_quantize_rows.argtypes = [P, I64, I64, P, P, I]
+    lib.oracle_quantize_blocks.argtypes = [P, I64, I64, I64, I64, I64, P, P, I]
     lib.oracle_gemm_i32.argtypes = [P, I64, P, I64, I64, P, I]
     lib.oracle_epilogue.argtypes = [P, P, I64, P, I64, P, I, P, I]
     lib.oracle_linear_bf16.argtypes = [P, I64, I64, P, I64, P, I, P, I]
@@ -116,6 +117,27 @@ def quantize_rows(x_bf16: np.ndarray, nthreads=None):
     s = np.empty((R,), np.float32)
     _check(_load().oracle_quantize_rows(_ptr(x), R, C, _ptr(q), _ptr(s), _threads(nthreads)),
            "oracle_quantize_rows")
+    return q, s
+
+
+def quantize_blocks(x_bf16: np.ndarray, batch: int, heads: int, block: int, nthreads=None):
+    """Per-block symmetric INT8 quantisation of attention Query / Key (the
+    attention paragraph of the 智猩猩 article, section 01.3, says Q and K are
+    quantised to INT8; block size and layout are a reading).
+
+    x_bf16: uint16 [batch * S, heads * D] token rows (or [batch, S, heads * D]);
+    a block is `block` consecutive tokens of one sample and one head.  Returns
+    (q int8 of x's shape, s float32 [batch, ceil(S / block), heads]).
+    """
+    x = _c(x_bf16, np.uint16)
+    rows, C = x.reshape(-1, x.shape[-1]).shape
+    assert rows % batch == 0 and C % heads == 0
+    S, D = rows // batch, C // heads
+    nblk = -(-S // block) if S else 0
+    q = np.empty(x.shape, np.int8)
+    s = np.empty((batch, nblk, heads), np.float32)
+    _check(_load().oracle_quantize_blocks(_ptr(x), batch, S, heads, D, block, _ptr(q), _ptr(s),
+                                          _threads(nthreads)), "oracle_quantize_blocks")
     return q, s
 
 

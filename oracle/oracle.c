@@ -25,6 +25,8 @@
  *   F  BF16 fallback: sum of exact products in float64, rounded once to bf16.
  *   G  guard: K % 128 == 0, 128 <= K <= 131072, N % 64 == 0, N >= 64.
  *   C  mask nonzero = valid; output keeps (sample, position) order.
+ *   QB attention Q / K: blocks of `block` tokens of one sample and one head of
+ *      a token-row matrix [B x S x H*D], each quantised as in Q over the block.
  *
  * Build: gcc -O2 -ffp-contract=off -fno-fast-math -shared -fPIC -pthread.
  */
@@ -161,6 +163,72 @@ int oracle_quantize_rows(const uint16_t* x, int64_t rows, int64_t cols, int8_t* 
     if (rows < 0 || cols < 0) return -1;
     quant_ctx c = {x, cols, q, scale};
     parallel_rows(quant_rows, &c, rows, nthreads);
+    return 0;
+}
+
+/* ---------------------------------------------------------------------- */
+/* QB: per-block symmetric INT8 quantisation of attention Query / Key.     */
+/*    The pages (智猩猩 article, section 01.3, the attention paragraph)    */
+/*    state only that Query and Key are quantised to INT8 for the sparse  */
+/*    attention; block size and granularity are a reading: x holds token  */
+/*    rows [B x S x H*D] (a projection's output, head h in columns        */
+/*    h*D .. h*D+D-1), and one block is `block` consecutive tokens of one */
+/*    sample and one head (the last block of a sample may be shorter).    */
+/*    Each block is quantised with the steps of Q above, the absolute     */
+/*    maximum taken over the whole block.  scale[(b*nblk + j)*H + h].     */
+/* ---------------------------------------------------------------------- */
+
+typedef struct {
+    const uint16_t* x; int64_t S, H, D, block, nblk; int8_t* q; float* s;
+} qblk_ctx;
+
+static void quant_blocks(void* p, int64_t i0, int64_t i1) {
+    qblk_ctx* c = (qblk_ctx*)p;
+    const int64_t C = c->H * c->D;
+    for (int64_t i = i0; i < i1; ++i) {          /* i = b * nblk + j: one token block */
+        const int64_t b = i / c->nblk, j = i % c->nblk;
+        const int64_t t0 = j * c->block;
+        const int64_t t1 = t0 + c->block < c->S ? t0 + c->block : c->S;
+        for (int64_t h = 0; h < c->H; ++h) {
+            /* 1. absolute maximum over the block's tokens and the head's columns */
+            float a = 0.0f;
+            for (int64_t t = t0; t < t1; ++t)
+                for (int64_t d = 0; d < c->D; ++d) {
+                    float v = fabsf(bf16_to_f32(c->x[(b * c->S + t) * C + h * c->D + d]));
+                    if (v > a) a = v;
+                }
+            float* sp = &c->s[i * c->H + h];
+            /* 2. degenerate blocks: scale 0, all codes 0 */
+            if (!(a >= 0x1p-100f)) {
+                *sp = 0.0f;
+                for (int64_t t = t0; t < t1; ++t)
+                    for (int64_t d = 0; d < c->D; ++d) c->q[(b * c->S + t) * C + h * c->D + d] = 0;
+                continue;
+            }
+            /* 3. scale and reciprocal, one correctly rounded division each */
+            float s = a / 127.0f;
+            float inv = 127.0f / a;
+            *sp = s;
+            /* 4. codes: round-half-even(x * inv), clamped */
+            for (int64_t t = t0; t < t1; ++t)
+                for (int64_t d = 0; d < c->D; ++d) {
+                    const int64_t e = (b * c->S + t) * C + h * c->D + d;
+                    float n = nearbyintf(bf16_to_f32(c->x[e]) * inv);
+                    if (n > 127.0f) n = 127.0f;
+                    if (n < -127.0f) n = -127.0f;
+                    c->q[e] = (int8_t)(int)n;
+                }
+        }
+    }
+}
+
+int oracle_quantize_blocks(const uint16_t* x, int64_t B, int64_t S, int64_t H, int64_t D,
+                           int64_t block, int8_t* q, float* scale, int nthreads) {
+    if (fegetround() != FE_TONEAREST) return -1;
+    if (B < 0 || S < 0 || H < 0 || D < 0 || block < 1) return -1;
+    const int64_t nblk = (S + block - 1) / block;
+    qblk_ctx c = {x, S, H, D, block, nblk, q, scale};
+    parallel_rows(quant_blocks, &c, B * nblk, nthreads);
     return 0;
 }
 

@@ -296,6 +296,98 @@ def test_quantize_empty_and_single_column():
 
 
 # ---------------------------------------------------------------------------
+# QB: per-block quantisation of attention Q / K
+# ---------------------------------------------------------------------------
+
+def _golden_block_cases():
+    cases = []
+    with open(os.path.join(GOLDEN, "quantize_blocks.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            dims, xs, qs, a = (p.strip() for p in line.split(";"))
+            B, S, H, D, blk = (int(v) for v in dims.split())
+            cases.append((B, S, H, D, blk, _parse_vals(xs), [int(v) for v in _parse_vals(qs)],
+                          _parse_vals(a)))
+    return cases
+
+
+@pytest.mark.parametrize("case", _golden_block_cases(), ids=lambda c: f"B{c[0]}S{c[1]}H{c[2]}")
+def test_quantize_blocks_hand_worked(case):
+    B, S, H, D, blk, xs, qs, amax = case
+    x = np.array([bf16_bits_of_value(v) for v in xs], np.uint16).reshape(B * S, H * D)
+    q, s = oracle.quantize_blocks(x, B, H, blk)
+    assert q.reshape(-1).tolist() == qs
+    exp = [float(rn32(Fr(a) / 127)) if a >= 2.0**-100 else 0.0 for a in amax]
+    assert s.reshape(-1).tolist() == exp
+
+
+def _blocks_as_rows(x, B, H, blk):
+    """Rearranges token rows [B*S, H*D] into one row per (sample, block, head),
+    padding each sample with zero tokens to whole blocks.  Plain data movement:
+    zeros change neither a block's absmax nor any code, so per-row quantisation
+    of these rows is per-block quantisation of x."""
+    rows, C = x.shape
+    S, D = rows // B, C // H
+    nblk = -(-S // blk)
+    pad = np.zeros((B, nblk * blk, H, D), x.dtype)
+    pad[:, :S] = x.reshape(B, S, H, D)
+    return pad.reshape(B, nblk, blk, H, D).transpose(0, 1, 3, 2, 4).reshape(B * nblk * H, blk * D)
+
+
+def _rows_as_blocks(r, B, S, H, D, blk):
+    nblk = -(-S // blk)
+    t = r.reshape(B, nblk, H, blk, D).transpose(0, 1, 3, 2, 4).reshape(B, nblk * blk, H, D)
+    return t[:, :S].reshape(B * S, H * D)
+
+
+@pytest.mark.parametrize("B,S,H,D,blk", [(1, 1, 1, 8, 1), (1, 37, 1, 16, 1), (2, 37, 3, 16, 8),
+                                         (3, 130, 4, 64, 64), (1, 257, 2, 128, 128),
+                                         (2, 5, 2, 8, 16), (1, 96, 8, 32, 32)])
+def test_quantize_blocks_reduces_to_per_row_quantisation(B, S, H, D, blk):
+    """Per-block quantisation equals the (separately pinned) per-row routine
+    applied to each block laid out as one row: pins the block layout, the
+    ragged last block of every sample, independence of samples and heads."""
+    rng = np.random.default_rng(B * 1000 + S * 10 + H + D + blk)
+    v = rng.standard_normal((B * S, H * D)).astype(np.float32)
+    v *= np.float32(2.0) ** rng.integers(-60, 60, (B * S, 1)).astype(np.float32)
+    x = wl.to_bf16_bits(v)
+    if B * S > 3:
+        x[B * S // 2, :D] = 0  # a zero token row inside a block
+    q, s = oracle.quantize_blocks(x, B, H, blk)
+    qr, sr = oracle.quantize_rows(_blocks_as_rows(x, B, H, blk))
+    assert np.array_equal(s.reshape(-1), sr)
+    assert np.array_equal(q, _rows_as_blocks(qr, B, S, H, D, blk))
+
+
+def test_quantize_blocks_one_token_blocks_equal_per_row_on_one_head():
+    rng = np.random.default_rng(12)
+    x = wl.to_bf16_bits(rng.standard_normal((50, 96)).astype(np.float32))
+    x[3] = 0
+    q, s = oracle.quantize_blocks(x, 1, 1, 1)
+    qr, sr = oracle.quantize_rows(x)
+    assert np.array_equal(q, qr) and np.array_equal(s.reshape(-1), sr)
+
+
+def test_quantize_blocks_invariants_and_degenerate_blocks():
+    rng = np.random.default_rng(13)
+    B, S, H, D, blk = 2, 70, 4, 16, 32
+    x = wl.to_bf16_bits(rng.standard_normal((B * S, H * D)).astype(np.float32))
+    x[:32, 16:32] = 0          # sample 0, block 0, head 1: all zero
+    x[S:S + 32, :16] = wl.to_bf16_bits(np.full((32, 16), 2.0**-101, np.float32))  # below 2^-100
+    q, s = oracle.quantize_blocks(x, B, H, blk)
+    assert s[0, 0, 1] == 0 and s[1, 0, 0] == 0
+    rows = _blocks_as_rows(x, B, H, blk)
+    _invariants(rows, _blocks_as_rows(q, B, H, blk), s.reshape(-1))
+
+
+def test_quantize_blocks_empty():
+    q, s = oracle.quantize_blocks(np.zeros((0, 32), np.uint16), 1, 2, 64)
+    assert q.shape == (0, 32) and s.shape == (1, 0, 2)
+
+
+# ---------------------------------------------------------------------------
 # I: INT32 product
 # ---------------------------------------------------------------------------
 
