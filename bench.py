@@ -364,6 +364,23 @@ def extra_benches(w8, wl, np, torch, dev, d, log):
     gbs = (3.0 * M * K + 4.0 * M) / (t * 1e-3) / 1e9
     out["quantize_24576x4096_rotating"] = {"us": round(t * 1e3, 2), "GB/s": round(gbs, 1),
                                            "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+    # per-block quantisation of the video self-attention Q and K (24576 tokens x
+    # 32 heads x 128; blocks of 128 tokens for Q, 64 for K), rotating over the
+    # same 4 inputs as the row quantiser
+    for name, blk in (("quantize_blocks_q_24576x32x128_b128", 128),
+                      ("quantize_blocks_k_24576x32x128_b64", 64)):
+        nsc = 32 * (-(-M // blk))
+        sbs = [torch.empty((1, -(-M // blk), 32), dtype=torch.float32, device=dev) for _ in range(4)]
+
+        def qblocks(blk=blk, sbs=sbs):
+            i = it[0] % 4
+            it[0] += 1
+            w8.quantize_blocks(xs[i], 1, 32, blk, q=qs[i], scale=sbs[i])
+
+        t = _time(qblocks, 20, torch)
+        nbytes = 3 * M * K + 4 * nsc
+        out[name] = {"us": round(t * 1e3, 2), "GB/s": round(nbytes / (t * 1e-3) / 1e9, 1),
+                     "frac_hbm": round(nbytes / (t * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
     del xs, qs, ss
     # compaction of the text rows [8 x 512 x 4096]
     g = wl.guarded_mixed()

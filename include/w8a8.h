@@ -71,6 +71,33 @@ typedef enum { W8A8_PATH_INT8 = 0, W8A8_PATH_BF16 = 1 } w8a8_path;
 W8A8_API int w8a8_quantize_rows(const uint16_t* x, int64_t rows, int64_t cols, int8_t* q, float* scale,
                        void* stream);
 
+/* Largest block (tokens x head_dim values) w8a8_quantize_blocks holds in registers. */
+#define W8A8_MAX_BLOCK_VALUES 32768
+
+/*
+ * Per-block symmetric INT8 quantisation of attention Query / Key (section
+ * 01.3, attention paragraph: the sparse attention quantises Query and Key to
+ * INT8; the page gives no block size or layout, so those are the caller's).
+ *
+ *   x     [batch x seq x heads*head_dim] bf16 token rows (a projection's output;
+ *         head h in columns h*head_dim .. h*head_dim + head_dim - 1)
+ *   q     [batch x seq x heads*head_dim] int8 codes out, same layout
+ *   scale [batch x ceil(seq/block) x heads] fp32 out, index (b*nblk + j)*heads + h
+ *
+ * A block is `block` consecutive tokens (the last block of each sample may be
+ * shorter) of one sample and one head: block x head_dim values with one
+ * scale, computed exactly as w8a8_quantize_rows computes a row's (a = max|x|
+ * over the block; a < 2^-100 gives scale 0 and zero codes).  With block = 1
+ * and heads = 1 it is w8a8_quantize_rows.
+ * Requirements (W8A8_EINVAL otherwise): head_dim % 8 == 0, head_dim >= 8;
+ * min(block, seq) * head_dim <= W8A8_MAX_BLOCK_VALUES; fewer than 2^31 blocks
+ * (batch * ceil(seq/block) * heads); x 16-byte, q 8-byte, scale 4-byte
+ * aligned.  batch, seq or heads = 0 is a no-op.
+ */
+W8A8_API int w8a8_quantize_blocks(const uint16_t* x, int64_t batch, int64_t seq, int64_t heads,
+                                  int64_t head_dim, int64_t block, int8_t* q, float* scale,
+                                  void* stream);
+
 /*
  * Fused GELU + per-row INT8 quantisation: the input of a linear that follows a
  * GELU-tanh (the FFN down projection, whose input is the up projection's

@@ -28,7 +28,7 @@ ACT_NONE, ACT_GELU_TANH = 0, 1
 PATH_INT8, PATH_BF16 = 0, 1
 MAX_K = 131072
 
-EXPORTS = ("w8a8_quantize_rows", "w8a8_gelu_quantize_rows", "w8a8_gelu_bf16", "w8a8_gemm", "w8a8_linear", "w8a8_linear_bf16",
+EXPORTS = ("w8a8_quantize_rows", "w8a8_quantize_blocks", "w8a8_gelu_quantize_rows", "w8a8_gelu_bf16", "w8a8_gemm", "w8a8_linear", "w8a8_linear_bf16",
            "compact_padded_rows", "w8a8_compact_quantize_rows", "w8a8_guard", "w8a8_linear_workspace_bytes",
            "w8a8_status_str")
 
@@ -52,6 +52,7 @@ def lib():
     L = ctypes.CDLL(LIB_PATH)
     P, I64, I, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
     L.w8a8_quantize_rows.argtypes = [P, I64, I64, P, P, P]
+    L.w8a8_quantize_blocks.argtypes = [P, I64, I64, I64, I64, I64, P, P, P]
     L.w8a8_gelu_quantize_rows.argtypes = [P, I64, I64, P, P, P]
     L.w8a8_gelu_bf16.argtypes = [P, I64, P, P]
     L.w8a8_gemm.argtypes = [P, P, I64, P, P, I64, I64, P, I, I, P, P]
@@ -137,6 +138,32 @@ def quantize_rows(x: torch.Tensor, q: Optional[torch.Tensor] = None,
     _need(scale, "scale", torch.float32, (R,))
     _check("w8a8_quantize_rows",
            lib().w8a8_quantize_rows(_p(x), R, C, _p(q), _p(scale), _stream(stream)))
+    return q, scale
+
+
+def quantize_blocks(x: torch.Tensor, batch: int, heads: int, block: int,
+                    q: Optional[torch.Tensor] = None, scale: Optional[torch.Tensor] = None,
+                    stream=None):
+    """Per-block symmetric INT8 quantisation of attention Q / K: x bf16 token rows
+    [batch * seq, heads * head_dim] (or [batch, seq, heads * head_dim]); one scale per
+    `block` consecutive tokens of one sample and one head.  Returns (q int8 of x's shape,
+    scale fp32 [batch, ceil(seq / block), heads])."""
+    _need(x, "x", torch.bfloat16)
+    if x.dim() not in (2, 3):
+        raise ValueError("x must be 2-D or 3-D")
+    rows, C = x.reshape(-1, x.shape[-1]).shape
+    if batch <= 0 or heads <= 0 or block <= 0 or rows % batch or C % heads:
+        raise ValueError("batch, heads and block must be positive and divide the shape")
+    S, D = rows // batch, C // heads
+    nblk = -(-S // block)
+    q = q if q is not None else torch.empty(x.shape, dtype=torch.int8, device=x.device)
+    scale = scale if scale is not None else torch.empty((batch, nblk, heads), dtype=torch.float32,
+                                                        device=x.device)
+    _need(q, "q", torch.int8, tuple(x.shape))
+    _need(scale, "scale", torch.float32, (batch, nblk, heads))
+    _check("w8a8_quantize_blocks",
+           lib().w8a8_quantize_blocks(_p(x), batch, S, heads, D, block, _p(q), _p(scale),
+                                      _stream(stream)))
     return q, scale
 
 

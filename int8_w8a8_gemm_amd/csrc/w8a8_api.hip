@@ -50,6 +50,24 @@ int w8a8_quantize_rows(const uint16_t* x, int64_t rows, int64_t cols, int8_t* q,
     return launched(w8a8::launch_quantize_rows(x, rows, cols, q, scale, as_stream(stream)));
 }
 
+int w8a8_quantize_blocks(const uint16_t* x, int64_t batch, int64_t seq, int64_t heads,
+                         int64_t head_dim, int64_t block, int8_t* q, float* scale, void* stream) {
+    if (batch < 0 || seq < 0 || heads < 0 || head_dim < 0 || block < 1) return W8A8_EINVAL;
+    if (batch == 0 || seq == 0 || heads == 0) return W8A8_OK;
+    if (head_dim < 8 || head_dim % 8 != 0) return W8A8_EINVAL;
+    // the block is held in registers: at most 256 threads x 16 chunks of 8 values
+    if ((seq < block ? seq : block) > W8A8_MAX_BLOCK_VALUES / head_dim) return W8A8_EINVAL;
+    const int64_t nblk = (seq + block - 1) / block;
+    if (heads > (kMaxRows - 1) / head_dim || nblk > (kMaxRows - 1) / heads ||
+        batch > (kMaxRows - 1) / (nblk * heads))
+        return W8A8_EINVAL;  // grid of batch * nblk * heads workgroups
+    if (seq > INT64_MAX / (heads * head_dim) / batch) return W8A8_EINVAL;
+    if (!x || !q || !scale || !aligned(x, 16) || !aligned(q, 8) || !aligned(scale, 4))
+        return W8A8_EINVAL;
+    return launched(w8a8::launch_quantize_blocks(x, batch, seq, heads, head_dim, block, q, scale,
+                                                 as_stream(stream)));
+}
+
 int w8a8_gelu_quantize_rows(const uint16_t* y, int64_t rows, int64_t cols, int8_t* q,
                             float* scale, void* stream) {
     if (rows < 0 || cols < 0 || rows >= kMaxRows) return W8A8_EINVAL;

@@ -178,6 +178,26 @@ def test_compact_quantize_rejects_bad_arguments():
     assert cq(A16, A16, 1 << 20, 1 << 12, 8, A16, A16, A16, A16) == w8.EINVAL  # B*L >= 2^31
 
 
+def test_quantize_blocks_rejects_bad_arguments():
+    L = w8.lib()
+    qb = lambda x, B, S, H, D, blk, q, sc: L.w8a8_quantize_blocks(x, B, S, H, D, blk, q, sc, NULL)
+    assert qb(A16, -1, 128, 2, 64, 64, A16, A16) == w8.EINVAL
+    assert qb(A16, 1, -1, 2, 64, 64, A16, A16) == w8.EINVAL
+    assert qb(A16, 1, 128, -2, 64, 64, A16, A16) == w8.EINVAL
+    assert qb(A16, 1, 128, 2, -64, 64, A16, A16) == w8.EINVAL
+    assert qb(A16, 1, 128, 2, 64, 0, A16, A16) == w8.EINVAL           # block >= 1
+    assert qb(A16, 1, 128, 2, 60, 64, A16, A16) == w8.EINVAL          # head_dim % 8
+    assert qb(A16, 1, 128, 2, 0, 64, A16, A16) == w8.EINVAL           # head_dim >= 8
+    assert qb(A16, 1, 1024, 2, 128, 512, A16, A16) == w8.EINVAL       # block too large to hold
+    assert qb(NULL, 1, 128, 2, 64, 64, A16, A16) == w8.EINVAL
+    assert qb(A16, 1, 128, 2, 64, 64, NULL, A16) == w8.EINVAL
+    assert qb(A16, 1, 128, 2, 64, 64, A16, NULL) == w8.EINVAL
+    assert qb(MIS, 1, 128, 2, 64, 64, A16, A16) == w8.EINVAL          # x not 16-byte aligned
+    assert qb(A16, 1, 1 << 40, 1 << 10, 64, 1, A16, A16) == w8.EINVAL  # 2^31 blocks or more
+    assert qb(A16, 0, 128, 2, 64, 64, NULL, NULL) == w8.OK            # empty: no-op
+    assert qb(A16, 1, 0, 2, 64, 64, NULL, NULL) == w8.OK
+
+
 def test_python_binding_refuses_cpu_tensors():
     import torch
     x = torch.zeros((4, 128), dtype=torch.bfloat16)

@@ -124,6 +124,82 @@ def test_quantize_empty_rows_is_noop():
 
 
 # ---------------------------------------------------------------------------
+# per-block quantisation of attention Q / K
+# ---------------------------------------------------------------------------
+
+def _block_input(B, S, H, D, seed):
+    rng = np.random.default_rng(seed)
+    v = rng.standard_normal((B * S, H * D)).astype(np.float32)
+    v *= np.float32(2.0) ** rng.integers(-40, 40, (B * S, 1)).astype(np.float32)
+    x = wl.to_bf16_bits(v)
+    if B * S >= 2 and H >= 2:
+        x[0:2, D:2 * D] = 0                                    # zero values in block (0, 0, 1)
+    return x
+
+
+# Shapes: one-token blocks, ragged last blocks, several samples and heads,
+# head_dim 8 .. 128, and each chunks-per-thread variant of the kernel (a block
+# of block x head_dim / 8 chunks: 1 .. 16 per thread for 256 threads).
+@pytest.mark.parametrize("B,S,H,D,blk", [(1, 1, 1, 8, 1), (1, 37, 1, 16, 1), (2, 37, 3, 16, 8),
+                                         (3, 130, 4, 64, 64), (1, 257, 2, 128, 128),
+                                         (2, 5, 2, 8, 16), (1, 96, 8, 32, 32), (2, 300, 4, 128, 256),
+                                         (1, 1000, 2, 64, 64), (2, 77, 3, 256, 32)])
+def test_quantize_blocks_matches_oracle(B, S, H, D, blk):
+    say(f"quantize blocks B={B} S={S} H={H} D={D} block={blk}")
+    x = _block_input(B, S, H, D, B * 7919 + S * 31 + H * 7 + D + blk)
+    q, s = w8.quantize_blocks(d_bf16(x), B, H, blk)
+    torch.cuda.synchronize()
+    qo, so = oracle.quantize_blocks(x, B, H, blk)
+    assert np.array_equal(h(s).view(np.uint32), so.view(np.uint32))
+    assert np.array_equal(h(q), qo)
+
+
+def test_quantize_blocks_degenerate_blocks():
+    say("quantize blocks: zero and sub-threshold blocks")
+    B, S, H, D, blk = 2, 70, 4, 16, 32
+    x = _block_input(B, S, H, D, 3)
+    x[:32, 16:32] = 0
+    x[S:S + 32, :16] = wl.to_bf16_bits(np.full((32, 16), 2.0**-101, np.float32))
+    q, s = w8.quantize_blocks(d_bf16(x), B, H, blk)
+    qo, so = oracle.quantize_blocks(x, B, H, blk)
+    assert np.array_equal(h(s).view(np.uint32), so.view(np.uint32)) and np.array_equal(h(q), qo)
+    assert h(s)[0, 0, 1] == 0 and h(s)[1, 0, 0] == 0
+
+
+@pytest.mark.parametrize("blk", [128, 64])
+def test_quantize_blocks_video_attention_full_size(blk):
+    """Video self-attention Q / K stand-in: 24576 tokens x 32 heads x 128, blocks
+    of 128 tokens (Q) and 64 (K), compared in full."""
+    say(f"quantize blocks video 24576 x 32 x 128 block={blk}")
+    rng = np.random.default_rng(blk)
+    x = wl.to_bf16_bits(rng.standard_normal((24576, 4096)).astype(np.float32))
+    q, s = w8.quantize_blocks(d_bf16(x), 1, 32, blk)
+    qo, so = oracle.quantize_blocks(x, 1, 32, blk)
+    assert np.array_equal(h(s).view(np.uint32), so.view(np.uint32))
+    assert np.array_equal(h(q), qo)
+
+
+def test_quantize_blocks_guard_bands():
+    say("quantize blocks guard bands")
+    B, S, H, D, blk = 2, 45, 3, 32, 16
+    x = _block_input(B, S, H, D, 9)
+    pad = 4096
+    n = B * S * H * D
+    big = torch.full((n + 2 * pad,), 0x5A, dtype=torch.int8, device=DEV)
+    nblk = -(-S // blk)
+    sbig = torch.full((B * nblk * H + 2 * 64,), -7.0, dtype=torch.float32, device=DEV)
+    q = big[pad:pad + n].view(B * S, H * D)
+    sc = sbig[64:64 + B * nblk * H].view(B, nblk, H)
+    w8.quantize_blocks(d_bf16(x), B, H, blk, q=q, scale=sc)
+    hb, hs = h(big), h(sbig)
+    assert np.all(hb[:pad] == 0x5A) and np.all(hb[pad + n:] == 0x5A)
+    assert np.all(hs[:64] == -7.0) and np.all(hs[64 + B * nblk * H:] == -7.0)
+    qo, so = oracle.quantize_blocks(x, B, H, blk)
+    assert np.array_equal(hb[pad:pad + n].reshape(B * S, H * D), qo)
+    assert np.array_equal(hs[64:64 + B * nblk * H].view(np.uint32), so.reshape(-1).view(np.uint32))
+
+
+# ---------------------------------------------------------------------------
 # INT8 GEMM: int32 accumulator and bf16 epilogue
 # ---------------------------------------------------------------------------
 
