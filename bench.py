@@ -53,6 +53,8 @@ def parse():
     p.add_argument("--probe-traffic", action="store_true",
                    help="run a known-size copy and the step's kernels a few times, for "
                         "rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs, then exit")
+    p.add_argument("--vendor", action="store_true",
+                   help="time torch._int_mm (hipBLASLt) beside w8a8_gemm on the video GEMM shapes")
     p.add_argument("--ceiling", action="store_true",
                    help="measure the INT8 MFMA rate and clock for several kinds of operand "
                         "data (the power-capped ceiling any INT8 GEMM faces), print JSON, exit")
@@ -161,7 +163,59 @@ def ceiling():
         out[name] = {"TOPS": round(tops, 1), "frac_of_5000": round(tops / PEAK_INT8_TOPS, 4),
                      "clock_GHz": round(c[0] / (c[1] / 100e6) / 1e9, 3),
                      "cycles_per_mfma": round(c[0] / (iters * 8), 2)}
+    # two waves per SIMD, Gaussian codes, with 0 / 3 / 6 of the 6 fragment registers
+    # refreshed from LDS (ds_read_b128) per 8 MFMAs, as a GEMM K loop does
+    lib.w8a8_probe_mfma_lds.argtypes = [P, P, P, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                        ctypes.POINTER(ctypes.c_float), P]
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    sink2 = torch.empty(cus * 512, dtype=torch.int32, device=dev)
+    t = torch.from_numpy(kinds["gaussian_sigma32"]).to(dev)
+    lds = {}
+    for reads in (0, 3, 6):
+        ms = ctypes.c_float(0)
+        rc = lib.w8a8_probe_mfma_lds(P(t.data_ptr()), P(sink2.data_ptr()), P(clk.data_ptr()),
+                                     iters * 4, reads, cus, ctypes.byref(ms),
+                                     P(torch.cuda.current_stream().cuda_stream))
+        assert rc == 0, rc
+        c = clk.cpu().tolist()
+        tops = cus * 8 * iters * 4 * 8 * 65536.0 / (ms.value * 1e-3) / 1e12
+        lds[f"lds_reads_per_8_mfma_{reads}"] = {
+            "TOPS": round(tops, 1), "frac_of_5000": round(tops / PEAK_INT8_TOPS, 4),
+            "clock_GHz": round(c[0] / (c[1] / 100e6) / 1e9, 3)}
     print(json.dumps({"probe": "v_mfma_i32_32x32x32_i8 loop, 1 wave/SIMD, 8 accumulators",
+                      "results": out,
+                      "probe_lds": "same loop at 2 waves/SIMD, Gaussian codes, fragments from LDS",
+                      "results_lds": lds}))
+
+
+def vendor():
+    """The vendor library's INT8 GEMM (torch._int_mm: hipBLASLt, INT8 -> INT32, no
+    scales, bias or bf16 output) beside this library's w8a8_gemm (bf16 output with
+    scales and bias) on the video GEMM shapes, same codes, alternating calls."""
+    import torch
+
+    import int8_w8a8_gemm_amd as w8
+
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev).manual_seed(0)
+    out = {}
+    for name, (M, N, K) in {"ffn_up_24576x16384x4096": (24576, 16384, 4096),
+                            "ffn_down_24576x4096x16384": (24576, 4096, 16384),
+                            "attn_proj_24576x4096x4096": (24576, 4096, 4096)}.items():
+        qa, sa = w8.quantize_rows(torch.randn((M, K), device=dev, generator=gen).to(torch.bfloat16))
+        qw, sw = w8.quantize_rows((torch.randn((N, K), device=dev, generator=gen) * 0.02)
+                                  .to(torch.bfloat16))
+        bias = (torch.randn((N,), device=dev, generator=gen) * 0.01).to(torch.bfloat16)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        ours, theirs = [], []
+        for _ in range(3):
+            ours.append(_time(lambda: w8.gemm(qa, sa, qw, sw, bias, out=y), 10, torch))
+            theirs.append(_time(lambda: torch._int_mm(qa, qw.t()), 10, torch))
+        o, v = sorted(ours)[1], sorted(theirs)[1]
+        out[name] = {"w8a8_gemm_ms": round(o, 4), "w8a8_gemm_TOPS": round(2.0 * M * N * K / o / 1e9, 1),
+                     "int_mm_ms": round(v, 4), "int_mm_TOPS": round(2.0 * M * N * K / v / 1e9, 1)}
+        del qa, qw, y
+    print(json.dumps({"vendor": "torch._int_mm (hipBLASLt) vs w8a8_gemm, median of 3 x 10 calls",
                       "results": out}))
 
 
@@ -172,6 +226,9 @@ def main():
         return
     if args.ceiling:
         ceiling()
+        return
+    if args.vendor:
+        vendor()
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: this path has no multi-GPU mode "

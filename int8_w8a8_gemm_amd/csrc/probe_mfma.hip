@@ -51,7 +51,99 @@ __global__ __launch_bounds__(256) void mfma_loop(const v4i* __restrict__ ops, in
     }
 }
 
+// The same MFMA loop at two waves per SIMD (8 waves, one workgroup per CU),
+// either with operands fixed in registers (READS = 0) or with READS of the 6
+// fragment registers refreshed from LDS by ds_read_b128 per 8 MFMAs, interleaved
+// with them like a GEMM's K loop (6 per 8 is the 256 x 256 GEMM tile's rate).
+// LDS holds 64 KB of the operand data; every read stays inside it.
+constexpr int kLdsBytes = 96 * 1024;  // more than half the CU's LDS: one workgroup per CU
+
+template <int READS>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void mfma_lds_loop(const v4i* __restrict__ ops, int* __restrict__ sink, long long* __restrict__ clk,
+                   int iters) {
+    __shared__ __attribute__((aligned(1024))) char lds[kLdsBytes];
+    for (int i = threadIdx.x; i < kOperands; i += 512) reinterpret_cast<v4i*>(lds)[i] = ops[i];
+    __syncthreads();
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    v4i fa[2], fb[4];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) fa[q] = ops[(threadIdx.x + q * 512) % kOperands];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) fb[q] = ops[(threadIdx.x * 7 + q * 911 + 5) % kOperands];
+    // never true (iters > 0): keeps the LDS array, and so one workgroup per CU,
+    // in the variant without reads
+    if (iters < 0) fa[0] = *reinterpret_cast<const v4i*>(lds + lane * 16);
+    v16i c[8] = {};
+    const long long t0 = __builtin_readcyclecounter();
+    const long long r0 = __builtin_amdgcn_s_memrealtime();
+    for (int it = 0; it < iters; ++it) {
+        v4i nf[6];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            c[j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fb[j >> 1], fa[j & 1], c[j], 0, 0, 0);
+            if (j < READS) {
+                // 1 KB-aligned slot ((..) & 63) of the 64 KB, 16 bytes per lane
+                const int off = (((it * 6 + j + wave * 5) & 63) << 10) + lane * 16;
+                nf[j] = *reinterpret_cast<const v4i*>(lds + off);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int j = 0; j < READS; ++j) {
+            if (j < 2) fa[j] = nf[j];
+            else fb[j - 2] = nf[j];
+        }
+    }
+    const long long t1 = __builtin_readcyclecounter();
+    const long long r1 = __builtin_amdgcn_s_memrealtime();
+    int s = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s += c[j][e];
+    sink[blockIdx.x * 512 + threadIdx.x] = s;
+    if (threadIdx.x == 0 && blockIdx.x == 0) {
+        clk[0] = t1 - t0;
+        clk[1] = r1 - r0;
+    }
+}
+
+template <int READS>
+hipError_t run_lds(const void* ops, int* sink, long long* clk, int iters, int cus, hipStream_t s) {
+    hipLaunchKernelGGL(mfma_lds_loop<READS>, dim3((unsigned)cus), dim3(512), 0, s,
+                       (const v4i*)ops, sink, clk, iters);
+    return hipGetLastError();
+}
+
 }  // namespace
+
+extern "C" __attribute__((visibility("default")))
+// As w8a8_probe_mfma, at two waves per SIMD (one 8-wave workgroup on each of
+// `cus` CUs; sink holds cus*512 ints) with `reads` (0, 3 or 6) fragment
+// registers refreshed from LDS per 8 MFMAs.
+int w8a8_probe_mfma_lds(const void* ops, int* sink, long long* clk, int iters, int reads, int cus,
+                        float* ms, void* stream) {
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (reads != 0 && reads != 3 && reads != 6) return -1;
+    if (cus <= 0 || iters <= 0) return -1;
+    auto launch = [&]() {
+        return reads == 0 ? run_lds<0>(ops, sink, clk, iters, cus, s)
+               : reads == 3 ? run_lds<3>(ops, sink, clk, iters, cus, s)
+                            : run_lds<6>(ops, sink, clk, iters, cus, s);
+    };
+    hipEvent_t e0, e1;
+    if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) return -3;
+    bool ok = launch() == hipSuccess;
+    ok = ok && hipEventRecord(e0, s) == hipSuccess;
+    ok = ok && launch() == hipSuccess;
+    ok = ok && hipEventRecord(e1, s) == hipSuccess;
+    ok = ok && hipEventSynchronize(e1) == hipSuccess;
+    ok = ok && hipEventElapsedTime(ms, e0, e1) == hipSuccess;
+    ok = (hipEventDestroy(e0) == hipSuccess) && ok;
+    ok = (hipEventDestroy(e1) == hipSuccess) && ok;
+    return ok ? 0 : -3;
+}
 
 extern "C" __attribute__((visibility("default")))
 // ops: device buffer of 4096 x 16 bytes of int8 operand data; sink: device int
