@@ -29,7 +29,7 @@ namespace {
 // A workgroup of WM x WN waves owns a BM x BN output tile; wave (wm, wn) owns
 // (BM/WM) x (BN/WN) outputs, i.e. MI x NI tiles of 32 x 32 MFMA accumulators.
 // K is staged BK bytes at a time through an NST-deep ring of LDS buffers.
-// Four configurations:
+// Five configurations:
 //   xl:    384 x 256 tile (INT8 without GELU only), 4 x 2 waves of 96 x 128:
 //          7 fragment reads per 12 MFMAs instead of 6 per 8, and 17% fewer
 //          operand bytes per MFMA.  Its two 80 KB K stages fill the LDS, so
@@ -55,7 +55,7 @@ namespace {
 //   16*l of that KB and is given the global chunk that belongs there under the
 //   swizzle below.  A lane's offsets are fixed per tile and the stage's K
 //   position is a scalar offset; each load's lane offset is formed from two
-//   per-lane values and wave-uniform terms as it is issued (see load_voff).
+//   per-lane values and wave-uniform terms as it is issued (stage_load_one).
 // * An LDS row r (BK bytes = BK/16 chunks) stores logical K-chunk c at physical
 //   chunk c ^ f(r).  A fragment read has lane l on row l % 32 at logical chunk
 //   l / 32; with f(r) = (r ^ (r >> 3)) & 7 for 128-byte rows and (r >> 2) & 3
@@ -70,7 +70,8 @@ namespace {
 //   the loads that refill the buffer just released.  The order of MFMAs, LDS
 //   reads and loads within a sub-step is fixed with sched_barrier.
 // * Tile order is XCD-aware: workgroup b runs on XCD b % 8, so each XCD is
-//   given a contiguous range of tiles, walked in groups of 1024 rows.
+//   given a contiguous range of tiles, walked in groups of GROUP_ROWS / BM
+//   tile-rows (1024 rows; 768 for the 384-row tiles).
 // ---------------------------------------------------------------------------
 constexpr int NUM_XCD = 8;
 #ifndef W8A8_GROUP_ROWS
@@ -210,7 +211,7 @@ template <class C>
 struct Ctx {
     rsrc_t rsrc[2];  // 0: activation panel, 1: weight panel
     // loads: lrow = (lane / CPR) * KB; lx = 16 x this lane's chunk before the
-    // wave-uniform part of the swizzle (see load_voff)
+    // wave-uniform part of the swizzle (see stage_load_one)
     uint32_t lrow, lx, kb;
     // fragment reads: LDS byte offset of this lane's row in the wave's first
     // activation / weight sub-tile, and 16 x the physical chunk of its K-chunk
