@@ -465,19 +465,19 @@ hipError_t launch_cq(const uint16_t* x, const uint8_t* mask, int64_t R, int64_t 
 // x holds token rows [B x S x H*D]; one block is up to `block` consecutive
 // tokens of one sample and one head, and gets one scale, with the arithmetic of
 // the per-row routine above (absmax over the block).  One workgroup per block
-// (blockIdx.x = (b * nblk + j) * H + h, the scale's index): each thread loads
-// its KPT 16-byte chunks of the block (a head's row of D values is D/8 chunks;
-// consecutive threads take consecutive chunks, so a wave reads whole 128-byte
-// lines), keeps them in registers through the absmax reduction and writes
-// their codes, so every element is read from HBM once.
+// (blockIdx.x = (b * nblk + j) * H + h, the scale's index) of NT threads:
+// each thread loads its KPT 16-byte chunks of the block (a head's row of D
+// values is D/8 chunks; consecutive threads take consecutive chunks, so a wave
+// reads whole 128-byte lines), keeps them in registers through the absmax
+// reduction and writes their codes, so every element is read from HBM once.
 // ---------------------------------------------------------------------------
-template <int KPT>
-__global__ __launch_bounds__(kBlock) void quantize_blocks_vec(const uint16_t* __restrict__ x,
-                                                              int64_t S, int64_t H, int64_t D,
-                                                              int64_t block, int64_t nblk,
-                                                              int8_t* __restrict__ q,
-                                                              float* __restrict__ scale) {
-    __shared__ uint32_t red[kBlock / 64];
+template <int KPT, int NT>
+__global__ __launch_bounds__(NT) void quantize_blocks_vec(const uint16_t* __restrict__ x,
+                                                          int64_t S, int64_t H, int64_t D,
+                                                          int64_t block, int64_t nblk,
+                                                          int8_t* __restrict__ q,
+                                                          float* __restrict__ scale) {
+    __shared__ uint32_t red[NT / 64];
     // the grid holds fewer than 2^31 blocks (checked by the caller): 32-bit index arithmetic
     const uint32_t i = blockIdx.x, h32 = (uint32_t)H, nb32 = (uint32_t)nblk;
     const uint32_t bj = i / h32, h = i - bj * h32;
@@ -485,7 +485,7 @@ __global__ __launch_bounds__(kBlock) void quantize_blocks_vec(const uint16_t* __
     const int64_t t0 = (int64_t)j * block;
     const int64_t ntok = (S - t0) < block ? (S - t0) : block;
     const uint32_t cpt = (uint32_t)(D >> 3);  // chunks per token row of the head
-    const uint32_t n = (uint32_t)ntok * cpt;  // chunks in the block (<= 256 * KPT)
+    const uint32_t n = (uint32_t)ntok * cpt;  // chunks in the block (<= NT * KPT)
     const int64_t C = H * D;
     const int64_t origin = ((int64_t)b * S + t0) * C + (int64_t)h * D;  // the block's first value
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -495,7 +495,7 @@ __global__ __launch_bounds__(kBlock) void quantize_blocks_vec(const uint16_t* __
     uint32_t amax = 0;
 #pragma unroll
     for (int k = 0; k < KPT; ++k) {
-        const uint32_t c = threadIdx.x + (uint32_t)k * kBlock;
+        const uint32_t c = threadIdx.x + (uint32_t)k * NT;
         const uint32_t tok = c / cpt;
         off[k] = origin + (int64_t)tok * C + (int64_t)(c - tok * cpt) * 8;
         if (c < n) v[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x + off[k]));
@@ -505,14 +505,15 @@ __global__ __launch_bounds__(kBlock) void quantize_blocks_vec(const uint16_t* __
     amax = wave_max_u32(amax);
     if (lane == 0) red[wave] = amax;
     __syncthreads();
-    amax = max(max(red[0], red[1]), max(red[2], red[3]));
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) amax = max(amax, red[w]);
     const float a = __uint_as_float(amax << 16);
     const bool zero = !(a >= 0x1p-100f);  // degenerate block: scale 0, all codes 0
     const float inv = zero ? 0.0f : __fdiv_rn(127.0f, a);
     if (threadIdx.x == 0) scale[i] = zero ? 0.0f : __fdiv_rn(a, 127.0f);
 #pragma unroll
     for (int k = 0; k < KPT; ++k) {
-        const uint32_t c = threadIdx.x + (uint32_t)k * kBlock;
+        const uint32_t c = threadIdx.x + (uint32_t)k * NT;
         if (c < n) {
             const uint2 o = zero ? make_uint2(0u, 0u) : quant8_pk(v[k], inv);
             uint32_t* qp = reinterpret_cast<uint32_t*>(q + off[k]);
@@ -522,11 +523,11 @@ __global__ __launch_bounds__(kBlock) void quantize_blocks_vec(const uint16_t* __
     }
 }
 
-template <int KPT>
+template <int KPT, int NT = kBlock>
 hipError_t launch_blocks(const uint16_t* x, int64_t B, int64_t S, int64_t H, int64_t D,
                          int64_t block, int8_t* q, float* scale, hipStream_t stream) {
     const int64_t nblk = (S + block - 1) / block;
-    hipLaunchKernelGGL(quantize_blocks_vec<KPT>, dim3((unsigned)(B * nblk * H)), dim3(kBlock), 0,
+    hipLaunchKernelGGL((quantize_blocks_vec<KPT, NT>), dim3((unsigned)(B * nblk * H)), dim3(NT), 0,
                        stream, x, S, H, D, block, nblk, q, scale);
     return hipGetLastError();
 }
@@ -595,11 +596,15 @@ int launch_quantize_blocks(const uint16_t* x, int64_t B, int64_t S, int64_t H, i
     if (B == 0 || S == 0 || H == 0) return 0;
     const int64_t chunks = (S < block ? S : block) * (D / 8);  // of the largest block
     hipError_t e;
+    // blocks of more than 4 x 256 chunks take 8-wave workgroups: 128 tokens x
+    // 128 values ran 6% faster than with 4 waves of 8 chunks per thread
     if (chunks <= kBlock) e = launch_blocks<1>(x, B, S, H, D, block, q, scale, stream);
     else if (chunks <= 2 * kBlock) e = launch_blocks<2>(x, B, S, H, D, block, q, scale, stream);
     else if (chunks <= 4 * kBlock) e = launch_blocks<4>(x, B, S, H, D, block, q, scale, stream);
-    else if (chunks <= 8 * kBlock) e = launch_blocks<8>(x, B, S, H, D, block, q, scale, stream);
-    else if (chunks <= 16 * kBlock) e = launch_blocks<16>(x, B, S, H, D, block, q, scale, stream);
+    else if (chunks <= 8 * kBlock)
+        e = launch_blocks<4, 2 * kBlock>(x, B, S, H, D, block, q, scale, stream);
+    else if (chunks <= 16 * kBlock)
+        e = launch_blocks<8, 2 * kBlock>(x, B, S, H, D, block, q, scale, stream);
     else return -1;
     return e == hipSuccess ? 0 : -1;
 }
