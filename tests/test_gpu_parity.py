@@ -429,6 +429,97 @@ def test_ffn_pipeline_fused_gelu_quantise(ffn):
     assert np.array_equal(y[rows], y_ref)
 
 
+def _small_ffn(seed, M=2048, D=1024, F=4096):
+    rng = np.random.default_rng(seed)
+    x = wl.to_bf16_bits(rng.standard_normal((M, D)).astype(np.float32))
+    w1 = wl.to_bf16_bits(rng.standard_normal((F, D)).astype(np.float32) * np.float32(0.03))
+    w2 = wl.to_bf16_bits(rng.standard_normal((D, F)).astype(np.float32) * np.float32(0.02))
+    b1 = wl.to_bf16_bits(rng.standard_normal(F).astype(np.float32) * np.float32(0.01))
+    b2 = wl.to_bf16_bits(rng.standard_normal(D).astype(np.float32) * np.float32(0.01))
+    return x, w1, b1, w2, b2
+
+
+class _FfnPipeline:
+    """The benchmark's pipeline (quantise X, up GEMM, GELU + quantise, down GEMM)
+    on preallocated buffers, so that it can be captured into a graph."""
+
+    def __init__(self, w1, b1, w2, b2, M):
+        self.qw1, self.sw1 = w8.quantize_rows(d_bf16(w1))
+        self.qw2, self.sw2 = w8.quantize_rows(d_bf16(w2))
+        self.b1, self.b2 = d_bf16(b1), d_bf16(b2)
+        F, D = self.qw1.shape[0], self.qw2.shape[0]
+        self.x = torch.empty((M, D), dtype=torch.bfloat16, device=DEV)
+        self.qx = torch.empty((M, D), dtype=torch.int8, device=DEV)
+        self.sx = torch.empty((M,), dtype=torch.float32, device=DEV)
+        self.u = torch.empty((M, F), dtype=torch.bfloat16, device=DEV)
+        self.qh = torch.empty((M, F), dtype=torch.int8, device=DEV)
+        self.sh = torch.empty((M,), dtype=torch.float32, device=DEV)
+        self.y = torch.empty((M, D), dtype=torch.bfloat16, device=DEV)
+
+    def step(self, stream=None):
+        w8.quantize_rows(self.x, self.qx, self.sx, stream=stream)
+        w8.gemm(self.qx, self.sx, self.qw1, self.sw1, self.b1, out=self.u, stream=stream)
+        w8.gelu_quantize_rows(self.u, self.qh, self.sh, stream=stream)
+        w8.gemm(self.qh, self.sh, self.qw2, self.sw2, self.b2, out=self.y, stream=stream)
+
+
+def test_ffn_pipeline_graph_capture_and_replay():
+    """The four entry points of a step captured into one graph (none allocates,
+    frees, synchronises or records a memset): each of three replays, on new
+    inputs and with eager work between them, equals an eager run bit for bit."""
+    say("ffn pipeline: graph capture and replay")
+    x, w1, b1, w2, b2 = _small_ffn(21)
+    M = x.shape[0]
+    pipe = _FfnPipeline(w1, b1, w2, b2, M)
+    eager = _FfnPipeline(w1, b1, w2, b2, M)
+    pipe.x.copy_(d_bf16(x))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        pipe.step()  # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        pipe.step()
+    rng = np.random.default_rng(22)
+    for r in range(3):
+        xr = wl.to_bf16_bits(rng.standard_normal(x.shape).astype(np.float32) * np.float32(1 + r))
+        pipe.x.copy_(d_bf16(xr))
+        eager.x.copy_(pipe.x)
+        g.replay()
+        torch.cuda.synchronize()
+        eager.step()          # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(pipe.y, eager.y), f"replay {r}"
+        assert torch.equal(pipe.qh, eager.qh) and torch.equal(pipe.sh, eager.sh), f"replay {r}"
+
+
+def test_two_pipelines_on_two_streams():
+    """Two steps on two streams at once (different inputs and weights) give
+    the results each gives alone: the library keeps no state between calls."""
+    say("two pipelines on two streams")
+    pa = _FfnPipeline(*_small_ffn(31)[1:], 1024)
+    pb = _FfnPipeline(*_small_ffn(32)[1:], 1024)
+    xa = _small_ffn(31, M=1024)[0]
+    xb = _small_ffn(32, M=1024)[0]
+    pa.x.copy_(d_bf16(xa))
+    pb.x.copy_(d_bf16(xb))
+    pa.step()
+    pb.step()
+    torch.cuda.synchronize()
+    ya, yb = pa.y.clone(), pb.y.clone()
+    pa.y.zero_()
+    pb.y.zero_()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    s1.wait_stream(torch.cuda.current_stream())
+    s2.wait_stream(torch.cuda.current_stream())
+    for _ in range(3):
+        pa.step(stream=s1)
+        pb.step(stream=s2)
+    torch.cuda.synchronize()
+    assert torch.equal(pa.y, ya) and torch.equal(pb.y, yb)
+
+
 def test_gelu_exhaustive_all_bf16_inputs():
     """GELU-tanh on every finite bf16 value, through the BF16 path with a 1x1
     identity weight (so the pre-activation is the input itself), against the
