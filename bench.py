@@ -53,6 +53,8 @@ def parse():
     p.add_argument("--probe-traffic", action="store_true",
                    help="run a known-size copy and the step's kernels a few times, for "
                         "rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs, then exit")
+    p.add_argument("--hbm-ceiling", action="store_true",
+                   help="practical HBM streaming rates (read, write, copy, 2:1 mix)")
     p.add_argument("--vendor", action="store_true",
                    help="time torch._int_mm (hipBLASLt) beside w8a8_gemm on the video GEMM shapes")
     p.add_argument("--ceiling", action="store_true",
@@ -188,6 +190,44 @@ def ceiling():
                       "results_lds": lds}))
 
 
+def hbm_ceiling():
+    """Practical HBM streaming rates (read, write, copy, and the quantisers' 2:1
+    read:write mix) over 805 MiB buffers used in turn, at 4, 8 and 16 workgroups
+    of 256 threads per CU: the reachable part of the 8 TB/s spec."""
+    import ctypes
+
+    import torch
+
+    lib = ctypes.CDLL(os.path.join(ROOT, "int8_w8a8_gemm_amd", "libw8a8_probe.so"))
+    P = ctypes.c_void_p
+    lib.w8a8_probe_stream.argtypes = [ctypes.c_int, P, P, ctypes.c_int, ctypes.c_size_t,
+                                      ctypes.c_int, ctypes.c_int, P,
+                                      ctypes.POINTER(ctypes.c_float), P]
+    dev = torch.device("cuda:0")
+    nbytes = 805 << 20
+    n16 = nbytes // 16
+    src = [torch.ones(nbytes // 4, dtype=torch.int32, device=dev) for _ in range(3)]
+    dst = [torch.empty(nbytes // 4, dtype=torch.int32, device=dev) for _ in range(3)]
+    sp = (ctypes.c_void_p * 3)(*[t.data_ptr() for t in src])
+    dp = (ctypes.c_void_p * 3)(*[t.data_ptr() for t in dst])
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    moved = {0: 1.0, 1: 1.0, 2: 2.0, 3: 1.5}
+    names = {0: "read", 1: "write", 2: "copy", 3: "read2_write1"}
+    out = {}
+    for per_cu in (4, 8, 16):
+        for kind in range(4):
+            ms = ctypes.c_float(0)
+            rc = lib.w8a8_probe_stream(kind, sp, dp, 3, n16, cus * per_cu, 30, P(sink.data_ptr()),
+                                       ctypes.byref(ms), P(torch.cuda.current_stream().cuda_stream))
+            assert rc == 0, rc
+            tbs = moved[kind] * nbytes / (ms.value * 1e-3) / 1e12
+            out[f"{names[kind]}_wg{per_cu}_per_cu"] = {"us": round(ms.value * 1e3, 1),
+                                                       "TB/s": round(tbs, 2)}
+    print(json.dumps({"probe": "16-byte nontemporal streaming over 3 x 805 MiB buffers",
+                      "results": out}))
+
+
 def vendor():
     """The vendor library's INT8 GEMM (torch._int_mm: hipBLASLt, INT8 -> INT32, no
     scales, bias or bf16 output) beside this library's w8a8_gemm (bf16 output with
@@ -229,6 +269,9 @@ def main():
         return
     if args.vendor:
         vendor()
+        return
+    if args.hbm_ceiling:
+        hbm_ceiling()
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: this path has no multi-GPU mode "

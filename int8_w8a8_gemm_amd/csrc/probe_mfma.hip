@@ -1,5 +1,6 @@
-// Measurement probe (not part of the W8A8 library's ABI): how fast the INT8
-// matrix cores run on this GPU for a given kind of operand data.
+// Measurement probes (not part of the W8A8 library's ABI): how fast the INT8
+// matrix cores run on this GPU for a given kind of operand data and LDS
+// traffic, and how fast plain streaming kernels move HBM data.
 //
 // MI355X is power-capped, and the energy of v_mfma_i32_32x32x32_i8 depends on
 // how much its operands toggle: the clock the part sustains, and so the
@@ -116,7 +117,79 @@ hipError_t run_lds(const void* ops, int* sink, long long* clk, int iters, int cu
     return hipGetLastError();
 }
 
+// Streaming kernels for the practical HBM ceiling: 16-byte nontemporal loads
+// and stores, grid-stride over n16 chunks (every index below n16).
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+__global__ __launch_bounds__(256) void stream_read(const u32x4* __restrict__ a, size_t n16,
+                                                   unsigned* __restrict__ sink) {
+    unsigned acc = 0;
+    for (size_t i = blockIdx.x * 256ull + threadIdx.x; i < n16; i += (size_t)gridDim.x * 256) {
+        const u32x4 v = __builtin_nontemporal_load(a + i);
+        acc ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
+    if (acc == 0x9e3779b9u) sink[0] = acc;  // keeps the loads
+}
+
+__global__ __launch_bounds__(256) void stream_write(u32x4* __restrict__ b, size_t n16) {
+    for (size_t i = blockIdx.x * 256ull + threadIdx.x; i < n16; i += (size_t)gridDim.x * 256)
+        __builtin_nontemporal_store((u32x4){1u, 2u, 3u, (unsigned)i}, b + i);
+}
+
+__global__ __launch_bounds__(256) void stream_copy(const u32x4* __restrict__ a,
+                                                   u32x4* __restrict__ b, size_t n16) {
+    for (size_t i = blockIdx.x * 256ull + threadIdx.x; i < n16; i += (size_t)gridDim.x * 256)
+        __builtin_nontemporal_store(__builtin_nontemporal_load(a + i), b + i);
+}
+
+// 16 bytes read, 8 written: the 2:1 mix of the quantisers (bf16 in, int8 out)
+__global__ __launch_bounds__(256) void stream_half(const u32x4* __restrict__ a,
+                                                   u32x2* __restrict__ b, size_t n16) {
+    for (size_t i = blockIdx.x * 256ull + threadIdx.x; i < n16; i += (size_t)gridDim.x * 256) {
+        const u32x4 v = __builtin_nontemporal_load(a + i);
+        __builtin_nontemporal_store((u32x2){v.x ^ v.y, v.z ^ v.w}, b + i);
+    }
+}
+
 }  // namespace
+
+extern "C" __attribute__((visibility("default")))
+// Practical HBM streaming rate.  kind 0: read n16 x 16 bytes of src; 1: write
+// them to dst; 2: copy src -> dst; 3: read 16 bytes and write 8 per chunk
+// (dst needs n16 x 8 bytes).  nbuf source / destination buffers (src[i],
+// dst[i], each n16 x 16 bytes) are used in turn so that caches cannot hold the
+// data; grid workgroups of 256 threads.  Runs `iters` untimed then `iters`
+// timed launches and returns the average time of one in *ms.
+int w8a8_probe_stream(int kind, void* const* src, void* const* dst, int nbuf, size_t n16, int grid,
+                      int iters, unsigned* sink, float* ms, void* stream) {
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (kind < 0 || kind > 3 || nbuf <= 0 || grid <= 0 || iters <= 0) return -1;
+    auto launch = [&](int i) {
+        const u32x4* a = static_cast<const u32x4*>(src[i % nbuf]);
+        void* b = dst[i % nbuf];
+        if (kind == 0)
+            hipLaunchKernelGGL(stream_read, dim3(grid), dim3(256), 0, s, a, n16, sink);
+        else if (kind == 1)
+            hipLaunchKernelGGL(stream_write, dim3(grid), dim3(256), 0, s, (u32x4*)b, n16);
+        else if (kind == 2)
+            hipLaunchKernelGGL(stream_copy, dim3(grid), dim3(256), 0, s, a, (u32x4*)b, n16);
+        else
+            hipLaunchKernelGGL(stream_half, dim3(grid), dim3(256), 0, s, a, (u32x2*)b, n16);
+    };
+    hipEvent_t e0, e1;
+    if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) return -3;
+    for (int i = 0; i < iters; ++i) launch(i);
+    bool ok = hipEventRecord(e0, s) == hipSuccess;
+    for (int i = 0; i < iters; ++i) launch(i);
+    ok = ok && hipEventRecord(e1, s) == hipSuccess;
+    ok = ok && hipEventSynchronize(e1) == hipSuccess;
+    ok = ok && hipEventElapsedTime(ms, e0, e1) == hipSuccess;
+    if (ok) *ms /= (float)iters;
+    ok = (hipEventDestroy(e0) == hipSuccess) && ok;
+    ok = (hipEventDestroy(e1) == hipSuccess) && ok;
+    return ok && hipGetLastError() == hipSuccess ? 0 : -3;
+}
 
 extern "C" __attribute__((visibility("default")))
 // As w8a8_probe_mfma, at two waves per SIMD (one 8-wave workgroup on each of
