@@ -78,6 +78,14 @@ constexpr int NUM_XCD = 8;
 #define W8A8_GROUP_ROWS 1024
 #endif
 constexpr int GROUP_ROWS = W8A8_GROUP_ROWS;
+// Cache policy of the operand loads: sc0 (bit 0).  Each stage's data is used
+// once per CU, so nothing is gained by keeping it in the CU's L1; measured
+// against no policy bits: FFN up 1.355 -> 1.324 ms, down 1.282 -> 1.267 ms,
+// 24576 x 4096 x 4096 1.2% faster; sc1 gained about half as much, and nt
+// (which lets L2 evict the operand panels other tiles still read) lost 5-7%.
+#ifndef W8A8_LOAD_POLICY
+#define W8A8_LOAD_POLICY 1
+#endif
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -285,7 +293,7 @@ __device__ __forceinline__ void stage_load_one(const Ctx<C>& c, uint32_t lrow, u
     char* dst = lds_stage + (is_a ? 0 : C::BM * C::BK) + r0 * C::BK;
 #if defined(__HIP_DEVICE_COMPILE__)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rsrc[is_a ? 0 : 1], (lds_void*)dst, 16, voff, k0,
-                                             0, 0);
+                                             0, W8A8_LOAD_POLICY);
 #else
     (void)dst;
     (void)voff;
