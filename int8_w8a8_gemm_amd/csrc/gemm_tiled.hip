@@ -86,6 +86,11 @@ constexpr int GROUP_ROWS = W8A8_GROUP_ROWS;
 #ifndef W8A8_LOAD_POLICY
 #define W8A8_LOAD_POLICY 1
 #endif
+// Output tiles leave with non-temporal stores (written once, read by the next
+// kernel): 0.5-1% faster on the FFN and attention shapes, 3.6% on 2048^3.
+#ifndef W8A8_STORE_NT
+#define W8A8_STORE_NT 1
+#endif
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -559,8 +564,13 @@ __device__ __forceinline__ void store_bf16(const Acc<C, E>& acc, uint16_t* __res
         uint16_t* gbase = y + row * N + n0 + 8 * cc;
         if (VEC_OUT && interior) {
 #pragma unroll
-            for (int i = 0; i < NI_OUT; ++i)
+            for (int i = 0; i < NI_OUT; ++i) {
+#if W8A8_STORE_NT
+                __builtin_nontemporal_store(d[i], reinterpret_cast<v4i*>(gbase + i * C::RPINS * N));
+#else
                 *reinterpret_cast<v4i*>(gbase + i * C::RPINS * N) = d[i];
+#endif
+            }
         } else if (VEC_OUT) {
 #pragma unroll
             for (int i = 0; i < NI_OUT; ++i)
