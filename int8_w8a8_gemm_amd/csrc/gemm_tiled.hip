@@ -70,12 +70,17 @@ namespace {
 //   the loads that refill the buffer just released.  The order of MFMAs, LDS
 //   reads and loads within a sub-step is fixed with sched_barrier.
 // * Tile order is XCD-aware: workgroup b runs on XCD b % 8, so each XCD is
-//   given a contiguous range of tiles, walked in groups of GROUP_ROWS / BM
-//   tile-rows (1024 rows; 768 for the 384-row tiles).
+//   given a contiguous range of tiles, walked in groups of GROUP_M tile-rows
+//   (1024 rows; 1536 for the 384-row tiles: the 32 tiles an XCD runs at once
+//   then form a 4 x 8 block, which halved the 384 x 256 kernel's operand
+//   fetches beyond L2 and made it 1.0-1.4% faster than 768-row groups).
 // ---------------------------------------------------------------------------
 constexpr int NUM_XCD = 8;
 #ifndef W8A8_GROUP_ROWS
 #define W8A8_GROUP_ROWS 1024
+#endif
+#ifndef W8A8_XL_GROUP_ROWS
+#define W8A8_XL_GROUP_ROWS 1536
 #endif
 constexpr int GROUP_ROWS = W8A8_GROUP_ROWS;
 // Cache policy of the operand loads: sc0 (bit 0).  Each stage's data is used
@@ -113,9 +118,10 @@ struct ElemBF16 {
     }
 };
 
-template <int BM_, int BN_, int WM_, int WN_, int BK_, int NST_>
+template <int BM_, int BN_, int WM_, int WN_, int BK_, int NST_, int GROUP_ROWS_ = GROUP_ROWS>
 struct Cfg {
     static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_, NST = NST_;
+    static constexpr int GROUP_M = GROUP_ROWS_ / BM;  // tile-rows per group of the raster
     static constexpr int WAVES = WM * WN;
     static constexpr int THREADS = WAVES * 64;
     static constexpr int TM = BM / WM, TN = BN / WN;  // outputs per wave
@@ -157,10 +163,11 @@ struct Cfg {
     static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile");
     static_assert(RPW % RPINS == 0 && 32 % RPW == 0, "copy-out rows per wave");
     static_assert(THREADS >= BM && THREADS >= BN, "scale staging");
+    static_assert(GROUP_M >= 1, "raster group");
 };
 
 #ifndef W8A8_XL_CFG
-#define W8A8_XL_CFG 384, 256, 4, 2, 128, 2
+#define W8A8_XL_CFG 384, 256, 4, 2, 128, 2, W8A8_XL_GROUP_ROWS
 #endif
 #ifndef W8A8_LARGE_CFG
 #define W8A8_LARGE_CFG 256, 256, 4, 2, 128, 2
@@ -465,7 +472,7 @@ __device__ __forceinline__ void k_stage(const Ctx<C>& c, char* smem, int kt, Acc
 template <class C>
 __device__ __forceinline__ void tile_of(int64_t bid, int64_t tm, int64_t tn, int64_t& tile_m,
                                         int64_t& tile_n) {
-    constexpr uint32_t GROUP_M = GROUP_ROWS / C::BM;
+    constexpr uint32_t GROUP_M = C::GROUP_M;
     const uint32_t tm32 = (uint32_t)tm, tn32 = (uint32_t)tn, total = tm32 * tn32;
     uint32_t t = (uint32_t)bid;
     if (total % NUM_XCD == 0) {
