@@ -76,6 +76,8 @@ namespace {
 //   fetches beyond L2 and made it 1.0-1.4% faster than 768-row groups).
 // ---------------------------------------------------------------------------
 constexpr int NUM_XCD = 8;
+// The W8A8_* macros below are the tuned defaults; each can be overridden on
+// the compiler command line to measure an alternative.
 #ifndef W8A8_GROUP_ROWS
 #define W8A8_GROUP_ROWS 1024
 #endif
@@ -166,6 +168,7 @@ struct Cfg {
     static_assert(GROUP_M >= 1, "raster group");
 };
 
+// Tile configurations: BM, BN, WM, WN, BK, NST[, raster group rows].
 #ifndef W8A8_XL_CFG
 #define W8A8_XL_CFG 384, 256, 4, 2, 128, 2, W8A8_XL_GROUP_ROWS
 #endif
