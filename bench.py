@@ -53,6 +53,10 @@ def parse():
     p.add_argument("--probe-traffic", action="store_true",
                    help="run a known-size copy and the step's kernels a few times, for "
                         "rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs, then exit")
+    p.add_argument("--probe-hbm", action="store_true",
+                   help="run the HBM-bound kernels on their workloads (for rocprofv3)")
+    p.add_argument("--hbm-from", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
+                   help="achieved HBM rate per kernel from rocprofv3 runs of --probe-hbm")
     p.add_argument("--hbm-ceiling", action="store_true",
                    help="practical HBM streaming rates (read, write, copy, 2:1 mix)")
     p.add_argument("--vendor", action="store_true",
@@ -197,6 +201,109 @@ def ceiling():
                       "results_lds": lds}))
 
 
+def probe_hbm():
+    """The HBM-bound kernels, each 5 times on its workload, for rocprofv3 (kernel trace,
+    FETCH_SIZE, WRITE_SIZE): the row quantiser on 4 rotating X [24576 x 4096], GELU +
+    quantise of U [24576 x 16384], the per-block Q / K quantiser (24576 tokens x 32 heads
+    x 128; blocks of 128 and 64), compaction and compaction + quantise of the text rows
+    [8 x 512 x 4096]; first a 1 GiB calibration copy."""
+    import numpy as np
+    import torch
+
+    import int8_w8a8_gemm_amd as w8
+    import workloads as wl
+
+    dev = torch.device("cuda:0")
+    src = torch.zeros((COPY_BYTES // 2,), dtype=torch.bfloat16, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    del src, dst
+    gen = torch.Generator(device=dev).manual_seed(0)
+    M, K = 24576, 4096
+    xs = [torch.randn((M, K), device=dev, generator=gen).to(torch.bfloat16) for _ in range(4)]
+    qs = [torch.empty((M, K), dtype=torch.int8, device=dev) for _ in range(4)]
+    ss = [torch.empty((M,), dtype=torch.float32, device=dev) for _ in range(4)]
+    for i in range(5):
+        w8.quantize_rows(xs[i % 4], qs[i % 4], ss[i % 4])
+    for blk in (128, 64):
+        sb = torch.empty((1, -(-M // blk), 32), dtype=torch.float32, device=dev)
+        for i in range(5):
+            w8.quantize_blocks(xs[i % 4], 1, 32, blk, q=qs[i % 4], scale=sb)
+    del xs, qs, ss
+    u = (torch.randn((M, 16384), device=dev, generator=gen) * 0.64).to(torch.bfloat16)
+    qh = torch.empty((M, 16384), dtype=torch.int8, device=dev)
+    sh = torch.empty((M,), dtype=torch.float32, device=dev)
+    for _ in range(5):
+        w8.gelu_quantize_rows(u, qh, sh)
+    del u, qh, sh
+    g = wl.guarded_mixed()
+    B, L, Dm = g.x.shape
+    xd = torch.from_numpy(np.ascontiguousarray(g.x.reshape(B * L, Dm)).view(np.int16)).to(dev)
+    xd = xd.view(torch.bfloat16).view(B, L, Dm)
+    md = torch.from_numpy(g.mask).to(dev)
+    buf = torch.empty((B * L, Dm), dtype=torch.bfloat16, device=dev)
+    qb = torch.empty((B * L, Dm), dtype=torch.int8, device=dev)
+    sb = torch.empty((B * L,), dtype=torch.float32, device=dev)
+    src_row = torch.empty((B * L,), dtype=torch.int32, device=dev)
+    cnt = torch.empty((1,), dtype=torch.int32, device=dev)
+    for _ in range(5):
+        w8.compact_padded_rows(xd, md, buf, src_row, cnt)
+    for _ in range(5):
+        w8.compact_quantize_rows(xd, md, qb, sb, src_row, cnt)
+    torch.cuda.synchronize()
+    log(f"hbm probe done (text rows kept: {int(cnt.item())})")
+
+
+def hbm_from(trace_dir, fetch_dir, write_dir):
+    """Per-kernel duration (kernel trace) and HBM bytes (FETCH_SIZE, WRITE_SIZE, each
+    scaled by what it reads for the calibration copy) of --probe-hbm: the achieved
+    HBM rate of each kernel as rocprofv3 sees it."""
+    import csv
+    import glob
+
+    def rows(d, pat):
+        out = []
+        for f in glob.glob(os.path.join(d, "**", pat), recursive=True):
+            out += list(csv.DictReader(open(f)))
+        return out
+
+    dur = {}
+    for r in rows(trace_dir, "*kernel_trace.csv"):
+        dur.setdefault(r["Kernel_Name"], []).append(
+            (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9)
+
+    def counter(d, name):
+        per = {}
+        for r in rows(d, "*counter_collection.csv"):
+            if r["Counter_Name"] == name:
+                k = (r["Kernel_Name"], r["Dispatch_Id"])
+                per[k] = per.get(k, 0.0) + float(r["Counter_Value"]) * 1024.0
+        by = {}
+        for (kn, _), v in per.items():
+            by.setdefault(kn, []).append(v)
+        return {k: sum(v) / len(v) for k, v in by.items()}
+
+    fetch, write = counter(fetch_dir, "FETCH_SIZE"), counter(write_dir, "WRITE_SIZE")
+    copy = [k for k in fetch if "neg" in k]
+    kf = COPY_BYTES / fetch[copy[0]]
+    kw = COPY_BYTES / write[[k for k in write if "neg" in k][0]]
+    out = {}
+    for k, ds in dur.items():
+        if "w8a8" not in k or k not in fetch or k not in write:
+            continue
+        t = sorted(ds)[len(ds) // 2]
+        rd, wr = fetch[k] * kf, write[k] * kw
+        import re
+        names = re.findall(r"(\w+(?:<[^()]*>)?)\(", k)  # the kernel name with its template arguments
+        short = names[-1] if names else k
+        out[short] = {"launches": len(ds), "median_us": round(t * 1e6, 2),
+                      "read_GB": round(rd / 1e9, 4), "write_GB": round(wr / 1e9, 4),
+                      "TB/s": round((rd + wr) / t / 1e12, 3),
+                      "frac_of_8TBs": round((rd + wr) / t / 1e12 / (PEAK_HBM_GBS / 1e3), 4)}
+    print(json.dumps(out, indent=1))
+
+
 def hbm_ceiling():
     """Practical HBM streaming rates (read, write, copy, and the quantisers' 2:1
     read:write mix) over 805 MiB buffers used in turn, at 4, 8 and 16 workgroups
@@ -279,6 +386,12 @@ def main():
         return
     if args.hbm_ceiling:
         hbm_ceiling()
+        return
+    if args.probe_hbm:
+        probe_hbm()
+        return
+    if args.hbm_from:
+        hbm_from(*args.hbm_from)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: this path has no multi-GPU mode "
