@@ -241,6 +241,24 @@ def test_gemm_int32_extremes_and_max_k():
     assert np.all(acc[0::2] == 16129 * K) and np.all(acc[1::2] == -16129 * K)
 
 
+def test_gemm_xl_tiles_max_k_closed_form():
+    """K = 131072 (the largest the guard admits: |acc| <= 127^2 K < 2^31) on the
+    384 x 256 tiles (4600 x 4096: 192 such tiles, one round, against two rounds
+    of 256 x 256 tiles; ragged M).  Codes are +-127 by row, so every accumulator
+    is +-16129 K: a closed form, checked on all outputs."""
+    M, N, K = 4600, 4096, 131072
+    say(f"gemm xl tiles max K M={M} N={N} K={K}")
+    sa = torch.where(torch.arange(M, device=DEV) % 3 == 0, -1, 1).to(torch.int8)
+    sw = torch.where(torch.arange(N, device=DEV) % 5 == 0, -1, 1).to(torch.int8)
+    qa = (sa[:, None] * 127).expand(M, K).contiguous()
+    qw = (sw[:, None] * 127).expand(N, K).contiguous()
+    acc = w8.gemm(qa, None, qw, None, out_kind=w8.OUT_I32)
+    torch.cuda.synchronize()
+    exp = (sa.to(torch.int64)[:, None] * sw.to(torch.int64)[None, :]) * (16129 * K)
+    assert torch.equal(acc.to(torch.int64), exp)
+    del qa, qw, acc
+
+
 @pytest.mark.parametrize("M,N,K", [(64, 128, 256), (129, 192, 384), (2048, 2048, 2048),
                                    (2000, 1984, 512), (4100, 4160, 128), (2378, 4096, 256),
                                    (3900, 3776, 128)])
