@@ -42,7 +42,8 @@ namespace {
 //          tile's work, for row counts where large tiles leave many CUs idle
 //          in their last round (the ~2300-row text projection: 160 large
 //          tiles or 208 mid ones on 256 CUs).
-//   small: 128 x 128 tile, 2 x 2 waves of 64 x 64.
+//   small: 128 x 128 tile, 2 x 2 waves of 64 x 64 (a 3-deep K ring for long
+//          K loops).
 //   tiny:  64 x 64 tile, 2 x 2 waves of 32 x 32.
 // The launcher takes the largest of large/small/tiny whose tile count covers
 // at least half of the CUs (a large tile on a CU still outruns four small
@@ -185,6 +186,8 @@ typedef Cfg<W8A8_LARGE_CFG> CfgLarge;
 #endif
 typedef Cfg<W8A8_MID_CFG> CfgMid;
 typedef Cfg<W8A8_SMALL_CFG> CfgSmall;
+// small tiles with a 3-deep ring, for K loops of 32 stages or more (see launch_tiles)
+typedef Cfg<128, 128, 2, 2, 128, 3> CfgSmallDeep;
 typedef Cfg<64, 64, 2, 2, 128, 2> CfgTiny;
 
 template <int BK>
@@ -834,9 +837,20 @@ hipError_t launch_tiles(const void* a, const float* sa, int64_t M, const void* w
         return launch_cfg<CfgLarge, E, OUT_I32, ACT, VEC_OUT>(a, sa, M, w, sw, N, K, bias, out, cus,
                                                              stream);
     }
-    if (2 * tile_count<CfgSmall>(M, N) >= cus)
+    if (2 * tile_count<CfgSmall>(M, N) >= cus) {
+        // A 3-deep ring keeps two stages of loads in flight: with one wave per
+        // SIMD and 512 cycles of MFMAs per stage, the 2-deep ring's per-stage
+        // load latency shows.  It pays on K loops of 32 stages or more
+        // (2048 x 2048 x 2050 BF16: 33.7 -> 27.1 us; 512 x 4096 x 4096 INT8:
+        // 22.4 -> 20.3 us) and costs 2-5% on 16 stages (2048^3 INT8); its
+        // 96 KB of LDS leaves one workgroup per CU, so only where the tiles
+        // take one round.
+        if (K * E::BYTES >= 32 * CfgSmallDeep::BK && tile_count<CfgSmallDeep>(M, N) <= cus)
+            return launch_cfg<CfgSmallDeep, E, OUT_I32, ACT, VEC_OUT>(a, sa, M, w, sw, N, K, bias,
+                                                                     out, cus, stream);
         return launch_cfg<CfgSmall, E, OUT_I32, ACT, VEC_OUT>(a, sa, M, w, sw, N, K, bias, out, cus,
                                                              stream);
+    }
     return launch_cfg<CfgTiny, E, OUT_I32, ACT, VEC_OUT>(a, sa, M, w, sw, N, K, bias, out, cus,
                                                         stream);
 }

@@ -209,14 +209,15 @@ def test_quantize_blocks_guard_bands():
 # rounds of tiles per CU cost less, and 384 x 256 (INT8 without GELU, long K
 # loops or many tiles).  A persistent workgroup takes several tiles when there
 # are more than 256.  Covered here: 64 x 64 tiles (the first seven shapes),
-# 128 x 128 tiles (2048^3 and 2000 x 1984, ragged), 192 x 256 tiles with ragged
+# 128 x 128 tiles (2048^3 and 2000 x 1984, ragged; 1000 x 2048 x 8192 with the
+# 3-deep K ring of long K loops), 192 x 256 tiles with ragged
 # M, with ragged N (4100 x 4096, 4096 x 4160, both with workgroups taking two
 # tiles) and on a text-projection row count (2378 x 4096), 256 x 256 tiles
 # with ragged M and N (3900 x 3776, 3900 x 4032).  The 384 x 256 tiles are
 # covered by test_gemm_xl_tiles_ragged_sampled and by the full-size FFN tests.
 GEMM_SHAPES = [(1, 64, 128), (64, 128, 256), (129, 192, 384), (300, 320, 1024), (257, 64, 4096),
                (1000, 448, 2048), (33, 256, 16384), (2048, 2048, 2048), (2000, 1984, 512),
-               (4100, 4096, 256), (4096, 4160, 128), (2378, 4096, 512), (3900, 3776, 128),
+               (1000, 2048, 8192), (4100, 4096, 256), (4096, 4160, 128), (2378, 4096, 512), (3900, 3776, 128),
                (3900, 4032, 128)]
 
 
@@ -260,7 +261,8 @@ def test_gemm_xl_tiles_max_k_closed_form():
 
 
 @pytest.mark.parametrize("M,N,K", [(64, 128, 256), (129, 192, 384), (2048, 2048, 2048),
-                                   (2000, 1984, 512), (4100, 4160, 128), (2378, 4096, 256),
+                                   (2000, 1984, 512), (1000, 2048, 4096), (4100, 4160, 128),
+                                   (2378, 4096, 256),
                                    (3900, 3776, 128)])
 @pytest.mark.parametrize("act", [w8.ACT_NONE, w8.ACT_GELU_TANH])
 @pytest.mark.parametrize("with_bias", [True, False])
