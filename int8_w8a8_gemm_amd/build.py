@@ -25,6 +25,8 @@ SOURCES = ["quantize_rows.hip", "compact_rows.hip", "gemm_tiled.hip", "gemm_bf16
 # measurement probe, a library of its own (not part of libw8a8's ABI)
 PROBE_SOURCES = ["probe_mfma.hip"]
 PROBE_LIB = os.path.join(HERE, "libw8a8_probe.so")
+ABI_CHECK_SRC = os.path.join(os.path.dirname(HERE), "tests", "c", "abi_check.cpp")
+ABI_CHECK = os.path.join(BUILD, "abi_check")
 ARCH = "gfx950"
 FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-ffp-contract=off",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -76,6 +78,9 @@ def build(verbose: bool = False, jobs: int = 5) -> str:
         tmp = lib + ".tmp"
         _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *part, "-o", tmp])
         os.replace(tmp, lib)
+    # the C-ABI check program of the tests (uses the library with no PyTorch)
+    _run([hipcc, "-O2", "-std=c++17", f"-I{INCLUDE}", ABI_CHECK_SRC, f"-L{HERE}", "-lw8a8",
+          "-Wl,-rpath,$ORIGIN/..", "-o", ABI_CHECK])
     return LIB
 
 

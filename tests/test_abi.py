@@ -203,3 +203,27 @@ def test_python_binding_refuses_cpu_tensors():
     x = torch.zeros((4, 128), dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         w8.quantize_rows(x)
+
+
+ABI_CHECK = os.path.join(ROOT, "int8_w8a8_gemm_amd", "_build", "abi_check")
+
+
+def test_c_program_links_only_the_library_and_hip():
+    """tests/c/abi_check.cpp is built against the header and libw8a8.so alone."""
+    assert os.path.exists(ABI_CHECK), "build first: __graft_entry__.build()"
+    import subprocess
+    out = subprocess.run(["readelf", "-d", ABI_CHECK], capture_output=True, text=True).stdout
+    needed = set(re.findall(r"\(NEEDED\)\s+Shared library: \[([^\]]+)\]", out))
+    assert "libw8a8.so" in needed
+    assert not any("torch" in n or "python" in n for n in needed), needed
+
+
+@pytest.mark.gpu
+def test_c_program_through_the_abi_on_the_gpu():
+    """A plain HIP program (its own hipMalloc buffers and stream, no PyTorch) runs
+    the INT8 GEMM against an integer loop, a hand-worked quantisation row, and the
+    guard's routing to the BF16 path; it exits 0 and prints "abi_check ok"."""
+    import subprocess
+    print("c abi check", flush=True)
+    p = subprocess.run([ABI_CHECK], capture_output=True, text=True, timeout=60)
+    assert p.returncode == 0 and "abi_check ok" in p.stdout, p.stdout + p.stderr
