@@ -10,7 +10,10 @@
 // (or the raw acc in int32 mode), and for BF16 operands
 //     acc[i][j] = sum_k x[i][k] * w[j][k]                (fp32 accumulation)
 //     y[i][j]   = bf16_RNE(acc + bias[j])
-// each with an optional GELU-tanh on the bf16 y.
+// each with an optional GELU-tanh on the bf16 y.  Without a bias the same
+// code adds -0.0, which leaves every value, and the sign of every zero, as
+// the product alone has it (x + -0 = x in round-to-nearest), so there is one
+// epilogue, not one per bias/no-bias case competing for registers.
 //
 // Both operands are K-contiguous ([M x K] and [N x K]), the layout the MFMA
 // A/B operands want: every lane feeds 16 consecutive K bytes of one row.
@@ -227,6 +230,20 @@ struct rsrc_t { int w[4]; };
 #if defined(__HIP_DEVICE_COMPILE__)
 constexpr int kRawBufferWord3 = 0x00020000;  // untyped 32-bit buffer access
 #endif
+
+// Element i of a bias vector of `count` elements that may be absent (NULL).
+// A buffer load over an empty range returns 0, so there is no branch on the
+// pointer: the load defines its register with no phi to resolve, and stays in
+// flight until its value is used.
+__device__ __forceinline__ uint32_t load_bias_bits(const uint16_t* bias, int count, int i) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)bias, (short)0, bias ? 2 * count : 0,
+                                                      kRawBufferWord3);
+    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, 2 * i, 0, 0);
+#else
+    return 0u;
+#endif
+}
 
 // Per-tile addressing.  Each operand is read through a buffer resource based
 // at the tile's first row and sized to the rows that exist, so rows past M
@@ -509,8 +526,9 @@ __device__ __forceinline__ void tile_of(int64_t bid, int64_t tm, int64_t tn, int
 // free of bank conflicts.  `stage` must not overlap the K buffer that the next
 // tile's first stage is being loaded into.  VEC_OUT: y rows are 16-byte
 // aligned and N % 8 == 0, so every 16-byte chunk is stored whole; otherwise
-// chunks are stored element by element.
-template <class C, class E, int ACT, bool HAS_BIAS, bool VEC_OUT>
+// chunks are stored element by element.  b_l holds the bias, -0.0 where
+// there is none.
+template <class C, class E, int ACT, bool VEC_OUT>
 __device__ __forceinline__ void store_bf16(const Acc<C, E>& acc, uint16_t* __restrict__ y, int64_t M,
                                            int64_t N, int64_t m0, int64_t n0, int wave, int wm,
                                            int wn, int lane, const float* sa_l, const float* sw_l,
@@ -539,7 +557,7 @@ __device__ __forceinline__ void store_bf16(const Acc<C, E>& acc, uint16_t* __res
             for (int g = 0; g < 4; ++g) {
                 const int cl = ncol + ni * 32 + 8 * g;
                 if constexpr (E::BYTES == 1) swv[g] = *reinterpret_cast<const v4f*>(sw_l + cl);
-                if (HAS_BIAS) bv[g] = *reinterpret_cast<const v4f*>(b_l + cl);
+                bv[g] = *reinterpret_cast<const v4f*>(b_l + cl);
             }
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
@@ -549,10 +567,10 @@ __device__ __forceinline__ void store_bf16(const Acc<C, E>& acc, uint16_t* __res
                     if constexpr (E::BYTES == 1) {
                         const float t = (float)acc[ni][p][4 * g + e];  // nearest even
                         const float u = __fmul_rn(sam, swv[g][e]);
-                        v[e] = HAS_BIAS ? __builtin_fmaf(t, u, bv[g][e]) : __fmul_rn(t, u);
+                        v[e] = __builtin_fmaf(t, u, bv[g][e]);
                     } else {
                         const float t = acc[ni][p][4 * g + e];
-                        v[e] = HAS_BIAS ? __fadd_rn(t, bv[g][e]) : t;
+                        v[e] = __fadd_rn(t, bv[g][e]);
                     }
                 }
                 uint2 o = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
@@ -691,7 +709,14 @@ void gemm_tiled(const void* __restrict__ a, const float* __restrict__ sa, int64_
         if (!OUT_I32) {
             const int64_t n = n0_ + tid < N ? n0_ + tid : N - 1;
             if (SCALES) nsw = sw[n];
-            nb = bias ? (uint32_t)bias[n] : 0u;
+            if constexpr (C::SCALES_IN_RING) {
+                // loaded during the last K stage: a branch on the pointer
+                // would make the wave wait for it there
+                const int64_t cnt = N - n0_ < BN ? N - n0_ : BN;
+                nb = load_bias_bits(bias ? bias + n0_ : nullptr, (int)cnt, (int)(n - n0_));
+            } else {
+                nb = bias ? (uint32_t)bias[n] : 0u;
+            }
         }
     };
     if constexpr (!C::SCALES_IN_RING) load_scales(m0, n0);
@@ -700,10 +725,19 @@ void gemm_tiled(const void* __restrict__ a, const float* __restrict__ sa, int64_
         // here, not kept in registers across the K loop
         int et = tid;
         asm volatile("" : "+v"(et));
+        if constexpr (C::SCALES_IN_RING) {
+            // every wave waits for its loads here, before the stores below
+            // branch: a wait left inside the branch would leave the loads
+            // pending, for the compiler, on the other path, and it would then
+            // wait for them at the next reuse of their registers, behind the
+            // next tile's first stage
+            if (SCALES) asm volatile("" ::"v"(nsa), "v"(nsw));
+            if (!OUT_I32) asm volatile("" ::"v"(nb));
+        }
         if (SCALES && et < BM) sa_l[et] = nsa;
         if (!OUT_I32 && et < BN) {
             if (SCALES) sw_l[et] = nsw;
-            b_l[et] = bf16_bits_to_float(nb);
+            b_l[et] = bf16_bits_to_float(bias ? nb : 0x8000u);  // -0.0 without a bias
         }
     };
     for (int s = 0; s < NST; ++s)
@@ -758,14 +792,8 @@ void gemm_tiled(const void* __restrict__ a, const float* __restrict__ sa, int64_
         if constexpr (OUT_I32 != 0) {
             store_i32<C>(acc, reinterpret_cast<int32_t*>(out), M, N, m0, n0, wm, wn, elane);
         } else {
-            if (bias)
-                store_bf16<C, E, ACT, true, VEC_OUT>(acc, reinterpret_cast<uint16_t*>(out), M, N,
-                                                     m0, n0, wave, wm, wn, elane, sa_l, sw_l, b_l,
-                                                     smem + C::STAGE);
-            else
-                store_bf16<C, E, ACT, false, VEC_OUT>(acc, reinterpret_cast<uint16_t*>(out), M,
-                                                      N, m0, n0, wave, wm, wn, elane, sa_l, sw_l,
-                                                      b_l, smem + C::STAGE);
+            store_bf16<C, E, ACT, VEC_OUT>(acc, reinterpret_cast<uint16_t*>(out), M, N, m0, n0,
+                                           wave, wm, wn, elane, sa_l, sw_l, b_l, smem + C::STAGE);
         }
         if (!has_next) break;
         // this tile's epilogue is done with the old values

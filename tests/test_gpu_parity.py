@@ -315,6 +315,32 @@ def test_gemm_xl_tiles_ragged_sampled():
     y = w8.gemm(qa_d, torch.from_numpy(sa).to(DEV), qw_d, torch.from_numpy(sw).to(DEV), d_bf16(b))
     ref = oracle.epilogue(acc_ref, np.ascontiguousarray(sa[rows]), sw, b)
     assert np.array_equal(h_u16(y)[rows], ref)
+    y = w8.gemm(qa_d, torch.from_numpy(sa).to(DEV), qw_d, torch.from_numpy(sw).to(DEV), None)
+    ref = oracle.epilogue(acc_ref, np.ascontiguousarray(sa[rows]), sw, None)
+    assert np.array_equal(h_u16(y)[rows], ref)
+
+
+@pytest.mark.parametrize("M,N,K", [(129, 192, 384), (2048, 2048, 2048), (6100, 4032, 8192)])
+def test_gemm_without_bias_keeps_the_sign_of_zero(M, N, K):
+    """Without a bias the output is the rounded product alone.  With scales whose
+    product underflows to +0 that product is +0 or -0 by the sign of the
+    accumulator, so the bf16 output is 0x8000 exactly where acc < 0 and 0x0000
+    elsewhere (the last shape runs the 384 x 256 tiles, the others the smaller
+    ones).  Rows compared: every tile edge, the tail and a random sample."""
+    say(f"gemm signed zero M={M} N={N} K={K}")
+    rng = np.random.default_rng(M + 7)
+    qa = rng.integers(-127, 128, (M, K), dtype=np.int8)
+    qw = rng.integers(-127, 128, (N, K), dtype=np.int8)
+    sa = np.full(M, 1e-30, dtype=np.float32)
+    sw = np.full(N, 1e-30, dtype=np.float32)
+    assert np.float32(sa[0]) * np.float32(sw[0]) == 0  # underflows in binary32
+    rows = _tile_edge_rows(M, 128, rng, extra=40)
+    y = h_u16(w8.gemm(d_i8(qa), torch.from_numpy(sa).to(DEV), d_i8(qw), torch.from_numpy(sw).to(DEV),
+                      None))[rows]
+    acc = oracle.gemm_i32(np.ascontiguousarray(qa[rows]), qw)
+    assert np.array_equal(y, np.where(acc < 0, 0x8000, 0).astype(np.uint16))
+    assert np.array_equal(y, oracle.epilogue(acc, np.ascontiguousarray(sa[rows]), sw, None))
+    assert (acc < 0).any() and (acc > 0).any()
 
 
 def test_gemm_rejects_unsupported_shape_on_device():
