@@ -57,6 +57,7 @@ def _load():
     lib.oracle_linear_bf16.argtypes = [P, I64, I64, P, I64, P, I, P, I]
     lib.oracle_w8a8_linear.argtypes = [P, I64, I64, P, I64, P, I, P, I]
     lib.oracle_compact_rows.argtypes = [P, P, I64, I64, I64, P, P, P]
+    lib.oracle_norm_mod.argtypes = [P, I64, I64, P, P, I64, I, ctypes.c_double, P, I]
     lib.oracle_guard.argtypes = [I64, I64]
     lib.oracle_guard.restype = I
     lib.oracle_bf16_to_f32.argtypes = [ctypes.c_uint16]
@@ -210,6 +211,42 @@ def gelu_rows(y, nthreads=None):
 def gelu_quantize_rows(y, nthreads=None):
     """Per-row INT8 quantisation of GELU-tanh(y): the down projection's input."""
     return quantize_rows(gelu_rows(y, nthreads), nthreads)
+
+
+NORM_LAYER = 0
+NORM_RMS = 1
+
+
+def norm_mod_bf16(x, shift=None, scale=None, rows_per_cond=None, norm=NORM_LAYER, eps=1e-6,
+                  nthreads=None):
+    """Normalisation and modulation of each row, the fused operators ahead of a
+    linear layer (paperlayer.ai summary, section C, names them; the formulas
+    are readings): LayerNorm without affine (norm=0) or RMSNorm (norm=1), then
+    z = y * (1 + scale[g]) + shift[g] for the row's conditioning group
+    g = row // rows_per_cond, in binary64, rounded once to bf16.
+
+    x: uint16 [R, D]; shift, scale: uint16 [G, D] or None.  Returns uint16 [R, D].
+    """
+    x = _c(x, np.uint16)
+    R, D = x.shape
+    rpc = int(rows_per_cond) if rows_per_cond else max(R, 1)
+    G = -(-R // rpc) if R else 0
+    sh = _c(shift, np.uint16) if shift is not None else None
+    sc = _c(scale, np.uint16) if scale is not None else None
+    for v in (sh, sc):
+        assert v is None or (v.shape[0] >= G and v.shape[1] == D)
+    y = np.empty_like(x)
+    _check(_load().oracle_norm_mod(_ptr(x), R, D, _ptr(sh), _ptr(sc), rpc, int(norm), float(eps),
+                                   _ptr(y), _threads(nthreads)), "oracle_norm_mod")
+    return y
+
+
+def norm_mod_quantize_rows(x, shift=None, scale=None, rows_per_cond=None, norm=NORM_LAYER,
+                           eps=1e-6, nthreads=None):
+    """The fused prologue of a W8A8 linear: per-row INT8 quantisation of the
+    bf16 normalised and modulated rows (norm_mod_bf16 then quantize_rows)."""
+    return quantize_rows(norm_mod_bf16(x, shift, scale, rows_per_cond, norm, eps, nthreads),
+                         nthreads)
 
 
 def guard(N: int, K: int) -> bool:

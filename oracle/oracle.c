@@ -27,6 +27,12 @@
  *   C  mask nonzero = valid; output keeps (sample, position) order.
  *   QB attention Q / K: blocks of `block` tokens of one sample and one head of
  *      a token-row matrix [B x S x H*D], each quantised as in Q over the block.
+ *   NM normalisation + modulation ahead of a linear layer (the fused operators
+ *      of the paperlayer.ai summary, section C): per row, LayerNorm without
+ *      affine (mean and variance over the row) or RMSNorm (mean square), then
+ *      z = y * (1 + scale) + shift with the modulation vectors of the row's
+ *      conditioning group; all in binary64, rounded once to bf16; the fused
+ *      variant quantises that bf16 row as in Q.
  *
  * Build: gcc -O2 -ffp-contract=off -fno-fast-math -shared -fPIC -pthread.
  */
@@ -414,5 +420,61 @@ int oracle_compact_rows(const uint16_t* x, const uint8_t* mask, int64_t B, int64
         }
     }
     *count = (int32_t)m;
+    return 0;
+}
+
+/* ---------------------------------------------------------------------- */
+/* NM: normalisation and modulation of each row, rounded once to bf16.     */
+/*   LayerNorm (norm 0): mu = sum(x)/D, var = sum((x - mu)^2)/D            */
+/*     (Ba, Kiros & Hinton 2016, without the elementwise affine);          */
+/*   RMSNorm (norm 1): mu = 0, var = sum(x^2)/D (Zhang & Sennrich 2019);   */
+/*   rstd = 1/sqrt(var + eps), 0 where var + eps is 0;                     */
+/*   z = (x - mu) * rstd * (1 + scale[g]) + shift[g], g = row / rpc        */
+/*     (adaptive-norm modulation as in DiT, Peebles & Xie 2023), with the  */
+/*     last multiply-add fused; NULL scale or shift reads as 0.            */
+/* ---------------------------------------------------------------------- */
+
+typedef struct {
+    const uint16_t *x, *shift, *scale; int64_t cols, rpc; int norm; double eps; uint16_t* y;
+} nm_ctx;
+
+static void nm_rows(void* p, int64_t r0, int64_t r1) {
+    nm_ctx* c = (nm_ctx*)p;
+    const int64_t D = c->cols;
+    for (int64_t r = r0; r < r1; ++r) {
+        const uint16_t* xr = c->x + r * D;
+        const int64_t g = r / c->rpc;
+        /* 1. the row's statistics, binary64 sums in index order */
+        double mu = 0.0;
+        if (c->norm == 0) {
+            double s1 = 0.0;
+            for (int64_t j = 0; j < D; ++j) s1 += (double)bf16_to_f32(xr[j]);
+            mu = s1 / (double)D;
+        }
+        double s2 = 0.0;
+        for (int64_t j = 0; j < D; ++j) {
+            const double d = (double)bf16_to_f32(xr[j]) - mu;
+            s2 += d * d;
+        }
+        const double v = s2 / (double)D + c->eps;
+        const double rstd = v > 0.0 ? 1.0 / sqrt(v) : 0.0;
+        /* 2. normalise, modulate, round once to bf16 */
+        for (int64_t j = 0; j < D; ++j) {
+            const double y = ((double)bf16_to_f32(xr[j]) - mu) * rstd;
+            const double sc = c->scale ? (double)bf16_to_f32(c->scale[g * D + j]) : 0.0;
+            const double sh = c->shift ? (double)bf16_to_f32(c->shift[g * D + j]) : 0.0;
+            c->y[r * D + j] = f64_to_bf16(fma(y, 1.0 + sc, sh));
+        }
+    }
+}
+
+int oracle_norm_mod(const uint16_t* x, int64_t rows, int64_t cols, const uint16_t* shift,
+                    const uint16_t* scale, int64_t rows_per_cond, int norm, double eps,
+                    uint16_t* y, int nthreads) {
+    if (fegetround() != FE_TONEAREST) return -1;
+    if (rows < 0 || cols < 1 || rows_per_cond < 1 || (norm != 0 && norm != 1) || !(eps >= 0.0))
+        return -1;
+    nm_ctx c = {x, shift, scale, cols, rows_per_cond, norm, eps, y};
+    parallel_rows(nm_rows, &c, rows, nthreads);
     return 0;
 }

@@ -692,3 +692,122 @@ def test_workload_recipe_shapes_and_outliers():
     g = wl.guarded_mixed(B=8, L=512, D=8)
     assert np.all((g.lengths >= 64) & (g.lengths <= 512))
     assert np.array_equal(g.mask.sum(axis=1), g.lengths)
+
+
+# ---------------------------------------------------------------------------
+# NM: normalisation + modulation ahead of a linear layer (paperlayer.ai
+# summary, section C names the fused operators; formulas are readings)
+# ---------------------------------------------------------------------------
+
+def _golden_nm_cases():
+    cases = []
+    for ln in open(os.path.join(GOLDEN, "norm_mod.txt"), encoding="utf-8"):
+        ln = ln.strip()
+        if not ln or ln.startswith("#"):
+            continue
+        head, xs, sc, sh, ys = [p.strip() for p in ln.split(";")]
+        norm, eps, rpc, D = head.split()
+        vals = lambda t: None if t == "-" else [float(v) for v in t.split()]
+        cases.append((oracle.NORM_LAYER if norm == "LN" else oracle.NORM_RMS, float(eps), int(rpc),
+                      int(D), vals(xs), vals(sc), vals(sh), vals(ys)))
+    return cases
+
+
+def _bits(vals, D):
+    return None if vals is None else np.array([bf16_bits_of_value(v) for v in vals],
+                                              np.uint16).reshape(-1, D)
+
+
+@pytest.mark.parametrize("case", _golden_nm_cases(), ids=lambda c: f"n{c[0]}e{c[1]}r{c[2]}")
+def test_norm_mod_hand_worked(case):
+    norm, eps, rpc, D, xs, sc, sh, ys = case
+    z = oracle.norm_mod_bf16(_bits(xs, D), _bits(sh, D), _bits(sc, D), rpc, norm, eps)
+    assert z.reshape(-1).tolist() == [bf16_bits_of_value(v) for v in ys]
+
+
+def _f64_to_bf16_value(v: np.ndarray) -> np.ndarray:
+    """Nearest bf16 value (ties to even) of float64 values in bf16's normal
+    range, by scaling each to its 8-bit grid and numpy's rint."""
+    m, e = np.frexp(np.abs(v))
+    r = np.ldexp(np.rint(np.ldexp(np.abs(v), 8 - e)), e - 8)
+    return np.where(v == 0, 0.0, np.copysign(r, v))
+
+
+def _tie_margin(v: np.ndarray) -> np.ndarray:
+    """Distance of |v| from the nearest bf16 rounding boundary, relative to the
+    bf16 spacing at v (0 on a tie, 0.5 on a representable value)."""
+    m, e = np.frexp(np.abs(v))
+    f = np.ldexp(np.abs(v), 8 - e)
+    return np.abs(np.abs(f - np.floor(f)) - 0.5)
+
+
+@pytest.mark.parametrize("norm", [oracle.NORM_LAYER, oracle.NORM_RMS])
+@pytest.mark.parametrize("R,D,rpc", [(7, 64, 7), (40, 256, 8), (9, 4096, 3)])
+def test_norm_mod_matches_torch_layer_and_rms_norm(norm, R, D, rpc):
+    """Reduces to library routines: torch's float64 layer_norm / rms_norm (no
+    affine) give y; the modulation y * (1 + scale) + shift is then one float64
+    multiply-add.  Equal after rounding to bf16 wherever the float64 values sit
+    clear of a bf16 rounding boundary (the two float64 computations differ only
+    in their last bits)."""
+    rng = np.random.default_rng(R * D + norm)
+    x = wl.to_bf16_bits(rng.standard_normal((R, D)).astype(np.float32) * np.float32(3.0) + 0.5)
+    G = -(-R // rpc)
+    sc = wl.to_bf16_bits(rng.standard_normal((G, D)).astype(np.float32) * np.float32(0.3))
+    sh = wl.to_bf16_bits(rng.standard_normal((G, D)).astype(np.float32) * np.float32(0.3))
+    eps = 1e-6
+    z = oracle.norm_mod_bf16(x, sh, sc, rpc, norm, eps)
+    xt = torch.from_numpy((x.astype(np.uint32) << 16).view(np.float32)).double()
+    if norm == oracle.NORM_LAYER:
+        y = torch.nn.functional.layer_norm(xt, (D,), eps=eps)
+    else:
+        y = torch.nn.functional.rms_norm(xt, (D,), eps=eps)
+    g = np.arange(R) // rpc
+    f = lambda b: (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    ref = y.numpy() * (1.0 + f(sc)[g]) + f(sh)[g]
+    got = f(z)
+    clear = _tie_margin(ref) > 2.0 ** -20
+    assert clear.mean() > 0.99
+    assert np.array_equal(got[clear], _f64_to_bf16_value(ref)[clear])
+
+
+@pytest.mark.parametrize("norm", [oracle.NORM_LAYER, oracle.NORM_RMS])
+def test_norm_mod_power_of_two_invariance(norm):
+    """With eps = 0, scaling a row by 2^k scales its mean and standard deviation
+    by 2^k exactly (binary64 sums, division and square root are exact under
+    power-of-two scaling), so the normalised row is bit-identical."""
+    rng = np.random.default_rng(31 + norm)
+    v = rng.standard_normal((12, 96)).astype(np.float32)
+    sc = wl.to_bf16_bits(rng.standard_normal((1, 96)).astype(np.float32) * np.float32(0.5))
+    sh = wl.to_bf16_bits(rng.standard_normal((1, 96)).astype(np.float32) * np.float32(0.5))
+    z0 = oracle.norm_mod_bf16(wl.to_bf16_bits(v), sh, sc, 12, norm, 0.0)
+    for k in (-40, -3, 1, 7, 60):
+        zk = oracle.norm_mod_bf16(wl.to_bf16_bits(v * np.float32(2.0 ** k)), sh, sc, 12, norm, 0.0)
+        assert np.array_equal(zk, z0), k
+
+
+def test_norm_mod_statistics_of_the_output():
+    """Without modulation a LayerNorm row has mean ~0 and variance ~1, an RMSNorm
+    row mean square ~1 (to the bf16 rounding of each element)."""
+    rng = np.random.default_rng(5)
+    x = wl.to_bf16_bits(rng.standard_normal((16, 1024)).astype(np.float32) * np.float32(7.0) + 2.0)
+    f = lambda b: (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    z = f(oracle.norm_mod_bf16(x, norm=oracle.NORM_LAYER, eps=0.0))
+    assert np.all(np.abs(z.mean(axis=1)) < 2.0 ** -8)
+    assert np.all(np.abs(z.var(axis=1) - 1.0) < 2.0 ** -7)
+    z = f(oracle.norm_mod_bf16(x, norm=oracle.NORM_RMS, eps=0.0))
+    assert np.all(np.abs((z * z).mean(axis=1) - 1.0) < 2.0 ** -7)
+
+
+def test_norm_mod_quantize_is_quantisation_of_the_bf16_rows_and_degenerate_inputs():
+    rng = np.random.default_rng(6)
+    x = wl.to_bf16_bits(rng.standard_normal((10, 64)).astype(np.float32))
+    x[4] = x[4, 0]  # constant row: normalises to 0, quantises to scale 0
+    q, s = oracle.norm_mod_quantize_rows(x, eps=0.0)
+    z = oracle.norm_mod_bf16(x, eps=0.0)
+    qr, sr = oracle.quantize_rows(z)
+    assert np.array_equal(q, qr) and np.array_equal(s, sr)
+    assert s[4] == 0 and not q[4].any()
+    e = oracle.norm_mod_bf16(np.zeros((0, 64), np.uint16))
+    assert e.shape == (0, 64)
+    with pytest.raises(RuntimeError):
+        oracle.norm_mod_bf16(x, eps=-1.0)
