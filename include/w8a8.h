@@ -98,6 +98,51 @@ W8A8_API int w8a8_quantize_blocks(const uint16_t* x, int64_t batch, int64_t seq,
                                   int64_t head_dim, int64_t block, int8_t* q, float* scale,
                                   void* stream);
 
+typedef enum { W8A8_NORM_LAYER = 0, W8A8_NORM_RMS = 1 } w8a8_norm;
+
+/*
+ * Normalisation + modulation of rows ahead of a linear layer: the
+ * normalisation and modulation that the fused operators of the joint
+ * Transformer take over (paperlayer.ai summary, section C).  The page names the
+ * operations only; the formulas are the textbook ones:
+ *
+ *   x      [rows x cols] bf16 input rows
+ *   shift, scale [G x cols] bf16 modulation rows, G = ceil(rows / rows_per_cond);
+ *          row r takes row g = r / rows_per_cond of each (a sample's tokens share
+ *          its conditioning); either may be NULL (read as 0)
+ *   norm   W8A8_NORM_LAYER: mu = mean(x), var = mean((x - mu)^2) (LayerNorm
+ *          without its elementwise affine);  W8A8_NORM_RMS: mu = 0,
+ *          var = mean(x^2) (RMSNorm)
+ *   eps    >= 0, added to var: rstd = 1/sqrt(var + eps), 0 if var + eps == 0
+ *   y      [rows x cols] bf16 out:
+ *          z = fma((x - mu) * rstd, 1 + scale[g], shift[g]) in binary64,
+ *          rounded once to bf16 (nearest, ties to even)
+ *
+ * The row sums are taken in binary64 in no fixed order, which can move them in
+ * their last bits only.  Alignment: 2-byte for every bf16 pointer; 16-byte x,
+ * shift, scale and y with cols % 8 == 0 and cols <= 32768 take the vector
+ * path.  rows = 0 is a no-op; cols >= 1, rows_per_cond >= 1 and fewer than
+ * 2^31 rows are required (W8A8_EINVAL otherwise).  y must not overlap x.
+ */
+W8A8_API int w8a8_norm_mod_bf16(const uint16_t* x, int64_t rows, int64_t cols,
+                                const uint16_t* shift, const uint16_t* scale,
+                                int64_t rows_per_cond, int norm, double eps, uint16_t* y,
+                                void* stream);
+
+/*
+ * The same normalisation and modulation fused with the per-row INT8
+ * quantisation of the following W8A8 linear's activations (section 01.3):
+ * q [rows x cols] int8 codes and qscale [rows] fp32 are exactly
+ * w8a8_quantize_rows applied to the bf16 rows w8a8_norm_mod_bf16 would write;
+ * those rows themselves are not written.  Requirements as w8a8_norm_mod_bf16,
+ * plus qscale 4-byte aligned (8-byte q with the vector path's conditions takes
+ * the vector path).
+ */
+W8A8_API int w8a8_norm_mod_quantize_rows(const uint16_t* x, int64_t rows, int64_t cols,
+                                         const uint16_t* shift, const uint16_t* scale,
+                                         int64_t rows_per_cond, int norm, double eps, int8_t* q,
+                                         float* qscale, void* stream);
+
 /*
  * Fused GELU + per-row INT8 quantisation: the input of a linear that follows a
  * GELU-tanh (the FFN down projection, whose input is the up projection's

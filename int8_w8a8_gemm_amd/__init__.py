@@ -26,11 +26,12 @@ OK, EINVAL, EUNSUPPORTED, EHIP = 0, -1, -2, -3
 OUT_BF16, OUT_I32 = 0, 1
 ACT_NONE, ACT_GELU_TANH = 0, 1
 PATH_INT8, PATH_BF16 = 0, 1
+NORM_LAYER, NORM_RMS = 0, 1
 MAX_K = 131072
 
 EXPORTS = ("w8a8_quantize_rows", "w8a8_quantize_blocks", "w8a8_gelu_quantize_rows", "w8a8_gelu_bf16", "w8a8_gemm", "w8a8_linear", "w8a8_linear_bf16",
            "compact_padded_rows", "w8a8_compact_quantize_rows", "w8a8_guard", "w8a8_linear_workspace_bytes",
-           "w8a8_status_str")
+           "w8a8_status_str", "w8a8_norm_mod_bf16", "w8a8_norm_mod_quantize_rows")
 
 _lib = None
 
@@ -55,6 +56,8 @@ def lib():
     L.w8a8_quantize_blocks.argtypes = [P, I64, I64, I64, I64, I64, P, P, P]
     L.w8a8_gelu_quantize_rows.argtypes = [P, I64, I64, P, P, P]
     L.w8a8_gelu_bf16.argtypes = [P, I64, P, P]
+    L.w8a8_norm_mod_bf16.argtypes = [P, I64, I64, P, P, I64, I, ctypes.c_double, P, P]
+    L.w8a8_norm_mod_quantize_rows.argtypes = [P, I64, I64, P, P, I64, I, ctypes.c_double, P, P, P]
     L.w8a8_gemm.argtypes = [P, P, I64, P, P, I64, I64, P, I, I, P, P]
     L.w8a8_linear.argtypes = [P, I64, I64, I64, P, P, P, P, I, P, P, SZ, P, P]
     L.w8a8_linear_bf16.argtypes = [P, I64, I64, P, I64, P, I, P, P]
@@ -182,6 +185,56 @@ def gelu_quantize_rows(y: torch.Tensor, q: Optional[torch.Tensor] = None,
     _check("w8a8_gelu_quantize_rows",
            lib().w8a8_gelu_quantize_rows(_p(y), R, C, _p(q), _p(scale), _stream(stream)))
     return q, scale
+
+
+def _norm_mod_args(x, shift, scale, rows_per_cond):
+    _need(x, "x", torch.bfloat16)
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D")
+    R, C = x.shape
+    rpc = int(rows_per_cond) if rows_per_cond else max(R, 1)
+    G = -(-R // rpc) if R else 0
+    for t, n in ((shift, "shift"), (scale, "scale")):
+        if t is not None:
+            _need(t, n, torch.bfloat16)
+            if t.dim() != 2 or t.shape[1] != C or t.shape[0] < G:
+                raise ValueError(f"{n} must be [>= {G}, {C}]")
+    return R, C, rpc
+
+
+def norm_mod_bf16(x: torch.Tensor, shift: Optional[torch.Tensor] = None,
+                  scale: Optional[torch.Tensor] = None, rows_per_cond: Optional[int] = None,
+                  norm: int = NORM_LAYER, eps: float = 1e-6, y: Optional[torch.Tensor] = None,
+                  stream=None):
+    """Normalisation (LayerNorm without affine, or RMSNorm) and modulation
+    z = y * (1 + scale[g]) + shift[g], g = row // rows_per_cond, of each row of
+    x bf16 [R, C]; shift, scale bf16 [G, C] or None.  Returns bf16 [R, C]."""
+    R, C, rpc = _norm_mod_args(x, shift, scale, rows_per_cond)
+    y = y if y is not None else torch.empty_like(x)
+    _need(y, "y", torch.bfloat16, (R, C))
+    _check("w8a8_norm_mod_bf16",
+           lib().w8a8_norm_mod_bf16(_p(x), R, C, _p(shift), _p(scale), rpc, int(norm), float(eps),
+                                    _p(y), _stream(stream)))
+    return y
+
+
+def norm_mod_quantize_rows(x: torch.Tensor, shift: Optional[torch.Tensor] = None,
+                           scale: Optional[torch.Tensor] = None,
+                           rows_per_cond: Optional[int] = None, norm: int = NORM_LAYER,
+                           eps: float = 1e-6, q: Optional[torch.Tensor] = None,
+                           qscale: Optional[torch.Tensor] = None, stream=None):
+    """norm_mod_bf16 fused with the per-row INT8 quantisation of its rows:
+    returns (q int8 [R, C], qscale fp32 [R]); the bf16 rows are not written."""
+    R, C, rpc = _norm_mod_args(x, shift, scale, rows_per_cond)
+    q = q if q is not None else torch.empty((R, C), dtype=torch.int8, device=x.device)
+    qscale = qscale if qscale is not None else torch.empty((R,), dtype=torch.float32,
+                                                           device=x.device)
+    _need(q, "q", torch.int8, (R, C))
+    _need(qscale, "qscale", torch.float32, (R,))
+    _check("w8a8_norm_mod_quantize_rows",
+           lib().w8a8_norm_mod_quantize_rows(_p(x), R, C, _p(shift), _p(scale), rpc, int(norm),
+                                             float(eps), _p(q), _p(qscale), _stream(stream)))
+    return q, qscale
 
 
 def gelu_bf16(x: torch.Tensor, y: Optional[torch.Tensor] = None, stream=None):

@@ -115,6 +115,11 @@ int launch_quantize_rows(const uint16_t* x, int64_t rows, int64_t cols, int8_t* 
                          hipStream_t stream, bool gelu = false);
 int launch_quantize_blocks(const uint16_t* x, int64_t B, int64_t S, int64_t H, int64_t D,
                            int64_t block, int8_t* q, float* scale, hipStream_t stream);
+// Normalisation + modulation of rows; q != NULL: fused with the per-row
+// quantisation (codes q, scales qscale), else the bf16 rows y.
+int launch_norm_mod(const uint16_t* x, int64_t rows, int64_t cols, const uint16_t* shift,
+                    const uint16_t* scale, int64_t rows_per_cond, int norm, double eps, int8_t* q,
+                    float* qscale, uint16_t* y, hipStream_t stream);
 int launch_compact_rows(const uint16_t* x, const uint8_t* mask, int64_t R, int64_t D,
                         uint16_t* out, int32_t* src_row, int32_t* count, hipStream_t stream);
 int launch_compact_quantize_rows(const uint16_t* x, const uint8_t* mask, int64_t R, int64_t D,

@@ -532,6 +532,279 @@ hipError_t launch_blocks(const uint16_t* x, int64_t B, int64_t S, int64_t H, int
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Normalisation + modulation ahead of a linear layer, alone (bf16 out) or fused
+// with the per-row quantisation (the fused operators of the paperlayer.ai
+// summary, section C; the formulas are readings).  Per row of D elements:
+//     LayerNorm:  mu = sum(x) / D,  var = sum((x - mu)^2) / D
+//     RMSNorm:    mu = 0,           var = sum(x^2) / D
+//     rstd = 1 / sqrt(var + eps), 0 where var + eps = 0
+//     z = fma((x - mu) * rstd, 1 + scale[g], shift[g]),  g = row / rows_per_cond
+// in binary64, z rounded once to bf16; the fused variant then quantises the
+// bf16 row exactly as quantize_rows does.  The sums' order is free: it moves
+// them only in their last binary64 bits, which reach the bf16 result only in
+// the rare case that z lies that close to a bf16 rounding boundary.  The
+// vector kernel keeps the row in registers (as quantize_rows_vec), so each
+// element is read from HBM once and the statistics cost no second pass.
+
+// binary64 -> bf16 bits, to nearest even, with a single effective rounding:
+// the conversion to binary32 is made round-to-odd (the nearest-even binary32
+// moved, when inexact, to its odd neighbour toward zero), and rounding that
+// to bf16, which keeps 16 bits fewer, gives the correctly rounded result.
+__device__ __forceinline__ uint32_t f64_to_bf16_bits(double d) {
+    const float f = (float)d;
+    uint32_t u = __float_as_uint(f);
+    if ((double)f != d) {
+        if (fabs((double)f) > fabs(d)) u -= 1u;
+        u |= 1u;
+    }
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+__device__ __forceinline__ double bf16_f64(uint32_t h) {
+    return (double)__uint_as_float((h & 0xffffu) << 16);
+}
+
+// z of one element: x, scale and shift as bf16 bits
+__device__ __forceinline__ uint32_t norm_mod1(uint32_t xh, uint32_t sch, uint32_t shh, double mu,
+                                              double rstd) {
+    const double y = (bf16_f64(xh) - mu) * rstd;
+    return f64_to_bf16_bits(__builtin_fma(y, 1.0 + bf16_f64(sch), bf16_f64(shh)));
+}
+
+// z of one chunk of 8 elements
+__device__ __forceinline__ u32x4 norm_mod8(u32x4 v, u32x4 sc, u32x4 sh, double mu, double rstd) {
+    u32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t lo = norm_mod1(v[i], sc[i], sh[i], mu, rstd);
+        const uint32_t hi = norm_mod1(v[i] >> 16, sc[i] >> 16, sh[i] >> 16, mu, rstd);
+        o[i] = lo | (hi << 16);
+    }
+    return o;
+}
+
+__device__ __forceinline__ double sum8_f64(u32x4 v) {
+    double t[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) t[i] = bf16_f64(v[i]) + bf16_f64(v[i] >> 16);
+    return (t[0] + t[1]) + (t[2] + t[3]);
+}
+
+__device__ __forceinline__ double sumsq8_f64(u32x4 v, double mu) {
+    double t[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const double a = bf16_f64(v[i]) - mu, b = bf16_f64(v[i] >> 16) - mu;
+        t[i] = __builtin_fma(a, a, b * b);
+    }
+    return (t[0] + t[1]) + (t[2] + t[3]);
+}
+
+__device__ __forceinline__ double rstd_of(double var, double eps) {
+    const double v = var + eps;
+    return v > 0.0 ? 1.0 / __builtin_sqrt(v) : 0.0;
+}
+
+// WPR waves per row, CPL 16-byte chunks per lane (cols % 8 == 0, rows of up to
+// WPR*64*CPL*8 elements); QUANT: codes and scale out, else the bf16 z.
+template <int WPR, int CPL, bool QUANT>
+__global__ __launch_bounds__(kBlock) void norm_mod_rows_vec(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, const uint16_t* __restrict__ shift,
+    const uint16_t* __restrict__ scale, int64_t rpc, int norm, double eps, int8_t* __restrict__ q,
+    float* __restrict__ qscale, uint16_t* __restrict__ y) {
+    constexpr int RPB = (kBlock / 64) / WPR;  // rows per block
+    __shared__ double red64[2][kBlock / 64];
+    __shared__ uint32_t red[kBlock / 64];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wr = wave % WPR, w0 = wave - wr;
+    const int64_t row = (int64_t)blockIdx.x * RPB + wave / WPR;
+    const bool live = row < rows;
+    const int64_t nchunk = cols >> 3;
+    const u32x4* xr = reinterpret_cast<const u32x4*>(x + (live ? row : 0) * cols);
+    const double D = (double)cols;
+    auto chunk = [&](int c) { return (int64_t)(c * WPR + wr) * 64 + lane; };
+    // sum over the row's WPR waves (every thread of the block takes part)
+    auto row_sum = [&](double t, int slot) {
+        t = wave_sum_f64(t);
+        if (WPR > 1) {
+            if (lane == 0) red64[slot][wave] = t;
+            __syncthreads();
+            t = 0.0;
+#pragma unroll
+            for (int i = 0; i < WPR; ++i) t += red64[slot][w0 + i];
+        }
+        return t;
+    };
+
+    u32x4 v[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c)
+        v[c] = (live && chunk(c) < nchunk) ? __builtin_nontemporal_load(xr + chunk(c))
+                                           : (u32x4){0u, 0u, 0u, 0u};
+    double mu = 0.0;
+    if (norm == 0) {
+        double t = 0.0;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) t += sum8_f64(v[c]);
+        mu = row_sum(t, 0) / D;
+    }
+    double t2 = 0.0;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c)
+        if (chunk(c) < nchunk) t2 += sumsq8_f64(v[c], mu);  // padding is not part of the row
+    const double rstd = rstd_of(row_sum(t2, 1) / D, eps);
+
+    const int64_t g = (live ? row : 0) / rpc;
+    const u32x4* scr = scale ? reinterpret_cast<const u32x4*>(scale + g * cols) : nullptr;
+    const u32x4* shr = shift ? reinterpret_cast<const u32x4*>(shift + g * cols) : nullptr;
+    uint32_t amax = 0;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+        const int64_t ch = chunk(c);
+        if (live && ch < nchunk) {
+            const u32x4 zero = {0u, 0u, 0u, 0u};
+            v[c] = norm_mod8(v[c], scr ? scr[ch] : zero, shr ? shr[ch] : zero, mu, rstd);
+            if (QUANT) amax = max(amax, absmax_bits(v[c]));
+            else __builtin_nontemporal_store(v[c], reinterpret_cast<u32x4*>(y + row * cols) + ch);
+        }
+    }
+    if constexpr (!QUANT) return;
+
+    amax = wave_max_u32(amax);
+    if (WPR > 1) {
+        if (lane == 0) red[wave] = amax;
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < WPR; ++i) amax = max(amax, red[w0 + i]);
+    }
+    if (!live) return;
+    const float a = __uint_as_float(amax << 16);
+    int8_t* qr = q + row * cols;
+    if (!(a >= 0x1p-100f)) {
+        if (wr == 0 && lane == 0) qscale[row] = 0.0f;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c)
+            if (chunk(c) < nchunk) reinterpret_cast<uint2*>(qr)[chunk(c)] = make_uint2(0, 0);
+        return;
+    }
+    const float inv = __fdiv_rn(127.0f, a);
+    if (wr == 0 && lane == 0) qscale[row] = __fdiv_rn(a, 127.0f);
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+        const int64_t ch = chunk(c);
+        if (ch < nchunk) {
+            const uint2 o = quant8_pk(v[c], inv);
+            __builtin_nontemporal_store(o.x, reinterpret_cast<uint32_t*>(qr) + 2 * ch);
+            __builtin_nontemporal_store(o.y, reinterpret_cast<uint32_t*>(qr) + 2 * ch + 1);
+        }
+    }
+}
+
+// Any cols, any alignment: one block per row, passes over the row in memory
+// (z is recomputed where it is needed again).
+template <bool QUANT>
+__global__ __launch_bounds__(kBlock) void norm_mod_rows_generic(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, const uint16_t* __restrict__ shift,
+    const uint16_t* __restrict__ scale, int64_t rpc, int norm, double eps, int8_t* __restrict__ q,
+    float* __restrict__ qscale, uint16_t* __restrict__ y) {
+    __shared__ double red64[kBlock / 64];
+    __shared__ uint32_t red[kBlock / 64];
+    const int64_t row = blockIdx.x;
+    if (row >= rows) return;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const uint16_t* xr = x + row * cols;
+    const int64_t g = row / rpc;
+    const double D = (double)cols;
+    auto block_sum = [&](double t) {
+        t = wave_sum_f64(t);
+        if (lane == 0) red64[wave] = t;
+        __syncthreads();
+        t = (red64[0] + red64[1]) + (red64[2] + red64[3]);
+        __syncthreads();
+        return t;
+    };
+    double mu = 0.0;
+    if (norm == 0) {
+        double t = 0.0;
+        for (int64_t k = threadIdx.x; k < cols; k += kBlock) t += bf16_f64(xr[k]);
+        mu = block_sum(t) / D;
+    }
+    double t2 = 0.0;
+    for (int64_t k = threadIdx.x; k < cols; k += kBlock) {
+        const double d = bf16_f64(xr[k]) - mu;
+        t2 = __builtin_fma(d, d, t2);
+    }
+    const double rstd = rstd_of(block_sum(t2) / D, eps);
+    auto z = [&](int64_t k) {
+        return norm_mod1(xr[k], scale ? scale[g * cols + k] : 0u, shift ? shift[g * cols + k] : 0u,
+                         mu, rstd);
+    };
+    if constexpr (!QUANT) {
+        for (int64_t k = threadIdx.x; k < cols; k += kBlock) y[row * cols + k] = (uint16_t)z(k);
+        return;
+    }
+    uint32_t amax = 0;
+    for (int64_t k = threadIdx.x; k < cols; k += kBlock) amax = max(amax, z(k) & 0x7fffu);
+    amax = wave_max_u32(amax);
+    if (lane == 0) red[wave] = amax;
+    __syncthreads();
+    amax = max(max(red[0], red[1]), max(red[2], red[3]));
+    const float a = __uint_as_float(amax << 16);
+    int8_t* qr = q + row * cols;
+    if (!(a >= 0x1p-100f)) {
+        if (threadIdx.x == 0) qscale[row] = 0.0f;
+        for (int64_t k = threadIdx.x; k < cols; k += kBlock) qr[k] = 0;
+        return;
+    }
+    const float inv = __fdiv_rn(127.0f, a);
+    if (threadIdx.x == 0) qscale[row] = __fdiv_rn(a, 127.0f);
+    for (int64_t k = threadIdx.x; k < cols; k += kBlock)
+        qr[k] = (int8_t)quant1(__uint_as_float(z(k) << 16), inv);
+}
+
+template <int WPR, int CPL, bool QUANT>
+hipError_t launch_nm(const uint16_t* x, int64_t rows, int64_t cols, const uint16_t* shift,
+                     const uint16_t* scale, int64_t rpc, int norm, double eps, int8_t* q,
+                     float* qscale, uint16_t* y, hipStream_t stream) {
+    constexpr int RPB = (kBlock / 64) / WPR;
+    const int64_t blocks = (rows + RPB - 1) / RPB;
+    hipLaunchKernelGGL((norm_mod_rows_vec<WPR, CPL, QUANT>), dim3((unsigned)blocks), dim3(kBlock), 0,
+                       stream, x, rows, cols, shift, scale, rpc, norm, eps, q, qscale, y);
+    return hipGetLastError();
+}
+
+template <bool QUANT>
+hipError_t launch_nm_any(const uint16_t* x, int64_t rows, int64_t cols, const uint16_t* shift,
+                         const uint16_t* scale, int64_t rpc, int norm, double eps, int8_t* q,
+                         float* qscale, uint16_t* y, hipStream_t stream) {
+    const bool a16 = reinterpret_cast<uintptr_t>(x) % 16 == 0 &&
+                     reinterpret_cast<uintptr_t>(shift) % 16 == 0 &&
+                     reinterpret_cast<uintptr_t>(scale) % 16 == 0 &&
+                     (QUANT ? reinterpret_cast<uintptr_t>(q) % 8 == 0
+                            : reinterpret_cast<uintptr_t>(y) % 16 == 0);
+    const int64_t nchunk = cols / 8;
+    const bool vec = cols % 8 == 0 && a16;
+#define W8A8_NM(W, C) launch_nm<W, C, QUANT>(x, rows, cols, shift, scale, rpc, norm, eps, q, qscale, y, stream)
+    if (vec && nchunk <= 64) return W8A8_NM(1, 1);
+    if (vec && nchunk <= 128) return W8A8_NM(1, 2);
+    if (vec && nchunk <= 256) return W8A8_NM(1, 4);
+    if (vec && nchunk <= 512) return W8A8_NM(1, 8);
+    if (vec && nchunk <= 1024) return W8A8_NM(2, 8);
+    if (vec && nchunk <= 2048) return W8A8_NM(4, 8);
+    if (vec && nchunk <= 4096) return W8A8_NM(4, 16);
+#undef W8A8_NM
+    hipLaunchKernelGGL(norm_mod_rows_generic<QUANT>, dim3((unsigned)rows), dim3(kBlock), 0, stream,
+                       x, rows, cols, shift, scale, rpc, norm, eps, q, qscale, y);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 int launch_compact_quantize_rows(const uint16_t* x, const uint8_t* mask, int64_t R, int64_t D,
@@ -606,6 +879,18 @@ int launch_quantize_blocks(const uint16_t* x, int64_t B, int64_t S, int64_t H, i
     else if (chunks <= 16 * kBlock)
         e = launch_blocks<8, 2 * kBlock>(x, B, S, H, D, block, q, scale, stream);
     else return -1;
+    return e == hipSuccess ? 0 : -1;
+}
+
+int launch_norm_mod(const uint16_t* x, int64_t rows, int64_t cols, const uint16_t* shift,
+                    const uint16_t* scale, int64_t rows_per_cond, int norm, double eps, int8_t* q,
+                    float* qscale, uint16_t* y, hipStream_t stream) {
+    if (rows == 0) return 0;
+    const hipError_t e =
+        q ? launch_nm_any<true>(x, rows, cols, shift, scale, rows_per_cond, norm, eps, q, qscale,
+                                nullptr, stream)
+          : launch_nm_any<false>(x, rows, cols, shift, scale, rows_per_cond, norm, eps, nullptr,
+                                 nullptr, y, stream);
     return e == hipSuccess ? 0 : -1;
 }
 

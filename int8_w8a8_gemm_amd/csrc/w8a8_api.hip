@@ -68,6 +68,42 @@ int w8a8_quantize_blocks(const uint16_t* x, int64_t batch, int64_t seq, int64_t 
                                                  as_stream(stream)));
 }
 
+namespace {
+int norm_mod_args(const uint16_t* x, int64_t rows, int64_t cols, const uint16_t* shift,
+                  const uint16_t* scale, int64_t rows_per_cond, int norm, double eps) {
+    if (rows < 0 || cols < 1 || rows >= kMaxRows || rows_per_cond < 1) return W8A8_EINVAL;
+    if (norm != W8A8_NORM_LAYER && norm != W8A8_NORM_RMS) return W8A8_EINVAL;
+    if (!(eps >= 0.0) || !(eps < 1.0e300)) return W8A8_EINVAL;
+    if (rows > 0 && (!x || !aligned(x, 2))) return W8A8_EINVAL;
+    if ((shift && !aligned(shift, 2)) || (scale && !aligned(scale, 2))) return W8A8_EINVAL;
+    if (rows > INT64_MAX / cols) return W8A8_EINVAL;
+    return W8A8_OK;
+}
+}  // namespace
+
+int w8a8_norm_mod_bf16(const uint16_t* x, int64_t rows, int64_t cols, const uint16_t* shift,
+                       const uint16_t* scale, int64_t rows_per_cond, int norm, double eps,
+                       uint16_t* y, void* stream) {
+    const int st = norm_mod_args(x, rows, cols, shift, scale, rows_per_cond, norm, eps);
+    if (st != W8A8_OK) return st;
+    if (rows == 0) return W8A8_OK;
+    if (!y || !aligned(y, 2)) return W8A8_EINVAL;
+    return launched(w8a8::launch_norm_mod(x, rows, cols, shift, scale, rows_per_cond, norm, eps,
+                                          nullptr, nullptr, y, as_stream(stream)));
+}
+
+int w8a8_norm_mod_quantize_rows(const uint16_t* x, int64_t rows, int64_t cols,
+                                const uint16_t* shift, const uint16_t* scale,
+                                int64_t rows_per_cond, int norm, double eps, int8_t* q,
+                                float* qscale, void* stream) {
+    const int st = norm_mod_args(x, rows, cols, shift, scale, rows_per_cond, norm, eps);
+    if (st != W8A8_OK) return st;
+    if (rows == 0) return W8A8_OK;
+    if (!q || !qscale || !aligned(qscale, 4)) return W8A8_EINVAL;
+    return launched(w8a8::launch_norm_mod(x, rows, cols, shift, scale, rows_per_cond, norm, eps, q,
+                                          qscale, nullptr, as_stream(stream)));
+}
+
 int w8a8_gelu_quantize_rows(const uint16_t* y, int64_t rows, int64_t cols, int8_t* q,
                             float* scale, void* stream) {
     if (rows < 0 || cols < 0 || rows >= kMaxRows) return W8A8_EINVAL;

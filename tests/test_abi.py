@@ -198,6 +198,32 @@ def test_quantize_blocks_rejects_bad_arguments():
     assert qb(A16, 1, 0, 2, 64, 64, NULL, NULL) == w8.OK
 
 
+def test_norm_mod_rejects_bad_arguments():
+    L = w8.lib()
+    nm = lambda x, R, C, sh, sc, rpc, norm, eps, y: L.w8a8_norm_mod_bf16(x, R, C, sh, sc, rpc, norm,
+                                                                         eps, y, NULL)
+    nq = lambda x, R, C, rpc, norm, eps, q, s: L.w8a8_norm_mod_quantize_rows(
+        x, R, C, NULL, NULL, rpc, norm, eps, q, s, NULL)
+    assert nm(A16, -1, 64, NULL, NULL, 1, 0, 1e-6, A16) == w8.EINVAL
+    assert nm(A16, 4, 0, NULL, NULL, 1, 0, 1e-6, A16) == w8.EINVAL     # cols >= 1
+    assert nm(A16, 4, 64, NULL, NULL, 0, 0, 1e-6, A16) == w8.EINVAL    # rows_per_cond >= 1
+    assert nm(A16, 4, 64, NULL, NULL, 1, 2, 1e-6, A16) == w8.EINVAL    # norm kind
+    assert nm(A16, 4, 64, NULL, NULL, 1, 0, -1.0, A16) == w8.EINVAL    # eps >= 0
+    assert nm(A16, 4, 64, NULL, NULL, 1, 0, float("nan"), A16) == w8.EINVAL
+    assert nm(A16, 4, 64, NULL, NULL, 1, 0, float("inf"), A16) == w8.EINVAL
+    assert nm(NULL, 4, 64, NULL, NULL, 1, 0, 1e-6, A16) == w8.EINVAL
+    assert nm(A16, 4, 64, NULL, NULL, 1, 0, 1e-6, NULL) == w8.EINVAL
+    assert nm(MIS, 4, 64, NULL, NULL, 1, 0, 1e-6, A16) == w8.EINVAL     # x 2-byte aligned
+    assert nm(A16, 4, 64, MIS, NULL, 1, 0, 1e-6, A16) == w8.EINVAL     # shift 2-byte aligned
+    assert nm(A16, 1 << 31, 64, NULL, NULL, 1, 0, 1e-6, A16) == w8.EINVAL  # 2^31 rows
+    assert nm(NULL, 0, 64, NULL, NULL, 1, 0, 1e-6, NULL) == w8.OK      # empty: no-op
+    assert nq(A16, 4, 64, 1, 1, 0.0, A16, NULL) == w8.EINVAL           # scales out needed
+    assert nq(A16, 4, 64, 1, 1, 0.0, NULL, A16) == w8.EINVAL
+    assert nq(A16, 4, 64, 1, 1, 0.0, A16, ctypes.c_void_p(0x10002)) == w8.EINVAL  # qscale 4-byte
+    assert nq(A16, 4, 64, 0, 1, 0.0, A16, A16) == w8.EINVAL
+    assert nq(NULL, 0, 64, 1, 1, 0.0, NULL, NULL) == w8.OK
+
+
 def test_python_binding_refuses_cpu_tensors():
     import torch
     x = torch.zeros((4, 128), dtype=torch.bfloat16)

@@ -179,6 +179,103 @@ def test_quantize_blocks_video_attention_full_size(blk):
     assert np.array_equal(h(q), qo)
 
 
+def _nm_input(R, D, G, seed, const_rows=True):
+    """Rows ~ 3 N(0,1) + 0.5 with 1% outlier columns x30, and (when there are
+    enough rows) one constant row and one zero row; modulation rows
+    ~ 0.3 N(0,1)."""
+    rng = np.random.default_rng(seed)
+    v = rng.standard_normal((R, D)).astype(np.float32) * np.float32(3.0) + np.float32(0.5)
+    cols = rng.choice(D, max(1, D // 100), replace=False)
+    v[:, cols] *= np.float32(30.0)
+    if const_rows and R >= 4:
+        v[1] = v[1, 0]
+        v[2] = 0.0
+    sc = rng.standard_normal((G, D)).astype(np.float32) * np.float32(0.3)
+    sh = rng.standard_normal((G, D)).astype(np.float32) * np.float32(0.3)
+    return wl.to_bf16_bits(v), wl.to_bf16_bits(sh), wl.to_bf16_bits(sc)
+
+
+NM_SHAPES = [(1, 8, 1), (7, 64, 3), (33, 1000, 5), (17, 1030, 4), (64, 4096, 16), (9, 8192, 3),
+             (5, 16384, 2), (3, 32768, 1), (2, 40000, 1), (300, 512, 100)]
+
+
+@pytest.mark.parametrize("R,D,rpc", NM_SHAPES)
+@pytest.mark.parametrize("norm", [w8.NORM_LAYER, w8.NORM_RMS])
+@pytest.mark.parametrize("mod", [True, False])
+def test_norm_mod_matches_oracle(R, D, rpc, norm, mod):
+    """bf16 rows bit-exact, and the fused quantisation's codes and scales
+    bit-exact, against the oracle (vector paths of every width; 1030 and 40000
+    columns take the generic kernel)."""
+    say(f"norm mod R={R} D={D} rpc={rpc} norm={norm} mod={mod}")
+    G = -(-R // rpc)
+    x, sh, sc = _nm_input(R, D, G, R * 7 + D + norm)
+    sh, sc = (sh, sc) if mod else (None, None)
+    eps = 1e-6
+    dx = d_bf16(x)
+    dsh, dsc = (d_bf16(sh), d_bf16(sc)) if mod else (None, None)
+    z = h_u16(w8.norm_mod_bf16(dx, dsh, dsc, rpc, norm, eps))
+    zr = oracle.norm_mod_bf16(x, sh, sc, rpc, norm, eps)
+    assert np.array_equal(z, zr)
+    q, s = w8.norm_mod_quantize_rows(dx, dsh, dsc, rpc, norm, eps)
+    qr, sr = oracle.norm_mod_quantize_rows(x, sh, sc, rpc, norm, eps)
+    assert np.array_equal(h(q), qr)
+    assert np.array_equal(h(s).view(np.uint32), sr.view(np.uint32))
+
+
+@pytest.mark.parametrize("norm", [w8.NORM_LAYER, w8.NORM_RMS])
+def test_norm_mod_eps_zero_and_degenerate_rows(norm):
+    """eps = 0: a constant row (LayerNorm) or a zero row normalises to 0 and
+    quantises to scale 0; with modulation its z is the shift row."""
+    R, D = 6, 256
+    x, sh, sc = _nm_input(R, D, R, 3 + norm)
+    z = h_u16(w8.norm_mod_bf16(d_bf16(x), d_bf16(sh), d_bf16(sc), 1, norm, 0.0))
+    assert np.array_equal(z, oracle.norm_mod_bf16(x, sh, sc, 1, norm, 0.0))
+    assert np.array_equal(z[2], sh[2])  # zero row: y = 0, z = shift
+    q, s = w8.norm_mod_quantize_rows(d_bf16(x), None, None, 1, norm, 0.0)
+    assert h(s)[2] == 0 and not h(q)[2].any()
+
+
+def test_norm_mod_video_tokens_full_size_sampled():
+    """24576 video token rows of 4096 in 8 conditioning groups of 3072 rows:
+    the fused quantisation compared on sampled rows (every step is row-local;
+    each sampled row is checked with its group's modulation rows)."""
+    R, D, rpc = 24576, 4096, 3072
+    say(f"norm mod full size R={R} D={D}")
+    x, sh, sc = _nm_input(R, D, R // rpc, 77)
+    q, s = w8.norm_mod_quantize_rows(d_bf16(x), d_bf16(sh), d_bf16(sc), rpc)
+    rng = np.random.default_rng(78)
+    rows = np.unique(np.concatenate([[0, 1, 2, rpc - 1, rpc, R - 1], rng.choice(R, 200, replace=False)]))
+    g = rows // rpc
+    qr, sr = oracle.norm_mod_quantize_rows(np.ascontiguousarray(x[rows]), np.ascontiguousarray(sh[g]),
+                                           np.ascontiguousarray(sc[g]), 1)
+    assert np.array_equal(h(q)[rows], qr)
+    assert np.array_equal(h(s)[rows].view(np.uint32), sr.view(np.uint32))
+
+
+def test_norm_mod_guard_bands():
+    say("norm mod guard bands")
+    R, D = 37, 1024
+    x, sh, sc = _nm_input(R, D, 1, 5)
+    pad = 4096
+    n = R * D
+    big = torch.full((n + 2 * pad,), 0x5A, dtype=torch.int8, device=DEV)
+    sbig = torch.full((R + 128,), -7.0, dtype=torch.float32, device=DEV)
+    ybig = torch.full((n + 2 * pad,), 0x7F7F, dtype=torch.int16, device=DEV)
+    q = big[pad:pad + n].view(R, D)
+    s = sbig[64:64 + R]
+    y = ybig[pad:pad + n].view(torch.bfloat16).view(R, D)
+    w8.norm_mod_quantize_rows(d_bf16(x), d_bf16(sh), d_bf16(sc), R, q=q, qscale=s)
+    w8.norm_mod_bf16(d_bf16(x), d_bf16(sh), d_bf16(sc), R, y=y)
+    hb, hs, hy = h(big), h(sbig), h(ybig)
+    assert np.all(hb[:pad] == 0x5A) and np.all(hb[pad + n:] == 0x5A)
+    assert np.all(hs[:64] == -7.0) and np.all(hs[64 + R:] == -7.0)
+    assert np.all(hy[:pad] == 0x7F7F) and np.all(hy[pad + n:] == 0x7F7F)
+    qr, sr = oracle.norm_mod_quantize_rows(x, sh, sc, R)
+    assert np.array_equal(hb[pad:pad + n].reshape(R, D), qr)
+    assert np.array_equal(hy[pad:pad + n].view(np.uint16).reshape(R, D),
+                          oracle.norm_mod_bf16(x, sh, sc, R))
+
+
 def test_quantize_blocks_guard_bands():
     say("quantize blocks guard bands")
     B, S, H, D, blk = 2, 45, 3, 32, 16
