@@ -203,7 +203,8 @@ def ceiling():
 
 def probe_hbm():
     """The HBM-bound kernels, each 5 times on its workload, for rocprofv3 (kernel trace,
-    FETCH_SIZE, WRITE_SIZE): the row quantiser on 4 rotating X [24576 x 4096], GELU +
+    FETCH_SIZE, WRITE_SIZE): the row quantiser on 4 rotating X [24576 x 4096] (then the
+    norm + modulation, fused with the quantiser and alone, on the same inputs), GELU +
     quantise of U [24576 x 16384], the per-block Q / K quantiser (24576 tokens x 32 heads
     x 128; blocks of 128 and 64), compaction and compaction + quantise of the text rows
     [8 x 512 x 4096]; first a 1 GiB calibration copy."""
@@ -230,7 +231,15 @@ def probe_hbm():
         sb = torch.empty((1, -(-M // blk), 32), dtype=torch.float32, device=dev)
         for i in range(5):
             w8.quantize_blocks(xs[i % 4], 1, 32, blk, q=qs[i % 4], scale=sb)
-    del xs, qs, ss
+    mods = [(torch.randn((8, K), device=dev, generator=gen) * 0.3).to(torch.bfloat16)
+            for _ in range(2)]
+    for i in range(5):
+        w8.norm_mod_quantize_rows(xs[i % 4], mods[0], mods[1], M // 8, q=qs[i % 4],
+                                  qscale=ss[i % 4])
+    y = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    for i in range(5):
+        w8.norm_mod_bf16(xs[i % 4], mods[0], mods[1], M // 8, y=y)
+    del xs, qs, ss, y
     u = (torch.randn((M, 16384), device=dev, generator=gen) * 0.64).to(torch.bfloat16)
     qh = torch.empty((M, 16384), dtype=torch.int8, device=dev)
     sh = torch.empty((M,), dtype=torch.float32, device=dev)
@@ -601,7 +610,37 @@ def extra_benches(w8, wl, np, torch, dev, d, log):
         nbytes = 3 * M * K + 4 * nsc
         out[name] = {"us": round(t * 1e3, 2), "GB/s": round(nbytes / (t * 1e-3) / 1e9, 1),
                      "frac_hbm": round(nbytes / (t * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
-    del xs, qs, ss
+    # LayerNorm + modulation of the same video token rows in 8 conditioning
+    # groups of 3072 rows, fused with the quantisation (int8 out) and alone
+    # (bf16 out), rotating over the same 4 inputs
+    G = 8
+    mods = [(torch.randn((G, K), device=dev, generator=gen) * 0.3).to(torch.bfloat16)
+            for _ in range(2)]
+
+    def nmq():
+        i = it[0] % 4
+        it[0] += 1
+        w8.norm_mod_quantize_rows(xs[i], mods[0], mods[1], M // G, q=qs[i], qscale=ss[i])
+
+    t = _time(nmq, 40, torch)
+    nbytes = 3.0 * M * K + 4.0 * M + 4.0 * G * K
+    out["norm_mod_quantize_24576x4096_rotating"] = {
+        "us": round(t * 1e3, 2), "GB/s": round(nbytes / (t * 1e-3) / 1e9, 1),
+        "frac_hbm": round(nbytes / (t * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    del qs
+    ys = [torch.empty((M, K), dtype=torch.bfloat16, device=dev) for _ in range(4)]
+
+    def nmb():
+        i = it[0] % 4
+        it[0] += 1
+        w8.norm_mod_bf16(xs[i], mods[0], mods[1], M // G, y=ys[i])
+
+    t = _time(nmb, 40, torch)
+    nbytes = 4.0 * M * K + 4.0 * G * K
+    out["norm_mod_bf16_24576x4096_rotating"] = {
+        "us": round(t * 1e3, 2), "GB/s": round(nbytes / (t * 1e-3) / 1e9, 1),
+        "frac_hbm": round(nbytes / (t * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    del xs, ss, ys
     # compaction of the text rows [8 x 512 x 4096]
     g = wl.guarded_mixed()
     B, L, Dm = g.x.shape

@@ -538,28 +538,16 @@ hipError_t launch_blocks(const uint16_t* x, int64_t B, int64_t S, int64_t H, int
 // summary, section C; the formulas are readings).  Per row of D elements:
 //     LayerNorm:  mu = sum(x) / D,  var = sum((x - mu)^2) / D
 //     RMSNorm:    mu = 0,           var = sum(x^2) / D
-//     rstd = 1 / sqrt(var + eps), 0 where var + eps = 0
-//     z = fma((x - mu) * rstd, 1 + scale[g], shift[g]),  g = row / rows_per_cond
-// in binary64, z rounded once to bf16; the fused variant then quantises the
-// bf16 row exactly as quantize_rows does.  The sums' order is free: it moves
-// them only in their last binary64 bits, which reach the bf16 result only in
-// the rare case that z lies that close to a bf16 rounding boundary.  The
+//     rstd = 1 / sqrt(var + eps), 0 where var + eps = 0       (binary64)
+//     d = RN32(x - mu),  y = RN32(d * RN32(rstd)),
+//     z = fmaf(y, RN32(1 + scale[g]), shift[g]),  g = row / rows_per_cond
+// and z rounded to bf16; the fused variant then quantises the bf16 row
+// exactly as quantize_rows does.  The sums' order is free: it moves them only
+// in their last binary64 bits, which reach the binary32 values mu and rstd
+// only in the rare case that those bits decide a binary32 rounding.  The
 // vector kernel keeps the row in registers (as quantize_rows_vec), so each
-// element is read from HBM once and the statistics cost no second pass.
-
-// binary64 -> bf16 bits, to nearest even, with a single effective rounding:
-// the conversion to binary32 is made round-to-odd (the nearest-even binary32
-// moved, when inexact, to its odd neighbour toward zero), and rounding that
-// to bf16, which keeps 16 bits fewer, gives the correctly rounded result.
-__device__ __forceinline__ uint32_t f64_to_bf16_bits(double d) {
-    const float f = (float)d;
-    uint32_t u = __float_as_uint(f);
-    if ((double)f != d) {
-        if (fabs((double)f) > fabs(d)) u -= 1u;
-        u |= 1u;
-    }
-    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-}
+// element is read from HBM once; the binary64 work is two or three operations
+// per element in the statistics, the rest is binary32.
 
 __device__ __forceinline__ double wave_sum_f64(double v) {
 #pragma unroll
@@ -567,44 +555,51 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
     return v;
 }
 
-__device__ __forceinline__ double bf16_f64(uint32_t h) {
-    return (double)__uint_as_float((h & 0xffffu) << 16);
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// binary32 -> bf16 bits, nearest even (finite values)
+__device__ __forceinline__ uint32_t f32_bf16_rn(float f) {
+    const uint32_t u = __float_as_uint(f);
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
-// z of one element: x, scale and shift as bf16 bits
-__device__ __forceinline__ uint32_t norm_mod1(uint32_t xh, uint32_t sch, uint32_t shh, double mu,
-                                              double rstd) {
-    const double y = (bf16_f64(xh) - mu) * rstd;
-    return f64_to_bf16_bits(__builtin_fma(y, 1.0 + bf16_f64(sch), bf16_f64(shh)));
+// The 8 values of a chunk as binary32 (exact), and their binary64 sum.
+__device__ __forceinline__ double unpack8(u32x4 v, float (&f)[8]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[2 * i] = bf16_lo(v[i]);
+        f[2 * i + 1] = bf16_hi(v[i]);
+    }
+    double t[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) t[i] = (double)f[2 * i] + (double)f[2 * i + 1];
+    return (t[0] + t[1]) + (t[2] + t[3]);
 }
 
-// z of one chunk of 8 elements
-__device__ __forceinline__ u32x4 norm_mod8(u32x4 v, u32x4 sc, u32x4 sh, double mu, double rstd) {
+// Deviations from mu of a chunk's values (in place, rounded to binary32); their
+// squares, in binary64, are added to t.
+__device__ __forceinline__ void dev8(float (&f)[8], double mu, double& t) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const double a = (double)f[e] - mu;
+        t = __builtin_fma(a, a, t);
+        f[e] = (float)a;
+    }
+}
+
+// z of one chunk from its deviations, as bf16 bits
+__device__ __forceinline__ u32x4 mod8(const float (&d)[8], float r, u32x4 sc, u32x4 sh) {
     u32x4 o;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const uint32_t lo = norm_mod1(v[i], sc[i], sh[i], mu, rstd);
-        const uint32_t hi = norm_mod1(v[i] >> 16, sc[i] >> 16, sh[i] >> 16, mu, rstd);
-        o[i] = lo | (hi << 16);
+        const float z0 = __builtin_fmaf(__fmul_rn(d[2 * i], r), __fadd_rn(1.0f, bf16_lo(sc[i])),
+                                        bf16_lo(sh[i]));
+        const float z1 = __builtin_fmaf(__fmul_rn(d[2 * i + 1], r),
+                                        __fadd_rn(1.0f, bf16_hi(sc[i])), bf16_hi(sh[i]));
+        o[i] = pack_bf16x2(z0, z1);
     }
     return o;
-}
-
-__device__ __forceinline__ double sum8_f64(u32x4 v) {
-    double t[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) t[i] = bf16_f64(v[i]) + bf16_f64(v[i] >> 16);
-    return (t[0] + t[1]) + (t[2] + t[3]);
-}
-
-__device__ __forceinline__ double sumsq8_f64(u32x4 v, double mu) {
-    double t[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const double a = bf16_f64(v[i]) - mu, b = bf16_f64(v[i] >> 16) - mu;
-        t[i] = __builtin_fma(a, a, b * b);
-    }
-    return (t[0] + t[1]) + (t[2] + t[3]);
 }
 
 __device__ __forceinline__ double rstd_of(double var, double eps) {
@@ -648,18 +643,17 @@ __global__ __launch_bounds__(kBlock) void norm_mod_rows_vec(
     for (int c = 0; c < CPL; ++c)
         v[c] = (live && chunk(c) < nchunk) ? __builtin_nontemporal_load(xr + chunk(c))
                                            : (u32x4){0u, 0u, 0u, 0u};
-    double mu = 0.0;
-    if (norm == 0) {
-        double t = 0.0;
+    float d[CPL][8];  // the values, then their deviations from the mean
+    double t = 0.0;
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) t += sum8_f64(v[c]);
-        mu = row_sum(t, 0) / D;
-    }
-    double t2 = 0.0;
+    for (int c = 0; c < CPL; ++c) t += unpack8(v[c], d[c]);  // padding adds 0
+    double mu = 0.0;
+    if (norm == 0) mu = row_sum(t, 0) / D;
+    double ta = 0.0, tb = 0.0;  // two chains of the sum of squared deviations
 #pragma unroll
     for (int c = 0; c < CPL; ++c)
-        if (chunk(c) < nchunk) t2 += sumsq8_f64(v[c], mu);  // padding is not part of the row
-    const double rstd = rstd_of(row_sum(t2, 1) / D, eps);
+        if (chunk(c) < nchunk) dev8(d[c], mu, (c & 1) ? tb : ta);  // padding is not in the row
+    const float r = (float)rstd_of(row_sum(ta + tb, 1) / D, eps);
 
     const int64_t g = (live ? row : 0) / rpc;
     const u32x4* scr = scale ? reinterpret_cast<const u32x4*>(scale + g * cols) : nullptr;
@@ -670,7 +664,7 @@ __global__ __launch_bounds__(kBlock) void norm_mod_rows_vec(
         const int64_t ch = chunk(c);
         if (live && ch < nchunk) {
             const u32x4 zero = {0u, 0u, 0u, 0u};
-            v[c] = norm_mod8(v[c], scr ? scr[ch] : zero, shr ? shr[ch] : zero, mu, rstd);
+            v[c] = mod8(d[c], r, scr ? scr[ch] : zero, shr ? shr[ch] : zero);
             if (QUANT) amax = max(amax, absmax_bits(v[c]));
             else __builtin_nontemporal_store(v[c], reinterpret_cast<u32x4*>(y + row * cols) + ch);
         }
@@ -733,18 +727,20 @@ __global__ __launch_bounds__(kBlock) void norm_mod_rows_generic(
     double mu = 0.0;
     if (norm == 0) {
         double t = 0.0;
-        for (int64_t k = threadIdx.x; k < cols; k += kBlock) t += bf16_f64(xr[k]);
+        for (int64_t k = threadIdx.x; k < cols; k += kBlock) t += (double)bf16_lo(xr[k]);
         mu = block_sum(t) / D;
     }
     double t2 = 0.0;
     for (int64_t k = threadIdx.x; k < cols; k += kBlock) {
-        const double d = bf16_f64(xr[k]) - mu;
-        t2 = __builtin_fma(d, d, t2);
+        const double dv = (double)bf16_lo(xr[k]) - mu;
+        t2 = __builtin_fma(dv, dv, t2);
     }
-    const double rstd = rstd_of(block_sum(t2) / D, eps);
+    const float r = (float)rstd_of(block_sum(t2) / D, eps);
     auto z = [&](int64_t k) {
-        return norm_mod1(xr[k], scale ? scale[g * cols + k] : 0u, shift ? shift[g * cols + k] : 0u,
-                         mu, rstd);
+        const float dk = (float)((double)bf16_lo(xr[k]) - mu);
+        const float sc = scale ? bf16_lo(scale[g * cols + k]) : 0.0f;
+        const float sh = shift ? bf16_lo(shift[g * cols + k]) : 0.0f;
+        return f32_bf16_rn(__builtin_fmaf(__fmul_rn(dk, r), __fadd_rn(1.0f, sc), sh));
     };
     if constexpr (!QUANT) {
         for (int64_t k = threadIdx.x; k < cols; k += kBlock) y[row * cols + k] = (uint16_t)z(k);
@@ -792,11 +788,15 @@ hipError_t launch_nm_any(const uint16_t* x, int64_t rows, int64_t cols, const ui
     const int64_t nchunk = cols / 8;
     const bool vec = cols % 8 == 0 && a16;
 #define W8A8_NM(W, C) launch_nm<W, C, QUANT>(x, rows, cols, shift, scale, rpc, norm, eps, q, qscale, y, stream)
+    // at most 4 chunks (32 values) per lane where the row allows: the values and
+    // their deviations stay in registers, and with 8 chunks per lane the
+    // occupancy falls to 3 waves per SIMD (24576 x 4096: 90 us with 2 waves of
+    // 4 chunks per row, 135 us with 1 wave of 8)
     if (vec && nchunk <= 64) return W8A8_NM(1, 1);
     if (vec && nchunk <= 128) return W8A8_NM(1, 2);
     if (vec && nchunk <= 256) return W8A8_NM(1, 4);
-    if (vec && nchunk <= 512) return W8A8_NM(1, 8);
-    if (vec && nchunk <= 1024) return W8A8_NM(2, 8);
+    if (vec && nchunk <= 512) return W8A8_NM(2, 4);
+    if (vec && nchunk <= 1024) return W8A8_NM(4, 4);
     if (vec && nchunk <= 2048) return W8A8_NM(4, 8);
     if (vec && nchunk <= 4096) return W8A8_NM(4, 16);
 #undef W8A8_NM

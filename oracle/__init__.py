@@ -223,7 +223,8 @@ def norm_mod_bf16(x, shift=None, scale=None, rows_per_cond=None, norm=NORM_LAYER
     linear layer (paperlayer.ai summary, section C, names them; the formulas
     are readings): LayerNorm without affine (norm=0) or RMSNorm (norm=1), then
     z = y * (1 + scale[g]) + shift[g] for the row's conditioning group
-    g = row // rows_per_cond, in binary64, rounded once to bf16.
+    g = row // rows_per_cond; row statistics in binary64, the elementwise
+    steps in binary32, z rounded to bf16.
 
     x: uint16 [R, D]; shift, scale: uint16 [G, D] or None.  Returns uint16 [R, D].
     """

@@ -195,7 +195,7 @@ def _nm_input(R, D, G, seed, const_rows=True):
     return wl.to_bf16_bits(v), wl.to_bf16_bits(sh), wl.to_bf16_bits(sc)
 
 
-NM_SHAPES = [(1, 8, 1), (7, 64, 3), (33, 1000, 5), (17, 1030, 4), (64, 4096, 16), (9, 8192, 3),
+NM_SHAPES = [(1, 8, 1), (7, 64, 3), (33, 1000, 5), (20, 2048, 4), (17, 1030, 4), (64, 4096, 16), (9, 8192, 3),
              (5, 16384, 2), (3, 32768, 1), (2, 40000, 1), (300, 512, 100)]
 
 
