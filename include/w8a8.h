@@ -114,9 +114,10 @@ typedef enum { W8A8_NORM_LAYER = 0, W8A8_NORM_RMS = 1 } w8a8_norm;
  *          without its elementwise affine);  W8A8_NORM_RMS: mu = 0,
  *          var = mean(x^2) (RMSNorm)
  *   eps    >= 0, added to var: rstd = 1/sqrt(var + eps), 0 if var + eps == 0
- *   y      [rows x cols] bf16 out:
- *          z = fma((x - mu) * rstd, 1 + scale[g], shift[g]) in binary64,
- *          rounded once to bf16 (nearest, ties to even)
+ *          (mu, var and rstd in binary64)
+ *   y      [rows x cols] bf16 out: in binary32, d = RN32(x - mu),
+ *          y' = RN32(d * RN32(rstd)), z = fmaf(y', RN32(1 + scale[g]), shift[g]),
+ *          then z rounded to bf16 (nearest, ties to even)
  *
  * The row sums are taken in binary64 in no fixed order, which can move them in
  * their last bits only.  Alignment: 2-byte for every bf16 pointer; 16-byte x,
