@@ -549,6 +549,24 @@ hipError_t launch_blocks(const uint16_t* x, int64_t B, int64_t S, int64_t H, int
 // element is read from HBM once; the binary64 work is two or three operations
 // per element in the statistics, the rest is binary32.
 
+// 16 bytes at byte offset off of a row of `bytes` bytes at p, read through a
+// buffer resource: zeros past the row's end, and for p == NULL, with no branch
+// (AUX: cache policy bits).  p must be wave-uniform.
+#if defined(__HIP_DEVICE_COMPILE__)
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+#endif
+template <int AUX>
+__device__ __forceinline__ u32x4 load16_row(const void* p, int bytes, int off) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0,
+                                                      p ? bytes : 0, 0x00020000);
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX));
+#else
+    (void)p; (void)bytes; (void)off;
+    return (u32x4){0u, 0u, 0u, 0u};
+#endif
+}
+
 __device__ __forceinline__ double wave_sum_f64(double v) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
@@ -617,12 +635,12 @@ __global__ __launch_bounds__(kBlock) void norm_mod_rows_vec(
     constexpr int RPB = (kBlock / 64) / WPR;  // rows per block
     __shared__ double red64[2][kBlock / 64];
     __shared__ uint32_t red[kBlock / 64];
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int wr = wave % WPR, w0 = wave - wr;
     const int64_t row = (int64_t)blockIdx.x * RPB + wave / WPR;
     const bool live = row < rows;
     const int64_t nchunk = cols >> 3;
-    const u32x4* xr = reinterpret_cast<const u32x4*>(x + (live ? row : 0) * cols);
+    const int rbytes = (int)cols * 2;  // <= 65536 on this path
     const double D = (double)cols;
     auto chunk = [&](int c) { return (int64_t)(c * WPR + wr) * 64 + lane; };
     // sum over the row's WPR waves (every thread of the block takes part)
@@ -638,11 +656,11 @@ __global__ __launch_bounds__(kBlock) void norm_mod_rows_vec(
         return t;
     };
 
+    // the row, zero past its end (and for a row past the last): nontemporal
     u32x4 v[CPL];
+    const uint16_t* xrow = live ? x + row * cols : nullptr;
 #pragma unroll
-    for (int c = 0; c < CPL; ++c)
-        v[c] = (live && chunk(c) < nchunk) ? __builtin_nontemporal_load(xr + chunk(c))
-                                           : (u32x4){0u, 0u, 0u, 0u};
+    for (int c = 0; c < CPL; ++c) v[c] = load16_row<2>(xrow, rbytes, (int)chunk(c) * 16);
     float d[CPL][8];  // the values, then their deviations from the mean
     double t = 0.0;
 #pragma unroll
@@ -656,17 +674,17 @@ __global__ __launch_bounds__(kBlock) void norm_mod_rows_vec(
     const float r = (float)rstd_of(row_sum(ta + tb, 1) / D, eps);
 
     const int64_t g = (live ? row : 0) / rpc;
-    const u32x4* scr = scale ? reinterpret_cast<const u32x4*>(scale + g * cols) : nullptr;
-    const u32x4* shr = shift ? reinterpret_cast<const u32x4*>(shift + g * cols) : nullptr;
+    const uint16_t* scr = scale ? scale + g * cols : nullptr;
+    const uint16_t* shr = shift ? shift + g * cols : nullptr;
     uint32_t amax = 0;
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
         const int64_t ch = chunk(c);
-        if (live && ch < nchunk) {
-            const u32x4 zero = {0u, 0u, 0u, 0u};
-            v[c] = mod8(d[c], r, scr ? scr[ch] : zero, shr ? shr[ch] : zero);
+        v[c] = mod8(d[c], r, load16_row<0>(scr, rbytes, (int)ch * 16),
+                    load16_row<0>(shr, rbytes, (int)ch * 16));
+        if (ch < nchunk) {
             if (QUANT) amax = max(amax, absmax_bits(v[c]));
-            else __builtin_nontemporal_store(v[c], reinterpret_cast<u32x4*>(y + row * cols) + ch);
+            else if (live) __builtin_nontemporal_store(v[c], reinterpret_cast<u32x4*>(y + row * cols) + ch);
         }
     }
     if constexpr (!QUANT) return;
