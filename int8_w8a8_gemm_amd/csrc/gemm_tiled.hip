@@ -837,10 +837,10 @@ hipError_t launch_cfg(const void* a, const float* sa, int64_t M, const void* w, 
 // clock under the power cap; smaller ones only pay off when the large ones
 // leave most CUs idle.  xl (1.5x the work of a large tile) is taken when it
 // needs no more rounds of persistent tiles than large does (rounds x 1.5 <=
-// large's rounds) and either K >= 8192 or there are at least 8 xl tiles per
+// large's rounds) and either K >= 8192 or there are at least 4 xl tiles per
 // CU: measured 2-3% faster on the FFN up (24576 x 16384 x 4096, 16 tiles per
-// CU) and down (K = 16384) projections, but 3-7% slower on 24576 x 4096 x 4096
-// (4 tiles per CU with a short K loop).
+// CU) and down (K = 16384) projections and 3.5% faster on 24576 x 4096 x 4096
+// and 12288 x 8192 x 4096 (4 tiles per CU); with 1 tile per CU it is not taken.
 template <class E, int OUT_I32, int ACT, bool VEC_OUT>
 hipError_t launch_tiles(const void* a, const float* sa, int64_t M, const void* w, const float* sw,
                         int64_t N, int64_t K, const uint16_t* bias, void* out,
@@ -850,7 +850,7 @@ hipError_t launch_tiles(const void* a, const float* sa, int64_t M, const void* w
     if constexpr (E::BYTES == 1 && ACT == 0) {
         const int64_t txl = tile_count<CfgXL>(M, N), tl = tile_count<CfgLarge>(M, N);
         const int64_t rounds_xl = (txl + cus - 1) / cus, rounds_l = (tl + cus - 1) / cus;
-        if (2 * txl >= cus && 3 * rounds_xl <= 2 * rounds_l && (K >= 8192 || txl >= 8 * (int64_t)cus))
+        if (2 * txl >= cus && 3 * rounds_xl <= 2 * rounds_l && (K >= 8192 || txl >= 4 * (int64_t)cus))
             return launch_cfg<CfgXL, E, OUT_I32, ACT, VEC_OUT>(a, sa, M, w, sw, N, K, bias, out,
                                                               cus, stream);
     }

@@ -417,6 +417,31 @@ def test_gemm_xl_tiles_ragged_sampled():
     assert np.array_equal(h_u16(y)[rows], ref)
 
 
+def test_gemm_xl_tiles_short_k_ragged_sampled():
+    """12000 x 8000 x 512: 1024 tiles of 384 x 256 (4 per CU on a 256-CU MI355X)
+    with a short K loop, ragged in M (96 rows in the last tile-row) and N (64
+    columns in the last tile-column): the 384 x 256 path by its tiles-per-CU
+    rule.  INT32 accumulators and the bf16 epilogue (with and without bias) on
+    sampled rows, both sides of every 384-row boundary included."""
+    M, N, K = 12000, 8000, 512
+    say(f"gemm xl short K M={M} N={N} K={K}")
+    rng = np.random.default_rng(512)
+    qa = rng.integers(-127, 128, (M, K), dtype=np.int8)
+    qw = rng.integers(-127, 128, (N, K), dtype=np.int8)
+    rows = _tile_edge_rows(M, 384, rng, extra=60)
+    qa_d, qw_d = d_i8(qa), d_i8(qw)
+    acc_ref = oracle.gemm_i32(np.ascontiguousarray(qa[rows]), qw)
+    assert np.array_equal(h(w8.gemm(qa_d, None, qw_d, None, out_kind=w8.OUT_I32))[rows], acc_ref)
+    sa = (rng.random(M, dtype=np.float32) * np.float32(1e-3) + np.float32(1e-5)).astype(np.float32)
+    sw = (rng.random(N, dtype=np.float32) * np.float32(1e-3) + np.float32(1e-5)).astype(np.float32)
+    b = wl.to_bf16_bits(rng.standard_normal(N).astype(np.float32))
+    for bias in (b, None):
+        y = w8.gemm(qa_d, torch.from_numpy(sa).to(DEV), qw_d, torch.from_numpy(sw).to(DEV),
+                    d_bf16(bias) if bias is not None else None)
+        ref = oracle.epilogue(acc_ref, np.ascontiguousarray(sa[rows]), sw, bias)
+        assert np.array_equal(h_u16(y)[rows], ref)
+
+
 @pytest.mark.parametrize("M,N,K", [(129, 192, 384), (2048, 2048, 2048), (6100, 4032, 8192)])
 def test_gemm_without_bias_keeps_the_sign_of_zero(M, N, K):
     """Without a bias the output is the rounded product alone.  With scales whose
