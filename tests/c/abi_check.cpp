@@ -1,5 +1,5 @@
 // Uses libw8a8 through its C ABI alone -- HIP runtime memory and a stream of
-// its own, no PyTorch -- and checks closed-form results.  Prints "abi_check ok"
+// its own, no PyTorch -- and checks closed-form and hand-worked results.  Prints "abi_check ok"
 // and exits 0 on success; prints the first failure and exits 1 otherwise.
 #include <hip/hip_runtime.h>
 
@@ -118,7 +118,48 @@ int main() {
                   "fallback y[%ld][%ld] = %04x, expected %04x", (long)i, (long)j, y[i * Nx + j],
                   xh[i * Kx + j]);
 
-    // 4. an argument error is reported before any launch
+    // 4. LayerNorm + modulation of the row 1 2 3 4 (eps = 0): mean 5/2, rstd 2/sqrt(5),
+    //    y = -1.3416 -0.4472 0.4472 1.3416 -> bf16 -1.34375 -0.447265625 ...; with scale
+    //    0 and shift 0 that is z, and the fused quantisation gives codes -127 -42 42 127
+    //    (0.447265625 * 127 / 1.34375 = 42.27) and scale RN32(1.34375 / 127)
+    {
+        const float xs[4] = {1.0f, 2.0f, 3.0f, 4.0f};
+        const uint16_t zexp[4] = {0xbfac, 0xbee5, 0x3ee5, 0x3fac};
+        const int8_t qexp4[4] = {-127, -42, 42, 127};
+        uint16_t xh4[4];
+        for (int i = 0; i < 4; ++i) xh4[i] = bf16_of(xs[i]);
+        uint16_t *dx4, *dz4;
+        int8_t* dq4;
+        float* ds4;
+        HIP_OK(hipMalloc(&dx4, 8));
+        HIP_OK(hipMalloc(&dz4, 8));
+        HIP_OK(hipMalloc(&dq4, 4));
+        HIP_OK(hipMalloc(&ds4, 4));
+        HIP_OK(hipMemcpy(dx4, xh4, 8, hipMemcpyHostToDevice));
+        rc = w8a8_norm_mod_bf16(dx4, 1, 4, nullptr, nullptr, 1, W8A8_NORM_LAYER, 0.0, dz4, s);
+        CHECK(rc == W8A8_OK, "w8a8_norm_mod_bf16: %s", w8a8_status_str(rc));
+        rc = w8a8_norm_mod_quantize_rows(dx4, 1, 4, nullptr, nullptr, 1, W8A8_NORM_LAYER, 0.0,
+                                         dq4, ds4, s);
+        CHECK(rc == W8A8_OK, "w8a8_norm_mod_quantize_rows: %s", w8a8_status_str(rc));
+        uint16_t z4[4];
+        int8_t q4[4];
+        float s4;
+        HIP_OK(hipStreamSynchronize(s));
+        HIP_OK(hipMemcpy(z4, dz4, 8, hipMemcpyDeviceToHost));
+        HIP_OK(hipMemcpy(q4, dq4, 4, hipMemcpyDeviceToHost));
+        HIP_OK(hipMemcpy(&s4, ds4, 4, hipMemcpyDeviceToHost));
+        for (int i = 0; i < 4; ++i) {
+            CHECK(z4[i] == zexp[i], "norm z[%d] = %04x, expected %04x", i, z4[i], zexp[i]);
+            CHECK(q4[i] == qexp4[i], "norm q[%d] = %d, expected %d", i, q4[i], qexp4[i]);
+        }
+        CHECK(s4 == 1.34375f / 127.0f, "norm scale %g", s4);
+        HIP_OK(hipFree(dx4));
+        HIP_OK(hipFree(dz4));
+        HIP_OK(hipFree(dq4));
+        HIP_OK(hipFree(ds4));
+    }
+
+    // 5. an argument error is reported before any launch
     CHECK(w8a8_gemm(nullptr, nullptr, M, dqw, nullptr, N, K, nullptr, 0, W8A8_OUT_I32, dacc, s) ==
               W8A8_EINVAL,
           "NULL operand accepted");
