@@ -582,13 +582,17 @@ __device__ __forceinline__ uint32_t f32_bf16_rn(float f) {
     return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
-// The 8 values of a chunk as binary32 (exact), and their binary64 sum.
-__device__ __forceinline__ double unpack8(u32x4 v, float (&f)[8]) {
+// The 8 values of a chunk as binary32 (exact).
+__device__ __forceinline__ void unpack8(u32x4 v, float (&f)[8]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         f[2 * i] = bf16_lo(v[i]);
         f[2 * i + 1] = bf16_hi(v[i]);
     }
+}
+
+// Their binary64 sum.
+__device__ __forceinline__ double sum8(const float (&f)[8]) {
     double t[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) t[i] = (double)f[2 * i] + (double)f[2 * i + 1];
@@ -662,11 +666,15 @@ __global__ __launch_bounds__(kBlock) void norm_mod_rows_vec(
 #pragma unroll
     for (int c = 0; c < CPL; ++c) v[c] = load16_row<2>(xrow, rbytes, (int)chunk(c) * 16);
     float d[CPL][8];  // the values, then their deviations from the mean
-    double t = 0.0;
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) t += unpack8(v[c], d[c]);  // padding adds 0
+    for (int c = 0; c < CPL; ++c) unpack8(v[c], d[c]);
     double mu = 0.0;
-    if (norm == 0) mu = row_sum(t, 0) / D;
+    if (norm == 0) {
+        double t = 0.0;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) t += sum8(d[c]);  // padding adds 0
+        mu = row_sum(t, 0) / D;
+    }
     double ta = 0.0, tb = 0.0;  // two chains of the sum of squared deviations
 #pragma unroll
     for (int c = 0; c < CPL; ++c)
