@@ -329,6 +329,38 @@ def test_gemm_int32_bit_exact(M, N, K):
     assert np.array_equal(h(acc), oracle.gemm_i32(qa, qw))
 
 
+def _random_gemm_shapes(n, seed):
+    """Seeded shapes the guard accepts: M any (1 .. 3000), N a multiple of 64
+    (64 .. 4096), K a multiple of 128 (128 .. 8192), so that every tile
+    configuration below the 384 x 256 one, full and ragged, is met."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        M = int(rng.integers(1, 3001))
+        N = 64 * int(rng.integers(1, 65))
+        K = 128 * int(rng.integers(1, 65))
+        out.append((M, N, K))
+    return out
+
+
+@pytest.mark.parametrize("M,N,K", _random_gemm_shapes(24, 2024))
+def test_gemm_random_shapes_int32_and_epilogue(M, N, K):
+    """INT32 accumulators bit-exact and the bf16 epilogue (bias) bit-exact on
+    seeded random shapes with random codes and scales."""
+    say(f"gemm random M={M} N={N} K={K}")
+    rng = np.random.default_rng(M * 31 + N * 7 + K)
+    qa = rng.integers(-127, 128, (M, K), dtype=np.int8)
+    qw = rng.integers(-127, 128, (N, K), dtype=np.int8)
+    qa_d, qw_d = d_i8(qa), d_i8(qw)
+    acc = oracle.gemm_i32(qa, qw)
+    assert np.array_equal(h(w8.gemm(qa_d, None, qw_d, None, out_kind=w8.OUT_I32)), acc)
+    sa = (rng.random(M, dtype=np.float32) * np.float32(1e-3) + np.float32(1e-6)).astype(np.float32)
+    sw = (rng.random(N, dtype=np.float32) * np.float32(1e-3) + np.float32(1e-6)).astype(np.float32)
+    b = wl.to_bf16_bits(rng.standard_normal(N).astype(np.float32))
+    y = w8.gemm(qa_d, torch.from_numpy(sa).to(DEV), qw_d, torch.from_numpy(sw).to(DEV), d_bf16(b))
+    assert np.array_equal(h_u16(y), oracle.epilogue(acc, sa, sw, b))
+
+
 def test_gemm_int32_extremes_and_max_k():
     say("gemm i32 extremes K=131072")
     M, N, K = 64, 64, 131072
