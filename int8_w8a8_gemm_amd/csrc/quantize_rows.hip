@@ -31,6 +31,24 @@ constexpr int kBlock = 256;  // 4 waves
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
+// 16 bytes at byte offset off of a row of `bytes` bytes at p, read through a
+// buffer resource: zeros past the row's end, and for p == NULL, with no branch
+// (AUX: cache policy bits).  p must be wave-uniform.
+#if defined(__HIP_DEVICE_COMPILE__)
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+#endif
+template <int AUX>
+__device__ __forceinline__ u32x4 load16_row(const void* p, int bytes, int off) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0,
+                                                      p ? bytes : 0, 0x00020000);
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX));
+#else
+    (void)p; (void)bytes; (void)off;
+    return (u32x4){0u, 0u, 0u, 0u};
+#endif
+}
+
 // GELU-tanh of every bf16 bit pattern, as bf16 bits (generated at build time).
 __device__ __attribute__((aligned(16))) const uint16_t kGeluTable[65536] = {
 #include "gelu_table.inc"
@@ -548,24 +566,6 @@ hipError_t launch_blocks(const uint16_t* x, int64_t B, int64_t S, int64_t H, int
 // vector kernel keeps the row in registers (as quantize_rows_vec), so each
 // element is read from HBM once; the binary64 work is two or three operations
 // per element in the statistics, the rest is binary32.
-
-// 16 bytes at byte offset off of a row of `bytes` bytes at p, read through a
-// buffer resource: zeros past the row's end, and for p == NULL, with no branch
-// (AUX: cache policy bits).  p must be wave-uniform.
-#if defined(__HIP_DEVICE_COMPILE__)
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-#endif
-template <int AUX>
-__device__ __forceinline__ u32x4 load16_row(const void* p, int bytes, int off) {
-#if defined(__HIP_DEVICE_COMPILE__)
-    const rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0,
-                                                      p ? bytes : 0, 0x00020000);
-    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX));
-#else
-    (void)p; (void)bytes; (void)off;
-    return (u32x4){0u, 0u, 0u, 0u};
-#endif
-}
 
 __device__ __forceinline__ double wave_sum_f64(double v) {
 #pragma unroll
