@@ -222,6 +222,32 @@ def test_norm_mod_matches_oracle(R, D, rpc, norm, mod):
     assert np.array_equal(h(s).view(np.uint32), sr.view(np.uint32))
 
 
+def _random_nm_cases(n, seed):
+    """Seeded (rows, cols, rows_per_cond, norm, eps): cols 1 .. 9000 (multiples of 8
+    and not), groups of 1 .. 64 rows, both norms, eps 0 or 1e-5."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        D = int(rng.integers(1, 1126)) * 8 if i % 3 else int(rng.integers(1, 9000))
+        out.append((int(rng.integers(1, 200)), D, int(rng.integers(1, 65)), i % 2,
+                    0.0 if i % 4 == 0 else 1e-5))
+    return out
+
+
+@pytest.mark.parametrize("R,D,rpc,norm,eps", _random_nm_cases(16, 77))
+def test_norm_mod_random_shapes(R, D, rpc, norm, eps):
+    say(f"norm mod random R={R} D={D} rpc={rpc} norm={norm} eps={eps}")
+    G = -(-R // rpc)
+    x, sh, sc = _nm_input(R, D, G, R + D + rpc)
+    dx, dsh, dsc = d_bf16(x), d_bf16(sh), d_bf16(sc)
+    assert np.array_equal(h_u16(w8.norm_mod_bf16(dx, dsh, dsc, rpc, norm, eps)),
+                          oracle.norm_mod_bf16(x, sh, sc, rpc, norm, eps))
+    q, s = w8.norm_mod_quantize_rows(dx, dsh, dsc, rpc, norm, eps)
+    qr, sr = oracle.norm_mod_quantize_rows(x, sh, sc, rpc, norm, eps)
+    assert np.array_equal(h(q), qr)
+    assert np.array_equal(h(s).view(np.uint32), sr.view(np.uint32))
+
+
 @pytest.mark.parametrize("norm", [w8.NORM_LAYER, w8.NORM_RMS])
 def test_norm_mod_eps_zero_and_degenerate_rows(norm):
     """eps = 0: a constant row (LayerNorm) or a zero row normalises to 0 and
