@@ -278,6 +278,30 @@ def test_norm_mod_video_tokens_full_size_sampled():
     assert np.array_equal(h(s)[rows].view(np.uint32), sr.view(np.uint32))
 
 
+def test_norm_mod_unaligned_rows_take_the_generic_kernel():
+    """x, the modulation rows and the outputs 2 bytes off 16-byte alignment (cols a
+    multiple of 8): the generic kernel, bit-exact as the vector one."""
+    R, D = 21, 512
+    x, sh, sc = _nm_input(R, D, 3, 9)
+    def off(a):
+        t = torch.zeros(a.size + 8, dtype=torch.int16, device=DEV)
+        v = t[1:1 + a.size]
+        v.copy_(torch.from_numpy(np.ascontiguousarray(a).reshape(-1).view(np.int16)).to(DEV))
+        return v.view(torch.bfloat16).view(a.shape)
+    dx, dsh, dsc = off(x), off(sh), off(sc)
+    assert dx.data_ptr() % 16 == 2
+    yb = torch.zeros(R * D + 8, dtype=torch.int16, device=DEV)
+    y = yb[1:1 + R * D].view(torch.bfloat16).view(R, D)
+    w8.norm_mod_bf16(dx, dsh, dsc, 7, w8.NORM_LAYER, 1e-6, y=y)
+    assert np.array_equal(h_u16(y), oracle.norm_mod_bf16(x, sh, sc, 7, oracle.NORM_LAYER, 1e-6))
+    qb = torch.zeros(R * D + 16, dtype=torch.int8, device=DEV)
+    q = qb[3:3 + R * D].view(R, D)
+    qs = torch.empty((R,), dtype=torch.float32, device=DEV)
+    w8.norm_mod_quantize_rows(dx, dsh, dsc, 7, w8.NORM_RMS, 1e-6, q=q, qscale=qs)
+    qr, sr = oracle.norm_mod_quantize_rows(x, sh, sc, 7, oracle.NORM_RMS, 1e-6)
+    assert np.array_equal(h(q), qr) and np.array_equal(h(qs).view(np.uint32), sr.view(np.uint32))
+
+
 def test_norm_mod_guard_bands():
     say("norm mod guard bands")
     R, D = 37, 1024
