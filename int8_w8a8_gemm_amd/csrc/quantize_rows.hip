@@ -876,7 +876,9 @@ int launch_quantize_rows(const uint16_t* x, int64_t rows, int64_t cols, int8_t* 
     if (vec && nchunk <= 64) e = launch_vec<1, 1>(x, rows, cols, q, scale, stream, gelu);
     else if (vec && nchunk <= 128) e = launch_vec<1, 2>(x, rows, cols, q, scale, stream, gelu);
     else if (vec && nchunk <= 256) e = launch_vec<1, 4>(x, rows, cols, q, scale, stream, gelu);
-    else if (vec && nchunk <= 512) e = launch_vec<1, 8>(x, rows, cols, q, scale, stream, gelu);
+    // 4096-wide rows: 2 waves of 4 chunks per row, 47.7 us on 24576 rows against
+    // 48.6 us for 1 wave of 8
+    else if (vec && nchunk <= 512) e = launch_vec<2, 4>(x, rows, cols, q, scale, stream, gelu);
     else if (vec && nchunk <= 1024) e = launch_vec<2, 8>(x, rows, cols, q, scale, stream, gelu);
     else if (vec && nchunk <= 2048) e = launch_vec<4, 8>(x, rows, cols, q, scale, stream, gelu);
     else if (vec && nchunk <= 4096) e = launch_vec<4, 16>(x, rows, cols, q, scale, stream, gelu);
