@@ -386,3 +386,16 @@ class W8A8Linear:
     def __call__(self, x: torch.Tensor, y=None, workspace=None, stream=None):
         return linear(x, self.N, self.qw, self.sw, self.w, self.bias, self.act, y, workspace,
                       stream)[0]
+
+    def normed(self, x: torch.Tensor, shift: Optional[torch.Tensor] = None,
+               scale: Optional[torch.Tensor] = None, rows_per_cond: Optional[int] = None,
+               norm: int = NORM_LAYER, eps: float = 1e-6, stream=None):
+        """The layer applied to the normalised and modulated rows of x: on the INT8
+        path the normalisation, modulation and activation quantisation are one
+        kernel (norm_mod_quantize_rows) followed by the GEMM; on the BF16 path the
+        bf16 rows of norm_mod_bf16 go through the native BF16 linear."""
+        if self.qw is not None:
+            q, s = norm_mod_quantize_rows(x, shift, scale, rows_per_cond, norm, eps, stream=stream)
+            return gemm(q, s, self.qw, self.sw, self.bias, act=self.act, stream=stream)
+        z = norm_mod_bf16(x, shift, scale, rows_per_cond, norm, eps, stream=stream)
+        return linear_bf16(z, self.w, self.bias, act=self.act, stream=stream)

@@ -302,6 +302,33 @@ def test_norm_mod_unaligned_rows_take_the_generic_kernel():
     assert np.array_equal(h(q), qr) and np.array_equal(h(qs).view(np.uint32), sr.view(np.uint32))
 
 
+@pytest.mark.parametrize("N,act", [(512, w8.ACT_NONE), (1024, w8.ACT_GELU_TANH), (100, w8.ACT_NONE)])
+def test_linear_on_normed_rows(N, act):
+    """W8A8Linear.normed: norm + modulation + quantisation fused, then the INT8 GEMM
+    (guarded shapes) -- bit-exact against the oracle's norm_mod_quantize_rows,
+    quantize_rows of W, INT32 product and epilogue; or, for N = 100, the bf16
+    rows of norm_mod_bf16 through the BF16 fallback, within its bound."""
+    M, K, rpc = 300, 1024, 100
+    say(f"linear on normed rows M={M} K={K} N={N} act={act}")
+    x, sh, sc = _nm_input(M, K, M // rpc, N)
+    rng = np.random.default_rng(N + 1)
+    w = wl.to_bf16_bits(rng.standard_normal((N, K)).astype(np.float32) * np.float32(0.03))
+    b = wl.to_bf16_bits(rng.standard_normal(N).astype(np.float32) * np.float32(0.1))
+    layer = w8.W8A8Linear.prepare(d_bf16(w), d_bf16(b), act)
+    y = h_u16(layer.normed(d_bf16(x), d_bf16(sh), d_bf16(sc), rpc))
+    if layer.path == w8.PATH_INT8:
+        qa, sa = oracle.norm_mod_quantize_rows(x, sh, sc, rpc)
+        qw, sw = oracle.quantize_rows(w)
+        ref = oracle.epilogue(oracle.gemm_i32(qa, qw), sa, sw, b, act=act)
+        d = ulp_dist_bf16(y, ref)
+        assert d.max() <= 1
+        if act == w8.ACT_NONE:
+            assert np.array_equal(y, ref)
+    else:
+        assert N == 100
+        _check_fallback(y, oracle.norm_mod_bf16(x, sh, sc, rpc), w, b)
+
+
 def test_norm_mod_guard_bands():
     say("norm mod guard bands")
     R, D = 37, 1024
