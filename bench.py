@@ -703,6 +703,31 @@ def extra_benches(w8, wl, np, torch, dev, d, log):
         tops = 2.0 * Mg * Ng * Kg / (t * 1e-3) / 1e12
         out[name] = {"us": round(t * 1e3, 2), "TOPS": round(tops, 1),
                      "frac_peak": round(tops / PEAK_INT8_TOPS, 4)}
+    # the attention projection with its LayerNorm + modulation prologue (8
+    # conditioning groups of 3072 rows): fused (one kernel, then the GEMM) and
+    # unfused (bf16 norm rows, quantise, GEMM)
+    Mg, Kg = 24576, 4096
+    xa = torch.randn((Mg, Kg), device=dev, generator=gen).to(torch.bfloat16)
+    mods = [(torch.randn((8, Kg), device=dev, generator=gen) * 0.3).to(torch.bfloat16)
+            for _ in range(2)]
+    wg = (torch.randn((Kg, Kg), device=dev, generator=gen) * 0.02).to(torch.bfloat16)
+    bias = (torch.randn((Kg,), device=dev, generator=gen) * 0.01).to(torch.bfloat16)
+    layer = w8.W8A8Linear.prepare(wg, bias)
+    del wg
+    t = _time(lambda: layer.normed(xa, mods[0], mods[1], Mg // 8), 10, torch)
+    out["normed_linear_attn_24576x4096x4096"] = {
+        "us": round(t * 1e3, 2), "TOPS": round(2.0 * Mg * Kg * Kg / (t * 1e-3) / 1e12, 1)}
+    zb = torch.empty_like(xa)
+
+    def unfused():
+        w8.norm_mod_bf16(xa, mods[0], mods[1], Mg // 8, y=zb)
+        q, sq = w8.quantize_rows(zb)
+        w8.gemm(q, sq, layer.qw, layer.sw, layer.bias)
+
+    t = _time(unfused, 10, torch)
+    out["normed_linear_attn_unfused_24576x4096x4096"] = {
+        "us": round(t * 1e3, 2), "TOPS": round(2.0 * Mg * Kg * Kg / (t * 1e-3) / 1e12, 1)}
+    del xa, zb
     log("extra: " + json.dumps(out))
     return out
 
