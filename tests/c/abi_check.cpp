@@ -159,7 +159,73 @@ int main() {
         HIP_OK(hipFree(ds4));
     }
 
-    // 5. an argument error is reported before any launch
+    // 5. compaction: B = 2 samples of L = 3 rows (D = 8), mask 1 0 1 / 0 1 1 keeps flat
+    //    rows 0 2 4 5 in that order, count 4 on the device; and the per-block
+    //    quantisation of one 2-token x 8-value block whose absmax is 127 (scale 1,
+    //    codes = x rounded half to even)
+    {
+        const int64_t B = 2, L = 3, D = 8;
+        std::vector<uint16_t> xh6(B * L * D);
+        for (int64_t i = 0; i < B * L * D; ++i) xh6[i] = bf16_of((float)(i / D * 10 + i % D));
+        const uint8_t mh[6] = {1, 0, 1, 0, 1, 1};
+        uint16_t *dx6, *dout;
+        uint8_t* dm;
+        int32_t *dsrc, *dcnt;
+        HIP_OK(hipMalloc(&dx6, B * L * D * 2));
+        HIP_OK(hipMalloc(&dm, 6));
+        HIP_OK(hipMalloc(&dout, B * L * D * 2));
+        HIP_OK(hipMalloc(&dsrc, 6 * 4));
+        HIP_OK(hipMalloc(&dcnt, 4));
+        HIP_OK(hipMemcpy(dx6, xh6.data(), B * L * D * 2, hipMemcpyHostToDevice));
+        HIP_OK(hipMemcpy(dm, mh, 6, hipMemcpyHostToDevice));
+        rc = compact_padded_rows(dx6, dm, B, L, D, dout, dsrc, dcnt, s);
+        CHECK(rc == W8A8_OK, "compact_padded_rows: %s", w8a8_status_str(rc));
+        int32_t cnt = -1, src[6];
+        std::vector<uint16_t> outh(B * L * D);
+        HIP_OK(hipStreamSynchronize(s));
+        HIP_OK(hipMemcpy(&cnt, dcnt, 4, hipMemcpyDeviceToHost));
+        HIP_OK(hipMemcpy(src, dsrc, 6 * 4, hipMemcpyDeviceToHost));
+        HIP_OK(hipMemcpy(outh.data(), dout, B * L * D * 2, hipMemcpyDeviceToHost));
+        const int32_t keep[4] = {0, 2, 4, 5};
+        CHECK(cnt == 4, "compaction count %d, expected 4", cnt);
+        for (int m = 0; m < 4; ++m) {
+            CHECK(src[m] == keep[m], "src_row[%d] = %d, expected %d", m, src[m], keep[m]);
+            for (int64_t d = 0; d < D; ++d)
+                CHECK(outh[m * D + d] == xh6[keep[m] * D + d], "compacted row %d col %ld", m,
+                      (long)d);
+        }
+        const float bv[16] = {127.0f, 2.5f, -0.5f, 1.5f, -3.5f, 0.25f, -127.0f, 64.0f,
+                              0.5f,   -2.5f, 3.5f, -1.5f, 100.0f, -0.75f, 7.0f, 126.5f};
+        const int8_t bq[16] = {127, 2, 0, 2, -4, 0, -127, 64, 0, -2, 4, -2, 100, -1, 7, 126};
+        uint16_t bh[16];
+        for (int i = 0; i < 16; ++i) bh[i] = bf16_of(bv[i]);
+        uint16_t* dxb;
+        int8_t* dqb;
+        float* dsb;
+        HIP_OK(hipMalloc(&dxb, 32));
+        HIP_OK(hipMalloc(&dqb, 16));
+        HIP_OK(hipMalloc(&dsb, 4));
+        HIP_OK(hipMemcpy(dxb, bh, 32, hipMemcpyHostToDevice));
+        rc = w8a8_quantize_blocks(dxb, 1, 2, 1, 8, 2, dqb, dsb, s);
+        CHECK(rc == W8A8_OK, "w8a8_quantize_blocks: %s", w8a8_status_str(rc));
+        int8_t qb[16];
+        float sb = 0.0f;
+        HIP_OK(hipStreamSynchronize(s));
+        HIP_OK(hipMemcpy(qb, dqb, 16, hipMemcpyDeviceToHost));
+        HIP_OK(hipMemcpy(&sb, dsb, 4, hipMemcpyDeviceToHost));
+        for (int i = 0; i < 16; ++i) CHECK(qb[i] == bq[i], "block q[%d] = %d, expected %d", i, qb[i], bq[i]);
+        CHECK(sb == 1.0f, "block scale %g, expected 1", sb);
+        HIP_OK(hipFree(dx6));
+        HIP_OK(hipFree(dm));
+        HIP_OK(hipFree(dout));
+        HIP_OK(hipFree(dsrc));
+        HIP_OK(hipFree(dcnt));
+        HIP_OK(hipFree(dxb));
+        HIP_OK(hipFree(dqb));
+        HIP_OK(hipFree(dsb));
+    }
+
+    // 6. an argument error is reported before any launch
     CHECK(w8a8_gemm(nullptr, nullptr, M, dqw, nullptr, N, K, nullptr, 0, W8A8_OUT_I32, dacc, s) ==
               W8A8_EINVAL,
           "NULL operand accepted");
