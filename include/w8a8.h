@@ -50,7 +50,8 @@ typedef enum { W8A8_OUT_BF16 = 0, W8A8_OUT_I32 = 1 } w8a8_out;
 typedef enum { W8A8_ACT_NONE = 0, W8A8_ACT_GELU_TANH = 1 } w8a8_act;
 typedef enum { W8A8_PATH_INT8 = 0, W8A8_PATH_BF16 = 1 } w8a8_path;
 
-/* Largest K the INT8 path admits: |acc| <= 127*127*K stays below 2^31. */
+/* Largest K the INT8 path admits: with codes in [-127, 127] (all that
+ * w8a8_quantize_rows produces), |acc| <= 127*127*K stays below 2^31. */
 #define W8A8_MAX_K 131072
 
 /*
@@ -114,13 +115,17 @@ typedef enum { W8A8_NORM_LAYER = 0, W8A8_NORM_RMS = 1 } w8a8_norm;
  *          without its elementwise affine);  W8A8_NORM_RMS: mu = 0,
  *          var = mean(x^2) (RMSNorm)
  *   eps    >= 0, added to var: rstd = 1/sqrt(var + eps), 0 if var + eps == 0
- *          (mu, var and rstd in binary64)
- *   y      [rows x cols] bf16 out: in binary32, d = RN32(x - mu),
- *          y' = RN32(d * RN32(rstd)), z = fmaf(y', RN32(1 + scale[g]), shift[g]),
- *          then z rounded to bf16 (nearest, ties to even)
+ *   y      [rows x cols] bf16 out: z = (x - mu) * rstd * (1 + scale[g]) + shift[g]
+ *          rounded to bf16
  *
- * The row sums are taken in binary64 in no fixed order, which can move them in
- * their last bits only.  Alignment: 2-byte for every bf16 pointer; 16-byte x,
+ * Precision: the value defined is z evaluated in binary64 and rounded once to
+ * bf16 (nearest, ties to even).  The kernels take mu, var and rstd in binary64
+ * (sums in no fixed order) and the elementwise steps in binary32:
+ * d = RN32(x - mu), y' = RN32(d * RN32(rstd)), z' = fmaf(y', RN32(1 + scale[g]),
+ * shift[g]), then z' to bf16.  Each output is within 1 bf16 ulp of the defined
+ * value, or, where the shift cancels most of the product, within
+ * ulp + 2^-21 (|P| + |shift|) of it, P = (x - mu) rstd (1 + scale).
+ * Alignment: 2-byte for every bf16 pointer; 16-byte x,
  * shift, scale and y with cols % 8 == 0 and cols <= 32768 take the vector
  * path.  rows = 0 is a no-op; cols >= 1, rows_per_cond >= 1 and fewer than
  * 2^31 rows are required (W8A8_EINVAL otherwise).  y must not overlap x.
@@ -134,8 +139,9 @@ W8A8_API int w8a8_norm_mod_bf16(const uint16_t* x, int64_t rows, int64_t cols,
  * The same normalisation and modulation fused with the per-row INT8
  * quantisation of the following W8A8 linear's activations (section 01.3):
  * q [rows x cols] int8 codes and qscale [rows] fp32 are exactly
- * w8a8_quantize_rows applied to the bf16 rows w8a8_norm_mod_bf16 would write;
- * those rows themselves are not written.  Requirements as w8a8_norm_mod_bf16,
+ * w8a8_quantize_rows applied to the bf16 rows w8a8_norm_mod_bf16 writes for
+ * the same arguments (the same arithmetic, bit for bit); those rows themselves
+ * are not written.  Requirements as w8a8_norm_mod_bf16,
  * plus qscale 4-byte aligned (8-byte q with the vector path's conditions takes
  * the vector path).
  */
@@ -192,6 +198,10 @@ W8A8_API int w8a8_gelu_bf16(const uint16_t* x, int64_t n, uint16_t* y, void* str
  *                  bias are ignored and may be NULL).
  * Shapes: w8a8_guard(N, K) must hold, else W8A8_EUNSUPPORTED (never a silent
  * fallback).  M is unrestricted.  qa, qw, out must be 16-byte aligned.
+ * Codes: every code in qa and qw must lie in [-127, 127], the range
+ * w8a8_quantize_rows produces; then the INT32 accumulator is exact for every K
+ * the guard admits.  The codes are not checked: a -128 code can take |acc| to
+ * 128*128*K, which for K = W8A8_MAX_K is 2^31 and wraps.
  */
 W8A8_API int w8a8_gemm(const int8_t* qa, const float* sa, int64_t M, const int8_t* qw, const float* sw,
               int64_t N, int64_t K, const uint16_t* bias, int act, int out_kind, void* out,

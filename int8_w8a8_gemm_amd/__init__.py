@@ -12,6 +12,7 @@ summary, section "C. Fused Multimodal Transformer Operations").
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 from dataclasses import dataclass
@@ -101,6 +102,15 @@ def _stream(stream=None):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _on(stream=None):
+    """Context for the allocations of a call that runs on `stream`: torch's caching
+    allocator ties a block to the stream that was current when it was allocated, so
+    temporaries (the linear's workspace, the normed layer's codes) and default outputs
+    are allocated with `stream` current.  Otherwise, once dropped, a temporary could be
+    handed to work on another stream while the kernels on `stream` still read it."""
+    return torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+
+
 def _p(t: Optional[torch.Tensor]):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else None
 
@@ -135,8 +145,10 @@ def quantize_rows(x: torch.Tensor, q: Optional[torch.Tensor] = None,
     if x.dim() != 2:
         raise ValueError("x must be 2-D")
     R, C = x.shape
-    q = q if q is not None else torch.empty((R, C), dtype=torch.int8, device=x.device)
-    scale = scale if scale is not None else torch.empty((R,), dtype=torch.float32, device=x.device)
+    with _on(stream):
+        q = q if q is not None else torch.empty((R, C), dtype=torch.int8, device=x.device)
+        scale = scale if scale is not None else torch.empty((R,), dtype=torch.float32,
+                                                            device=x.device)
     _need(q, "q", torch.int8, (R, C))
     _need(scale, "scale", torch.float32, (R,))
     _check("w8a8_quantize_rows",
@@ -159,9 +171,10 @@ def quantize_blocks(x: torch.Tensor, batch: int, heads: int, block: int,
         raise ValueError("batch, heads and block must be positive and divide the shape")
     S, D = rows // batch, C // heads
     nblk = -(-S // block)
-    q = q if q is not None else torch.empty(x.shape, dtype=torch.int8, device=x.device)
-    scale = scale if scale is not None else torch.empty((batch, nblk, heads), dtype=torch.float32,
-                                                        device=x.device)
+    with _on(stream):
+        q = q if q is not None else torch.empty(x.shape, dtype=torch.int8, device=x.device)
+        scale = scale if scale is not None else torch.empty((batch, nblk, heads),
+                                                            dtype=torch.float32, device=x.device)
     _need(q, "q", torch.int8, tuple(x.shape))
     _need(scale, "scale", torch.float32, (batch, nblk, heads))
     _check("w8a8_quantize_blocks",
@@ -178,8 +191,10 @@ def gelu_quantize_rows(y: torch.Tensor, q: Optional[torch.Tensor] = None,
     if y.dim() != 2:
         raise ValueError("y must be 2-D")
     R, C = y.shape
-    q = q if q is not None else torch.empty((R, C), dtype=torch.int8, device=y.device)
-    scale = scale if scale is not None else torch.empty((R,), dtype=torch.float32, device=y.device)
+    with _on(stream):
+        q = q if q is not None else torch.empty((R, C), dtype=torch.int8, device=y.device)
+        scale = scale if scale is not None else torch.empty((R,), dtype=torch.float32,
+                                                            device=y.device)
     _need(q, "q", torch.int8, (R, C))
     _need(scale, "scale", torch.float32, (R,))
     _check("w8a8_gelu_quantize_rows",
@@ -210,7 +225,8 @@ def norm_mod_bf16(x: torch.Tensor, shift: Optional[torch.Tensor] = None,
     z = y * (1 + scale[g]) + shift[g], g = row // rows_per_cond, of each row of
     x bf16 [R, C]; shift, scale bf16 [G, C] or None.  Returns bf16 [R, C]."""
     R, C, rpc = _norm_mod_args(x, shift, scale, rows_per_cond)
-    y = y if y is not None else torch.empty_like(x)
+    with _on(stream):
+        y = y if y is not None else torch.empty_like(x)
     _need(y, "y", torch.bfloat16, (R, C))
     _check("w8a8_norm_mod_bf16",
            lib().w8a8_norm_mod_bf16(_p(x), R, C, _p(shift), _p(scale), rpc, int(norm), float(eps),
@@ -226,9 +242,10 @@ def norm_mod_quantize_rows(x: torch.Tensor, shift: Optional[torch.Tensor] = None
     """norm_mod_bf16 fused with the per-row INT8 quantisation of its rows:
     returns (q int8 [R, C], qscale fp32 [R]); the bf16 rows are not written."""
     R, C, rpc = _norm_mod_args(x, shift, scale, rows_per_cond)
-    q = q if q is not None else torch.empty((R, C), dtype=torch.int8, device=x.device)
-    qscale = qscale if qscale is not None else torch.empty((R,), dtype=torch.float32,
-                                                           device=x.device)
+    with _on(stream):
+        q = q if q is not None else torch.empty((R, C), dtype=torch.int8, device=x.device)
+        qscale = qscale if qscale is not None else torch.empty((R,), dtype=torch.float32,
+                                                               device=x.device)
     _need(q, "q", torch.int8, (R, C))
     _need(qscale, "qscale", torch.float32, (R,))
     _check("w8a8_norm_mod_quantize_rows",
@@ -240,7 +257,8 @@ def norm_mod_quantize_rows(x: torch.Tensor, shift: Optional[torch.Tensor] = None
 def gelu_bf16(x: torch.Tensor, y: Optional[torch.Tensor] = None, stream=None):
     """Elementwise GELU-tanh on bf16: y = g(x) rounded to bf16, as the GELU epilogue."""
     _need(x, "x", torch.bfloat16)
-    y = y if y is not None else torch.empty_like(x)
+    with _on(stream):
+        y = y if y is not None else torch.empty_like(x)
     _need(y, "y", torch.bfloat16, tuple(x.shape))
     _check("w8a8_gelu_bf16", lib().w8a8_gelu_bf16(_p(x), x.numel(), _p(y), _stream(stream)))
     return y
@@ -262,7 +280,8 @@ def gemm(qa, sa, qw, sw, bias=None, act=ACT_NONE, out_kind=OUT_BF16, out=None, s
     if bias is not None:
         _need(bias, "bias", torch.bfloat16, (N,))
     odt = torch.int32 if out_kind == OUT_I32 else torch.bfloat16
-    out = out if out is not None else torch.empty((M, N), dtype=odt, device=qa.device)
+    with _on(stream):
+        out = out if out is not None else torch.empty((M, N), dtype=odt, device=qa.device)
     _need(out, "out", odt, (M, N))
     _check("w8a8_gemm", lib().w8a8_gemm(_p(qa), _p(sa), M, _p(qw), _p(sw), N, K, _p(bias),
                                         int(act), int(out_kind), _p(out), _stream(stream)))
@@ -279,7 +298,8 @@ def linear_bf16(x, w, bias=None, act=ACT_NONE, y=None, stream=None):
         raise ValueError("x and w disagree on K")
     if bias is not None:
         _need(bias, "bias", torch.bfloat16, (N,))
-    y = y if y is not None else torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    with _on(stream):
+        y = y if y is not None else torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
     _need(y, "y", torch.bfloat16, (M, N))
     _check("w8a8_linear_bf16", lib().w8a8_linear_bf16(_p(x), M, K, _p(w), N, _p(bias), int(act),
                                                       _p(y), _stream(stream)))
@@ -300,11 +320,12 @@ def linear(x, N, qw=None, sw=None, w=None, bias=None, act=ACT_NONE, y=None, work
         _need(w, "w", torch.bfloat16, (N, K))
     if bias is not None:
         _need(bias, "bias", torch.bfloat16, (N,))
-    y = y if y is not None else torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
-    _need(y, "y", torch.bfloat16, (M, N))
     ws_bytes = linear_workspace_bytes(M, K) if guard(N, K) else 0
-    if workspace is None and ws_bytes > 0:
-        workspace = torch.empty((ws_bytes,), dtype=torch.uint8, device=x.device)
+    with _on(stream):
+        y = y if y is not None else torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+        if workspace is None and ws_bytes > 0:
+            workspace = torch.empty((ws_bytes,), dtype=torch.uint8, device=x.device)
+    _need(y, "y", torch.bfloat16, (M, N))
     if workspace is not None:
         _need(workspace, "workspace", torch.uint8)
     path = ctypes.c_int(-1)
@@ -324,9 +345,11 @@ def compact_padded_rows(x, mask, out=None, src_row=None, count=None, stream=None
     if tuple(mask.shape) != (B, L):
         raise ValueError("mask must be [B, L]")
     dev = x.device
-    out = out if out is not None else torch.empty((B * L, D), dtype=torch.bfloat16, device=dev)
-    src_row = src_row if src_row is not None else torch.empty((B * L,), dtype=torch.int32, device=dev)
-    count = count if count is not None else torch.empty((1,), dtype=torch.int32, device=dev)
+    with _on(stream):
+        out = out if out is not None else torch.empty((B * L, D), dtype=torch.bfloat16, device=dev)
+        src_row = src_row if src_row is not None else torch.empty((B * L,), dtype=torch.int32,
+                                                                  device=dev)
+        count = count if count is not None else torch.empty((1,), dtype=torch.int32, device=dev)
     _need(out, "out", torch.bfloat16, (B * L, D))
     _need(src_row, "src_row", torch.int32, (B * L,))
     _need(count, "count", torch.int32, (1,))
@@ -345,10 +368,13 @@ def compact_quantize_rows(x, mask, q=None, scale=None, src_row=None, count=None,
     if tuple(mask.shape) != (B, L):
         raise ValueError("mask must be [B, L]")
     dev = x.device
-    q = q if q is not None else torch.empty((B * L, D), dtype=torch.int8, device=dev)
-    scale = scale if scale is not None else torch.empty((B * L,), dtype=torch.float32, device=dev)
-    src_row = src_row if src_row is not None else torch.empty((B * L,), dtype=torch.int32, device=dev)
-    count = count if count is not None else torch.empty((1,), dtype=torch.int32, device=dev)
+    with _on(stream):
+        q = q if q is not None else torch.empty((B * L, D), dtype=torch.int8, device=dev)
+        scale = scale if scale is not None else torch.empty((B * L,), dtype=torch.float32,
+                                                            device=dev)
+        src_row = src_row if src_row is not None else torch.empty((B * L,), dtype=torch.int32,
+                                                                  device=dev)
+        count = count if count is not None else torch.empty((1,), dtype=torch.int32, device=dev)
     _need(q, "q", torch.int8, (B * L, D))
     _need(scale, "scale", torch.float32, (B * L,))
     _need(src_row, "src_row", torch.int32, (B * L,))

@@ -557,15 +557,19 @@ hipError_t launch_blocks(const uint16_t* x, int64_t B, int64_t S, int64_t H, int
 //     LayerNorm:  mu = sum(x) / D,  var = sum((x - mu)^2) / D
 //     RMSNorm:    mu = 0,           var = sum(x^2) / D
 //     rstd = 1 / sqrt(var + eps), 0 where var + eps = 0       (binary64)
-//     d = RN32(x - mu),  y = RN32(d * RN32(rstd)),
-//     z = fmaf(y, RN32(1 + scale[g]), shift[g]),  g = row / rows_per_cond
-// and z rounded to bf16; the fused variant then quantises the bf16 row
-// exactly as quantize_rows does.  The sums' order is free: it moves them only
-// in their last binary64 bits, which reach the binary32 values mu and rstd
-// only in the rare case that those bits decide a binary32 rounding.  The
-// vector kernel keeps the row in registers (as quantize_rows_vec), so each
-// element is read from HBM once; the binary64 work is two or three operations
-// per element in the statistics, the rest is binary32.
+//     z = (x - mu) * rstd * (1 + scale[g]) + shift[g],  g = row / rows_per_cond
+// The value defined is z in binary64 rounded once to bf16.  Here the
+// statistics are binary64 (sums in the order the reduction takes) and the
+// elementwise steps binary32, d = RN32(x - mu), y = RN32(d * RN32(rstd)),
+// z' = fmaf(y, RN32(1 + scale[g]), shift[g]), then z' to bf16: z' is within
+// 2^-24 |z| + 4.01 * 2^-24 |(x - mu) rstd (1 + scale)| of z, so the bf16 result
+// is within one bf16 ulp of the defined value except where the shift cancels
+// most of the product.  The fused variant quantises the bf16 row it computes
+// exactly as quantize_rows does.  The vector kernel keeps the row in registers
+// (as quantize_rows_vec), so each element is read from HBM once; the binary64
+// work is two or three operations per element in the statistics, the rest is
+// binary32 (binary64 elementwise would double the VALU work of a kernel that
+// is already bound by VALU issue).
 
 __device__ __forceinline__ double wave_sum_f64(double v) {
 #pragma unroll

@@ -31,9 +31,9 @@
  *      of the paperlayer.ai summary, section C): per row, LayerNorm without
  *      affine (mean and variance over the row) or RMSNorm (mean square), then
  *      z = y * (1 + scale) + shift with the modulation vectors of the row's
- *      conditioning group; the row statistics in binary64, the elementwise
- *      steps in binary32 (a fixed sequence of roundings), z rounded to bf16;
- *      the fused variant quantises that bf16 row as in Q.
+ *      conditioning group; the real-valued formula evaluated in binary64 and
+ *      rounded once to bf16 (the page gives no precision); the fused variant
+ *      quantises that bf16 row as in Q.
  *
  * Build: gcc -O2 -ffp-contract=off -fno-fast-math -shared -fPIC -pthread.
  */
@@ -429,11 +429,12 @@ int oracle_compact_rows(const uint16_t* x, const uint8_t* mask, int64_t B, int64
 /*   LayerNorm (norm 0): mu = sum(x)/D, var = sum((x - mu)^2)/D            */
 /*     (Ba, Kiros & Hinton 2016, without the elementwise affine);          */
 /*   RMSNorm (norm 1): mu = 0, var = sum(x^2)/D (Zhang & Sennrich 2019);   */
-/*   rstd = 1/sqrt(var + eps), 0 where var + eps is 0 (all binary64);     */
+/*   rstd = 1/sqrt(var + eps), 0 where var + eps is 0;                    */
 /*   z = (x - mu) * rstd * (1 + scale[g]) + shift[g], g = row / rpc        */
-/*     (adaptive-norm modulation as in DiT, Peebles & Xie 2023), evaluated */
-/*     in binary32 as d = RN32(x - mu), y = RN32(d * RN32(rstd)),          */
-/*     z = fmaf(y, RN32(1 + scale), shift); NULL scale or shift reads as 0.*/
+/*     (adaptive-norm modulation as in DiT, Peebles & Xie 2023); NULL      */
+/*     scale or shift reads as 0.                                          */
+/* Every step in binary64, sums in index order; z is rounded once, from    */
+/* binary64, to the nearest bf16 (ties to even).                           */
 /* ---------------------------------------------------------------------- */
 
 typedef struct {
@@ -446,7 +447,7 @@ static void nm_rows(void* p, int64_t r0, int64_t r1) {
     for (int64_t r = r0; r < r1; ++r) {
         const uint16_t* xr = c->x + r * D;
         const int64_t g = r / c->rpc;
-        /* 1. the row's statistics, binary64 sums in index order */
+        /* 1. the row's statistics */
         double mu = 0.0;
         if (c->norm == 0) {
             double s1 = 0.0;
@@ -460,14 +461,12 @@ static void nm_rows(void* p, int64_t r0, int64_t r1) {
         }
         const double v = s2 / (double)D + c->eps;
         const double rstd = v > 0.0 ? 1.0 / sqrt(v) : 0.0;
-        /* 2. normalise and modulate in binary32, round to bf16 */
-        const float r32 = (float)rstd;
+        /* 2. normalise, modulate, round once */
         for (int64_t j = 0; j < D; ++j) {
-            const float d = (float)((double)bf16_to_f32(xr[j]) - mu);
-            const float y = d * r32;
-            const float sc = c->scale ? bf16_to_f32(c->scale[g * D + j]) : 0.0f;
-            const float sh = c->shift ? bf16_to_f32(c->shift[g * D + j]) : 0.0f;
-            c->y[r * D + j] = f32_to_bf16(fmaf(y, 1.0f + sc, sh));
+            const double y = ((double)bf16_to_f32(xr[j]) - mu) * rstd;
+            const double sc = c->scale ? (double)bf16_to_f32(c->scale[g * D + j]) : 0.0;
+            const double sh = c->shift ? (double)bf16_to_f32(c->shift[g * D + j]) : 0.0;
+            c->y[r * D + j] = f64_to_bf16(y * (1.0 + sc) + sh);
         }
     }
 }

@@ -89,6 +89,7 @@ def test_quantize_tiny_and_audio():
 
 
 def test_quantize_video_and_ffn_full_size(attn, ffn):
+    _check_quant(ffn.x, "ffn.x")
     _check_quant(attn.x, "attn.x")
     _check_quant(attn.w, "attn.w")
     _check_quant(ffn.w1, "ffn.w1")
@@ -195,6 +196,58 @@ def _nm_input(R, D, G, seed, const_rows=True):
     return wl.to_bf16_bits(v), wl.to_bf16_bits(sh), wl.to_bf16_bits(sc)
 
 
+def _f32(b):
+    return (np.asarray(b).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def _bf16_ulp(v):
+    """Spacing of bf16 numbers at |v| (2^-133 at 0 and among subnormals)."""
+    e = np.frexp(np.abs(v))[1]
+    return np.ldexp(1.0, np.maximum(e - 8, -133))
+
+
+def _check_norm_mod(z, x, sh, sc, rpc, norm, eps, label=""):
+    """The kernel's bf16 rows against the oracle's binary64 values rounded once.
+    The kernel takes the row statistics in binary64 and the elementwise steps in
+    binary32: d = RN32(x - mu), y = RN32(d RN32(rstd)), z = fmaf(y, RN32(1 + scale),
+    shift), so before its bf16 rounding it is off the exact value by at most
+    u|z| + 4.01u|P| (u = 2^-24, P = (x - mu) rstd (1 + scale)), plus the binary64
+    statistics' D 2^-53 relative terms.  Accepted: within 1 bf16 ulp of the oracle,
+    or within ulp(oracle) + E with E = 2^-21 (|P| + |shift|) + D 2^-50 (mean|x| rstd
+    |1 + scale| + |P|).  Returns the fraction of bit-equal values."""
+    zr = oracle.norm_mod_bf16(x, sh, sc, rpc, norm, eps)
+    if z.size == 0:
+        return 1.0
+    R, D = x.shape
+    xf = _f32(x)
+    mu = xf.mean(axis=1, keepdims=True) if norm == w8.NORM_LAYER else np.zeros((R, 1))
+    var = ((xf - mu) ** 2).mean(axis=1, keepdims=True) + eps
+    rstd = np.where(var > 0, 1.0 / np.sqrt(np.where(var > 0, var, 1.0)), 0.0)
+    g = np.arange(R) // rpc
+    c = 1.0 + (_f32(sc)[g] if sc is not None else 0.0)
+    shf = _f32(sh)[g] if sh is not None else 0.0
+    P = (xf - mu) * rstd * c
+    E = 2.0 ** -21 * (np.abs(P) + np.abs(shf)) + D * 2.0 ** -50 * (
+        np.abs(xf).mean(axis=1, keepdims=True) * rstd * np.abs(c) + np.abs(P))
+    gf, rf = _f32(z), _f32(zr)
+    ok = (ulp_dist_bf16(z, zr) <= 1) | (np.abs(gf - rf) <= _bf16_ulp(rf) + E)
+    assert ok.all(), f"{label}: {int((~ok).sum())} values outside the bound"
+    rate = float(np.mean(z == zr))
+    say(f"{label} norm/mod exact-match rate {rate:.6f}")
+    assert rate > 0.95
+    return rate
+
+
+def _check_norm_mod_quant(q, s, z_gpu, x, sh, sc, rpc, norm, eps, label=""):
+    """Fused codes and scales: the oracle's quantiser applied to the kernel's own
+    bf16 rows, bit for bit (the rows themselves are held to _check_norm_mod)."""
+    qr, sr = oracle.quantize_rows(z_gpu)
+    assert np.array_equal(q, qr), label
+    assert np.array_equal(s.view(np.uint32), sr.view(np.uint32)), label
+    qo, _ = oracle.norm_mod_quantize_rows(x, sh, sc, rpc, norm, eps)
+    say(f"{label} codes equal to the all-oracle chain: {float(np.mean(q == qo)):.6f}")
+
+
 NM_SHAPES = [(1, 8, 1), (7, 64, 3), (33, 1000, 5), (20, 2048, 4), (17, 1030, 4), (64, 4096, 16), (9, 8192, 3),
              (5, 16384, 2), (3, 32768, 1), (2, 40000, 1), (300, 512, 100)]
 
@@ -203,9 +256,10 @@ NM_SHAPES = [(1, 8, 1), (7, 64, 3), (33, 1000, 5), (20, 2048, 4), (17, 1030, 4),
 @pytest.mark.parametrize("norm", [w8.NORM_LAYER, w8.NORM_RMS])
 @pytest.mark.parametrize("mod", [True, False])
 def test_norm_mod_matches_oracle(R, D, rpc, norm, mod):
-    """bf16 rows bit-exact, and the fused quantisation's codes and scales
-    bit-exact, against the oracle (vector paths of every width; 1030 and 40000
-    columns take the generic kernel)."""
+    """bf16 rows within the norm/modulation bound of the oracle, and the fused
+    quantisation's codes and scales bit-exact against the oracle's quantiser on
+    those rows (vector paths of every width; 1030 and 40000 columns take the
+    generic kernel)."""
     say(f"norm mod R={R} D={D} rpc={rpc} norm={norm} mod={mod}")
     G = -(-R // rpc)
     x, sh, sc = _nm_input(R, D, G, R * 7 + D + norm)
@@ -214,12 +268,9 @@ def test_norm_mod_matches_oracle(R, D, rpc, norm, mod):
     dx = d_bf16(x)
     dsh, dsc = (d_bf16(sh), d_bf16(sc)) if mod else (None, None)
     z = h_u16(w8.norm_mod_bf16(dx, dsh, dsc, rpc, norm, eps))
-    zr = oracle.norm_mod_bf16(x, sh, sc, rpc, norm, eps)
-    assert np.array_equal(z, zr)
+    _check_norm_mod(z, x, sh, sc, rpc, norm, eps, f"R={R} D={D}")
     q, s = w8.norm_mod_quantize_rows(dx, dsh, dsc, rpc, norm, eps)
-    qr, sr = oracle.norm_mod_quantize_rows(x, sh, sc, rpc, norm, eps)
-    assert np.array_equal(h(q), qr)
-    assert np.array_equal(h(s).view(np.uint32), sr.view(np.uint32))
+    _check_norm_mod_quant(h(q), h(s), z, x, sh, sc, rpc, norm, eps, f"R={R} D={D}")
 
 
 def _random_nm_cases(n, seed):
@@ -240,12 +291,10 @@ def test_norm_mod_random_shapes(R, D, rpc, norm, eps):
     G = -(-R // rpc)
     x, sh, sc = _nm_input(R, D, G, R + D + rpc)
     dx, dsh, dsc = d_bf16(x), d_bf16(sh), d_bf16(sc)
-    assert np.array_equal(h_u16(w8.norm_mod_bf16(dx, dsh, dsc, rpc, norm, eps)),
-                          oracle.norm_mod_bf16(x, sh, sc, rpc, norm, eps))
+    z = h_u16(w8.norm_mod_bf16(dx, dsh, dsc, rpc, norm, eps))
+    _check_norm_mod(z, x, sh, sc, rpc, norm, eps, f"R={R} D={D}")
     q, s = w8.norm_mod_quantize_rows(dx, dsh, dsc, rpc, norm, eps)
-    qr, sr = oracle.norm_mod_quantize_rows(x, sh, sc, rpc, norm, eps)
-    assert np.array_equal(h(q), qr)
-    assert np.array_equal(h(s).view(np.uint32), sr.view(np.uint32))
+    _check_norm_mod_quant(h(q), h(s), z, x, sh, sc, rpc, norm, eps, f"R={R} D={D}")
 
 
 @pytest.mark.parametrize("norm", [w8.NORM_LAYER, w8.NORM_RMS])
@@ -255,8 +304,9 @@ def test_norm_mod_eps_zero_and_degenerate_rows(norm):
     R, D = 6, 256
     x, sh, sc = _nm_input(R, D, R, 3 + norm)
     z = h_u16(w8.norm_mod_bf16(d_bf16(x), d_bf16(sh), d_bf16(sc), 1, norm, 0.0))
-    assert np.array_equal(z, oracle.norm_mod_bf16(x, sh, sc, 1, norm, 0.0))
+    _check_norm_mod(z, x, sh, sc, 1, norm, 0.0, "eps 0")
     assert np.array_equal(z[2], sh[2])  # zero row: y = 0, z = shift
+    assert np.array_equal(z[2], oracle.norm_mod_bf16(x, sh, sc, 1, norm, 0.0)[2])
     q, s = w8.norm_mod_quantize_rows(d_bf16(x), None, None, 1, norm, 0.0)
     assert h(s)[2] == 0 and not h(q)[2].any()
 
@@ -268,14 +318,16 @@ def test_norm_mod_video_tokens_full_size_sampled():
     R, D, rpc = 24576, 4096, 3072
     say(f"norm mod full size R={R} D={D}")
     x, sh, sc = _nm_input(R, D, R // rpc, 77)
-    q, s = w8.norm_mod_quantize_rows(d_bf16(x), d_bf16(sh), d_bf16(sc), rpc)
+    dx, dsh, dsc = d_bf16(x), d_bf16(sh), d_bf16(sc)
+    q, s = w8.norm_mod_quantize_rows(dx, dsh, dsc, rpc)
+    z = h_u16(w8.norm_mod_bf16(dx, dsh, dsc, rpc))
     rng = np.random.default_rng(78)
     rows = np.unique(np.concatenate([[0, 1, 2, rpc - 1, rpc, R - 1], rng.choice(R, 200, replace=False)]))
     g = rows // rpc
-    qr, sr = oracle.norm_mod_quantize_rows(np.ascontiguousarray(x[rows]), np.ascontiguousarray(sh[g]),
-                                           np.ascontiguousarray(sc[g]), 1)
-    assert np.array_equal(h(q)[rows], qr)
-    assert np.array_equal(h(s)[rows].view(np.uint32), sr.view(np.uint32))
+    xs, shs, scs = (np.ascontiguousarray(a) for a in (x[rows], sh[g], sc[g]))
+    _check_norm_mod(z[rows], xs, shs, scs, 1, w8.NORM_LAYER, 1e-6, "video tokens")
+    _check_norm_mod_quant(h(q)[rows], h(s)[rows], np.ascontiguousarray(z[rows]), xs, shs, scs, 1,
+                          w8.NORM_LAYER, 1e-6, "video tokens")
 
 
 def test_norm_mod_unaligned_rows_take_the_generic_kernel():
@@ -293,19 +345,23 @@ def test_norm_mod_unaligned_rows_take_the_generic_kernel():
     yb = torch.zeros(R * D + 8, dtype=torch.int16, device=DEV)
     y = yb[1:1 + R * D].view(torch.bfloat16).view(R, D)
     w8.norm_mod_bf16(dx, dsh, dsc, 7, w8.NORM_LAYER, 1e-6, y=y)
-    assert np.array_equal(h_u16(y), oracle.norm_mod_bf16(x, sh, sc, 7, oracle.NORM_LAYER, 1e-6))
+    z_ln = h_u16(y)
+    _check_norm_mod(z_ln, x, sh, sc, 7, w8.NORM_LAYER, 1e-6, "unaligned LN")
     qb = torch.zeros(R * D + 16, dtype=torch.int8, device=DEV)
     q = qb[3:3 + R * D].view(R, D)
     qs = torch.empty((R,), dtype=torch.float32, device=DEV)
     w8.norm_mod_quantize_rows(dx, dsh, dsc, 7, w8.NORM_RMS, 1e-6, q=q, qscale=qs)
-    qr, sr = oracle.norm_mod_quantize_rows(x, sh, sc, 7, oracle.NORM_RMS, 1e-6)
-    assert np.array_equal(h(q), qr) and np.array_equal(h(qs).view(np.uint32), sr.view(np.uint32))
+    w8.norm_mod_bf16(dx, dsh, dsc, 7, w8.NORM_RMS, 1e-6, y=y)
+    z_rms = h_u16(y)
+    _check_norm_mod(z_rms, x, sh, sc, 7, w8.NORM_RMS, 1e-6, "unaligned RMS")
+    _check_norm_mod_quant(h(q), h(qs), z_rms, x, sh, sc, 7, w8.NORM_RMS, 1e-6, "unaligned RMS")
 
 
 @pytest.mark.parametrize("N,act", [(512, w8.ACT_NONE), (1024, w8.ACT_GELU_TANH), (100, w8.ACT_NONE)])
 def test_linear_on_normed_rows(N, act):
     """W8A8Linear.normed: norm + modulation + quantisation fused, then the INT8 GEMM
-    (guarded shapes) -- bit-exact against the oracle's norm_mod_quantize_rows,
+    (guarded shapes) -- bit-exact against the oracle's quantize_rows of the
+    kernel's normalised rows (themselves within the norm/modulation bound),
     quantize_rows of W, INT32 product and epilogue; or, for N = 100, the bf16
     rows of norm_mod_bf16 through the BF16 fallback, within its bound."""
     M, K, rpc = 300, 1024, 100
@@ -316,8 +372,10 @@ def test_linear_on_normed_rows(N, act):
     b = wl.to_bf16_bits(rng.standard_normal(N).astype(np.float32) * np.float32(0.1))
     layer = w8.W8A8Linear.prepare(d_bf16(w), d_bf16(b), act)
     y = h_u16(layer.normed(d_bf16(x), d_bf16(sh), d_bf16(sc), rpc))
+    z = h_u16(w8.norm_mod_bf16(d_bf16(x), d_bf16(sh), d_bf16(sc), rpc))
+    _check_norm_mod(z, x, sh, sc, rpc, w8.NORM_LAYER, 1e-6, "normed linear")
     if layer.path == w8.PATH_INT8:
-        qa, sa = oracle.norm_mod_quantize_rows(x, sh, sc, rpc)
+        qa, sa = oracle.quantize_rows(z)
         qw, sw = oracle.quantize_rows(w)
         ref = oracle.epilogue(oracle.gemm_i32(qa, qw), sa, sw, b, act=act)
         d = ulp_dist_bf16(y, ref)
@@ -326,7 +384,7 @@ def test_linear_on_normed_rows(N, act):
             assert np.array_equal(y, ref)
     else:
         assert N == 100
-        _check_fallback(y, oracle.norm_mod_bf16(x, sh, sc, rpc), w, b)
+        _check_fallback(y, z, w, b)
 
 
 def test_norm_mod_guard_bands():
@@ -347,10 +405,10 @@ def test_norm_mod_guard_bands():
     assert np.all(hb[:pad] == 0x5A) and np.all(hb[pad + n:] == 0x5A)
     assert np.all(hs[:64] == -7.0) and np.all(hs[64 + R:] == -7.0)
     assert np.all(hy[:pad] == 0x7F7F) and np.all(hy[pad + n:] == 0x7F7F)
-    qr, sr = oracle.norm_mod_quantize_rows(x, sh, sc, R)
-    assert np.array_equal(hb[pad:pad + n].reshape(R, D), qr)
-    assert np.array_equal(hy[pad:pad + n].view(np.uint16).reshape(R, D),
-                          oracle.norm_mod_bf16(x, sh, sc, R))
+    z = hy[pad:pad + n].view(np.uint16).reshape(R, D)
+    _check_norm_mod(z, x, sh, sc, R, w8.NORM_LAYER, 1e-6, "guard bands")
+    _check_norm_mod_quant(hb[pad:pad + n].reshape(R, D), hs[64:64 + R], np.ascontiguousarray(z),
+                          x, sh, sc, R, w8.NORM_LAYER, 1e-6, "guard bands")
 
 
 def test_quantize_blocks_guard_bands():
@@ -643,14 +701,24 @@ def _sampled_linear(x_u16, w_u16, b_u16, rows, act=w8.ACT_NONE, label=""):
     return got, ref
 
 
+def _video_rows(M, n=512, tile=384, seed=1):
+    """n seeded rows of [0, M): both rows at every boundary of the 384-row tiles
+    the video GEMMs run on, the first and the last row, and seeded random rows
+    to make up n (M = 24576: 128 edge rows and 384 random ones)."""
+    edges = {0, M - 1} | {r for b in range(tile, M, tile) for r in (b - 1, b)}
+    rng = np.random.Generator(np.random.PCG64(seed))
+    rest = [int(r) for r in rng.permutation(M) if int(r) not in edges][:max(0, n - len(edges))]
+    return np.array(sorted(edges | set(rest)), dtype=np.int64)
+
+
 def test_linear_video_attn_proj_sampled(attn):
-    rows = wl.sample_rows(attn.x.shape[0], 512)
+    rows = _video_rows(attn.x.shape[0])
     got, ref = _sampled_linear(attn.x, attn.w, attn.bias, rows, label="attn-proj")
     assert np.array_equal(got[rows], ref)
 
 
 def test_linear_video_ffn_up_gelu_sampled(ffn):
-    rows = wl.sample_rows(ffn.x.shape[0], 256)
+    rows = _video_rows(ffn.x.shape[0])
     got, ref = _sampled_linear(ffn.x, ffn.w1, ffn.b1, rows, act=w8.ACT_GELU_TANH, label="ffn-up")
     d = ulp_dist_bf16(got[rows], ref)
     say(f"  ffn-up: exact {np.mean(d == 0):.6f}, max ulp {d.max()}")
@@ -660,7 +728,7 @@ def test_linear_video_ffn_up_gelu_sampled(ffn):
 def test_linear_video_ffn_down_on_oracle_h(ffn):
     """Down projection fed the oracle's own H rows (the GELU output), so both
     sides quantise the same bf16 input: bit-exact."""
-    rows = wl.sample_rows(ffn.x.shape[0], 256)
+    rows = _video_rows(ffn.x.shape[0])
     say("oracle ffn-up rows for the down projection")
     h_ref, _ = oracle.w8a8_linear(np.ascontiguousarray(ffn.x[rows]), ffn.w1, ffn.b1,
                                   act=oracle.ACT_GELU_TANH)
@@ -671,7 +739,7 @@ def test_linear_video_ffn_down_on_oracle_h(ffn):
 def test_linear_video_ffn_chain_end_to_end(ffn):
     """Whole pair on the GPU (GPU H feeds the GPU down projection) against the
     oracle chain: both sides round GELU's binary64 value once, so bit-exact."""
-    rows = wl.sample_rows(ffn.x.shape[0], 128)
+    rows = _video_rows(ffn.x.shape[0])
     say("ffn chain on GPU (GELU in the up-projection epilogue)")
     up = w8.W8A8Linear.prepare(d_bf16(ffn.w1), d_bf16(ffn.b1), w8.ACT_GELU_TANH)
     down = w8.W8A8Linear.prepare(d_bf16(ffn.w2), d_bf16(ffn.b2))
@@ -685,8 +753,12 @@ def test_linear_video_ffn_chain_end_to_end(ffn):
 
 def test_ffn_pipeline_fused_gelu_quantise(ffn):
     """The benchmark's pipeline: quantise X, up GEMM without activation, fused
-    GELU + quantise of its output, down GEMM: bit-exact against the oracle chain."""
-    rows = wl.sample_rows(ffn.x.shape[0], 128)
+    GELU + quantise of its output U, down GEMM.  X's codes and scales, and the
+    codes and scales of the whole GELU output (24576 x 16384, from the GPU's own
+    U), in full; U and the output on 512 sampled rows with every tile edge;
+    all bit-exact against the oracle."""
+    M = ffn.x.shape[0]
+    rows = _video_rows(M)
     say("ffn fused pipeline on GPU")
     qw1, sw1 = w8.quantize_rows(d_bf16(ffn.w1))
     qw2, sw2 = w8.quantize_rows(d_bf16(ffn.w2))
@@ -694,15 +766,26 @@ def test_ffn_pipeline_fused_gelu_quantise(ffn):
     y1 = w8.gemm(qx, sx, qw1, sw1, d_bf16(ffn.b1))
     qh, sh = w8.gelu_quantize_rows(y1)
     y = h_u16(w8.gemm(qh, sh, qw2, sw2, d_bf16(ffn.b2)))
-    rd = torch.from_numpy(rows).to(DEV)
-    qh_rows, sh_rows = h(qh[rd]), h(sh[rd])
-    say("ffn chain on the oracle")
+    torch.cuda.synchronize()
+    say("ffn: X quantisation in full")
+    qx_ref, sx_ref = oracle.quantize_rows(ffn.x)
+    assert np.array_equal(h(sx).view(np.uint32), sx_ref.view(np.uint32))
+    assert np.array_equal(h(qx), qx_ref)
+    del qx_ref
+    u = h_u16(y1)
+    del y1
+    say("ffn: U on sampled rows")
     y1_ref, _ = oracle.w8a8_linear(np.ascontiguousarray(ffn.x[rows]), ffn.w1, ffn.b1)
-    qh_ref, sh_ref = oracle.gelu_quantize_rows(y1_ref)
-    assert np.array_equal(sh_rows.view(np.uint32), sh_ref.view(np.uint32))
-    assert np.array_equal(qh_rows, qh_ref)
-    y_ref = oracle.epilogue(oracle.gemm_i32(qh_ref, oracle.quantize_rows(ffn.w2)[0]), sh_ref,
-                            oracle.quantize_rows(ffn.w2)[1], ffn.b2)
+    assert np.array_equal(u[rows], y1_ref)
+    say("ffn: GELU + quantisation of the whole U")
+    qh_ref, sh_ref = oracle.gelu_quantize_rows(u)
+    del u
+    assert np.array_equal(h(sh).view(np.uint32), sh_ref.view(np.uint32))
+    assert np.array_equal(h(qh), qh_ref)
+    say("ffn: down projection on sampled rows")
+    qw2_ref, sw2_ref = oracle.quantize_rows(ffn.w2)
+    y_ref = oracle.epilogue(oracle.gemm_i32(np.ascontiguousarray(qh_ref[rows]), qw2_ref),
+                            np.ascontiguousarray(sh_ref[rows]), sw2_ref, ffn.b2)
     assert np.array_equal(y[rows], y_ref)
 
 
@@ -769,6 +852,48 @@ def test_ffn_pipeline_graph_capture_and_replay():
         torch.cuda.synchronize()
         assert torch.equal(pipe.y, eager.y), f"replay {r}"
         assert torch.equal(pipe.qh, eager.qh) and torch.equal(pipe.sh, eager.sh), f"replay {r}"
+
+
+def test_layer_on_a_side_stream_allocates_there():
+    """W8A8Linear(x, stream=s) and .normed(..., stream=s) on a stream that is not
+    the current one, kept busy so that their kernels run after the calls return:
+    the workspace and the normed layer's codes they allocate and drop belong to
+    s, so the current stream's allocations and writes made in between cannot
+    land in them.  Every result bit-exact against the oracle."""
+    say("layer calls on a side stream")
+    M, K, N, rpc = 768, 2048, 1536, 256
+    rng = np.random.default_rng(41)
+    x = wl.to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+    w = wl.to_bf16_bits(rng.standard_normal((N, K)).astype(np.float32) * np.float32(0.02))
+    b = wl.to_bf16_bits(rng.standard_normal(N).astype(np.float32) * np.float32(0.01))
+    _, sh, sc = _nm_input(M, K, M // rpc, 42)
+    layer = w8.W8A8Linear.prepare(d_bf16(w), d_bf16(b))
+    dx, dsh, dsc = d_bf16(x), d_bf16(sh), d_bf16(sc)
+    z = h_u16(w8.norm_mod_bf16(dx, dsh, dsc, rpc))  # the normed rows, on the current stream
+    busy_a = torch.randint(-127, 128, (8192, 8192), dtype=torch.int8, device=DEV)
+    busy_s = torch.ones(8192, dtype=torch.float32, device=DEV)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    outs, normed = [], []
+    for i in range(3):
+        w8.gemm(busy_a, busy_s, busy_a, busy_s, stream=side)  # keeps `side` busy
+        outs.append(layer(dx, stream=side))
+        normed.append(layer.normed(dx, dsh, dsc, rpc, stream=side))
+        # current-stream allocations of the sizes just dropped, written at once
+        junk = [torch.full((layer_ws,), 0x55 + i, dtype=torch.uint8, device=DEV)
+                for layer_ws in (w8.linear_workspace_bytes(M, K), M * K, 4 * M)]
+        del junk
+    torch.cuda.synchronize()
+    qw, sw = oracle.quantize_rows(w)
+    qa, sa = oracle.quantize_rows(x)
+    ref = oracle.epilogue(oracle.gemm_i32(qa, qw), sa, sw, b)
+    qz, sz = oracle.quantize_rows(z)
+    ref_n = oracle.epilogue(oracle.gemm_i32(qz, qw), sz, sw, b)
+    _check_norm_mod(z, x, sh, sc, rpc, w8.NORM_LAYER, 1e-6, "side stream")
+    for i in range(3):
+        assert np.array_equal(h_u16(outs[i]), ref), f"call {i}"
+        assert np.array_equal(h_u16(normed[i]), ref_n), f"normed call {i}"
 
 
 def test_two_pipelines_on_two_streams():
