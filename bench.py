@@ -57,13 +57,6 @@ def parse():
                    help="run the HBM-bound kernels on their workloads (for rocprofv3)")
     p.add_argument("--hbm-from", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                    help="achieved HBM rate per kernel from rocprofv3 runs of --probe-hbm")
-    p.add_argument("--hbm-ceiling", action="store_true",
-                   help="practical HBM streaming rates (read, write, copy, 2:1 mix)")
-    p.add_argument("--vendor", action="store_true",
-                   help="time torch._int_mm (hipBLASLt) beside w8a8_gemm on the video GEMM shapes")
-    p.add_argument("--ceiling", action="store_true",
-                   help="measure the INT8 MFMA rate and clock for several kinds of operand "
-                        "data (the power-capped ceiling any INT8 GEMM faces), print JSON, exit")
     p.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                    help="turn the two rocprofv3 counter outputs of --probe-traffic into "
                         + TRAFFIC_FILE + " and exit (no GPU needed)")
@@ -141,64 +134,6 @@ def traffic_from(fetch_dir, write_dir):
         json.dump(out, f, indent=1)
     print(json.dumps(out, indent=1))
 
-
-def ceiling():
-    """INT8 MFMA throughput and shader clock for zero, constant, uniform-random and
-    Gaussian (sigma 32, like quantised N(0,1) rows) int8 operands."""
-    import ctypes
-
-    import numpy as np
-    import torch
-
-    lib = ctypes.CDLL(os.path.join(ROOT, "int8_w8a8_gemm_amd", "libw8a8_probe.so"))
-    P = ctypes.c_void_p
-    lib.w8a8_probe_mfma.argtypes = [P, P, P, ctypes.c_int, ctypes.POINTER(ctypes.c_float), P]
-    dev = torch.device("cuda:0")
-    rng = np.random.default_rng(0)
-    kinds = {
-        "zero": np.zeros(4096 * 16, np.int8),
-        "constant": np.tile(np.arange(1, 17, dtype=np.int8), 4096),
-        "uniform_random": rng.integers(-128, 128, 4096 * 16).astype(np.int8),
-        "gaussian_sigma32": np.clip(np.rint(rng.standard_normal(4096 * 16) * 32), -127, 127).astype(np.int8),
-    }
-    sink = torch.empty(1024 * 256, dtype=torch.int32, device=dev)
-    clk = torch.zeros(2, dtype=torch.int64, device=dev)
-    iters = 4000
-    out = {}
-    for name, ops in kinds.items():
-        t = torch.from_numpy(ops).to(dev)
-        ms = ctypes.c_float(0)
-        rc = lib.w8a8_probe_mfma(P(t.data_ptr()), P(sink.data_ptr()), P(clk.data_ptr()), iters,
-                                 ctypes.byref(ms), P(torch.cuda.current_stream().cuda_stream))
-        assert rc == 0, rc
-        c = clk.cpu().tolist()
-        tops = 1024 * 4 * iters * 8 * 65536.0 / (ms.value * 1e-3) / 1e12
-        out[name] = {"TOPS": round(tops, 1), "frac_of_5000": round(tops / PEAK_INT8_TOPS, 4),
-                     "clock_GHz": round(c[0] / (c[1] / 100e6) / 1e9, 3),
-                     "cycles_per_mfma": round(c[0] / (iters * 8), 2)}
-    # two waves per SIMD, Gaussian codes, with 0 / 3 / 6 of the 6 fragment registers
-    # refreshed from LDS (ds_read_b128) per 8 MFMAs, as a GEMM K loop does
-    lib.w8a8_probe_mfma_lds.argtypes = [P, P, P, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                                        ctypes.POINTER(ctypes.c_float), P]
-    cus = torch.cuda.get_device_properties(dev).multi_processor_count
-    sink2 = torch.empty(cus * 512, dtype=torch.int32, device=dev)
-    t = torch.from_numpy(kinds["gaussian_sigma32"]).to(dev)
-    lds = {}
-    for reads in (0, 3, 6):
-        ms = ctypes.c_float(0)
-        rc = lib.w8a8_probe_mfma_lds(P(t.data_ptr()), P(sink2.data_ptr()), P(clk.data_ptr()),
-                                     iters * 4, reads, cus, ctypes.byref(ms),
-                                     P(torch.cuda.current_stream().cuda_stream))
-        assert rc == 0, rc
-        c = clk.cpu().tolist()
-        tops = cus * 8 * iters * 4 * 8 * 65536.0 / (ms.value * 1e-3) / 1e12
-        lds[f"lds_reads_per_8_mfma_{reads}"] = {
-            "TOPS": round(tops, 1), "frac_of_5000": round(tops / PEAK_INT8_TOPS, 4),
-            "clock_GHz": round(c[0] / (c[1] / 100e6) / 1e9, 3)}
-    print(json.dumps({"probe": "v_mfma_i32_32x32x32_i8 loop, 1 wave/SIMD, 8 accumulators",
-                      "results": out,
-                      "probe_lds": "same loop at 2 waves/SIMD, Gaussian codes, fragments from LDS",
-                      "results_lds": lds}))
 
 
 def probe_hbm():
@@ -313,88 +248,12 @@ def hbm_from(trace_dir, fetch_dir, write_dir):
     print(json.dumps(out, indent=1))
 
 
-def hbm_ceiling():
-    """Practical HBM streaming rates (read, write, copy, and the quantisers' 2:1
-    read:write mix) over 805 MiB buffers used in turn, at 4, 8 and 16 workgroups
-    of 256 threads per CU: the reachable part of the 8 TB/s spec."""
-    import ctypes
-
-    import torch
-
-    lib = ctypes.CDLL(os.path.join(ROOT, "int8_w8a8_gemm_amd", "libw8a8_probe.so"))
-    P = ctypes.c_void_p
-    lib.w8a8_probe_stream.argtypes = [ctypes.c_int, P, P, ctypes.c_int, ctypes.c_size_t,
-                                      ctypes.c_int, ctypes.c_int, P,
-                                      ctypes.POINTER(ctypes.c_float), P]
-    dev = torch.device("cuda:0")
-    nbytes = 805 << 20
-    n16 = nbytes // 16
-    src = [torch.ones(nbytes // 4, dtype=torch.int32, device=dev) for _ in range(3)]
-    dst = [torch.empty(nbytes // 4, dtype=torch.int32, device=dev) for _ in range(3)]
-    sp = (ctypes.c_void_p * 3)(*[t.data_ptr() for t in src])
-    dp = (ctypes.c_void_p * 3)(*[t.data_ptr() for t in dst])
-    sink = torch.zeros(1, dtype=torch.int32, device=dev)
-    cus = torch.cuda.get_device_properties(dev).multi_processor_count
-    moved = {0: 1.0, 1: 1.0, 2: 2.0, 3: 1.5}
-    names = {0: "read", 1: "write", 2: "copy", 3: "read2_write1"}
-    out = {}
-    for per_cu in (4, 8, 16):
-        for kind in range(4):
-            ms = ctypes.c_float(0)
-            rc = lib.w8a8_probe_stream(kind, sp, dp, 3, n16, cus * per_cu, 30, P(sink.data_ptr()),
-                                       ctypes.byref(ms), P(torch.cuda.current_stream().cuda_stream))
-            assert rc == 0, rc
-            tbs = moved[kind] * nbytes / (ms.value * 1e-3) / 1e12
-            out[f"{names[kind]}_wg{per_cu}_per_cu"] = {"us": round(ms.value * 1e3, 1),
-                                                       "TB/s": round(tbs, 2)}
-    print(json.dumps({"probe": "16-byte nontemporal streaming over 3 x 805 MiB buffers",
-                      "results": out}))
-
-
-def vendor():
-    """The vendor library's INT8 GEMM (torch._int_mm: hipBLASLt, INT8 -> INT32, no
-    scales, bias or bf16 output) beside this library's w8a8_gemm (bf16 output with
-    scales and bias) on the video GEMM shapes, same codes, alternating calls."""
-    import torch
-
-    import int8_w8a8_gemm_amd as w8
-
-    dev = torch.device("cuda:0")
-    gen = torch.Generator(device=dev).manual_seed(0)
-    out = {}
-    for name, (M, N, K) in {"ffn_up_24576x16384x4096": (24576, 16384, 4096),
-                            "ffn_down_24576x4096x16384": (24576, 4096, 16384),
-                            "attn_proj_24576x4096x4096": (24576, 4096, 4096)}.items():
-        qa, sa = w8.quantize_rows(torch.randn((M, K), device=dev, generator=gen).to(torch.bfloat16))
-        qw, sw = w8.quantize_rows((torch.randn((N, K), device=dev, generator=gen) * 0.02)
-                                  .to(torch.bfloat16))
-        bias = (torch.randn((N,), device=dev, generator=gen) * 0.01).to(torch.bfloat16)
-        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-        ours, theirs = [], []
-        for _ in range(3):
-            ours.append(_time(lambda: w8.gemm(qa, sa, qw, sw, bias, out=y), 10, torch))
-            theirs.append(_time(lambda: torch._int_mm(qa, qw.t()), 10, torch))
-        o, v = sorted(ours)[1], sorted(theirs)[1]
-        out[name] = {"w8a8_gemm_ms": round(o, 4), "w8a8_gemm_TOPS": round(2.0 * M * N * K / o / 1e9, 1),
-                     "int_mm_ms": round(v, 4), "int_mm_TOPS": round(2.0 * M * N * K / v / 1e9, 1)}
-        del qa, qw, y
-    print(json.dumps({"vendor": "torch._int_mm (hipBLASLt) vs w8a8_gemm, median of 3 x 10 calls",
-                      "results": out}))
 
 
 def main():
     args = parse()
     if args.traffic_from:
         traffic_from(*args.traffic_from)
-        return
-    if args.ceiling:
-        ceiling()
-        return
-    if args.vendor:
-        vendor()
-        return
-    if args.hbm_ceiling:
-        hbm_ceiling()
         return
     if args.probe_hbm:
         probe_hbm()
@@ -487,6 +346,18 @@ def main():
         return float(np.mean([events[i][a].elapsed_time(events[i][b]) for i in range(args.steps)]))
 
     t_qx, t_up, t_qh, t_down = avg(0, 1), avg(1, 2), avg(2, 3), avg(3, 4)
+    # medians over 50 more event-timed steps, run after the timed region (they
+    # do not enter `value` or ms_per_step)
+    NMED = 50
+    ev_med = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(NMED)]
+    for i in range(NMED):
+        step(ev_med[i])
+    torch.cuda.synchronize()
+
+    def med(a, b):
+        return float(np.median([ev_med[i][a].elapsed_time(ev_med[i][b]) for i in range(NMED)]))
+
+    m_qx, m_up, m_qh, m_down, m_step = med(0, 1), med(1, 2), med(2, 3), med(3, 4), med(0, 4)
     tops_up = ops_gemm / (t_up * 1e-3) / 1e12
     tops_down = ops_gemm / (t_down * 1e-3) / 1e12
     bytes_qx = 3.0 * M * D + 4.0 * M
@@ -528,16 +399,23 @@ def main():
                    "M": M, "D": D, "F": F, "act_up": "gelu_tanh", "parallelism": "single GPU"},
         "roofline": roofline,
         "kernels": {
-            "quantize_x": {"us": round(t_qx * 1e3, 2),
+            "timing": f"mean over the {args.steps} timed steps; median_* over {NMED} further "
+                      "event-timed steps run after them",
+            "quantize_x": {"us": round(t_qx * 1e3, 2), "median_us": round(m_qx * 1e3, 2),
                            "GB/s": round(bytes_qx / (t_qx * 1e-3) / 1e9, 1),
                            "frac_hbm": round(bytes_qx / (t_qx * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
-            "gemm_up": {"ms": round(t_up, 4), "TOPS": round(tops_up, 1),
-                        "frac_peak": round(tops_up / PEAK_INT8_TOPS, 4)},
-            "gelu_quantize_u": {"us": round(t_qh * 1e3, 2),
+            "gemm_up": {"ms": round(t_up, 4), "median_ms": round(m_up, 4),
+                        "TOPS": round(tops_up, 1),
+                        "frac_peak": round(tops_up / PEAK_INT8_TOPS, 4),
+                        "median_frac_peak": round(ops_gemm / (m_up * 1e-3) / 1e12 / PEAK_INT8_TOPS, 4)},
+            "gelu_quantize_u": {"us": round(t_qh * 1e3, 2), "median_us": round(m_qh * 1e3, 2),
                            "GB/s": round(bytes_qh / (t_qh * 1e-3) / 1e9, 1),
                            "frac_hbm": round(bytes_qh / (t_qh * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
-            "gemm_down": {"ms": round(t_down, 4), "TOPS": round(tops_down, 1),
-                          "frac_peak": round(tops_down / PEAK_INT8_TOPS, 4)},
+            "gemm_down": {"ms": round(t_down, 4), "median_ms": round(m_down, 4),
+                          "TOPS": round(tops_down, 1),
+                          "frac_peak": round(tops_down / PEAK_INT8_TOPS, 4),
+                          "median_frac_peak": round(ops_gemm / (m_down * 1e-3) / 1e12 / PEAK_INT8_TOPS, 4)},
+            "step_median_ms": round(m_step, 4),
         },
     }
 
@@ -762,6 +640,10 @@ def cpu_baseline(ffn, rows, np, log):
     t = run(rows)
     ops = 2 * (2.0 * rows * ffn.w1.shape[0] * ffn.w1.shape[1])
     return {"value": round(ops / t / 1e12, 6), "unit": "TOPS", "cores": threads, "kind": "oracle",
+            "threads": threads, "host_cores": os.cpu_count(),
+            "usable_cores": oracle.usable_cores(),
+            "omp_num_threads": os.environ.get("OMP_NUM_THREADS"),
+            "cpu_model": oracle.cpu_model(),
             "seconds": round(t, 2),
             "sample": f"first {rows} of {ffn.x.shape[0]} rows of the video FFN pair step "
                       f"(quantise, INT32 GEMM, epilogue, GELU + quantise, INT32 GEMM, epilogue)"}

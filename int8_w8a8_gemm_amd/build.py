@@ -22,9 +22,6 @@ LIB = os.path.join(HERE, "libw8a8.so")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 
 SOURCES = ["quantize_rows.hip", "compact_rows.hip", "gemm_tiled.hip", "gemm_bf16.hip", "w8a8_api.hip"]
-# measurement probe, a library of its own (not part of libw8a8's ABI)
-PROBE_SOURCES = ["probe_mfma.hip"]
-PROBE_LIB = os.path.join(HERE, "libw8a8_probe.so")
 ABI_CHECK_SRC = os.path.join(os.path.dirname(HERE), "tests", "c", "abi_check.cpp")
 ABI_CHECK = os.path.join(BUILD, "abi_check")
 ARCH = "gfx950"
@@ -72,12 +69,10 @@ def build(verbose: bool = False, jobs: int = 5) -> str:
         return obj
 
     with ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(compile_one, SOURCES + PROBE_SOURCES))
-    for lib, n in ((LIB, len(SOURCES)), (PROBE_LIB, None)):
-        part = objs[:n] if n is not None else objs[len(SOURCES):]
-        tmp = lib + ".tmp"
-        _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *part, "-o", tmp])
-        os.replace(tmp, lib)
+        objs = list(ex.map(compile_one, SOURCES))
+    tmp = LIB + ".tmp"
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
+    os.replace(tmp, LIB)
     # the C-ABI check program of the tests (uses the library with no PyTorch)
     _run([hipcc, "-O2", "-std=c++17", f"-I{INCLUDE}", ABI_CHECK_SRC, f"-L{HERE}", "-lw8a8",
           "-Wl,-rpath,$ORIGIN/..", "-o", ABI_CHECK])

@@ -75,14 +75,38 @@ def _load():
     return lib
 
 
-def default_threads() -> int:
-    """Host threads the oracle uses by default: the cores this process may run
-    on, capped at 16 (one GPU's share of a shared host)."""
+def usable_cores() -> int:
+    """Cores this process may run on (its CPU affinity set)."""
     try:
-        n = len(os.sched_getaffinity(0))
+        return len(os.sched_getaffinity(0))
     except AttributeError:  # pragma: no cover
-        n = os.cpu_count() or 1
-    return max(1, min(n, 16))
+        return os.cpu_count() or 1
+
+
+def default_threads() -> int:
+    """Host threads the oracle uses by default: every core this process may run
+    on, limited only where the host fixes the process's CPU share through
+    OMP_NUM_THREADS (a host shared between GPUs does)."""
+    n = usable_cores()
+    try:
+        share = int(os.environ.get("OMP_NUM_THREADS", "0"))
+    except ValueError:
+        share = 0
+    if share > 0:
+        n = min(n, share)
+    return max(1, n)
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (first "model name" line of /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.lower().startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return "unknown"
 
 
 def _threads(nthreads):
