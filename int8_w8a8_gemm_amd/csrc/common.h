@@ -122,6 +122,14 @@ int launch_norm_mod(const uint16_t* x, int64_t rows, int64_t cols, const uint16_
                     float* qscale, uint16_t* y, hipStream_t stream);
 int launch_compact_rows(const uint16_t* x, const uint8_t* mask, int64_t R, int64_t D,
                         uint16_t* out, int32_t* src_row, int32_t* count, hipStream_t stream);
+// Compaction up to this many rows takes one launch (its per-block prefix
+// rescans at most that many mask bytes); more rows take the linear-time path.
+bool compact_single_pass(int64_t R);
+// The linear-time path's scan: src_row and *count from the mask, with up to
+// scratch_ints int32 of scratch for the chunk counts (memory of an output that
+// only a later launch writes).
+int launch_compact_scan(const uint8_t* mask, int64_t R, int32_t* scratch, int64_t scratch_ints,
+                        int32_t* src_row, int32_t* count, hipStream_t stream);
 int launch_compact_quantize_rows(const uint16_t* x, const uint8_t* mask, int64_t R, int64_t D,
                                  int8_t* q, float* scale, int32_t* src_row, int32_t* count,
                                  hipStream_t stream);

@@ -394,22 +394,12 @@ __device__ __forceinline__ void cq_rank(const uint8_t* __restrict__ mask, int64_
     nvalid = __builtin_popcountll(bal);
 }
 
+// One wave quantises source row r of x [* x D] into output row m of q and
+// scale (the row held in registers, CPL 16-byte chunks per lane).
 template <int CPL>
-__global__ __launch_bounds__(kCqBlock) void compact_quantize_rows_vec(
-    const uint16_t* __restrict__ x, const uint8_t* __restrict__ mask, int64_t R, int64_t D,
-    int8_t* __restrict__ q, float* __restrict__ scale, int32_t* __restrict__ src_row,
-    int32_t* __restrict__ count, int mask_words) {
-    __shared__ int red[kCqRows];
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int64_t r0 = (int64_t)blockIdx.x * kCqRows;
-    int base, rank, nvalid;
-    bool valid;
-    cq_rank(mask, R, r0, mask_words, red, base, rank, nvalid, valid);
-    if (blockIdx.x == gridDim.x - 1 && threadIdx.x == 0) *count = base + nvalid;
-    if (!valid) return;
-    const int64_t r = r0 + wave, m = base + rank;
-    if (lane == 0) src_row[m] = (int32_t)r;
-
+__device__ __forceinline__ void cq_quantize_row_vec(const uint16_t* __restrict__ x, int64_t D,
+                                                    int64_t r, int64_t m, int8_t* __restrict__ q,
+                                                    float* __restrict__ scale, int lane) {
     const int64_t nchunk = D >> 3;
     const u32x4* xr = reinterpret_cast<const u32x4*>(x + r * D);
     u32x4 v[CPL];
@@ -437,8 +427,8 @@ __global__ __launch_bounds__(kCqBlock) void compact_quantize_rows_vec(
     }
 }
 
-// Any D and alignment: each wave reads its row twice, element by element.
-__global__ __launch_bounds__(kCqBlock) void compact_quantize_rows_generic(
+template <int CPL>
+__global__ __launch_bounds__(kCqBlock) void compact_quantize_rows_vec(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ mask, int64_t R, int64_t D,
     int8_t* __restrict__ q, float* __restrict__ scale, int32_t* __restrict__ src_row,
     int32_t* __restrict__ count, int mask_words) {
@@ -452,6 +442,27 @@ __global__ __launch_bounds__(kCqBlock) void compact_quantize_rows_generic(
     if (!valid) return;
     const int64_t r = r0 + wave, m = base + rank;
     if (lane == 0) src_row[m] = (int32_t)r;
+    cq_quantize_row_vec<CPL>(x, D, r, m, q, scale, lane);
+}
+
+// The linear-time path's last step: output rows m < *count quantised from
+// source rows src_row[m], one wave per row in a grid-stride loop.
+template <int CPL>
+__global__ __launch_bounds__(kCqBlock) void gather_quantize_rows_vec(
+    const uint16_t* __restrict__ x, int64_t D, const int32_t* __restrict__ src_row,
+    const int32_t* __restrict__ count, int8_t* __restrict__ q, float* __restrict__ scale) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t n = *count;
+    for (int64_t m = (int64_t)blockIdx.x * kCqRows + wave; m < n;
+         m += (int64_t)gridDim.x * kCqRows)
+        cq_quantize_row_vec<CPL>(x, D, (int64_t)src_row[m], m, q, scale, lane);
+}
+
+// Any D and alignment: each wave reads its row twice, element by element.
+__device__ __forceinline__ void cq_quantize_row_generic(const uint16_t* __restrict__ x, int64_t D,
+                                                        int64_t r, int64_t m,
+                                                        int8_t* __restrict__ q,
+                                                        float* __restrict__ scale, int lane) {
     const uint16_t* xr = x + r * D;
     int8_t* qr = q + m * D;
     uint32_t amax = 0;
@@ -469,12 +480,43 @@ __global__ __launch_bounds__(kCqBlock) void compact_quantize_rows_generic(
         qr[k] = (int8_t)quant1(__uint_as_float((uint32_t)xr[k] << 16), inv);
 }
 
+__global__ __launch_bounds__(kCqBlock) void compact_quantize_rows_generic(
+    const uint16_t* __restrict__ x, const uint8_t* __restrict__ mask, int64_t R, int64_t D,
+    int8_t* __restrict__ q, float* __restrict__ scale, int32_t* __restrict__ src_row,
+    int32_t* __restrict__ count, int mask_words) {
+    __shared__ int red[kCqRows];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t r0 = (int64_t)blockIdx.x * kCqRows;
+    int base, rank, nvalid;
+    bool valid;
+    cq_rank(mask, R, r0, mask_words, red, base, rank, nvalid, valid);
+    if (blockIdx.x == gridDim.x - 1 && threadIdx.x == 0) *count = base + nvalid;
+    if (!valid) return;
+    const int64_t r = r0 + wave, m = base + rank;
+    if (lane == 0) src_row[m] = (int32_t)r;
+    cq_quantize_row_generic(x, D, r, m, q, scale, lane);
+}
+
+__global__ __launch_bounds__(kCqBlock) void gather_quantize_rows_generic(
+    const uint16_t* __restrict__ x, int64_t D, const int32_t* __restrict__ src_row,
+    const int32_t* __restrict__ count, int8_t* __restrict__ q, float* __restrict__ scale) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t n = *count;
+    for (int64_t m = (int64_t)blockIdx.x * kCqRows + wave; m < n;
+         m += (int64_t)gridDim.x * kCqRows)
+        cq_quantize_row_generic(x, D, (int64_t)src_row[m], m, q, scale, lane);
+}
+
 template <int CPL>
 hipError_t launch_cq(const uint16_t* x, const uint8_t* mask, int64_t R, int64_t D, int8_t* q,
                      float* scale, int32_t* src_row, int32_t* count, int mask_words,
-                     int64_t blocks, hipStream_t stream) {
-    hipLaunchKernelGGL(compact_quantize_rows_vec<CPL>, dim3((unsigned)blocks), dim3(kCqBlock), 0,
-                       stream, x, mask, R, D, q, scale, src_row, count, mask_words);
+                     int64_t blocks, bool gather, hipStream_t stream) {
+    if (gather)
+        hipLaunchKernelGGL(gather_quantize_rows_vec<CPL>, dim3((unsigned)blocks), dim3(kCqBlock), 0,
+                           stream, x, D, src_row, count, q, scale);
+    else
+        hipLaunchKernelGGL(compact_quantize_rows_vec<CPL>, dim3((unsigned)blocks), dim3(kCqBlock),
+                           0, stream, x, mask, R, D, q, scale, src_row, count, mask_words);
     return hipGetLastError();
 }
 
@@ -840,20 +882,37 @@ hipError_t launch_nm_any(const uint16_t* x, int64_t rows, int64_t cols, const ui
 int launch_compact_quantize_rows(const uint16_t* x, const uint8_t* mask, int64_t R, int64_t D,
                                  int8_t* q, float* scale, int32_t* src_row, int32_t* count,
                                  hipStream_t stream) {
-    const int64_t blocks = R > 0 ? (R + kCqRows - 1) / kCqRows : 1;
+    int64_t blocks = R > 0 ? (R + kCqRows - 1) / kCqRows : 1;
     const int mask_words = reinterpret_cast<uintptr_t>(mask) % 4 == 0 ? 1 : 0;
+    const bool gather = !compact_single_pass(R);
+    if (gather) {
+        // the linear-time path: src_row and *count first (the chunk counts kept
+        // in scale, which only the quantisation below writes), then the rows
+        // they list are quantised in a grid-stride loop
+        if (launch_compact_scan(mask, R, reinterpret_cast<int32_t*>(scale), R, src_row, count,
+                                stream) != 0)
+            return -1;
+        const int cus = cu_count();
+        if (cus <= 0) return -1;
+        if (blocks > (int64_t)cus * 16) blocks = (int64_t)cus * 16;
+    }
     const bool vec = D > 0 && D % 8 == 0 && reinterpret_cast<uintptr_t>(x) % 16 == 0 &&
                      reinterpret_cast<uintptr_t>(q) % 8 == 0;
     const int64_t nchunk = D / 8;
     hipError_t e;
-    if (vec && nchunk <= 64) e = launch_cq<1>(x, mask, R, D, q, scale, src_row, count, mask_words, blocks, stream);
-    else if (vec && nchunk <= 128) e = launch_cq<2>(x, mask, R, D, q, scale, src_row, count, mask_words, blocks, stream);
-    else if (vec && nchunk <= 256) e = launch_cq<4>(x, mask, R, D, q, scale, src_row, count, mask_words, blocks, stream);
-    else if (vec && nchunk <= 512) e = launch_cq<8>(x, mask, R, D, q, scale, src_row, count, mask_words, blocks, stream);
-    else if (vec && nchunk <= 1024) e = launch_cq<16>(x, mask, R, D, q, scale, src_row, count, mask_words, blocks, stream);
+    if (vec && nchunk <= 64) e = launch_cq<1>(x, mask, R, D, q, scale, src_row, count, mask_words, blocks, gather, stream);
+    else if (vec && nchunk <= 128) e = launch_cq<2>(x, mask, R, D, q, scale, src_row, count, mask_words, blocks, gather, stream);
+    else if (vec && nchunk <= 256) e = launch_cq<4>(x, mask, R, D, q, scale, src_row, count, mask_words, blocks, gather, stream);
+    else if (vec && nchunk <= 512) e = launch_cq<8>(x, mask, R, D, q, scale, src_row, count, mask_words, blocks, gather, stream);
+    else if (vec && nchunk <= 1024) e = launch_cq<16>(x, mask, R, D, q, scale, src_row, count, mask_words, blocks, gather, stream);
     else {
-        hipLaunchKernelGGL(compact_quantize_rows_generic, dim3((unsigned)blocks), dim3(kCqBlock), 0,
-                           stream, x, mask, R, D, q, scale, src_row, count, mask_words);
+        if (gather)
+            hipLaunchKernelGGL(gather_quantize_rows_generic, dim3((unsigned)blocks), dim3(kCqBlock),
+                               0, stream, x, D, src_row, count, q, scale);
+        else
+            hipLaunchKernelGGL(compact_quantize_rows_generic, dim3((unsigned)blocks),
+                               dim3(kCqBlock), 0, stream, x, mask, R, D, q, scale, src_row, count,
+                               mask_words);
         e = hipGetLastError();
     }
     return e == hipSuccess ? 0 : -1;

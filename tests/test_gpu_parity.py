@@ -1309,3 +1309,53 @@ def test_compaction_commutes_with_linear_on_gpu():
     y2, _, cnt2 = w8.compact_padded_rows(yfull, md)
     assert int(cnt2.item()) == n
     assert np.array_equal(y1, h_u16(y2[:n]))
+
+
+def _general_mask(rng, R):
+    """A general mask: runs of valid and padded rows of random lengths (1 .. 3000),
+    nonzero values other than 1, and scattered single flips."""
+    m = np.zeros(R, np.uint8)
+    i, on = 0, bool(rng.integers(0, 2))
+    while i < R:
+        n = int(rng.integers(1, 3000))
+        if on:
+            m[i:i + n] = rng.integers(1, 256, min(n, R - i)).astype(np.uint8)
+        i += n
+        on = not on
+    flips = rng.choice(R, R // 50, replace=False)
+    m[flips] = np.where(m[flips] != 0, 0, 7).astype(np.uint8)
+    return m
+
+
+# The linear-time compaction path (more than 8192 rows: chunk counts, chunk
+# scans, then the gather), against the oracle: 64 x 8192 rows with a general
+# mask on the 16-byte and element paths, all / no rows valid, the first sizes
+# past the single-launch path, and an unaligned mask (byte-wise chunk scans).
+@pytest.mark.parametrize("B,L,D,kind,mask_off", [
+    (64, 8192, 64, "general", 0), (64, 8192, 20, "general", 0), (16, 8192, 8, "all", 0),
+    (16, 8192, 8, "none", 0), (1, 8193, 8, "general", 0), (2, 4100, 16, "general", 1),
+    (3, 100003, 8, "general", 3), (1, 8192, 8, "general", 0)])
+def test_compaction_linear_path_matches_oracle(B, L, D, kind, mask_off):
+    say(f"compact linear path B={B} L={L} D={D} {kind} mask offset {mask_off}")
+    rng = np.random.default_rng(B + L + D + mask_off)
+    R = B * L
+    x = wl.to_bf16_bits(rng.standard_normal((R, D)).astype(np.float32))
+    mask = {"general": lambda: _general_mask(rng, R), "all": lambda: np.ones(R, np.uint8),
+            "none": lambda: np.zeros(R, np.uint8)}[kind]().reshape(B, L)
+    mbuf = torch.zeros(R + 16, dtype=torch.uint8, device=DEV)
+    mbuf[mask_off:mask_off + R] = torch.from_numpy(mask.ravel()).to(DEV)
+    md = mbuf[mask_off:mask_off + R].view(B, L)
+    xd = d_bf16(x).view(B, L, D)
+    out, src, cnt = w8.compact_padded_rows(xd, md)
+    n = int(cnt.item())
+    o_out, o_src, o_n = oracle.compact_rows(x.reshape(B, L, D), mask)
+    assert n == o_n
+    assert np.array_equal(h(src)[:n], o_src)
+    assert np.array_equal(h_u16(out[:n]), o_out)
+    q, sc, src2, cnt2 = w8.compact_quantize_rows(xd, md)
+    assert int(cnt2.item()) == n
+    assert np.array_equal(h(src2)[:n], o_src)
+    if n:
+        qo, so = oracle.quantize_rows(o_out)
+        assert np.array_equal(h(sc)[:n].view(np.uint32), so.view(np.uint32))
+        assert np.array_equal(h(q)[:n], qo)
