@@ -43,7 +43,8 @@ typedef enum {
     W8A8_OK = 0,
     W8A8_EINVAL = -1,       /* bad argument: NULL, negative size, misalignment, combo */
     W8A8_EUNSUPPORTED = -2, /* shape the INT8 GEMM does not serve (see w8a8_guard)     */
-    W8A8_EHIP = -3          /* a HIP launch failed                                     */
+    W8A8_EHIP = -3,         /* a HIP launch failed                                     */
+    W8A8_ESCRATCH = -4      /* input beyond the static scratch of w8a8_linear_noalloc  */
 } w8a8_status;
 
 typedef enum { W8A8_OUT_BF16 = 0, W8A8_OUT_I32 = 1 } w8a8_out;
@@ -223,6 +224,31 @@ W8A8_API int w8a8_gemm(const int8_t* qa, const float* sa, int64_t M, const int8_
 W8A8_API int w8a8_linear(const uint16_t* x, int64_t M, int64_t K, int64_t N, const int8_t* qw,
                 const float* sw, const uint16_t* w, const uint16_t* bias, int act, uint16_t* y,
                 void* workspace, size_t workspace_bytes, int* path_taken, void* stream);
+
+/* Size of the device scratch array of w8a8_linear_noalloc (64 MiB per GPU). */
+#define W8A8_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/*
+ * w8a8_linear without a workspace argument, for callers that cannot allocate
+ * device memory: code being captured into a HIP graph, tight serving loops,
+ * harnesses that forbid hipMalloc.  Arguments, result and routing are those of
+ * w8a8_linear.  The INT8 path's workspace (x's codes and row scales) is a
+ * static device array of W8A8_NOALLOC_SCRATCH_BYTES in the library, one per
+ * GPU, held from the first call on that GPU until the process ends; its device
+ * address is looked up on that first call (hipGetSymbolAddress).  No call
+ * allocates or frees anything.
+ *
+ * Limits: w8a8_linear_workspace_bytes(M, K) must not exceed
+ * W8A8_NOALLOC_SCRATCH_BYTES (returns W8A8_ESCRATCH and launches nothing).
+ * Every call on one GPU uses that GPU's array, and it keeps what the last call
+ * wrote (each call writes all it reads, so nothing needs clearing): calls that
+ * overlap on one GPU (on two streams, or two threads) race and must be
+ * serialised by the caller.  The BF16 path uses no scratch.
+ */
+W8A8_API int w8a8_linear_noalloc(const uint16_t* x, int64_t M, int64_t K, int64_t N,
+                                 const int8_t* qw, const float* sw, const uint16_t* w,
+                                 const uint16_t* bias, int act, uint16_t* y, int* path_taken,
+                                 void* stream);
 
 /*
  * Native BF16 linear, the fallback of the guarded layer (section 01.3: branches

@@ -23,16 +23,18 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libw8a8.so")
 
-OK, EINVAL, EUNSUPPORTED, EHIP = 0, -1, -2, -3
+OK, EINVAL, EUNSUPPORTED, EHIP, ESCRATCH = 0, -1, -2, -3, -4
 OUT_BF16, OUT_I32 = 0, 1
 ACT_NONE, ACT_GELU_TANH = 0, 1
 PATH_INT8, PATH_BF16 = 0, 1
 NORM_LAYER, NORM_RMS = 0, 1
 MAX_K = 131072
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 EXPORTS = ("w8a8_quantize_rows", "w8a8_quantize_blocks", "w8a8_gelu_quantize_rows", "w8a8_gelu_bf16", "w8a8_gemm", "w8a8_linear", "w8a8_linear_bf16",
            "compact_padded_rows", "w8a8_compact_quantize_rows", "w8a8_guard", "w8a8_linear_workspace_bytes",
-           "w8a8_status_str", "w8a8_norm_mod_bf16", "w8a8_norm_mod_quantize_rows")
+           "w8a8_status_str", "w8a8_norm_mod_bf16", "w8a8_norm_mod_quantize_rows",
+           "w8a8_linear_noalloc")
 
 _lib = None
 
@@ -62,6 +64,7 @@ def lib():
     L.w8a8_gemm.argtypes = [P, P, I64, P, P, I64, I64, P, I, I, P, P]
     L.w8a8_linear.argtypes = [P, I64, I64, I64, P, P, P, P, I, P, P, SZ, P, P]
     L.w8a8_linear_bf16.argtypes = [P, I64, I64, P, I64, P, I, P, P]
+    L.w8a8_linear_noalloc.argtypes = [P, I64, I64, I64, P, P, P, P, I, P, P, P]
     L.compact_padded_rows.argtypes = [P, P, I64, I64, I64, P, P, P, P]
     L.w8a8_compact_quantize_rows.argtypes = [P, P, I64, I64, I64, P, P, P, P, P]
     L.w8a8_guard.argtypes = [I64, I64]
@@ -70,7 +73,7 @@ def lib():
     L.w8a8_status_str.argtypes = [I]
     L.w8a8_status_str.restype = ctypes.c_char_p
     for name in ("w8a8_quantize_rows", "w8a8_gelu_quantize_rows", "w8a8_gemm", "w8a8_linear", "w8a8_linear_bf16",
-                 "compact_padded_rows", "w8a8_guard"):
+                 "compact_padded_rows", "w8a8_guard", "w8a8_linear_noalloc"):
         getattr(L, name).restype = I
     _lib = L
     return L
@@ -332,6 +335,30 @@ def linear(x, N, qw=None, sw=None, w=None, bias=None, act=ACT_NONE, y=None, work
     _check("w8a8_linear", lib().w8a8_linear(
         _p(x), M, K, N, _p(qw), _p(sw), _p(w), _p(bias), int(act), _p(y), _p(workspace),
         workspace.numel() if workspace is not None else 0, ctypes.byref(path), _stream(stream)))
+    return y, path.value
+
+
+def linear_noalloc(x, N, qw=None, sw=None, w=None, bias=None, act=ACT_NONE, y=None, stream=None):
+    """The guarded W8A8 linear with the INT8 path's workspace in the library's static
+    device scratch (w8a8_linear_noalloc: nothing is allocated by the call).  Returns
+    (y bf16 [M, N], path).  Calls that overlap on one GPU race on the scratch."""
+    _need(x, "x", torch.bfloat16)
+    M, K = x.shape
+    if qw is not None:
+        _need(qw, "qw", torch.int8, (N, K))
+    if sw is not None:
+        _need(sw, "sw", torch.float32, (N,))
+    if w is not None:
+        _need(w, "w", torch.bfloat16, (N, K))
+    if bias is not None:
+        _need(bias, "bias", torch.bfloat16, (N,))
+    with _on(stream):
+        y = y if y is not None else torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _need(y, "y", torch.bfloat16, (M, N))
+    path = ctypes.c_int(-1)
+    _check("w8a8_linear_noalloc", lib().w8a8_linear_noalloc(
+        _p(x), M, K, N, _p(qw), _p(sw), _p(w), _p(bias), int(act), _p(y), ctypes.byref(path),
+        _stream(stream)))
     return y, path.value
 
 

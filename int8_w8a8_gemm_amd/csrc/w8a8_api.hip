@@ -6,6 +6,8 @@
 #include "../../include/w8a8.h"
 #include "common.h"
 
+#include <atomic>
+
 namespace {
 
 constexpr int64_t kMaxRows = (int64_t)1 << 31;  // grid limits of the row-wise kernels
@@ -37,6 +39,7 @@ const char* w8a8_status_str(int status) {
         case W8A8_EINVAL: return "invalid argument";
         case W8A8_EUNSUPPORTED: return "shape not supported by the INT8 GEMM";
         case W8A8_EHIP: return "HIP launch failed";
+        case W8A8_ESCRATCH: return "input larger than the no-allocation scratch";
         default: return "unknown status";
     }
 }
@@ -151,22 +154,48 @@ int w8a8_linear_bf16(const uint16_t* x, int64_t M, int64_t K, const uint16_t* w,
     return launched(w8a8::launch_gemm_bf16(x, M, K, w, N, bias, act, y, as_stream(stream)));
 }
 
-int w8a8_linear(const uint16_t* x, int64_t M, int64_t K, int64_t N, const int8_t* qw,
+}  // extern "C"
+
+namespace {
+// The checks of the guarded linear's arguments other than the workspace, for
+// the path the guard picks (int8); W8A8_OK if they pass.
+int linear_args(const uint16_t* x, int64_t M, int64_t K, int64_t N, const int8_t* qw,
                 const float* sw, const uint16_t* w, const uint16_t* bias, int act, uint16_t* y,
-                void* workspace, size_t workspace_bytes, int* path_taken, void* stream) {
+                bool int8) {
     if (M < 0 || N < 0 || K < 0 || M >= kMaxRows) return W8A8_EINVAL;
     if (!act_ok(act)) return W8A8_EINVAL;
-    const bool int8 = w8a8_guard(N, K) != 0;
     if (int8) {
         if (!qw || !sw) return W8A8_EINVAL;
         if (M > 0) {
             if (!x || !y || !aligned(x, 2) || !aligned(y, 16)) return W8A8_EINVAL;
             if (!aligned(qw, 16) || !aligned(sw, 4) || (bias && !aligned(bias, 2)))
                 return W8A8_EINVAL;
-            if (!workspace || !aligned(workspace, 256) ||
-                workspace_bytes < w8a8_linear_workspace_bytes(M, K))
-                return W8A8_EINVAL;
         }
+        return W8A8_OK;
+    }
+    if (!w && M > 0 && N > 0 && K > 0) return W8A8_EINVAL;
+    if (M > 0 && N > 0) {
+        if (!y || !aligned(y, 2)) return W8A8_EINVAL;
+        if (K > 0 && (!x || !aligned(x, 2) || !aligned(w, 2))) return W8A8_EINVAL;
+        if (bias && !aligned(bias, 2)) return W8A8_EINVAL;
+        if (N >= kMaxRows) return W8A8_EINVAL;
+    }
+    return W8A8_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int w8a8_linear(const uint16_t* x, int64_t M, int64_t K, int64_t N, const int8_t* qw,
+                const float* sw, const uint16_t* w, const uint16_t* bias, int act, uint16_t* y,
+                void* workspace, size_t workspace_bytes, int* path_taken, void* stream) {
+    const bool int8 = w8a8_guard(N, K) != 0;
+    const int st = linear_args(x, M, K, N, qw, sw, w, bias, act, y, int8);
+    if (st != W8A8_OK) return st;
+    if (int8) {
+        if (M > 0 && (!workspace || !aligned(workspace, 256) ||
+                      workspace_bytes < w8a8_linear_workspace_bytes(M, K)))
+            return W8A8_EINVAL;
         if (path_taken) *path_taken = W8A8_PATH_INT8;
         if (M == 0) return W8A8_OK;
         int8_t* qx = static_cast<int8_t*>(workspace);
@@ -176,16 +205,53 @@ int w8a8_linear(const uint16_t* x, int64_t M, int64_t K, int64_t N, const int8_t
         if (w8a8::launch_quantize_rows(x, M, K, qx, sx, s) != 0) return W8A8_EHIP;
         return launched(w8a8::launch_gemm_i8(qx, sx, M, qw, sw, N, K, bias, act, W8A8_OUT_BF16, y, s));
     }
-    if (!w && M > 0 && N > 0 && K > 0) return W8A8_EINVAL;
-    if (M > 0 && N > 0) {
-        if (!y || !aligned(y, 2)) return W8A8_EINVAL;
-        if (K > 0 && (!x || !aligned(x, 2) || !aligned(w, 2))) return W8A8_EINVAL;
-        if (bias && !aligned(bias, 2)) return W8A8_EINVAL;
-        if (N >= kMaxRows) return W8A8_EINVAL;
-    }
     if (path_taken) *path_taken = W8A8_PATH_BF16;
     if (M == 0 || N == 0) return W8A8_OK;
     return launched(w8a8::launch_gemm_bf16(x, M, K, w, N, bias, act, y, as_stream(stream)));
+}
+
+}  // extern "C"
+
+// ---- the no-allocation variant of w8a8_linear ----
+// The INT8 path's workspace in a static device array: each GPU the library
+// runs on holds its own copy, at its own address, until the process ends.
+// Host code never uses the array's name as an address (on the host it is only
+// a stand-in for the symbol); it uses the device address looked up below.
+static __device__ __align__(256) unsigned char scratch[W8A8_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void*> scratch_address[kMaxDevices];
+
+// Device address of the current device's scratch, looked up on the first call
+// on that device (with it current) and kept; NULL on failure.
+void* device_scratch() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    void* p = scratch_address[dev].load(std::memory_order_acquire);
+    if (p) return p;
+    void* q = nullptr;
+    if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || q == nullptr) return nullptr;
+    scratch_address[dev].store(q, std::memory_order_release);
+    return q;
+}
+}  // namespace
+
+extern "C" {
+
+int w8a8_linear_noalloc(const uint16_t* x, int64_t M, int64_t K, int64_t N, const int8_t* qw,
+                        const float* sw, const uint16_t* w, const uint16_t* bias, int act,
+                        uint16_t* y, int* path_taken, void* stream) {
+    const bool int8 = w8a8_guard(N, K) != 0;
+    const int st = linear_args(x, M, K, N, qw, sw, w, bias, act, y, int8);
+    if (st != W8A8_OK) return st;
+    if (!int8 || M == 0)  // BF16 path or nothing to do: no scratch
+        return w8a8_linear(x, M, K, N, qw, sw, w, bias, act, y, nullptr, 0, path_taken, stream);
+    const size_t need = w8a8_linear_workspace_bytes(M, K);
+    if (need > (size_t)W8A8_NOALLOC_SCRATCH_BYTES) return W8A8_ESCRATCH;
+    void* ws = device_scratch();
+    if (!ws) return W8A8_EHIP;
+    return w8a8_linear(x, M, K, N, qw, sw, w, bias, act, y, ws, need, path_taken, stream);
 }
 
 int compact_padded_rows(const uint16_t* x, const uint8_t* mask, int64_t B, int64_t L, int64_t D,

@@ -51,6 +51,30 @@ def test_workspace_bytes():
     assert w8.linear_workspace_bytes(M, K) == M * K + 4 * M
 
 
+def test_linear_noalloc_rejects_on_the_host():
+    """Inputs beyond the static scratch return ESCRATCH, bad arguments EINVAL,
+    before any HIP call (the pointers are never dereferenced)."""
+    L = w8.lib()
+    path = ctypes.c_int(-7)
+
+    def lin(x, M, K, N, qw, sw, w, b, act, y):
+        return L.w8a8_linear_noalloc(x, M, K, N, qw, sw, w, b, act, y, ctypes.byref(path), NULL)
+
+    K = 4096
+    M_max = w8.NOALLOC_SCRATCH_BYTES // (K + 4)
+    assert w8.linear_workspace_bytes(M_max, K) <= w8.NOALLOC_SCRATCH_BYTES
+    assert w8.linear_workspace_bytes(M_max + 64, K) > w8.NOALLOC_SCRATCH_BYTES
+    assert lin(A16, M_max + 64, K, 64, A16, A16, NULL, NULL, 0, A16) == w8.ESCRATCH
+    assert lin(A16, -1, K, 64, A16, A16, NULL, NULL, 0, A16) == w8.EINVAL
+    assert lin(A16, 1 << 31, K, 64, A16, A16, NULL, NULL, 0, A16) == w8.EINVAL
+    assert lin(A16, 4, 130, 64, NULL, NULL, NULL, NULL, 0, A16) == w8.EINVAL  # BF16 path needs w
+    assert lin(A16, 4, 128, 64, A16, A16, NULL, NULL, 3, A16) == w8.EINVAL    # bad act
+    path.value = -7
+    assert lin(NULL, 0, 128, 64, A16, A16, NULL, NULL, 0, NULL) == w8.OK      # empty
+    assert path.value == w8.PATH_INT8
+    assert "scratch" in w8.status_str(w8.ESCRATCH)
+
+
 def test_status_strings():
     assert w8.status_str(0) == "ok"
     assert "invalid" in w8.status_str(-1)
