@@ -55,6 +55,12 @@ def parse():
                         "rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs, then exit")
     p.add_argument("--probe-hbm", action="store_true",
                    help="run the HBM-bound kernels on their workloads (for rocprofv3)")
+    p.add_argument("--probe-small", action="store_true",
+                   help="run the small MFMA-bound kernels (audio 2048^3 and text-projection INT8 "
+                        "GEMMs, both BF16 fallbacks) on their workloads (for rocprofv3)")
+    p.add_argument("--power-clock", action="store_true",
+                   help="sample the GPU's gfx clock and socket power (amdsmi) while each main "
+                        "kernel runs back to back; print JSON, exit")
     p.add_argument("--hbm-from", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                    help="achieved HBM rate per kernel from rocprofv3 runs of --probe-hbm")
     p.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -137,7 +143,8 @@ def traffic_from(fetch_dir, write_dir):
 
 
 def probe_hbm():
-    """The HBM-bound kernels, each 5 times on its workload, for rocprofv3 (kernel trace,
+    """The HBM-bound kernels, each REPS times back to back on its workload (the median
+    launch of a kernel is then one at settled clocks), for rocprofv3 (kernel trace,
     FETCH_SIZE, WRITE_SIZE): the row quantiser on 4 rotating X [24576 x 4096] (then the
     norm + modulation, fused with the quantiser and alone, on the same inputs), GELU +
     quantise of U [24576 x 16384], the per-block Q / K quantiser (24576 tokens x 32 heads
@@ -150,6 +157,7 @@ def probe_hbm():
     import workloads as wl
 
     dev = torch.device("cuda:0")
+    REPS = 30
     src = torch.zeros((COPY_BYTES // 2,), dtype=torch.bfloat16, device=dev)
     dst = torch.empty_like(src)
     for _ in range(3):
@@ -160,25 +168,25 @@ def probe_hbm():
     xs = [torch.randn((M, K), device=dev, generator=gen).to(torch.bfloat16) for _ in range(4)]
     qs = [torch.empty((M, K), dtype=torch.int8, device=dev) for _ in range(4)]
     ss = [torch.empty((M,), dtype=torch.float32, device=dev) for _ in range(4)]
-    for i in range(5):
+    for i in range(REPS):
         w8.quantize_rows(xs[i % 4], qs[i % 4], ss[i % 4])
     for blk in (128, 64):
         sb = torch.empty((1, -(-M // blk), 32), dtype=torch.float32, device=dev)
-        for i in range(5):
+        for i in range(REPS):
             w8.quantize_blocks(xs[i % 4], 1, 32, blk, q=qs[i % 4], scale=sb)
     mods = [(torch.randn((8, K), device=dev, generator=gen) * 0.3).to(torch.bfloat16)
             for _ in range(2)]
-    for i in range(5):
+    for i in range(REPS):
         w8.norm_mod_quantize_rows(xs[i % 4], mods[0], mods[1], M // 8, q=qs[i % 4],
                                   qscale=ss[i % 4])
     y = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
-    for i in range(5):
+    for i in range(REPS):
         w8.norm_mod_bf16(xs[i % 4], mods[0], mods[1], M // 8, y=y)
     del xs, qs, ss, y
     u = (torch.randn((M, 16384), device=dev, generator=gen) * 0.64).to(torch.bfloat16)
     qh = torch.empty((M, 16384), dtype=torch.int8, device=dev)
     sh = torch.empty((M,), dtype=torch.float32, device=dev)
-    for _ in range(5):
+    for _ in range(REPS):
         w8.gelu_quantize_rows(u, qh, sh)
     del u, qh, sh
     g = wl.guarded_mixed()
@@ -191,12 +199,219 @@ def probe_hbm():
     sb = torch.empty((B * L,), dtype=torch.float32, device=dev)
     src_row = torch.empty((B * L,), dtype=torch.int32, device=dev)
     cnt = torch.empty((1,), dtype=torch.int32, device=dev)
-    for _ in range(5):
+    for _ in range(REPS):
         w8.compact_padded_rows(xd, md, buf, src_row, cnt)
-    for _ in range(5):
+    for _ in range(REPS):
         w8.compact_quantize_rows(xd, md, qb, sb, src_row, cnt)
     torch.cuda.synchronize()
     log(f"hbm probe done (text rows kept: {int(cnt.item())})")
+
+
+def _small_workloads(torch, w8, wl, np, dev):
+    """Operands of the small MFMA-bound kernels, as the bench's extras build them:
+    the audio GEMM 2048^3 on quantised N(0,1) activations and N(0, 0.02^2)
+    weights, the text projection on the fused compaction + quantisation's codes
+    of the text rows [8 x 512 x 4096], and both BF16 fallbacks."""
+    gen = torch.Generator(device=dev).manual_seed(0)
+    out = {}
+    xa = torch.randn((2048, 2048), device=dev, generator=gen).to(torch.bfloat16)
+    wa = (torch.randn((2048, 2048), device=dev, generator=gen) * 0.02).to(torch.bfloat16)
+    qa, sa = w8.quantize_rows(xa)
+    qw, sw = w8.quantize_rows(wa)
+    ba = (torch.randn((2048,), device=dev, generator=gen) * 0.01).to(torch.bfloat16)
+    ya = torch.empty((2048, 2048), dtype=torch.bfloat16, device=dev)
+    out["gemm_audio_2048^3"] = (lambda: w8.gemm(qa, sa, qw, sw, ba, out=ya), 2.0 * 2048 ** 3, "int8")
+    g = wl.guarded_mixed()
+    B, L, Dm = g.x.shape
+
+    def d(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    xd = d(g.x.reshape(B * L, Dm)).view(B, L, Dm)
+    md = torch.from_numpy(g.mask).to(dev)
+    qb, sb, src, cnt = w8.compact_quantize_rows(xd, md)
+    mc = int(cnt.item())
+    lw = w8.W8A8Linear.prepare(d(g.w), d(g.b))
+    yc = torch.empty((mc, 4096), dtype=torch.bfloat16, device=dev)
+    out["gemm_int8_text_Mc_x4096x4096"] = (
+        lambda: w8.gemm(qb[:mc], sb[:mc], lw.qw, lw.sw, lw.bias, out=yc), 2.0 * mc * 4096 * 4096, "int8")
+    buf, _, _ = w8.compact_padded_rows(xd, md)
+    xc = buf[:mc]
+    wfa, bfa = d(g.w_a), d(g.b_a)
+    yfa = torch.empty((mc, 4100), dtype=torch.bfloat16, device=dev)
+    out["fallback_bf16_N4100"] = (lambda: w8.linear_bf16(xc, wfa, bfa, y=yfa),
+                                  2.0 * mc * 4100 * 4096, "bf16")
+    xb, wfb, bfb = d(g.x_b), d(g.w_b), d(g.b_b)
+    yfb = torch.empty((2048, 2048), dtype=torch.bfloat16, device=dev)
+    out["fallback_bf16_K2050"] = (lambda: w8.linear_bf16(xb, wfb, bfb, y=yfb),
+                                  2.0 * 2048 * 2048 * 2050, "bf16")
+    return out, mc
+
+
+def probe_small():
+    """The small MFMA-bound kernels, each 10 times back to back on its workload,
+    for rocprofv3 (kernel trace and counters)."""
+    import numpy as np
+    import torch
+
+    import int8_w8a8_gemm_amd as w8
+    import workloads as wl
+
+    dev = torch.device("cuda:0")
+    work, mc = _small_workloads(torch, w8, wl, np, dev)
+    for name, (fn, _, _) in work.items():
+        for _ in range(10):
+            fn()
+        torch.cuda.synchronize()
+        log(f"probe-small: {name} done")
+    log(f"probe-small done (text rows kept: {mc})")
+
+
+def power_clock():
+    """Shader clock and package power while each main kernel runs back to back for
+    1.5 s.  A thread reads amdsmi's GPU metrics table every ~5 ms and keeps each
+    new table (its firmware timestamp changed): gfx clock of every XCD, the energy
+    accumulator, and the accumulated time the package power tracking (PPT) limit
+    held the clock down.  Reported per kernel: mean clock, power from the energy
+    accumulator over the window, the share of the window spent PPT-limited, and
+    the rate as a fraction of the peak at the measured clock."""
+    import threading
+
+    import amdsmi
+    import numpy as np
+    import torch
+
+    import int8_w8a8_gemm_amd as w8
+    import workloads as wl
+
+    amdsmi.amdsmi_init()
+    handle = amdsmi.amdsmi_get_processor_handles()[0]
+    dev = torch.device("cuda:0")
+    info = {}
+    try:
+        cap = amdsmi.amdsmi_get_power_cap_info(handle)
+        info["power_cap_W"] = float(cap.get("power_cap", 0)) / 1e6
+    except Exception as e:  # pragma: no cover - depends on the driver
+        info["power_cap_error"] = repr(e)
+    try:
+        e = amdsmi.amdsmi_get_energy_count(handle)
+        info["energy_counter_resolution_uJ"] = float(e.get("counter_resolution", 0.0))
+    except Exception as e:  # pragma: no cover
+        info["energy_error"] = repr(e)
+    res_uj = info.get("energy_counter_resolution_uJ") or 15.3
+
+    def num(v):
+        return float(v) if isinstance(v, (int, float)) else None
+
+    def snapshot():
+        m = amdsmi.amdsmi_get_gpu_metrics_info(handle)
+        clks = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, (int, float)) and 0 < c < 10000]
+        return {"ts": num(m.get("system_clock_counter")), "energy": num(m.get("energy_accumulator")),
+                "ppt": num(m.get("ppt_residency_acc")), "acc": num(m.get("accumulation_counter")),
+                "clk": float(np.mean(clks)) if clks else num(m.get("current_gfxclk")),
+                "power": num(m.get("current_socket_power"))}
+
+    def run(fn, seconds=1.5):
+        snaps = []
+        stop = threading.Event()
+
+        def sampler():
+            last = None
+            while not stop.is_set():
+                try:
+                    sn = snapshot()
+                    if sn["ts"] != last:
+                        snaps.append(sn)
+                        last = sn["ts"]
+                except Exception:
+                    pass
+                time.sleep(0.005)
+
+        for _ in range(10):   # settle the clocks on this kernel first
+            fn()
+        torch.cuda.synchronize()
+        th = threading.Thread(target=sampler)
+        th.start()
+        time.sleep(0.05)
+        t0 = time.perf_counter()
+        n = 0
+        s_ev, e_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s_ev.record()
+        while time.perf_counter() - t0 < seconds:
+            for _ in range(8):
+                fn()
+                n += 1
+            torch.cuda.synchronize()
+        e_ev.record()
+        e_ev.synchronize()
+        stop.set()
+        th.join()
+        out = {"calls": n, "ms_per_call": s_ev.elapsed_time(e_ev) / n, "tables": len(snaps)}
+        inner = snaps[1:-1] if len(snaps) > 3 else snaps   # tables inside the busy window
+        clk = [x["clk"] for x in inner if x["clk"]]
+        if clk:
+            out["gfxclk_MHz_mean"] = round(float(np.mean(clk)), 1)
+            out["gfxclk_MHz_min_max"] = [min(clk), max(clk)]
+        pw = [x["power"] for x in inner if x["power"]]
+        if pw:
+            out["socket_power_W_mean"] = round(float(np.mean(pw)), 1)
+        a, b = (inner[0], inner[-1]) if len(inner) >= 2 else (None, None)
+        if a and b and a["ts"] and b["ts"] and b["ts"] > a["ts"]:
+            dt = (b["ts"] - a["ts"]) / 1e8                         # 100 MHz timestamp
+            if a["energy"] is not None and b["energy"] is not None:
+                out["energy_power_W"] = round((b["energy"] - a["energy"]) * res_uj * 1e-6 / dt, 1)
+            if a["ppt"] is not None and a["acc"] and b["acc"] > a["acc"]:
+                out["ppt_limited_frac"] = round((b["ppt"] - a["ppt"]) / (b["acc"] - a["acc"]), 3)
+            out["window_s"] = round(dt, 3)
+        return out
+
+    res = {}
+    M, D, F = 24576, 4096, 16384
+    ffn = wl.video_ffn(M=M)
+
+    def d(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    x = d(ffn.x)
+    qw1, sw1 = w8.quantize_rows(d(ffn.w1))
+    qw2, sw2 = w8.quantize_rows(d(ffn.w2))
+    b1, b2 = d(ffn.b1), d(ffn.b2)
+    qx, sx = w8.quantize_rows(x)
+    u = w8.gemm(qx, sx, qw1, sw1, b1)
+    qh, sh = w8.gelu_quantize_rows(u)
+    y = torch.empty((M, D), dtype=torch.bfloat16, device=dev)
+    ops = 2.0 * M * F * D
+    for name, fn, work, unit in (
+            ("gemm_up", lambda: w8.gemm(qx, sx, qw1, sw1, b1, out=u), ops, "int8"),
+            ("gemm_down", lambda: w8.gemm(qh, sh, qw2, sw2, b2, out=y), ops, "int8"),
+            ("quantize_x", lambda: w8.quantize_rows(x, qx, sx), 3.0 * M * D + 4 * M, "bytes"),
+            ("gelu_quantize_u", lambda: w8.gelu_quantize_rows(u, qh, sh), 3.0 * M * F + 4 * M, "bytes")):
+        r = run(fn)
+        t = r["ms_per_call"] * 1e-3
+        if unit == "int8":
+            r["TOPS"] = round(work / t / 1e12, 1)
+            r["frac_of_5000"] = round(work / t / 1e12 / PEAK_INT8_TOPS, 4)
+            if r.get("gfxclk_MHz_mean"):
+                # the same rate against the peak at the clock the kernel ran at: the
+                # share of the matrix cores' cycles spent on MFMAs
+                r["frac_of_peak_at_measured_clock"] = round(
+                    r["frac_of_5000"] * 2400.0 / r["gfxclk_MHz_mean"], 4)
+            if r.get("energy_power_W"):
+                r["nJ_per_MFMA_32x32x32"] = round(r["energy_power_W"] / (work / t / 65536.0) * 1e9, 2)
+        else:
+            r["TB/s"] = round(work / t / 1e12, 3)
+        res[name] = r
+        log(f"{name}: {json.dumps(r)}")
+    del u, qh, y
+    small, _ = _small_workloads(torch, w8, wl, np, dev)
+    for name, (fn, work, kind) in small.items():
+        r = run(fn, 1.0)
+        peak = PEAK_INT8_TOPS if kind == "int8" else PEAK_BF16_TFLOPS
+        r["TOPS"] = round(work / (r["ms_per_call"] * 1e-3) / 1e12, 1)
+        r["frac_peak"] = round(r["TOPS"] / peak, 4)
+        res[name] = r
+        log(f"{name}: {json.dumps(r)}")
+    print(json.dumps({"power_clock": res, "device": info}))
 
 
 def hbm_from(trace_dir, fetch_dir, write_dir):
@@ -257,6 +472,12 @@ def main():
         return
     if args.probe_hbm:
         probe_hbm()
+        return
+    if args.probe_small:
+        probe_small()
+        return
+    if args.power_clock:
+        power_clock()
         return
     if args.hbm_from:
         hbm_from(*args.hbm_from)
@@ -542,6 +763,32 @@ def extra_benches(w8, wl, np, torch, dev, d, log):
     out["compact_quantize_8x512x4096"] = {"us": round(t * 1e3, 2), "rows_kept": mc,
                                           "GB/s": round(nbytes / (t * 1e-3) / 1e9, 1),
                                           "frac_hbm": round(nbytes / (t * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    # the linear-time compaction path (more than 8192 rows): 64 x 8192 rows of 4096
+    # under a general mask (runs of valid and padded rows, about half valid)
+    Bl, Ll = 64, 8192
+    gl = torch.Generator(device=dev).manual_seed(1)
+    xl = torch.randn((Bl * Ll, Dm), device=dev, generator=gl).to(torch.bfloat16).view(Bl, Ll, Dm)
+    runs = torch.randint(1, 3000, (4096,), device=dev, generator=gl)
+    starts = torch.cumsum(runs, 0)
+    run_id = torch.searchsorted(starts, torch.arange(Bl * Ll, device=dev), right=True)
+    ml = ((run_id % 2) == 0).to(torch.uint8).view(Bl, Ll)
+    bufl = torch.empty((Bl * Ll, Dm), dtype=torch.bfloat16, device=dev)
+    srcl = torch.empty((Bl * Ll,), dtype=torch.int32, device=dev)
+    t = _time(lambda: w8.compact_padded_rows(xl, ml, bufl, srcl, cnt), 10, torch)
+    mcl = int(cnt.item())
+    nbytes = 4.0 * mcl * Dm + Bl * Ll + 4.0 * mcl + 4   # algorithmic: the mask once
+    out["compact_64x8192x4096_linear_path"] = {
+        "us": round(t * 1e3, 2), "rows_kept": mcl, "GB/s": round(nbytes / (t * 1e-3) / 1e9, 1),
+        "frac_hbm": round(nbytes / (t * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    del bufl
+    qbl = torch.empty((Bl * Ll, Dm), dtype=torch.int8, device=dev)
+    sbl = torch.empty((Bl * Ll,), dtype=torch.float32, device=dev)
+    t = _time(lambda: w8.compact_quantize_rows(xl, ml, qbl, sbl, srcl, cnt), 10, torch)
+    nbytes = 3.0 * mcl * Dm + Bl * Ll + 8.0 * mcl + 4
+    out["compact_quantize_64x8192x4096_linear_path"] = {
+        "us": round(t * 1e3, 2), "rows_kept": mcl, "GB/s": round(nbytes / (t * 1e-3) / 1e9, 1),
+        "frac_hbm": round(nbytes / (t * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    del xl, qbl, sbl, srcl, ml
     # the text projection both ways: guarded linear on the compacted bf16 rows
     # (quantise + GEMM), and the INT8 GEMM on the fused kernel's codes
     xc = buf[:mc]
@@ -581,6 +828,25 @@ def extra_benches(w8, wl, np, torch, dev, d, log):
         tops = 2.0 * Mg * Ng * Kg / (t * 1e-3) / 1e12
         out[name] = {"us": round(t * 1e3, 2), "TOPS": round(tops, 1),
                      "frac_peak": round(tops / PEAK_INT8_TOPS, 4)}
+    # a short sequence through the FFN down projection (256 x 4096 x 16384): the
+    # tiles cover a quarter of the CUs; split-K across workgroups against the
+    # plain GEMM, same codes
+    Mg, Ng, Kg = 256, 4096, 16384
+    qa, sa = w8.quantize_rows(torch.randn((Mg, Kg), device=dev, generator=gen).to(torch.bfloat16))
+    qb, sb = w8.quantize_rows((torch.randn((Ng, Kg), device=dev, generator=gen) * 0.02)
+                              .to(torch.bfloat16))
+    bias = (torch.randn((Ng,), device=dev, generator=gen) * 0.01).to(torch.bfloat16)
+    yo = torch.empty((Mg, Ng), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty((w8.gemm_splitk_workspace_bytes(Mg, Ng, Kg),), dtype=torch.uint8, device=dev)
+    for name, fn in (("gemm_256x4096x16384", lambda: w8.gemm(qa, sa, qb, sb, bias, out=yo)),
+                     ("gemm_splitk_256x4096x16384",
+                      lambda: w8.gemm_splitk(qa, sa, qb, sb, bias, out=yo, workspace=ws))):
+        t = _time(fn, 20, torch)
+        tops = 2.0 * Mg * Ng * Kg / (t * 1e-3) / 1e12
+        out[name] = {"us": round(t * 1e3, 2), "TOPS": round(tops, 1),
+                     "frac_peak": round(tops / PEAK_INT8_TOPS, 4)}
+    out["gemm_splitk_256x4096x16384"]["slices"] = ws.numel() // (Mg * Ng * 4)
+    del qa, qb, ws
     # the attention projection with its LayerNorm + modulation prologue (8
     # conditioning groups of 3072 rows): fused (one kernel, then the GEMM) and
     # unfused (bf16 norm rows, quantise, GEMM)

@@ -209,6 +209,33 @@ W8A8_API int w8a8_gemm(const int8_t* qa, const float* sa, int64_t M, const int8_
               void* stream);
 
 /*
+ * w8a8_gemm with the K loop split across workgroups, for shapes whose tiles
+ * leave most compute units idle (few rows and columns, long K: a short
+ * sequence through a down projection, say).  Section 01.3 applies the scale
+ * and bias once after the whole INT32 accumulation, so the accumulation may be
+ * cut into K slices whose INT32 partial sums are added exactly before the
+ * epilogue: the result is w8a8_gemm's, bit for bit, for every shape.
+ *
+ *   Arguments as w8a8_gemm, plus
+ *   workspace [workspace_bytes] device memory, 16-byte aligned, at least
+ *             w8a8_gemm_splitk_workspace_bytes(M, N, K) bytes; it holds the
+ *             slices' INT32 partial sums (S x M x N) and is overwritten.
+ * When that size is 0 the shape is not split: the call is w8a8_gemm and the
+ * workspace may be NULL.  Errors as w8a8_gemm, and W8A8_EINVAL for a missing,
+ * misaligned or too small workspace.
+ */
+W8A8_API int w8a8_gemm_splitk(const int8_t* qa, const float* sa, int64_t M, const int8_t* qw,
+                              const float* sw, int64_t N, int64_t K, const uint16_t* bias, int act,
+                              int out_kind, void* out, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/* Workspace bytes w8a8_gemm_splitk needs: S * M * N * 4 for a shape cut into S
+ * K slices (S = 2 .. 8: when the 128 x 128 tiles fill fewer than half of the
+ * 256 compute units, as many slices as fill them, each of at least 8 K stages
+ * of 128 bytes), 0 for a shape that is not split or not served.  Host only. */
+W8A8_API size_t w8a8_gemm_splitk_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/*
  * The guarded W8A8 linear y = X W^T + b (section 01.3; paperlayer.ai section C,
  * "guarded acceleration according to architectural role and shape").
  *

@@ -34,7 +34,7 @@ NOALLOC_SCRATCH_BYTES = 64 << 20
 EXPORTS = ("w8a8_quantize_rows", "w8a8_quantize_blocks", "w8a8_gelu_quantize_rows", "w8a8_gelu_bf16", "w8a8_gemm", "w8a8_linear", "w8a8_linear_bf16",
            "compact_padded_rows", "w8a8_compact_quantize_rows", "w8a8_guard", "w8a8_linear_workspace_bytes",
            "w8a8_status_str", "w8a8_norm_mod_bf16", "w8a8_norm_mod_quantize_rows",
-           "w8a8_linear_noalloc")
+           "w8a8_linear_noalloc", "w8a8_gemm_splitk", "w8a8_gemm_splitk_workspace_bytes")
 
 _lib = None
 
@@ -65,6 +65,10 @@ def lib():
     L.w8a8_linear.argtypes = [P, I64, I64, I64, P, P, P, P, I, P, P, SZ, P, P]
     L.w8a8_linear_bf16.argtypes = [P, I64, I64, P, I64, P, I, P, P]
     L.w8a8_linear_noalloc.argtypes = [P, I64, I64, I64, P, P, P, P, I, P, P, P]
+    L.w8a8_gemm_splitk.argtypes = [P, P, I64, P, P, I64, I64, P, I, I, P, P, SZ, P]
+    L.w8a8_gemm_splitk.restype = I
+    L.w8a8_gemm_splitk_workspace_bytes.argtypes = [I64, I64, I64]
+    L.w8a8_gemm_splitk_workspace_bytes.restype = SZ
     L.compact_padded_rows.argtypes = [P, P, I64, I64, I64, P, P, P, P]
     L.w8a8_compact_quantize_rows.argtypes = [P, P, I64, I64, I64, P, P, P, P, P]
     L.w8a8_guard.argtypes = [I64, I64]
@@ -288,6 +292,42 @@ def gemm(qa, sa, qw, sw, bias=None, act=ACT_NONE, out_kind=OUT_BF16, out=None, s
     _need(out, "out", odt, (M, N))
     _check("w8a8_gemm", lib().w8a8_gemm(_p(qa), _p(sa), M, _p(qw), _p(sw), N, K, _p(bias),
                                         int(act), int(out_kind), _p(out), _stream(stream)))
+    return out
+
+
+def gemm_splitk_workspace_bytes(M: int, N: int, K: int) -> int:
+    """Workspace of gemm_splitk for (M, N, K); 0 when the shape is not split."""
+    return int(lib().w8a8_gemm_splitk_workspace_bytes(int(M), int(N), int(K)))
+
+
+def gemm_splitk(qa, sa, qw, sw, bias=None, act=ACT_NONE, out_kind=OUT_BF16, out=None,
+                workspace=None, stream=None):
+    """gemm with the K loop split across workgroups where the shape leaves most compute
+    units idle (same result, bit for bit).  workspace: uint8 device tensor of at least
+    gemm_splitk_workspace_bytes(M, N, K) bytes, allocated here when None."""
+    _need(qa, "qa", torch.int8)
+    _need(qw, "qw", torch.int8)
+    M, K = qa.shape
+    N = qw.shape[0]
+    if qw.shape[1] != K:
+        raise ValueError("qa and qw disagree on K")
+    if out_kind == OUT_BF16:
+        _need(sa, "sa", torch.float32, (M,))
+        _need(sw, "sw", torch.float32, (N,))
+    if bias is not None:
+        _need(bias, "bias", torch.bfloat16, (N,))
+    odt = torch.int32 if out_kind == OUT_I32 else torch.bfloat16
+    need = gemm_splitk_workspace_bytes(M, N, K)
+    with _on(stream):
+        out = out if out is not None else torch.empty((M, N), dtype=odt, device=qa.device)
+        if workspace is None and need > 0:
+            workspace = torch.empty((need,), dtype=torch.uint8, device=qa.device)
+    _need(out, "out", odt, (M, N))
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8)
+    _check("w8a8_gemm_splitk", lib().w8a8_gemm_splitk(
+        _p(qa), _p(sa), M, _p(qw), _p(sw), N, K, _p(bias), int(act), int(out_kind), _p(out),
+        _p(workspace), workspace.numel() if workspace is not None else 0, _stream(stream)))
     return out
 
 

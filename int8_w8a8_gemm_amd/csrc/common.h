@@ -136,6 +136,15 @@ int launch_compact_quantize_rows(const uint16_t* x, const uint8_t* mask, int64_t
 int launch_gemm_i8(const int8_t* qa, const float* sa, int64_t M, const int8_t* qw,
                    const float* sw, int64_t N, int64_t K, const uint16_t* bias, int act,
                    int out_kind, void* out, hipStream_t stream);
+// Split-K of the INT8 GEMM across workgroups (K slices of 128 x 128 tiles, exact
+// INT32 sum of the slices, then the epilogue): slices for a shape (1: not
+// split), the workspace it needs, and the launch (falls back to
+// launch_gemm_i8 when the shape is not split).
+int splitk_slices(int64_t M, int64_t N, int64_t K);
+size_t splitk_workspace_bytes(int64_t M, int64_t N, int64_t K);
+int launch_gemm_i8_splitk(const int8_t* qa, const float* sa, int64_t M, const int8_t* qw,
+                          const float* sw, int64_t N, int64_t K, const uint16_t* bias, int act,
+                          int out_kind, void* out, void* workspace, hipStream_t stream);
 int launch_gemm_bf16(const uint16_t* x, int64_t M, int64_t K, const uint16_t* w, int64_t N,
                      const uint16_t* bias, int act, uint16_t* y, hipStream_t stream);
 // The tiled MFMA path for BF16 operands (gemm_tiled.hip) and the shapes it serves.

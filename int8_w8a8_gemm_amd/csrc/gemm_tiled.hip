@@ -23,6 +23,7 @@
 #include "common.h"
 
 #include <type_traits>
+#include <utility>
 
 namespace w8a8 {
 
@@ -124,11 +125,21 @@ struct ElemBF16 {
     }
 };
 
-template <int BM_, int BN_, int WM_, int WN_, int BK_, int NST_, int GROUP_ROWS_ = GROUP_ROWS>
+template <int BM_, int BN_, int WM_, int WN_, int BK_, int NST_, int GROUP_ROWS_ = GROUP_ROWS,
+          int KS_ = 1, bool SPLIT_ = false>
 struct Cfg {
     static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_, NST = NST_;
     static constexpr int GROUP_M = GROUP_ROWS_ / BM;  // tile-rows per group of the raster
-    static constexpr int WAVES = WM * WN;
+    // KS > 1 splits K inside the workgroup: KS groups of WM x WN waves each own
+    // the whole tile, group g taking sub-steps g, g + KS, ... of every stage
+    // (the stage's loads are shared by all waves); after the K loop the groups'
+    // accumulators are added exactly through LDS, and group 0 holds the sums.
+    static constexpr int KS = KS_;
+    // SPLIT: split-K across workgroups; a work item is a (tile, K slice) pair
+    // and its INT32 partial sums go to a slice of the workspace (see splitk_reduce)
+    static constexpr bool SPLIT = SPLIT_;
+    static constexpr int WG = WM * WN;                // waves per K group
+    static constexpr int WAVES = WG * KS;
     static constexpr int THREADS = WAVES * 64;
     static constexpr int TM = BM / WM, TN = BN / WN;  // outputs per wave
     static constexpr int MI = TM / 32;                 // 32-row MFMA tiles per wave along M
@@ -144,6 +155,7 @@ struct Cfg {
     static constexpr int RPI = 64 / CPR;               // rows one 1-KB wave instruction fills
     static constexpr int STAGE = (BM + BN) * BK;       // bytes per stage (A tile then B tile)
     static constexpr int SUB = BK / 32;                // 32-byte MFMA sub-steps per stage
+    static constexpr int SUBW = SUB / KS;              // ... of them for each wave
     static constexpr int LPW_A = BM / WAVES / RPI;     // A load instructions per wave per stage
     static constexpr int LPW_B = BN / WAVES / RPI;     // B load instructions per wave per stage
     static constexpr int NLOAD = LPW_A + LPW_B;
@@ -159,7 +171,11 @@ struct Cfg {
     // row scales, column scales and bias as binary32.  Where the ring fills the
     // 160 KB of LDS, the scales go in the ring above the staging area instead:
     // they are then written only once the K loop is done with the ring.
-    static constexpr int RING = NST * STAGE > STAGE + EPI_BYTES ? NST * STAGE : STAGE + EPI_BYTES;
+    // bytes the groups g > 0 pass their accumulators through (KS > 1)
+    static constexpr int RED_WAVE = NI * MI * 16 * 64 * 4;
+    static constexpr int RED_BYTES = (KS - 1) * WG * RED_WAVE;
+    static constexpr int RING0 = NST * STAGE > STAGE + EPI_BYTES ? NST * STAGE : STAGE + EPI_BYTES;
+    static constexpr int RING = RING0 > RED_BYTES ? RING0 : RED_BYTES;
     static constexpr int SCALE_BYTES = (BM + 2 * BN) * 4;
     static constexpr bool SCALES_IN_RING = RING + SCALE_BYTES > 160 * 1024;
     static constexpr int SCALE_OFF = SCALES_IN_RING ? STAGE + EPI_BYTES : RING;
@@ -168,8 +184,11 @@ struct Cfg {
     static_assert(BM % (WAVES * RPI) == 0 && BN % (WAVES * RPI) == 0, "load split");
     static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile");
     static_assert(RPW % RPINS == 0 && 32 % RPW == 0, "copy-out rows per wave");
-    static_assert(THREADS >= BM && THREADS >= BN, "scale staging");
+    static constexpr int SA_PT = (BM + THREADS - 1) / THREADS;  // row scales per thread
+    static constexpr int SW_PT = (BN + THREADS - 1) / THREADS;  // column scales per thread
     static_assert(GROUP_M >= 1, "raster group");
+    static_assert(KS >= 1 && SUB % KS == 0, "sub-steps per K group");
+    static_assert(KS == 1 || !SCALES_IN_RING, "the K-group reduction uses the ring");
 };
 
 // Tile configurations: BM, BN, WM, WN, BK, NST[, raster group rows].
@@ -190,8 +209,37 @@ typedef Cfg<W8A8_LARGE_CFG> CfgLarge;
 typedef Cfg<W8A8_MID_CFG> CfgMid;
 typedef Cfg<W8A8_SMALL_CFG> CfgSmall;
 // small tiles with a 3-deep ring, for K loops of 32 stages or more (see launch_tiles)
-typedef Cfg<128, 128, 2, 2, 128, 3> CfgSmallDeep;
+#ifndef W8A8_SMALL_DEEP_CFG
+#define W8A8_SMALL_DEEP_CFG 128, 128, 2, 2, 128, 3
+#endif
+typedef Cfg<W8A8_SMALL_DEEP_CFG> CfgSmallDeep;
 typedef Cfg<64, 64, 2, 2, 128, 2> CfgTiny;
+// INT8 variants of the small tiers split K between two groups of waves (two
+// waves per SIMD, so each hides the other's fragment-read latency); BF16 keeps
+// one group, so its fp32 sums keep the order of a single chain.
+#ifndef W8A8_SMALL_I8_CFG
+#define W8A8_SMALL_I8_CFG 128, 128, 2, 2, 128, 2, GROUP_ROWS, 2
+#endif
+#ifndef W8A8_SMALL_DEEP_I8_CFG
+#define W8A8_SMALL_DEEP_I8_CFG 128, 128, 2, 2, 128, 3, GROUP_ROWS, 2
+#endif
+#ifndef W8A8_TINY_I8_CFG
+#define W8A8_TINY_I8_CFG 64, 64, 2, 2, 128, 2
+#endif
+typedef Cfg<W8A8_SMALL_I8_CFG> CfgSmallI8;
+typedef Cfg<W8A8_SMALL_DEEP_I8_CFG> CfgSmallDeepI8;
+typedef Cfg<W8A8_TINY_I8_CFG> CfgTinyI8;
+// The small tiers for element type E.
+template <class E> struct SmallTiers {
+    typedef CfgSmall Small;
+    typedef CfgSmallDeep Deep;
+    typedef CfgTiny Tiny;
+};
+template <> struct SmallTiers<ElemI8> {
+    typedef CfgSmallI8 Small;
+    typedef CfgSmallDeepI8 Deep;
+    typedef CfgTinyI8 Tiny;
+};
 
 template <int BK>
 __device__ __forceinline__ int swz(int r, int c) {
@@ -256,11 +304,12 @@ struct Ctx {
     // loads: lrow = (lane / CPR) * KB; lx = 16 x this lane's chunk before the
     // wave-uniform part of the swizzle (see stage_load_one)
     uint32_t lrow, lx, kb;
+    int kofs;  // first K byte of the work item's slice (split-K), else 0
     // fragment reads: LDS byte offset of this lane's row in the wave's first
     // activation / weight sub-tile, and 16 x the physical chunk of its K-chunk
     // (lane >> 5) in that row; every other read adds compile-time constants
     uint32_t fa, fw, ga, gw;
-    int wave, lane, wm, wn;
+    int wave, lane, wm, wn, kg;  // kg: the wave's K group
 };
 
 // Points the context's buffer resources at the operand panels of the tile
@@ -293,17 +342,21 @@ __device__ __forceinline__ void lane_ctx(Ctx<C>& c, int lane) {
     const int ra = c.wm * C::TM + (lane & 31), rw = c.wn * C::TN + (lane & 31);
     c.fa = (uint32_t)(ra * C::BK);
     c.fw = (uint32_t)(C::BM * C::BK + rw * C::BK);
-    c.ga = 16u * (uint32_t)swz<C::BK>(ra, hi);
-    c.gw = 16u * (uint32_t)swz<C::BK>(rw, hi);
+    // a K group's sub-steps are kg, kg + KS, ...: 32 * kg shares no bit with
+    // 32 * KS * (the wave's own sub-step), so it joins the per-lane XOR term
+    c.ga = (16u * (uint32_t)swz<C::BK>(ra, hi)) ^ (32u * (uint32_t)c.kg);
+    c.gw = (16u * (uint32_t)swz<C::BK>(rw, hi)) ^ (32u * (uint32_t)c.kg);
 }
 
 template <class C>
 __device__ __forceinline__ void make_ctx(Ctx<C>& c, int64_t KB, int wave, int lane) {
     c.kb = (uint32_t)KB;
+    c.kofs = 0;
     c.wave = wave;
     c.lane = lane;
-    c.wm = wave % C::WM;
-    c.wn = wave / C::WM;
+    c.kg = C::KS > 1 ? wave / C::WG : 0;
+    c.wm = (wave % C::WG) % C::WM;
+    c.wn = (wave % C::WG) / C::WM;
     lane_ctx<C>(c, lane);
 }
 
@@ -327,7 +380,8 @@ __device__ __forceinline__ void stage_load_one(const Ctx<C>& c, uint32_t lrow, u
     const uint32_t voff = lrow + r0 * c.kb + (lx ^ xr);
     char* dst = lds_stage + (is_a ? 0 : C::BM * C::BK) + r0 * C::BK;
 #if defined(__HIP_DEVICE_COMPILE__)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rsrc[is_a ? 0 : 1], (lds_void*)dst, 16, voff, k0,
+    const int kpos = C::SPLIT ? k0 + c.kofs : k0;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rsrc[is_a ? 0 : 1], (lds_void*)dst, 16, voff, kpos,
                                              0, W8A8_LOAD_POLICY);
 #else
     (void)dst;
@@ -397,7 +451,7 @@ __device__ __forceinline__ v4i keep_bytes(v4i v, int valid) {
 // valid bytes of that stage.
 template <class C>
 __device__ __forceinline__ void mask_tail(Frags<C>& f, const Ctx<C>& c, int ks, int tail) {
-    const int valid = tail - (32 * ks + 16 * (c.lane >> 5));
+    const int valid = tail - (32 * (ks + c.kg) + 16 * (c.lane >> 5));
 #pragma unroll
     for (int q = 0; q < C::MI; ++q) f.a[q] = keep_bytes(f.a[q], valid);
 #pragma unroll
@@ -472,13 +526,15 @@ __device__ __forceinline__ void k_stage(const Ctx<C>& c, char* smem, int kt, Acc
     // stage (the INT8 path has whole stages)
     constexpr bool MAYBE_TAIL = !NEXT && E::BYTES == 2;
     char* buf = smem + (kt % C::NST) * C::STAGE;
+    // the wave's sub-steps of the stage: KS * j (+ its group's kg, folded into
+    // the fragment offsets), j = 0 .. SUBW - 1
 #pragma unroll
-    for (int ks = 0; ks + 1 < C::SUB; ++ks) {
-        if (MAYBE_TAIL && tail < C::BK) mask_tail<C>(cur, c, ks, tail);
-        mfma_step<C, E, true, false>(c, acc, cur, buf, ks + 1, nullptr, 0);
+    for (int j = 0; j + 1 < C::SUBW; ++j) {
+        if (MAYBE_TAIL && tail < C::BK) mask_tail<C>(cur, c, C::KS * j, tail);
+        mfma_step<C, E, true, false>(c, acc, cur, buf, C::KS * (j + 1), nullptr, 0);
     }
     char* next_buf = smem + ((kt + 1) % C::NST) * C::STAGE;
-    if (MAYBE_TAIL && tail < C::BK) mask_tail<C>(cur, c, C::SUB - 1, tail);
+    if (MAYBE_TAIL && tail < C::BK) mask_tail<C>(cur, c, C::KS * (C::SUBW - 1), tail);
     if (NEXT) {
         // my loads of stage kt+1 have landed and my reads of stage kt are done ...
         if (STEADY) wait_vm_lgkm0<C::NLOAD * (C::NST - 2)>();
@@ -513,6 +569,12 @@ __device__ __forceinline__ void tile_of(int64_t bid, int64_t tm, int64_t tn, int
     tile_n = (int64_t)rn;
 }
 
+// Calls f(integral_constant<int, P>) for P = 0, 1, ... in order.
+template <class F, int... P>
+__device__ __forceinline__ void for_each_pass(F& f, std::integer_sequence<int, P...>) {
+    (f(std::integral_constant<int, P>{}), ...);
+}
+
 // Epilogue.  acc[ni][mi][i] holds D[n][m] for m = m0 + wm*TM + mi*32 +
 // (lane & 31) and n = n0 + wn*TN + ni*32 + 8*(i/4) + 4*(lane >> 5) + (i & 3):
 // four consecutive columns per group of four registers.
@@ -532,7 +594,7 @@ template <class C, class E, int ACT, bool VEC_OUT>
 __device__ __forceinline__ void store_bf16(const Acc<C, E>& acc, uint16_t* __restrict__ y, int64_t M,
                                            int64_t N, int64_t m0, int64_t n0, int wave, int wm,
                                            int wn, int lane, const float* sa_l, const float* sw_l,
-                                           const float* b_l, char* stage) {
+                                           const float* b_l, char* stage, int kg) {
     const int half = lane >> 5;
     const int ncol = wn * C::TN + 4 * half;  // tile-local column of this lane's first group
     char* wbase = stage + (wm * 32 + (lane & 31)) * C::OUT_ROW + ncol * 2;
@@ -550,8 +612,9 @@ __device__ __forceinline__ void store_bf16(const Acc<C, E>& acc, uint16_t* __res
         constexpr int p = decltype(pc)::value;
         float sam = 0.f;
         if constexpr (E::BYTES == 1) sam = sa_l[wm * C::TM + p * 32 + (lane & 31)];
+        // with K groups only group 0 holds the sums; every wave copies out
 #pragma unroll
-        for (int ni = 0; ni < C::NI; ++ni) {
+        for (int ni = 0; ni < (kg == 0 ? C::NI : 0); ++ni) {
             v4f swv[4], bv[4];
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
@@ -620,11 +683,54 @@ __device__ __forceinline__ void store_bf16(const Acc<C, E>& acc, uint16_t* __res
         }
         lds_barrier();  // the staging area is free again
     };
-    static_assert(C::MI >= 1 && C::MI <= 4, "epilogue passes");
-    pass(std::integral_constant<int, 0>{});
-    if constexpr (C::MI > 1) pass(std::integral_constant<int, 1>{});
-    if constexpr (C::MI > 2) pass(std::integral_constant<int, 2>{});
-    if constexpr (C::MI > 3) pass(std::integral_constant<int, 3>{});
+    for_each_pass(pass, std::make_integer_sequence<int, C::MI>{});
+}
+
+// K groups g > 0 hand their accumulators to group 0 through LDS (the ring,
+// which the K loop is done with), and group 0 adds them in order g = 1, 2, ...:
+// exact for INT32, a fixed order for fp32.  Lane l's values of accumulator
+// register group q of MFMA tile (ni, mi) sit at ((ni*MI + mi)*4 + q)*1 KB +
+// 16*l of the wave's area, so each 16-byte access of a wave is contiguous.
+// Every wave calls it (it holds two barriers).
+template <class C, class E>
+__device__ __forceinline__ void reduce_k_groups(Acc<C, E>& acc, char* smem, int kg, int slot,
+                                                int lane) {
+    if constexpr (C::KS > 1) {
+        typedef typename E::acc_t A;
+        typedef std::conditional_t<E::BYTES == 1, v4i, v4f> V4;
+        if (kg > 0) {
+            char* dst = smem + ((kg - 1) * C::WG + slot) * C::RED_WAVE + 16 * lane;
+#pragma unroll
+            for (int ni = 0; ni < C::NI; ++ni)
+#pragma unroll
+                for (int mi = 0; mi < C::MI; ++mi)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const A& a = acc[ni][mi];
+                        const V4 v = {a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
+                        *reinterpret_cast<V4*>(dst + ((ni * C::MI + mi) * 4 + q) * 1024) = v;
+                    }
+        }
+        lds_barrier();
+        if (kg == 0) {
+#pragma unroll
+            for (int g = 1; g < C::KS; ++g) {
+                const char* src = smem + ((g - 1) * C::WG + slot) * C::RED_WAVE + 16 * lane;
+#pragma unroll
+                for (int ni = 0; ni < C::NI; ++ni)
+#pragma unroll
+                    for (int mi = 0; mi < C::MI; ++mi)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const V4 v = *reinterpret_cast<const V4*>(
+                                src + ((ni * C::MI + mi) * 4 + q) * 1024);
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) acc[ni][mi][4 * q + e] += v[e];
+                        }
+            }
+        }
+        lds_barrier();  // the ring is free again
+    }
 }
 
 template <class C>
@@ -663,7 +769,7 @@ __global__ __launch_bounds__(C::THREADS)
 __attribute__((amdgpu_waves_per_eu(C::WAVES_PER_SIMD, C::WAVES_PER_SIMD)))
 void gemm_tiled(const void* __restrict__ a, const float* __restrict__ sa, int64_t M,
                 const void* __restrict__ w, const float* __restrict__ sw, int64_t N, int64_t K,
-                const uint16_t* __restrict__ bias, void* __restrict__ out) {
+                const uint16_t* __restrict__ bias, void* __restrict__ out, int kt_split) {
     constexpr int BM = C::BM, BN = C::BN, BK = C::BK, NST = C::NST, MI = C::MI;
     constexpr bool SCALES = !OUT_I32 && E::BYTES == 1;
     // K ring (from byte STAGE on, also the output staging area) and the
@@ -679,17 +785,30 @@ void gemm_tiled(const void* __restrict__ a, const float* __restrict__ sa, int64_
     const char* wb = static_cast<const char*>(w);
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave % C::WM, wn = wave / C::WM;
-    const int64_t tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN, total = tm * tn;
+    const int kg = C::KS > 1 ? wave / C::WG : 0;       // K group (KS > 1)
+    const int wm = (wave % C::WG) % C::WM, wn = (wave % C::WG) / C::WM;
+    const int64_t tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN, tiles = tm * tn;
     const int64_t KB = K * E::BYTES;
+    // split-K: K / BK stages in slices of kt_split, work item t = slice * tiles + tile
+    const int64_t nslice = C::SPLIT ? (KB / BK) / kt_split : 1;
+    const int64_t total = tiles * nslice;
     // INT8 rows are whole stages; a BF16 row may end inside its last stage
-    const int KT = E::BYTES == 1 ? (int)(KB / BK) : (int)((KB + BK - 1) / BK);
+    const int KT = C::SPLIT ? kt_split : E::BYTES == 1 ? (int)(KB / BK) : (int)((KB + BK - 1) / BK);
     const int tail = (int)(KB - (int64_t)(KT - 1) * BK);  // valid bytes in the last stage
     int64_t t = blockIdx.x, tile_m, tile_n;
-    tile_of<C>(t, tm, tn, tile_m, tile_n);
+    int slice = 0;
+    auto item = [&](int64_t ti) {
+        if constexpr (C::SPLIT) {
+            slice = (int)(ti / tiles);
+            ti -= (int64_t)slice * tiles;
+        }
+        tile_of<C>(ti, tm, tn, tile_m, tile_n);
+    };
+    item(t);
     int64_t m0 = tile_m * BM, n0 = tile_n * BN;
     Ctx<C> c;
     make_ctx<C>(c, KB, wave, lane);
+    if constexpr (C::SPLIT) c.kofs = slice * kt_split * BK;
     set_tile<C>(c, ab, wb, M, N, KB, m0, n0);
 
     // Epilogue operands of a tile: row scales, column scales and bias (the
@@ -702,20 +821,27 @@ void gemm_tiled(const void* __restrict__ a, const float* __restrict__ sa, int64_
     // Every thread loads (clamped indices; only threads below BM / BN store),
     // so that each load defines its register anew and nothing carries over
     // from the previous tile.
-    float nsa = 0.f, nsw = 0.f;
-    uint32_t nb = 0;
+    float nsa[C::SA_PT] = {}, nsw[C::SW_PT] = {};
+    uint32_t nb[C::SW_PT] = {};
     auto load_scales = [&](int64_t m0_, int64_t n0_) {
-        if (SCALES) nsa = sa[m0_ + tid < M ? m0_ + tid : M - 1];
+#pragma unroll
+        for (int i = 0; i < C::SA_PT; ++i) {
+            const int64_t m = m0_ + tid + i * C::THREADS;
+            if (SCALES) nsa[i] = sa[m < M ? m : M - 1];
+        }
         if (!OUT_I32) {
-            const int64_t n = n0_ + tid < N ? n0_ + tid : N - 1;
-            if (SCALES) nsw = sw[n];
-            if constexpr (C::SCALES_IN_RING) {
-                // loaded during the last K stage: a branch on the pointer
-                // would make the wave wait for it there
-                const int64_t cnt = N - n0_ < BN ? N - n0_ : BN;
-                nb = load_bias_bits(bias ? bias + n0_ : nullptr, (int)cnt, (int)(n - n0_));
-            } else {
-                nb = bias ? (uint32_t)bias[n] : 0u;
+#pragma unroll
+            for (int i = 0; i < C::SW_PT; ++i) {
+                const int64_t n = n0_ + tid + i * C::THREADS < N ? n0_ + tid + i * C::THREADS : N - 1;
+                if (SCALES) nsw[i] = sw[n];
+                if constexpr (C::SCALES_IN_RING) {
+                    // loaded during the last K stage: a branch on the pointer
+                    // would make the wave wait for it there
+                    const int64_t cnt = N - n0_ < BN ? N - n0_ : BN;
+                    nb[i] = load_bias_bits(bias ? bias + n0_ : nullptr, (int)cnt, (int)(n - n0_));
+                } else {
+                    nb[i] = bias ? (uint32_t)bias[n] : 0u;
+                }
             }
         }
     };
@@ -731,13 +857,25 @@ void gemm_tiled(const void* __restrict__ a, const float* __restrict__ sa, int64_
             // pending, for the compiler, on the other path, and it would then
             // wait for them at the next reuse of their registers, behind the
             // next tile's first stage
-            if (SCALES) asm volatile("" ::"v"(nsa), "v"(nsw));
-            if (!OUT_I32) asm volatile("" ::"v"(nb));
+#pragma unroll
+            for (int i = 0; i < C::SA_PT; ++i)
+                if (SCALES) asm volatile("" ::"v"(nsa[i]));
+#pragma unroll
+            for (int i = 0; i < C::SW_PT; ++i) {
+                if (SCALES) asm volatile("" ::"v"(nsw[i]));
+                if (!OUT_I32) asm volatile("" ::"v"(nb[i]));
+            }
         }
-        if (SCALES && et < BM) sa_l[et] = nsa;
-        if (!OUT_I32 && et < BN) {
-            if (SCALES) sw_l[et] = nsw;
-            b_l[et] = bf16_bits_to_float(bias ? nb : 0x8000u);  // -0.0 without a bias
+#pragma unroll
+        for (int i = 0; i < C::SA_PT; ++i)
+            if (SCALES && et + i * C::THREADS < BM) sa_l[et + i * C::THREADS] = nsa[i];
+#pragma unroll
+        for (int i = 0; i < C::SW_PT; ++i) {
+            const int e = et + i * C::THREADS;
+            if (!OUT_I32 && e < BN) {
+                if (SCALES) sw_l[e] = nsw[i];
+                b_l[e] = bf16_bits_to_float(bias ? nb[i] : 0x8000u);  // -0.0 without a bias
+            }
         }
     };
     for (int s = 0; s < NST; ++s)
@@ -772,16 +910,19 @@ void gemm_tiled(const void* __restrict__ a, const float* __restrict__ sa, int64_
         const bool has_next = PERSIST && t_next < total;
         int64_t m0n = 0, n0n = 0;
         lds_barrier();  // every wave is done reading the K ring
+        reduce_k_groups<C, E>(acc, smem, kg, wave % C::WG, lane);
         if constexpr (C::SCALES_IN_RING) {
             put_scales();
             lds_barrier();
         }
+        const int slice_now = slice;
         if (has_next) {
-            tile_of<C>(t_next, tm, tn, tile_m, tile_n);
+            item(t_next);
             m0n = tile_m * BM;
             n0n = tile_n * BN;
             if constexpr (!C::SCALES_IN_RING) load_scales(m0n, n0n);
             set_tile<C>(c, ab, wb, M, N, KB, m0n, n0n);
+            if constexpr (C::SPLIT) c.kofs = slice * kt_split * BK;
             stage_load<C>(c, 0, smem);  // next tile's stage 0 -> buffer 0
         }
         // The epilogue's lane addresses depend only on the lane, and hoisted out
@@ -790,10 +931,13 @@ void gemm_tiled(const void* __restrict__ a, const float* __restrict__ sa, int64_
         int elane = lane;
         asm volatile("" : "+v"(elane));
         if constexpr (OUT_I32 != 0) {
-            store_i32<C>(acc, reinterpret_cast<int32_t*>(out), M, N, m0, n0, wm, wn, elane);
+            if (kg == 0)
+                store_i32<C>(acc, reinterpret_cast<int32_t*>(out) + (int64_t)slice_now * M * N, M, N,
+                             m0, n0, wm, wn, elane);
         } else {
             store_bf16<C, E, ACT, VEC_OUT>(acc, reinterpret_cast<uint16_t*>(out), M, N, m0, n0,
-                                           wave, wm, wn, elane, sa_l, sw_l, b_l, smem + C::STAGE);
+                                           wave, wm, wn, elane, sa_l, sw_l, b_l, smem + C::STAGE,
+                                           kg);
         }
         if (!has_next) break;
         // this tile's epilogue is done with the old values
@@ -817,8 +961,9 @@ int64_t tile_count(int64_t M, int64_t N) {
 template <class C, class E, int OUT_I32, int ACT, bool VEC_OUT>
 hipError_t launch_cfg(const void* a, const float* sa, int64_t M, const void* w, const float* sw,
                       int64_t N, int64_t K, const uint16_t* bias, void* out, int cus,
-                      hipStream_t stream) {
-    const int64_t tiles = tile_count<C>(M, N);
+                      hipStream_t stream, int nslice = 1) {
+    const int64_t tiles = tile_count<C>(M, N) * nslice;
+    const int kt_split = C::SPLIT ? (int)(K * E::BYTES / C::BK / nslice) : 0;
     if (tiles >= (int64_t(1) << 31)) return hipErrorInvalidValue;  // tile indices are 32-bit
     constexpr bool persist = ACT == 0;
     // workgroups that fit on one CU at once (160 KB of LDS is the limit)
@@ -829,7 +974,7 @@ hipError_t launch_cfg(const void* a, const float* sa, int64_t M, const void* w, 
         grid = tiles < slots ? tiles : slots;
     }
     hipLaunchKernelGGL((gemm_tiled<C, E, OUT_I32, ACT, persist, VEC_OUT>), dim3((unsigned)grid),
-                       dim3(C::THREADS), 0, stream, a, sa, M, w, sw, N, K, bias, out);
+                       dim3(C::THREADS), 0, stream, a, sa, M, w, sw, N, K, bias, out, kt_split);
     return hipGetLastError();
 }
 
@@ -865,7 +1010,10 @@ hipError_t launch_tiles(const void* a, const float* sa, int64_t M, const void* w
         return launch_cfg<CfgLarge, E, OUT_I32, ACT, VEC_OUT>(a, sa, M, w, sw, N, K, bias, out, cus,
                                                              stream);
     }
-    if (2 * tile_count<CfgSmall>(M, N) >= cus) {
+    typedef typename SmallTiers<E>::Small CSmall;
+    typedef typename SmallTiers<E>::Deep CDeep;
+    typedef typename SmallTiers<E>::Tiny CTiny;
+    if (2 * tile_count<CSmall>(M, N) >= cus) {
         // A 3-deep ring keeps two stages of loads in flight: with one wave per
         // SIMD and 512 cycles of MFMAs per stage, the 2-deep ring's per-stage
         // load latency shows.  It pays on K loops of 32 stages or more
@@ -873,17 +1021,113 @@ hipError_t launch_tiles(const void* a, const float* sa, int64_t M, const void* w
         // 22.4 -> 20.3 us) and costs 2-5% on 16 stages (2048^3 INT8); its
         // 96 KB of LDS leaves one workgroup per CU, so only where the tiles
         // take one round.
-        if (K * E::BYTES >= 32 * CfgSmallDeep::BK && tile_count<CfgSmallDeep>(M, N) <= cus)
-            return launch_cfg<CfgSmallDeep, E, OUT_I32, ACT, VEC_OUT>(a, sa, M, w, sw, N, K, bias,
-                                                                     out, cus, stream);
-        return launch_cfg<CfgSmall, E, OUT_I32, ACT, VEC_OUT>(a, sa, M, w, sw, N, K, bias, out, cus,
-                                                             stream);
+        if (K * E::BYTES >= 32 * CDeep::BK && tile_count<CDeep>(M, N) <= cus)
+            return launch_cfg<CDeep, E, OUT_I32, ACT, VEC_OUT>(a, sa, M, w, sw, N, K, bias, out, cus,
+                                                              stream);
+        return launch_cfg<CSmall, E, OUT_I32, ACT, VEC_OUT>(a, sa, M, w, sw, N, K, bias, out, cus,
+                                                           stream);
     }
-    return launch_cfg<CfgTiny, E, OUT_I32, ACT, VEC_OUT>(a, sa, M, w, sw, N, K, bias, out, cus,
-                                                        stream);
+    return launch_cfg<CTiny, E, OUT_I32, ACT, VEC_OUT>(a, sa, M, w, sw, N, K, bias, out, cus,
+                                                      stream);
+}
+
+// ---- split-K across workgroups ----
+// Shapes whose tiles leave most CUs idle (few rows or columns) and have a long
+// K loop: the K stages are cut into S slices, the 128 x 128 tiles of all slices
+// run at once (writing INT32 partial sums to S slices of the workspace), then
+// splitk_reduce adds the slices in order s = 0 .. S-1 (exact in INT32: the
+// scales come only after the whole accumulation) and applies the same
+// epilogue as the tiled kernel, so the result is w8a8_gemm's bit for bit.
+typedef Cfg<128, 128, 2, 2, 128, 2, GROUP_ROWS, 2, true> CfgSplit;
+
+// Four consecutive outputs of one row per thread (N is a multiple of 64), in a
+// grid-stride loop: acc = sum of the S partials, then exactly store_bf16's
+// arithmetic (or the raw INT32 sum).
+template <int OUT_I32, int ACT>
+__global__ __launch_bounds__(256) void splitk_reduce(const int32_t* __restrict__ part, int nslice,
+                                                     int64_t M, int64_t N,
+                                                     const float* __restrict__ sa,
+                                                     const float* __restrict__ sw,
+                                                     const uint16_t* __restrict__ bias,
+                                                     void* __restrict__ out) {
+    const int64_t MN = M * N, quads = MN / 4;
+    for (int64_t qd = (int64_t)blockIdx.x * 256 + threadIdx.x; qd < quads;
+         qd += (int64_t)gridDim.x * 256) {
+        const int64_t e0 = 4 * qd;
+        v4i acc = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(part + e0));
+        for (int sl = 1; sl < nslice; ++sl)
+            acc += __builtin_nontemporal_load(reinterpret_cast<const v4i*>(part + sl * MN + e0));
+        if constexpr (OUT_I32 != 0) {
+            __builtin_nontemporal_store(acc, reinterpret_cast<v4i*>(static_cast<int32_t*>(out) + e0));
+        } else {
+            const int64_t row = e0 / N, col = e0 - row * N;
+            const float sam = sa[row];
+            float v[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float b = bf16_bits_to_float(bias ? (uint32_t)bias[col + e] : 0x8000u);
+                const float t = (float)acc[e];  // nearest even
+                const float u = __fmul_rn(sam, sw[col + e]);
+                v[e] = __builtin_fmaf(t, u, b);
+            }
+            uint2 o = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+            if (ACT == 1)
+                o = make_uint2(gelu_bf16_rn(o.x & 0xffffu) | (gelu_bf16_rn(o.x >> 16) << 16),
+                               gelu_bf16_rn(o.y & 0xffffu) | (gelu_bf16_rn(o.y >> 16) << 16));
+            typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+            const u32x2 ov = {o.x, o.y};
+            __builtin_nontemporal_store(ov, reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + e0));
+        }
+    }
 }
 
 }  // namespace
+
+int splitk_slices(int64_t M, int64_t N, int64_t K) {
+    // The slice count is a property of the shape alone (the library targets the
+    // 256 CUs of an MI355X), so the workspace size needs no device query.
+    constexpr int64_t kCUs = 256;
+    if (M <= 0 || N <= 0) return 1;
+    // only shapes the large tiles and the 128 x 128 tiles leave mostly idle
+    if (2 * tile_count<CfgLarge>(M, N) >= kCUs || 2 * tile_count<CfgSplit>(M, N) >= kCUs) return 1;
+    const int64_t tiles = tile_count<CfgSplit>(M, N), stages = K / CfgSplit::BK;
+    int64_t S = kCUs / tiles;
+    if (S > 8) S = 8;
+    // whole stages per slice, at least 8 of them
+    while (S > 1 && (stages % S != 0 || stages / S < 8)) --S;
+    return (int)S;
+}
+
+size_t splitk_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    const int S = splitk_slices(M, N, K);
+    return S > 1 ? (size_t)S * (size_t)M * (size_t)N * sizeof(int32_t) : 0;
+}
+
+int launch_gemm_i8_splitk(const int8_t* qa, const float* sa, int64_t M, const int8_t* qw,
+                          const float* sw, int64_t N, int64_t K, const uint16_t* bias, int act,
+                          int out_kind, void* out, void* workspace, hipStream_t stream) {
+    const int S = splitk_slices(M, N, K);
+    if (S <= 1) return launch_gemm_i8(qa, sa, M, qw, sw, N, K, bias, act, out_kind, out, stream);
+    const int cus = cu_count();
+    if (cus <= 0) return -1;
+    hipError_t e = launch_cfg<CfgSplit, ElemI8, 1, 0, true>(qa, sa, M, qw, sw, N, K, nullptr,
+                                                          workspace, cus, stream, S);
+    if (e != hipSuccess) return -1;
+    const int64_t quads = M * N / 4;
+    int64_t blocks = (quads + 255) / 256;
+    if (blocks > (int64_t)cus * 8) blocks = (int64_t)cus * 8;
+    const int32_t* part = static_cast<const int32_t*>(workspace);
+    if (out_kind == 1)
+        hipLaunchKernelGGL((splitk_reduce<1, 0>), dim3((unsigned)blocks), dim3(256), 0, stream, part,
+                           S, M, N, sa, sw, bias, out);
+    else if (act == 1)
+        hipLaunchKernelGGL((splitk_reduce<0, 1>), dim3((unsigned)blocks), dim3(256), 0, stream, part,
+                           S, M, N, sa, sw, bias, out);
+    else
+        hipLaunchKernelGGL((splitk_reduce<0, 0>), dim3((unsigned)blocks), dim3(256), 0, stream, part,
+                           S, M, N, sa, sw, bias, out);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
 
 int launch_gemm_i8(const int8_t* qa, const float* sa, int64_t M, const int8_t* qw,
                    const float* sw, int64_t N, int64_t K, const uint16_t* bias, int act,

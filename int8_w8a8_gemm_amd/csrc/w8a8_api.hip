@@ -123,9 +123,12 @@ int w8a8_gelu_bf16(const uint16_t* x, int64_t n, uint16_t* y, void* stream) {
     return launched(w8a8::launch_gelu_bf16(x, n, y, as_stream(stream)));
 }
 
-int w8a8_gemm(const int8_t* qa, const float* sa, int64_t M, const int8_t* qw, const float* sw,
-              int64_t N, int64_t K, const uint16_t* bias, int act, int out_kind, void* out,
-              void* stream) {
+}  // extern "C"
+
+namespace {
+// The checks of w8a8_gemm's arguments; W8A8_OK if they pass.
+int gemm_args(const int8_t* qa, const float* sa, int64_t M, const int8_t* qw, const float* sw,
+              int64_t N, int64_t K, const uint16_t* bias, int act, int out_kind, void* out) {
     if (M < 0 || N < 0 || K < 0) return W8A8_EINVAL;
     if (!act_ok(act)) return W8A8_EINVAL;
     if (out_kind != W8A8_OUT_BF16 && out_kind != W8A8_OUT_I32) return W8A8_EINVAL;
@@ -139,8 +142,37 @@ int w8a8_gemm(const int8_t* qa, const float* sa, int64_t M, const int8_t* qw, co
         if (!sa || !sw || !aligned(sa, 4) || !aligned(sw, 4)) return W8A8_EINVAL;
         if (bias && !aligned(bias, 2)) return W8A8_EINVAL;
     }
+    return W8A8_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int w8a8_gemm(const int8_t* qa, const float* sa, int64_t M, const int8_t* qw, const float* sw,
+              int64_t N, int64_t K, const uint16_t* bias, int act, int out_kind, void* out,
+              void* stream) {
+    const int st = gemm_args(qa, sa, M, qw, sw, N, K, bias, act, out_kind, out);
+    if (st != W8A8_OK || M == 0) return st;
     return launched(w8a8::launch_gemm_i8(qa, sa, M, qw, sw, N, K, bias, act, out_kind, out,
                                          as_stream(stream)));
+}
+
+size_t w8a8_gemm_splitk_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    if (M <= 0 || N <= 0 || K <= 0 || M >= kMaxRows || !w8a8_guard(N, K)) return 0;
+    return w8a8::splitk_workspace_bytes(M, N, K);
+}
+
+int w8a8_gemm_splitk(const int8_t* qa, const float* sa, int64_t M, const int8_t* qw,
+                     const float* sw, int64_t N, int64_t K, const uint16_t* bias, int act,
+                     int out_kind, void* out, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+    const int st = gemm_args(qa, sa, M, qw, sw, N, K, bias, act, out_kind, out);
+    if (st != W8A8_OK || M == 0) return st;
+    const size_t need = w8a8_gemm_splitk_workspace_bytes(M, N, K);
+    if (need > 0 && (!workspace || !aligned(workspace, 16) || workspace_bytes < need))
+        return W8A8_EINVAL;
+    return launched(w8a8::launch_gemm_i8_splitk(qa, sa, M, qw, sw, N, K, bias, act, out_kind, out,
+                                                workspace, as_stream(stream)));
 }
 
 int w8a8_linear_bf16(const uint16_t* x, int64_t M, int64_t K, const uint16_t* w, int64_t N,

@@ -75,6 +75,29 @@ def test_linear_noalloc_rejects_on_the_host():
     assert "scratch" in w8.status_str(w8.ESCRATCH)
 
 
+def test_gemm_splitk_workspace_and_rejections():
+    """Split-K sizing is a property of the shape (host only): S * M * N * 4 bytes for
+    shapes the 128 x 128 tiles leave mostly idle with long K, else 0; a missing or
+    short workspace is rejected before any HIP call."""
+    ws = w8.gemm_splitk_workspace_bytes
+    assert ws(256, 4096, 16384) == 4 * 256 * 4096 * 4
+    assert ws(100, 512, 8192) == 8 * 100 * 512 * 4
+    assert ws(300, 640, 4096) == 4 * 300 * 640 * 4          # 8 slices would be < 8 stages
+    for shape in [(2048, 2048, 2048), (24576, 16384, 4096), (512, 4096, 4096), (64, 64, 1024),
+                  (0, 4096, 4096), (256, 4100, 16384), (256, 4096, 2050)]:
+        assert ws(*shape) == 0, shape
+    L = w8.lib()
+    g = lambda M, N, K, wsp, wsb: L.w8a8_gemm_splitk(A16, A16, M, A16b, A16c, N, K, NULL, 0, 0,
+                                                     A16, wsp, wsb, NULL)
+    need = ws(256, 4096, 16384)
+    assert g(256, 4096, 16384, NULL, 0) == w8.EINVAL
+    assert g(256, 4096, 16384, A16, need - 1) == w8.EINVAL
+    assert g(256, 4096, 16384, MIS, need) == w8.EINVAL
+    assert g(256, 4100, 16384, A16, need) == w8.EUNSUPPORTED
+    assert g(-1, 4096, 16384, A16, need) == w8.EINVAL
+    assert g(0, 4096, 16384, NULL, 0) == w8.OK
+
+
 def test_status_strings():
     assert w8.status_str(0) == "ok"
     assert "invalid" in w8.status_str(-1)

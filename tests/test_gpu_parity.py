@@ -496,6 +496,76 @@ def test_gemm_random_shapes_int32_and_epilogue(M, N, K):
     assert np.array_equal(h_u16(y), oracle.epilogue(acc, sa, sw, b))
 
 
+@pytest.mark.parametrize("M,N,K", [(2048, 2048, 2048), (512, 4096, 4096), (1000, 640, 384),
+                                   (1024, 1024, 4096), (256, 512, 8192)])
+def test_gemm_k_groups_exact(M, N, K):
+    """The INT8 128 x 128 tiers (2-deep and 3-deep rings; 2048^3, 512 x 4096 x 4096,
+    ragged 1000 x 640) split each 128-byte K stage between two groups of waves, 32
+    bytes at a time (group g takes K bytes with (k // 32) % 2 == g), and add the
+    groups' INT32 accumulators through LDS after the K loop.  Codes nonzero only in
+    one group's bytes give that group's sum alone; then all codes, the raw INT32
+    and the bf16 epilogue with and without GELU, all bit-exact."""
+    say(f"gemm K groups M={M} N={N} K={K}")
+    rng = np.random.default_rng(M + N + K)
+    qa = rng.integers(-127, 128, (M, K), dtype=np.int8)
+    qw = rng.integers(-127, 128, (N, K), dtype=np.int8)
+    qw_d = d_i8(qw)
+    grp = (np.arange(K) // 32) % 2
+    for g in (0, 1):
+        qg = np.where(grp[None, :] == g, qa, 0).astype(np.int8)
+        acc = w8.gemm(d_i8(qg), None, qw_d, None, out_kind=w8.OUT_I32)
+        assert np.array_equal(h(acc), oracle.gemm_i32(qg, qw)), f"group {g}"
+    acc_ref = oracle.gemm_i32(qa, qw)
+    qa_d = d_i8(qa)
+    assert np.array_equal(h(w8.gemm(qa_d, None, qw_d, None, out_kind=w8.OUT_I32)), acc_ref)
+    sa = (rng.random(M, dtype=np.float32) * np.float32(2e-4) + np.float32(1e-6)).astype(np.float32)
+    sw = (rng.random(N, dtype=np.float32) * np.float32(2e-4) + np.float32(1e-6)).astype(np.float32)
+    b = wl.to_bf16_bits(rng.standard_normal(N).astype(np.float32))
+    sa_d, sw_d = torch.from_numpy(sa).to(DEV), torch.from_numpy(sw).to(DEV)
+    for act in (w8.ACT_NONE, w8.ACT_GELU_TANH):
+        y = w8.gemm(qa_d, sa_d, qw_d, sw_d, d_bf16(b), act=act)
+        assert np.array_equal(h_u16(y), oracle.epilogue(acc_ref, sa, sw, b, act=act)), act
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 4096, 16384), (1024, 1024, 4096), (100, 512, 8192),
+                                   (300, 640, 4096), (77, 192, 131072), (2048, 2048, 2048)])
+def test_gemm_splitk_matches_oracle(M, N, K):
+    """Split-K across workgroups (K slices of 128 x 128 tiles, INT32 partials added
+    in slice order, then the epilogue): raw INT32 and bf16 with and without GELU
+    bit-exact against the oracle and equal to w8a8_gemm; codes nonzero only in one
+    slice give that slice's sum alone; 2048^3 is not split (workspace 0)."""
+    need = w8.gemm_splitk_workspace_bytes(M, N, K)
+    S = need // (M * N * 4)
+    say(f"gemm split-K M={M} N={N} K={K} slices={S}")
+    assert (S > 1) == ((M, N, K) != (2048, 2048, 2048))
+    rng = np.random.default_rng(M * 3 + N + K)
+    qa = rng.integers(-127, 128, (M, K), dtype=np.int8)
+    qw = rng.integers(-127, 128, (N, K), dtype=np.int8)
+    qa_d, qw_d = d_i8(qa), d_i8(qw)
+    ws = torch.full((max(need, 16) + 64,), 0x5A, dtype=torch.uint8, device=DEV)
+    acc_ref = oracle.gemm_i32(qa, qw)
+    got = w8.gemm_splitk(qa_d, None, qw_d, None, out_kind=w8.OUT_I32, workspace=ws[:max(need, 16)])
+    assert np.array_equal(h(got), acc_ref)
+    assert bool((ws[max(need, 16):] == 0x5A).all())     # nothing past the workspace
+    if S > 1:
+        sl = np.arange(K) // (K // S)
+        qs = np.where(sl[None, :] == S - 1, qa, 0).astype(np.int8)
+        got = w8.gemm_splitk(d_i8(qs), None, qw_d, None, out_kind=w8.OUT_I32)
+        assert np.array_equal(h(got), oracle.gemm_i32(qs, qw)), "last slice alone"
+    sa = (rng.random(M, dtype=np.float32) * np.float32(2e-4) + np.float32(1e-6)).astype(np.float32)
+    sw = (rng.random(N, dtype=np.float32) * np.float32(2e-4) + np.float32(1e-6)).astype(np.float32)
+    b = wl.to_bf16_bits(rng.standard_normal(N).astype(np.float32))
+    sa_d, sw_d = torch.from_numpy(sa).to(DEV), torch.from_numpy(sw).to(DEV)
+    for act in (w8.ACT_NONE, w8.ACT_GELU_TANH):
+        for bias in (b, None):
+            y = h_u16(w8.gemm_splitk(qa_d, sa_d, qw_d, sw_d, d_bf16(bias) if bias is not None
+                                     else None, act=act))
+            assert np.array_equal(y, oracle.epilogue(acc_ref, sa, sw, bias, act=act)), (act, bias is None)
+            y2 = h_u16(w8.gemm(qa_d, sa_d, qw_d, sw_d, d_bf16(bias) if bias is not None else None,
+                               act=act))
+            assert np.array_equal(y, y2)
+
+
 def test_gemm_int32_extremes_and_max_k():
     say("gemm i32 extremes K=131072")
     M, N, K = 64, 64, 131072
