@@ -63,6 +63,8 @@ def parse():
                         "kernel runs back to back; print JSON, exit")
     p.add_argument("--hbm-from", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                    help="achieved HBM rate per kernel from rocprofv3 runs of --probe-hbm")
+    p.add_argument("--small-from", nargs=2, metavar=("TRACE_DIR", "PMC_DIR"),
+                   help="per-kernel duration and MFMA counters from rocprofv3 runs of --probe-small")
     p.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                    help="turn the two rocprofv3 counter outputs of --probe-traffic into "
                         + TRAFFIC_FILE + " and exit (no GPU needed)")
@@ -93,6 +95,8 @@ def stored_traffic():
 
 
 COPY_BYTES = 1 << 30  # the calibration copy reads and writes 1 GiB
+HBM_PROBE_WARM, HBM_PROBE_REPS = 20, 30  # launches per kernel in --probe-hbm
+SMALL_PROBE_WARM, SMALL_PROBE_REPS = 20, 10  # ... and in --probe-small
 
 
 def traffic_from(fetch_dir, write_dir):
@@ -143,8 +147,9 @@ def traffic_from(fetch_dir, write_dir):
 
 
 def probe_hbm():
-    """The HBM-bound kernels, each REPS times back to back on its workload (the median
-    launch of a kernel is then one at settled clocks), for rocprofv3 (kernel trace,
+    """The HBM-bound kernels, each WARM + REPS times back to back on its workload
+    (--hbm-from takes the median of each kernel's last REPS launches, at settled clocks
+    and with its buffers' translations cached), for rocprofv3 (kernel trace,
     FETCH_SIZE, WRITE_SIZE): the row quantiser on 4 rotating X [24576 x 4096] (then the
     norm + modulation, fused with the quantiser and alone, on the same inputs), GELU +
     quantise of U [24576 x 16384], the per-block Q / K quantiser (24576 tokens x 32 heads
@@ -157,7 +162,7 @@ def probe_hbm():
     import workloads as wl
 
     dev = torch.device("cuda:0")
-    REPS = 30
+    REPS = HBM_PROBE_WARM + HBM_PROBE_REPS
     src = torch.zeros((COPY_BYTES // 2,), dtype=torch.bfloat16, device=dev)
     dst = torch.empty_like(src)
     for _ in range(3):
@@ -211,7 +216,8 @@ def _small_workloads(torch, w8, wl, np, dev):
     """Operands of the small MFMA-bound kernels, as the bench's extras build them:
     the audio GEMM 2048^3 on quantised N(0,1) activations and N(0, 0.02^2)
     weights, the text projection on the fused compaction + quantisation's codes
-    of the text rows [8 x 512 x 4096], and both BF16 fallbacks."""
+    of the text rows [8 x 512 x 4096], both BF16 fallbacks, and a 256-row
+    sequence through the FFN down projection, plain and split-K."""
     gen = torch.Generator(device=dev).manual_seed(0)
     out = {}
     xa = torch.randn((2048, 2048), device=dev, generator=gen).to(torch.bfloat16)
@@ -245,12 +251,26 @@ def _small_workloads(torch, w8, wl, np, dev):
     yfb = torch.empty((2048, 2048), dtype=torch.bfloat16, device=dev)
     out["fallback_bf16_K2050"] = (lambda: w8.linear_bf16(xb, wfb, bfb, y=yfb),
                                   2.0 * 2048 * 2048 * 2050, "bf16")
+    # a short sequence through the FFN down projection, plain and split-K
+    Ms, Ns, Ks = 256, 4096, 16384
+    qs, ss = w8.quantize_rows(torch.randn((Ms, Ks), device=dev, generator=gen).to(torch.bfloat16))
+    qws, sws = w8.quantize_rows((torch.randn((Ns, Ks), device=dev, generator=gen) * 0.02)
+                                .to(torch.bfloat16))
+    bs = (torch.randn((Ns,), device=dev, generator=gen) * 0.01).to(torch.bfloat16)
+    ys = torch.empty((Ms, Ns), dtype=torch.bfloat16, device=dev)
+    wss = torch.empty((w8.gemm_splitk_workspace_bytes(Ms, Ns, Ks),), dtype=torch.uint8, device=dev)
+    out["gemm_256x4096x16384"] = (lambda: w8.gemm(qs, ss, qws, sws, bs, out=ys),
+                                  2.0 * Ms * Ns * Ks, "int8")
+    out["gemm_splitk_256x4096x16384"] = (
+        lambda: w8.gemm_splitk(qs, ss, qws, sws, bs, out=ys, workspace=wss), 2.0 * Ms * Ns * Ks,
+        "int8")
     return out, mc
 
 
 def probe_small():
-    """The small MFMA-bound kernels, each 10 times back to back on its workload,
-    for rocprofv3 (kernel trace and counters)."""
+    """The small MFMA-bound kernels, each SMALL_PROBE_WARM + SMALL_PROBE_REPS times back
+    to back on its workload, for rocprofv3 (kernel trace and counters; a summary takes
+    each kernel's last SMALL_PROBE_REPS launches)."""
     import numpy as np
     import torch
 
@@ -260,7 +280,7 @@ def probe_small():
     dev = torch.device("cuda:0")
     work, mc = _small_workloads(torch, w8, wl, np, dev)
     for name, (fn, _, _) in work.items():
-        for _ in range(10):
+        for _ in range(SMALL_PROBE_WARM + SMALL_PROBE_REPS):
             fn()
         torch.cuda.synchronize()
         log(f"probe-small: {name} done")
@@ -269,10 +289,12 @@ def probe_small():
 
 def power_clock():
     """Shader clock and package power while each main kernel runs back to back for
-    1.5 s.  A thread reads amdsmi's GPU metrics table every ~5 ms and keeps each
-    new table (its firmware timestamp changed): gfx clock of every XCD, the energy
-    accumulator, and the accumulated time the package power tracking (PPT) limit
-    held the clock down.  Reported per kernel: mean clock, power from the energy
+    4 s (small kernels 3 s).  A thread reads amdsmi's GPU metrics table every ~2 ms
+    and keeps each new table (the firmware refreshes it a few times a second): gfx
+    clock of every XCD, the energy accumulator, and the accumulated time the package
+    power tracking (PPT) limit held the clock down.  Power = energy between the
+    first and the last new table inside the busy window over the host time between
+    them.  Reported per kernel: mean clock, power from the energy
     accumulator over the window, the share of the window spent PPT-limited, and
     the rate as a fraction of the peak at the measured clock."""
     import threading
@@ -311,7 +333,7 @@ def power_clock():
                 "clk": float(np.mean(clks)) if clks else num(m.get("current_gfxclk")),
                 "power": num(m.get("current_socket_power"))}
 
-    def run(fn, seconds=1.5):
+    def run(fn, seconds=4.0):
         snaps = []
         stop = threading.Event()
 
@@ -321,11 +343,12 @@ def power_clock():
                 try:
                     sn = snapshot()
                     if sn["ts"] != last:
+                        sn["host"] = time.perf_counter()
                         snaps.append(sn)
                         last = sn["ts"]
                 except Exception:
                     pass
-                time.sleep(0.005)
+                time.sleep(0.002)
 
         for _ in range(10):   # settle the clocks on this kernel first
             fn()
@@ -357,7 +380,9 @@ def power_clock():
             out["socket_power_W_mean"] = round(float(np.mean(pw)), 1)
         a, b = (inner[0], inner[-1]) if len(inner) >= 2 else (None, None)
         if a and b and a["ts"] and b["ts"] and b["ts"] > a["ts"]:
-            dt = (b["ts"] - a["ts"]) / 1e8                         # 100 MHz timestamp
+            dt = b["host"] - a["host"]          # between the first and last new tables
+            out["table_period_s"] = round(dt / (len(inner) - 1), 3)
+            out["firmware_ticks_per_s"] = round((b["ts"] - a["ts"]) / dt, -6)
             if a["energy"] is not None and b["energy"] is not None:
                 out["energy_power_W"] = round((b["energy"] - a["energy"]) * res_uj * 1e-6 / dt, 1)
             if a["ppt"] is not None and a["acc"] and b["acc"] > a["acc"]:
@@ -405,7 +430,7 @@ def power_clock():
     del u, qh, y
     small, _ = _small_workloads(torch, w8, wl, np, dev)
     for name, (fn, work, kind) in small.items():
-        r = run(fn, 1.0)
+        r = run(fn, 3.0)
         peak = PEAK_INT8_TOPS if kind == "int8" else PEAK_BF16_TFLOPS
         r["TOPS"] = round(work / (r["ms_per_call"] * 1e-3) / 1e12, 1)
         r["frac_peak"] = round(r["TOPS"] / peak, 4)
@@ -428,9 +453,11 @@ def hbm_from(trace_dir, fetch_dir, write_dir):
         return out
 
     dur = {}
-    for r in rows(trace_dir, "*kernel_trace.csv"):
+    for r in sorted(rows(trace_dir, "*kernel_trace.csv"), key=lambda r: int(r["Start_Timestamp"])):
         dur.setdefault(r["Kernel_Name"], []).append(
             (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9)
+    # each kernel's last HBM_PROBE_REPS launches (the first HBM_PROBE_WARM warm up)
+    dur = {k: v[-HBM_PROBE_REPS:] for k, v in dur.items()}
 
     def counter(d, name):
         per = {}
@@ -463,6 +490,57 @@ def hbm_from(trace_dir, fetch_dir, write_dir):
     print(json.dumps(out, indent=1))
 
 
+def small_from(trace_dir, pmc_dir):
+    """Per-kernel duration (kernel trace, median of each kernel's last SMALL_PROBE_REPS
+    launches) and MFMA counters (SQ_INSTS_MFMA, SQ_VALU_MFMA_BUSY_CYCLES, median launch)
+    of --probe-small: the rate the matrix cores were issued at, and their busy share of
+    the 1024 SIMDs at 2.4 GHz over the kernel's duration."""
+    import csv
+    import glob
+    import re
+
+    def rows(d, pat):
+        out = []
+        for f in glob.glob(os.path.join(d, "**", pat), recursive=True):
+            out += list(csv.DictReader(open(f)))
+        return out
+
+    def short(k):  # the kernel with its template arguments, without namespaces and parameters
+        k = re.sub(r"w8a8::\(anonymous namespace\)::", "", k)
+        return re.sub(r"^void |\([^()]*\)$", "", k)
+
+    def mine(k):
+        return "gemm_tiled" in k or "splitk_reduce" in k
+
+    dur = {}
+    for r in sorted(rows(trace_dir, "*kernel_trace.csv"), key=lambda r: int(r["Start_Timestamp"])):
+        if mine(r["Kernel_Name"]):
+            dur.setdefault(short(r["Kernel_Name"]), []).append(
+                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9)
+    per = {}
+    for r in rows(pmc_dir, "*counter_collection.csv"):
+        if mine(r["Kernel_Name"]):
+            k = (short(r["Kernel_Name"]), r["Dispatch_Id"])
+            per.setdefault(k, {}).setdefault(r["Counter_Name"], 0.0)
+            per[k][r["Counter_Name"]] += float(r["Counter_Value"])
+    cnt = {}
+    for (kn, _), v in per.items():
+        cnt.setdefault(kn, []).append(v)
+    out = {}
+    for k, ds in dur.items():
+        ds = ds[-SMALL_PROBE_REPS:]
+        t = sorted(ds)[len(ds) // 2]
+        r = {"launches": len(ds), "median_us": round(t * 1e6, 2)}
+        cs = cnt.get(k, [])
+        if cs and "SQ_INSTS_MFMA" in cs[0]:
+            c = cs[len(cs) // 2]
+            n, busy = c["SQ_INSTS_MFMA"], c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0)
+            ops = n * (65536 if "ElemI8" in k else 32768)  # 32x32x32 int8 / 32x32x16 bf16
+            r.update({"mfma": int(n), "mfma_busy_cycles": int(busy),
+                      "issued_TOPS": round(ops / t / 1e12, 1),
+                      "mfma_busy_frac_at_2.4GHz": round(busy / (1024 * t * 2.4e9), 4)})
+        out[k] = r
+    print(json.dumps(out, indent=1))
 
 
 def main():
@@ -481,6 +559,9 @@ def main():
         return
     if args.hbm_from:
         hbm_from(*args.hbm_from)
+        return
+    if args.small_from:
+        small_from(*args.small_from)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: this path has no multi-GPU mode "
