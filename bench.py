@@ -405,12 +405,18 @@ def power_clock():
     u = w8.gemm(qx, sx, qw1, sw1, b1)
     qh, sh = w8.gelu_quantize_rows(u)
     y = torch.empty((M, D), dtype=torch.bfloat16, device=dev)
+    gen = torch.Generator(device=dev).manual_seed(0)
+    shm, scm = [(torch.randn((8, D), device=dev, generator=gen) * 0.3).to(torch.bfloat16)
+                for _ in range(2)]
     ops = 2.0 * M * F * D
     for name, fn, work, unit in (
             ("gemm_up", lambda: w8.gemm(qx, sx, qw1, sw1, b1, out=u), ops, "int8"),
             ("gemm_down", lambda: w8.gemm(qh, sh, qw2, sw2, b2, out=y), ops, "int8"),
             ("quantize_x", lambda: w8.quantize_rows(x, qx, sx), 3.0 * M * D + 4 * M, "bytes"),
-            ("gelu_quantize_u", lambda: w8.gelu_quantize_rows(u, qh, sh), 3.0 * M * F + 4 * M, "bytes")):
+            ("gelu_quantize_u", lambda: w8.gelu_quantize_rows(u, qh, sh), 3.0 * M * F + 4 * M, "bytes"),
+            ("norm_mod_quantize_x", lambda: w8.norm_mod_quantize_rows(x, shm, scm, M // 8, q=qx, qscale=sx),
+             3.0 * M * D + 4 * M, "bytes"),
+            ("norm_mod_bf16_x", lambda: w8.norm_mod_bf16(x, shm, scm, M // 8, y=y), 4.0 * M * D, "bytes")):
         r = run(fn)
         t = r["ms_per_call"] * 1e-3
         if unit == "int8":

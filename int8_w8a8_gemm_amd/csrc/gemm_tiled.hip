@@ -203,43 +203,24 @@ struct Cfg {
 #endif
 typedef Cfg<W8A8_XL_CFG> CfgXL;
 typedef Cfg<W8A8_LARGE_CFG> CfgLarge;
-#ifndef W8A8_SMALL_CFG
-#define W8A8_SMALL_CFG 128, 128, 2, 2, 128, 2
-#endif
 typedef Cfg<W8A8_MID_CFG> CfgMid;
+// The small tiers split K between two groups of waves (two waves per SIMD, so
+// each hides the other's fragment-read latency): INT8 2048^3 and 512 x 4096 x
+// 4096 20.4 -> 18.0 us; BF16 2048^3 22.1 -> 20.7 us, 512 x 4096 x 4096
+// 36.4 -> 30.2 us (the BF16 fp32 sums then add two partial chains).
+#ifndef W8A8_SMALL_CFG
+#define W8A8_SMALL_CFG 128, 128, 2, 2, 128, 2, GROUP_ROWS, 2
+#endif
 typedef Cfg<W8A8_SMALL_CFG> CfgSmall;
 // small tiles with a 3-deep ring, for K loops of 32 stages or more (see launch_tiles)
 #ifndef W8A8_SMALL_DEEP_CFG
-#define W8A8_SMALL_DEEP_CFG 128, 128, 2, 2, 128, 3
+#define W8A8_SMALL_DEEP_CFG 128, 128, 2, 2, 128, 3, GROUP_ROWS, 2
 #endif
 typedef Cfg<W8A8_SMALL_DEEP_CFG> CfgSmallDeep;
-typedef Cfg<64, 64, 2, 2, 128, 2> CfgTiny;
-// INT8 variants of the small tiers split K between two groups of waves (two
-// waves per SIMD, so each hides the other's fragment-read latency); BF16 keeps
-// one group, so its fp32 sums keep the order of a single chain.
-#ifndef W8A8_SMALL_I8_CFG
-#define W8A8_SMALL_I8_CFG 128, 128, 2, 2, 128, 2, GROUP_ROWS, 2
+#ifndef W8A8_TINY_CFG
+#define W8A8_TINY_CFG 64, 64, 2, 2, 128, 2
 #endif
-#ifndef W8A8_SMALL_DEEP_I8_CFG
-#define W8A8_SMALL_DEEP_I8_CFG 128, 128, 2, 2, 128, 3, GROUP_ROWS, 2
-#endif
-#ifndef W8A8_TINY_I8_CFG
-#define W8A8_TINY_I8_CFG 64, 64, 2, 2, 128, 2
-#endif
-typedef Cfg<W8A8_SMALL_I8_CFG> CfgSmallI8;
-typedef Cfg<W8A8_SMALL_DEEP_I8_CFG> CfgSmallDeepI8;
-typedef Cfg<W8A8_TINY_I8_CFG> CfgTinyI8;
-// The small tiers for element type E.
-template <class E> struct SmallTiers {
-    typedef CfgSmall Small;
-    typedef CfgSmallDeep Deep;
-    typedef CfgTiny Tiny;
-};
-template <> struct SmallTiers<ElemI8> {
-    typedef CfgSmallI8 Small;
-    typedef CfgSmallDeepI8 Deep;
-    typedef CfgTinyI8 Tiny;
-};
+typedef Cfg<W8A8_TINY_CFG> CfgTiny;
 
 template <int BK>
 __device__ __forceinline__ int swz(int r, int c) {
@@ -1010,9 +991,9 @@ hipError_t launch_tiles(const void* a, const float* sa, int64_t M, const void* w
         return launch_cfg<CfgLarge, E, OUT_I32, ACT, VEC_OUT>(a, sa, M, w, sw, N, K, bias, out, cus,
                                                              stream);
     }
-    typedef typename SmallTiers<E>::Small CSmall;
-    typedef typename SmallTiers<E>::Deep CDeep;
-    typedef typename SmallTiers<E>::Tiny CTiny;
+    typedef CfgSmall CSmall;
+    typedef CfgSmallDeep CDeep;
+    typedef CfgTiny CTiny;
     if (2 * tile_count<CSmall>(M, N) >= cus) {
         // A 3-deep ring keeps two stages of loads in flight: with one wave per
         // SIMD and 512 cycles of MFMAs per stage, the 2-deep ring's per-stage
