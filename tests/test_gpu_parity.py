@@ -1193,10 +1193,14 @@ def test_fallback_tiled_path(M, N, K, act):
 
 # The tiled BF16 path with a K tail (K even, K % 64 != 0, rows 4-byte aligned):
 # the last stage's loads run on into the next row and are masked.  K = 2 is a
-# single partial stage; 2048 x 2048 x 2050 is the fallback workload; 4100 x
-# 4100 runs 192 x 256 tiles, 3900 x 4032 256 x 256 tiles.
+# single partial stage; 2048 x 2048 x 2050 is the fallback workload (128 x 128
+# tiles, K split between two wave groups, 3-deep ring); 1024 x 2048 x 1026 and
+# x 1042 the same tiles on the 2-deep ring with last stages of 4 and 36 bytes
+# (the second reaches the other wave group's 32-byte sub-step); 4100 x 4100
+# runs 192 x 256 tiles, 3900 x 4032 256 x 256 tiles.
 @pytest.mark.parametrize("M,N,K", [(300, 100, 2), (97, 256, 66), (257, 192, 130),
-                                   (2048, 2048, 2050), (4100, 4100, 190), (3900, 4032, 130)])
+                                   (2048, 2048, 2050), (1024, 2048, 1026), (1024, 2048, 1042),
+                                   (4100, 4100, 190), (3900, 4032, 130)])
 @pytest.mark.parametrize("act", [w8.ACT_NONE, w8.ACT_GELU_TANH])
 def test_fallback_tiled_k_tail(M, N, K, act):
     say(f"fallback tiled K tail M={M} N={N} K={K} act={act}")
