@@ -31,29 +31,41 @@ namespace {
 
 // ---------------------------------------------------------------------------
 // A workgroup of WM x WN waves owns a BM x BN output tile; wave (wm, wn) owns
-// (BM/WM) x (BN/WN) outputs, i.e. MI x NI tiles of 32 x 32 MFMA accumulators.
+// (BM/WM) x (BN/WN) outputs, i.e. MI x NI MFMA tiles of MT x MT accumulators.
 // K is staged BK bytes at a time through an NST-deep ring of LDS buffers.
-// Five configurations:
-//   xl:    384 x 256 tile (INT8 without GELU only), 4 x 2 waves of 96 x 128:
-//          7 fragment reads per 12 MFMAs instead of 6 per 8, and 17% fewer
-//          operand bytes per MFMA.  Its two 80 KB K stages fill the LDS, so
-//          the tile's scales live in the ring once the K loop is done, and its
-//          192 accumulators leave no room for a second set of fragments.
+// Two MFMA shapes, both 1024 multiply-adds per SIMD per clock:
+// v_mfma_i32_32x32x32_i8 / v_mfma_f32_32x32x16_bf16 (MT = 32: 32 bytes of K
+// per instruction, 16 accumulator registers per lane) and
+// v_mfma_i32_16x16x64_i8 / v_mfma_f32_16x16x32_bf16 (MT = 16: 64 bytes of K,
+// 4 registers).  The INT8 GEMM's rate is set by the package power limit, so
+// energy per operation is what counts: a loop of MFMAs alone on quantised
+// N(0,1)-like codes ran the 16 x 16 shape at 4.08 POPS (0.64 pJ per
+// multiply-add) against 3.50 POPS (0.74 pJ) for 32 x 32, on the same GPU.  A
+// 16 x 16 sub-step covers 64 bytes of K, so a wave holds twice as many live
+// fragments; the tiers whose registers allow it take that shape.
+// Four configurations:
 //   large: 256 x 256 tile, 4 x 2 waves (two per SIMD, so one wave's load issue,
 //          LDS waits and barrier arrival overlap the other's MFMAs), each wave
-//          64 x 128.
-//   mid:   192 x 256 tile, 2 x 4 waves of 96 x 64: three quarters of a large
-//          tile's work, for row counts where large tiles leave many CUs idle
-//          in their last round (the ~2300-row text projection: 160 large
-//          tiles or 208 mid ones on 256 CUs).
-//   small: 128 x 128 tile, 2 x 2 waves of 64 x 64 (a 3-deep K ring for long
-//          K loops).
+//          64 x 128; 16 x 16 MFMAs (INT8 and BF16).  The 32 x 32 version of
+//          the same tile ran FFN up 24576 x 16384 x 4096 in 1332 us against
+//          1243 us, and a 384 x 256 tile of 96 x 128 per wave (17% fewer
+//          operand bytes per MFMA, 32 x 32 MFMAs: with 16 x 16 its accumulators
+//          and fragments outgrow the 256 registers of a wave at two per SIMD)
+//          ran 1280 us, 8192^3 7.7% and 4096^3 8.5% slower than this tile.
+//   mid:   192 x 256 tile, 2 x 4 waves of 96 x 64, 16 x 16 MFMAs for INT8:
+//          three quarters of a large tile's work, for row counts where large
+//          tiles leave many CUs idle in their last round (the ~2300-row text
+//          projection: 160 large tiles or 208 mid ones on 256 CUs; 16 x 16
+//          MFMAs took it from 41.1 to 39.6 us).
+//   small: 128 x 128 tile, 2 x 2 waves of 64 x 64, K split between two groups
+//          of waves (a 3-deep K ring for long K loops); 32 x 32 MFMAs (16 x 16
+//          ran 2048^3 and 512 x 4096 x 4096 12-15% slower).
 //   tiny:  64 x 64 tile, 2 x 2 waves of 32 x 32.
 // The launcher takes the largest of large/small/tiny whose tile count covers
 // at least half of the CUs (a large tile on a CU still outruns four small
 // ones; measured on the 2378-row text projection, the 2048^3 audio GEMM and
-// 1024 x 1024 x 4096), then xl or mid instead of large where their rounds of
-// tiles per CU cost less (see launch_tiles).
+// 1024 x 1024 x 4096), then mid instead of large where its rounds of tiles per
+// CU cost less (see launch_tiles).
 //
 // * Operands go global -> LDS directly (buffer_load_dwordx4 ... lds): a wave
 //   instruction moves 1 KB (64 lanes x 16 bytes); lane l lands at LDS offset
@@ -62,8 +74,9 @@ namespace {
 //   position is a scalar offset; each load's lane offset is formed from two
 //   per-lane values and wave-uniform terms as it is issued (stage_load_one).
 // * An LDS row r (BK bytes = BK/16 chunks) stores logical K-chunk c at physical
-//   chunk c ^ f(r).  A fragment read has lane l on row l % 32 at logical chunk
-//   l / 32; with f(r) = (r ^ (r >> 3)) & 7 for 128-byte rows and (r >> 2) & 3
+//   chunk c ^ f(r).  A fragment read has lane l on row l % MT at logical chunk
+//   l / MT of the sub-step (each 16 lanes read 16 consecutive rows at one
+//   chunk); with f(r) = (r ^ (r >> 3)) & 7 for 128-byte rows and (r >> 2) & 3
 //   for 64-byte rows these reads are free of LDS bank conflicts on gfx950
 //   (measured with the SQ_LDS_BANK_CONFLICT counter; LDS serves 256 bytes per
 //   clock, so a conflict-free ds_read_b128 takes 4 clocks).
@@ -76,18 +89,13 @@ namespace {
 //   reads and loads within a sub-step is fixed with sched_barrier.
 // * Tile order is XCD-aware: workgroup b runs on XCD b % 8, so each XCD is
 //   given a contiguous range of tiles, walked in groups of GROUP_M tile-rows
-//   (1024 rows; 1536 for the 384-row tiles: the 32 tiles an XCD runs at once
-//   then form a 4 x 8 block, which halved the 384 x 256 kernel's operand
-//   fetches beyond L2 and made it 1.0-1.4% faster than 768-row groups).
+//   (1024 rows: the 32 large tiles an XCD runs at once form a 4 x 8 block).
 // ---------------------------------------------------------------------------
 constexpr int NUM_XCD = 8;
 // The W8A8_* macros below are the tuned defaults; each can be overridden on
 // the compiler command line to measure an alternative.
 #ifndef W8A8_GROUP_ROWS
 #define W8A8_GROUP_ROWS 1024
-#endif
-#ifndef W8A8_XL_GROUP_ROWS
-#define W8A8_XL_GROUP_ROWS 1536
 #endif
 constexpr int GROUP_ROWS = W8A8_GROUP_ROWS;
 // Cache policy of the operand loads: sc0 (bit 0).  Each stage's data is used
@@ -106,27 +114,47 @@ constexpr int GROUP_ROWS = W8A8_GROUP_ROWS;
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Operand element types.  mfma() takes 16 bytes of weight row (A operand) and
-// activation row (B operand) per lane and accumulates a 32 x 32 tile.
+// Operand element types.  Mfma<MT>::run takes 16 bytes of weight row (A
+// operand) and activation row (B operand) per lane and accumulates an MT x MT
+// tile over 32 bytes of K (MT = 32) or 64 bytes (MT = 16).
 struct ElemI8 {
     static constexpr int BYTES = 1;
+    template <int MT> struct Mfma;
+};
+template <> struct ElemI8::Mfma<32> {
     typedef v16i acc_t;
-    static __device__ __forceinline__ acc_t mfma(v4i w, v4i a, acc_t c) {
+    static __device__ __forceinline__ acc_t run(v4i w, v4i a, acc_t c) {
         return __builtin_amdgcn_mfma_i32_32x32x32_i8(w, a, c, 0, 0, 0);
+    }
+};
+template <> struct ElemI8::Mfma<16> {
+    typedef v4i acc_t;
+    static __device__ __forceinline__ acc_t run(v4i w, v4i a, acc_t c) {
+        return __builtin_amdgcn_mfma_i32_16x16x64_i8(w, a, c, 0, 0, 0);
     }
 };
 
 struct ElemBF16 {
     static constexpr int BYTES = 2;
+    template <int MT> struct Mfma;
+};
+template <> struct ElemBF16::Mfma<32> {
     typedef v16f acc_t;
-    static __device__ __forceinline__ acc_t mfma(v4i w, v4i a, acc_t c) {
+    static __device__ __forceinline__ acc_t run(v4i w, v4i a, acc_t c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, w),
+                                                       __builtin_bit_cast(v8bf, a), c, 0, 0, 0);
+    }
+};
+template <> struct ElemBF16::Mfma<16> {
+    typedef v4f acc_t;
+    static __device__ __forceinline__ acc_t run(v4i w, v4i a, acc_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, w),
                                                        __builtin_bit_cast(v8bf, a), c, 0, 0, 0);
     }
 };
 
 template <int BM_, int BN_, int WM_, int WN_, int BK_, int NST_, int GROUP_ROWS_ = GROUP_ROWS,
-          int KS_ = 1, bool SPLIT_ = false>
+          int KS_ = 1, bool SPLIT_ = false, int MT_ = 32>
 struct Cfg {
     static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_, NST = NST_;
     static constexpr int GROUP_M = GROUP_ROWS_ / BM;  // tile-rows per group of the raster
@@ -142,19 +170,24 @@ struct Cfg {
     static constexpr int WAVES = WG * KS;
     static constexpr int THREADS = WAVES * 64;
     static constexpr int TM = BM / WM, TN = BN / WN;  // outputs per wave
-    static constexpr int MI = TM / 32;                 // 32-row MFMA tiles per wave along M
-    static constexpr int NI = TN / 32;                 // 32-col MFMA tiles per wave along N
+    // MFMA tile: MT x MT outputs over KSUB bytes of K, ACC_N accumulator
+    // registers per lane (32 x 32 x 32 bytes or 16 x 16 x 64 bytes)
+    static constexpr int MT = MT_;
+    static constexpr int KSUB = MT == 16 ? 64 : 32;
+    static constexpr int ACC_N = MT * MT / 64;
+    static constexpr int MI = TM / MT;                 // MFMA tiles per wave along M
+    static constexpr int NI = TN / MT;                 // MFMA tiles per wave along N
     static constexpr int NQ = MI + NI;                 // fragments per sub-step
     static constexpr int NMFMA = MI * NI;              // MFMAs per sub-step
     // Fragment registers: with room to spare the next sub-step's fragments go
     // to fresh registers early in the sub-step; where the accumulators leave
     // no room (RECYCLE) each is read into the register of the fragment it
     // replaces, right after that fragment's last MFMA.
-    static constexpr bool RECYCLE = NMFMA * 16 + 2 * NQ * 4 > 200;
+    static constexpr bool RECYCLE = NMFMA * ACC_N + 2 * NQ * 4 > 200;
     static constexpr int CPR = BK / 16;                // 16-byte chunks per LDS row
     static constexpr int RPI = 64 / CPR;               // rows one 1-KB wave instruction fills
     static constexpr int STAGE = (BM + BN) * BK;       // bytes per stage (A tile then B tile)
-    static constexpr int SUB = BK / 32;                // 32-byte MFMA sub-steps per stage
+    static constexpr int SUB = BK / KSUB;              // MFMA sub-steps per stage
     static constexpr int SUBW = SUB / KS;              // ... of them for each wave
     static constexpr int LPW_A = BM / WAVES / RPI;     // A load instructions per wave per stage
     static constexpr int LPW_B = BN / WAVES / RPI;     // B load instructions per wave per stage
@@ -162,7 +195,9 @@ struct Cfg {
     static constexpr int WAVES_PER_SIMD = (WAVES + 3) / 4;
     // epilogue staging (see store_bf16)
     static constexpr int OUT_ROW = BN * 2 + 16;        // bytes per staged output row
-    static constexpr int SROWS = BM / MI;              // staged rows per pass (= WM * 32)
+    static constexpr int PM = 32 / MT;                 // MFMA row tiles per staging pass
+    static constexpr int NPASS = MI / PM;              // staging passes
+    static constexpr int SROWS = WM * 32;              // staged rows per pass
     static constexpr int RCH = BN / 8;                 // 16-byte chunks per output row
     static constexpr int RPINS = 64 / RCH;             // output rows per copy-out instruction
     static constexpr int RPW = SROWS / WAVES;          // staged rows each wave copies per pass
@@ -172,7 +207,7 @@ struct Cfg {
     // 160 KB of LDS, the scales go in the ring above the staging area instead:
     // they are then written only once the K loop is done with the ring.
     // bytes the groups g > 0 pass their accumulators through (KS > 1)
-    static constexpr int RED_WAVE = NI * MI * 16 * 64 * 4;
+    static constexpr int RED_WAVE = NI * MI * ACC_N * 64 * 4;
     static constexpr int RED_BYTES = (KS - 1) * WG * RED_WAVE;
     static constexpr int RING0 = NST * STAGE > STAGE + EPI_BYTES ? NST * STAGE : STAGE + EPI_BYTES;
     static constexpr int RING = RING0 > RED_BYTES ? RING0 : RED_BYTES;
@@ -183,6 +218,7 @@ struct Cfg {
     static_assert(SMEM <= 160 * 1024 && SCALE_OFF + SCALE_BYTES <= SMEM, "LDS budget");
     static_assert(BM % (WAVES * RPI) == 0 && BN % (WAVES * RPI) == 0, "load split");
     static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile");
+    static_assert((MT == 16 || MT == 32) && BK % KSUB == 0, "MFMA tile");
     static_assert(RPW % RPINS == 0 && 32 % RPW == 0, "copy-out rows per wave");
     static constexpr int SA_PT = (BM + THREADS - 1) / THREADS;  // row scales per thread
     static constexpr int SW_PT = (BN + THREADS - 1) / THREADS;  // column scales per thread
@@ -191,36 +227,67 @@ struct Cfg {
     static_assert(KS == 1 || !SCALES_IN_RING, "the K-group reduction uses the ring");
 };
 
-// Tile configurations: BM, BN, WM, WN, BK, NST[, raster group rows].
-#ifndef W8A8_XL_CFG
-#define W8A8_XL_CFG 384, 256, 4, 2, 128, 2, W8A8_XL_GROUP_ROWS
-#endif
+// Tile configurations: BM, BN, WM, WN, BK, NST, raster group rows, K groups,
+// split-K; the MFMA tile edge (32 or 16) is set per tier and element type below.
 #ifndef W8A8_LARGE_CFG
-#define W8A8_LARGE_CFG 256, 256, 4, 2, 128, 2
+#define W8A8_LARGE_CFG 256, 256, 4, 2, 128, 2, GROUP_ROWS, 1, false
 #endif
 #ifndef W8A8_MID_CFG
-#define W8A8_MID_CFG 192, 256, 2, 4, 128, 2
+#define W8A8_MID_CFG 192, 256, 2, 4, 128, 2, GROUP_ROWS, 1, false
 #endif
-typedef Cfg<W8A8_XL_CFG> CfgXL;
-typedef Cfg<W8A8_LARGE_CFG> CfgLarge;
-typedef Cfg<W8A8_MID_CFG> CfgMid;
 // The small tiers split K between two groups of waves (two waves per SIMD, so
 // each hides the other's fragment-read latency): INT8 2048^3 and 512 x 4096 x
 // 4096 20.4 -> 18.0 us; BF16 2048^3 22.1 -> 20.7 us, 512 x 4096 x 4096
 // 36.4 -> 30.2 us (the BF16 fp32 sums then add two partial chains).
 #ifndef W8A8_SMALL_CFG
-#define W8A8_SMALL_CFG 128, 128, 2, 2, 128, 2, GROUP_ROWS, 2
+#define W8A8_SMALL_CFG 128, 128, 2, 2, 128, 2, GROUP_ROWS, 2, false
 #endif
-typedef Cfg<W8A8_SMALL_CFG> CfgSmall;
 // small tiles with a 3-deep ring, for K loops of 32 stages or more (see launch_tiles)
 #ifndef W8A8_SMALL_DEEP_CFG
-#define W8A8_SMALL_DEEP_CFG 128, 128, 2, 2, 128, 3, GROUP_ROWS, 2
+#define W8A8_SMALL_DEEP_CFG 128, 128, 2, 2, 128, 3, GROUP_ROWS, 2, false
 #endif
-typedef Cfg<W8A8_SMALL_DEEP_CFG> CfgSmallDeep;
 #ifndef W8A8_TINY_CFG
-#define W8A8_TINY_CFG 64, 64, 2, 2, 128, 2
+#define W8A8_TINY_CFG 64, 64, 2, 2, 128, 2, GROUP_ROWS, 1, false
 #endif
-typedef Cfg<W8A8_TINY_CFG> CfgTiny;
+// MFMA tile edge of each tier, INT8 and BF16.
+#ifndef W8A8_I8_LARGE_MT
+#define W8A8_I8_LARGE_MT 16
+#endif
+#ifndef W8A8_I8_MID_MT
+#define W8A8_I8_MID_MT 16
+#endif
+#ifndef W8A8_I8_SMALL_MT
+#define W8A8_I8_SMALL_MT 32
+#endif
+#ifndef W8A8_I8_TINY_MT
+#define W8A8_I8_TINY_MT 32
+#endif
+#ifndef W8A8_BF16_LARGE_MT
+#define W8A8_BF16_LARGE_MT 16
+#endif
+#ifndef W8A8_BF16_MID_MT
+#define W8A8_BF16_MID_MT 32
+#endif
+#ifndef W8A8_BF16_SMALL_MT
+#define W8A8_BF16_SMALL_MT 32
+#endif
+#ifndef W8A8_BF16_TINY_MT
+#define W8A8_BF16_TINY_MT 32
+#endif
+template <class E> struct Tiers {  // BF16
+    typedef Cfg<W8A8_LARGE_CFG, W8A8_BF16_LARGE_MT> Large;
+    typedef Cfg<W8A8_MID_CFG, W8A8_BF16_MID_MT> Mid;
+    typedef Cfg<W8A8_SMALL_CFG, W8A8_BF16_SMALL_MT> Small;
+    typedef Cfg<W8A8_SMALL_DEEP_CFG, W8A8_BF16_SMALL_MT> Deep;
+    typedef Cfg<W8A8_TINY_CFG, W8A8_BF16_TINY_MT> Tiny;
+};
+template <> struct Tiers<ElemI8> {
+    typedef Cfg<W8A8_LARGE_CFG, W8A8_I8_LARGE_MT> Large;
+    typedef Cfg<W8A8_MID_CFG, W8A8_I8_MID_MT> Mid;
+    typedef Cfg<W8A8_SMALL_CFG, W8A8_I8_SMALL_MT> Small;
+    typedef Cfg<W8A8_SMALL_DEEP_CFG, W8A8_I8_SMALL_MT> Deep;
+    typedef Cfg<W8A8_TINY_CFG, W8A8_I8_TINY_MT> Tiny;
+};
 
 template <int BK>
 __device__ __forceinline__ int swz(int r, int c) {
@@ -288,7 +355,7 @@ struct Ctx {
     int kofs;  // first K byte of the work item's slice (split-K), else 0
     // fragment reads: LDS byte offset of this lane's row in the wave's first
     // activation / weight sub-tile, and 16 x the physical chunk of its K-chunk
-    // (lane >> 5) in that row; every other read adds compile-time constants
+    // (lane / MT) in that row; every other read adds compile-time constants
     uint32_t fa, fw, ga, gw;
     int wave, lane, wm, wn, kg;  // kg: the wave's K group
 };
@@ -319,14 +386,17 @@ __device__ __forceinline__ void lane_ctx(Ctx<C>& c, int lane) {
     // 128-byte rows: swz(r0 + rsub, pc) = pc ^ rsub ^ ((r0 >> 3) & 7) for r0 % 8 == 0;
     // 64-byte rows: swz(r0 + rsub, pc) = pc ^ ((rsub >> 2) & 3) for r0 % 16 == 0
     c.lx = C::BK == 128 ? 16u * (uint32_t)(pc ^ rsub) : 16u * (uint32_t)(pc ^ ((rsub >> 2) & 3));
-    const int hi = (int)((unsigned)lane >> 5);
-    const int ra = c.wm * C::TM + (lane & 31), rw = c.wn * C::TN + (lane & 31);
+    // lane l reads row l % MT of a sub-tile at K-chunk l / MT of the sub-step
+    const int hi = (int)((unsigned)lane / C::MT);
+    const int lr = (int)((unsigned)lane % C::MT);
+    const int ra = c.wm * C::TM + lr, rw = c.wn * C::TN + lr;
     c.fa = (uint32_t)(ra * C::BK);
     c.fw = (uint32_t)(C::BM * C::BK + rw * C::BK);
-    // a K group's sub-steps are kg, kg + KS, ...: 32 * kg shares no bit with
-    // 32 * KS * (the wave's own sub-step), so it joins the per-lane XOR term
-    c.ga = (16u * (uint32_t)swz<C::BK>(ra, hi)) ^ (32u * (uint32_t)c.kg);
-    c.gw = (16u * (uint32_t)swz<C::BK>(rw, hi)) ^ (32u * (uint32_t)c.kg);
+    // a K group's sub-steps are kg, kg + KS, ...: KSUB * kg shares no bit with
+    // KSUB * KS * (the wave's own sub-step) or with 16 * hi, so it joins the
+    // per-lane XOR term
+    c.ga = (16u * (uint32_t)swz<C::BK>(ra, hi)) ^ ((uint32_t)C::KSUB * (uint32_t)c.kg);
+    c.gw = (16u * (uint32_t)swz<C::BK>(rw, hi)) ^ ((uint32_t)C::KSUB * (uint32_t)c.kg);
 }
 
 template <class C>
@@ -385,14 +455,17 @@ struct Frags {
 };
 
 template <class C, class E>
-using Acc = typename E::acc_t[C::NI][C::MI];
+using AccT = typename E::template Mfma<C::MT>::acc_t;
+template <class C, class E>
+using Acc = AccT<C, E>[C::NI][C::MI];
 
 // Fragment q of sub-step ks: q < MI -> activation sub-tile q, else weight
-// sub-tile q - MI.  Lane l reads row l % 32 of the sub-tile at K-chunk
-// ch = 2*ks + l/32, stored at physical chunk ch ^ f(row).  Sub-tile i starts
-// 32*i rows further on, where f changes by 4*(i & 1) for 128-byte rows and not
-// at all for 64-byte rows; so 16 * (ch ^ f(row)) = g ^ (32*ks) ^ (64*(i & 1))
-// (128-byte rows) with g = 16 * ((l/32) ^ f(first row)) from the context:
+// sub-tile q - MI.  Lane l reads row l % MT of the sub-tile at K-chunk
+// ch = (KSUB/16)*ks + l/MT, stored at physical chunk ch ^ f(row).  Sub-tile i
+// starts MT*i rows further on, where f changes by ((MT/8)*i) & 7 for 128-byte
+// rows (4*(i & 1) for MT = 32, 2*(i & 3) for MT = 16) and not at all for
+// 64-byte rows; so 16 * (ch ^ f(row)) = g ^ (KSUB*ks) ^ 16*(((MT/8)*i) & 7)
+// (128-byte rows) with g = 16 * ((l/MT) ^ f(first row)) from the context:
 // one XOR-add per read.  ga, gw are that g for the two operands.
 // The four per-lane fragment-read values of the context.
 struct FragBase {
@@ -410,9 +483,10 @@ __device__ __forceinline__ void read_frag(const char* lds_stage, const FragBase&
                                           Frags<C>& f) {
     const bool is_a = q < C::MI;
     const int i = is_a ? q : q - C::MI;
-    const uint32_t k = (uint32_t)(32 * ks) ^ (C::BK == 128 ? 64u * (uint32_t)(i & 1) : 0u);
+    const uint32_t k = (uint32_t)(C::KSUB * ks) ^
+                       (C::BK == 128 ? 16u * (uint32_t)(((C::MT / 8) * i) & 7) : 0u);
     const uint32_t off = ((is_a ? fb.ga : fb.gw) ^ k) + (is_a ? fb.fa : fb.fw);
-    const v4i v = *reinterpret_cast<const v4i*>(lds_stage + off + i * 32 * C::BK);
+    const v4i v = *reinterpret_cast<const v4i*>(lds_stage + off + i * C::MT * C::BK);
     if (is_a) f.a[i] = v;
     else f.w[i] = v;
 }
@@ -432,7 +506,7 @@ __device__ __forceinline__ v4i keep_bytes(v4i v, int valid) {
 // valid bytes of that stage.
 template <class C>
 __device__ __forceinline__ void mask_tail(Frags<C>& f, const Ctx<C>& c, int ks, int tail) {
-    const int valid = tail - (32 * (ks + c.kg) + 16 * (c.lane >> 5));
+    const int valid = tail - (C::KSUB * (ks + c.kg) + 16 * (int)((unsigned)c.lane / C::MT));
 #pragma unroll
     for (int q = 0; q < C::MI; ++q) f.a[q] = keep_bytes(f.a[q], valid);
 #pragma unroll
@@ -442,7 +516,7 @@ __device__ __forceinline__ void mask_tail(Frags<C>& f, const Ctx<C>& c, int ks, 
 template <class C, class E>
 __device__ __forceinline__ void mfma_one(Acc<C, E>& acc, const Frags<C>& f, int j) {
     const int ni = j / C::MI, mi = j % C::MI;
-    acc[ni][mi] = E::mfma(f.w[ni], f.a[mi], acc[ni][mi]);
+    acc[ni][mi] = E::template Mfma<C::MT>::run(f.w[ni], f.a[mi], acc[ni][mi]);
 }
 
 // The MFMAs of one sub-step, with (READ) the fragment reads of sub-step rks
@@ -556,13 +630,15 @@ __device__ __forceinline__ void for_each_pass(F& f, std::integer_sequence<int, P
     (f(std::integral_constant<int, P>{}), ...);
 }
 
-// Epilogue.  acc[ni][mi][i] holds D[n][m] for m = m0 + wm*TM + mi*32 +
-// (lane & 31) and n = n0 + wn*TN + ni*32 + 8*(i/4) + 4*(lane >> 5) + (i & 3):
-// four consecutive columns per group of four registers.
+// Epilogue.  acc[ni][mi][i] holds D[n][m] for m = m0 + wm*TM + mi*MT +
+// (lane % MT) and n = n0 + wn*TN + ni*MT + (MT/4)*(i/4) + 4*(lane / MT) +
+// (i & 3): four consecutive columns per group of four registers (four groups
+// for MT = 32, one for MT = 16).
 //
 // Stored straight from the accumulator layout, one wave instruction would
 // touch 32 rows with 16 bytes each.  Instead the bf16 tile goes through LDS,
-// in MI passes of BM/MI rows (pass p holds the rows of MFMA sub-tile mi = p),
+// in NPASS passes of WM*32 rows (pass p holds the rows of MFMA sub-tiles
+// mi = p*PM .. p*PM + PM - 1, the wave's rows 32p .. 32p + 31),
 // and is copied out so that each wave instruction writes whole tile rows
 // (64 lanes x 16 bytes).  Staged rows are padded by 16 bytes: every LDS address
 // is a per-lane base plus a compile-time offset, and the 16-byte row reads are
@@ -576,9 +652,11 @@ __device__ __forceinline__ void store_bf16(const Acc<C, E>& acc, uint16_t* __res
                                            int64_t N, int64_t m0, int64_t n0, int wave, int wm,
                                            int wn, int lane, const float* sa_l, const float* sw_l,
                                            const float* b_l, char* stage, int kg) {
-    const int half = lane >> 5;
-    const int ncol = wn * C::TN + 4 * half;  // tile-local column of this lane's first group
-    char* wbase = stage + (wm * 32 + (lane & 31)) * C::OUT_ROW + ncol * 2;
+    constexpr int G = C::ACC_N / 4;  // groups of 4 consecutive columns per MFMA tile
+    constexpr int GS = C::MT / 4;    // column step between them
+    const int lr = (int)((unsigned)lane % C::MT);
+    const int ncol = wn * C::TN + 4 * (int)((unsigned)lane / C::MT);  // this lane's first column
+    char* wbase = stage + (wm * 32 + lr) * C::OUT_ROW + ncol * 2;
     const bool interior = (m0 + C::BM <= M) && (n0 + C::BN <= N);
     const int cc = (int)((unsigned)lane % C::RCH);  // this lane's 16-byte chunk of a row
     // copy-out: staged row s = wave*RPW + i*RPINS + lane/RCH is tile row
@@ -591,43 +669,48 @@ __device__ __forceinline__ void store_bf16(const Acc<C, E>& acc, uint16_t* __res
     // where the GELU body made the loop too large to unroll)
     auto pass = [&](auto pc) {
         constexpr int p = decltype(pc)::value;
-        float sam = 0.f;
-        if constexpr (E::BYTES == 1) sam = sa_l[wm * C::TM + p * 32 + (lane & 31)];
-        // with K groups only group 0 holds the sums; every wave copies out
 #pragma unroll
-        for (int ni = 0; ni < (kg == 0 ? C::NI : 0); ++ni) {
-            v4f swv[4], bv[4];
+        for (int q = 0; q < C::PM; ++q) {
+            const int mi = p * C::PM + q;
+            float sam = 0.f;
+            if constexpr (E::BYTES == 1) sam = sa_l[wm * C::TM + mi * C::MT + lr];
+            // with K groups only group 0 holds the sums; every wave copies out
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int cl = ncol + ni * 32 + 8 * g;
-                if constexpr (E::BYTES == 1) swv[g] = *reinterpret_cast<const v4f*>(sw_l + cl);
-                bv[g] = *reinterpret_cast<const v4f*>(b_l + cl);
-            }
+            for (int ni = 0; ni < (kg == 0 ? C::NI : 0); ++ni) {
+                v4f swv[G], bv[G];
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                float v[4];
+                for (int g = 0; g < G; ++g) {
+                    const int cl = ncol + ni * C::MT + GS * g;
+                    if constexpr (E::BYTES == 1) swv[g] = *reinterpret_cast<const v4f*>(sw_l + cl);
+                    bv[g] = *reinterpret_cast<const v4f*>(b_l + cl);
+                }
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    if constexpr (E::BYTES == 1) {
-                        const float t = (float)acc[ni][p][4 * g + e];  // nearest even
-                        const float u = __fmul_rn(sam, swv[g][e]);
-                        v[e] = __builtin_fmaf(t, u, bv[g][e]);
-                    } else {
-                        const float t = acc[ni][p][4 * g + e];
-                        v[e] = __fadd_rn(t, bv[g][e]);
+                for (int g = 0; g < G; ++g) {
+                    float v[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        if constexpr (E::BYTES == 1) {
+                            const float t = (float)acc[ni][mi][4 * g + e];  // nearest even
+                            const float u = __fmul_rn(sam, swv[g][e]);
+                            v[e] = __builtin_fmaf(t, u, bv[g][e]);
+                        } else {
+                            const float t = acc[ni][mi][4 * g + e];
+                            v[e] = __fadd_rn(t, bv[g][e]);
+                        }
                     }
+                    uint2 o = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+                    if (ACT == 1) {
+                        // GELU-tanh of the bf16-rounded value, rounded to bf16 (gelu_bf16_rn)
+                        o = make_uint2(gelu_bf16_rn(o.x & 0xffffu) | (gelu_bf16_rn(o.x >> 16) << 16),
+                                       gelu_bf16_rn(o.y & 0xffffu) | (gelu_bf16_rn(o.y >> 16) << 16));
+                    }
+                    *reinterpret_cast<uint2*>(wbase + q * C::MT * C::OUT_ROW +
+                                              (ni * C::MT + GS * g) * 2) = o;
                 }
-                uint2 o = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-                if (ACT == 1) {
-                    // GELU-tanh of the bf16-rounded value, rounded to bf16 (gelu_bf16_rn)
-                    o = make_uint2(gelu_bf16_rn(o.x & 0xffffu) | (gelu_bf16_rn(o.x >> 16) << 16),
-                                   gelu_bf16_rn(o.y & 0xffffu) | (gelu_bf16_rn(o.y >> 16) << 16));
-                }
-                *reinterpret_cast<uint2*>(wbase + (ni * 32 + 8 * g) * 2) = o;
+                // register-tight tiles: keep the next column group's scale reads
+                // from being hoisted next to this one's (they would spill)
+                if constexpr (C::RECYCLE) __builtin_amdgcn_sched_barrier(0);
             }
-            // register-tight tiles: keep the next column group's scale reads
-            // from being hoisted next to this one's (they would spill)
-            if constexpr (C::RECYCLE) __builtin_amdgcn_sched_barrier(0);
         }
         lds_barrier();
         constexpr int NI_OUT = C::RPW / C::RPINS;  // copy-out instructions per wave per pass
@@ -664,21 +747,22 @@ __device__ __forceinline__ void store_bf16(const Acc<C, E>& acc, uint16_t* __res
         }
         lds_barrier();  // the staging area is free again
     };
-    for_each_pass(pass, std::make_integer_sequence<int, C::MI>{});
+    for_each_pass(pass, std::make_integer_sequence<int, C::NPASS>{});
 }
 
 // K groups g > 0 hand their accumulators to group 0 through LDS (the ring,
 // which the K loop is done with), and group 0 adds them in order g = 1, 2, ...:
 // exact for INT32, a fixed order for fp32.  Lane l's values of accumulator
-// register group q of MFMA tile (ni, mi) sit at ((ni*MI + mi)*4 + q)*1 KB +
+// register group q of MFMA tile (ni, mi) sit at ((ni*MI + mi)*G + q)*1 KB +
 // 16*l of the wave's area, so each 16-byte access of a wave is contiguous.
 // Every wave calls it (it holds two barriers).
 template <class C, class E>
 __device__ __forceinline__ void reduce_k_groups(Acc<C, E>& acc, char* smem, int kg, int slot,
                                                 int lane) {
     if constexpr (C::KS > 1) {
-        typedef typename E::acc_t A;
+        typedef AccT<C, E> A;
         typedef std::conditional_t<E::BYTES == 1, v4i, v4f> V4;
+        constexpr int G = C::ACC_N / 4;
         if (kg > 0) {
             char* dst = smem + ((kg - 1) * C::WG + slot) * C::RED_WAVE + 16 * lane;
 #pragma unroll
@@ -686,10 +770,10 @@ __device__ __forceinline__ void reduce_k_groups(Acc<C, E>& acc, char* smem, int 
 #pragma unroll
                 for (int mi = 0; mi < C::MI; ++mi)
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
+                    for (int q = 0; q < G; ++q) {
                         const A& a = acc[ni][mi];
                         const V4 v = {a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
-                        *reinterpret_cast<V4*>(dst + ((ni * C::MI + mi) * 4 + q) * 1024) = v;
+                        *reinterpret_cast<V4*>(dst + ((ni * C::MI + mi) * G + q) * 1024) = v;
                     }
         }
         lds_barrier();
@@ -702,9 +786,9 @@ __device__ __forceinline__ void reduce_k_groups(Acc<C, E>& acc, char* smem, int 
 #pragma unroll
                     for (int mi = 0; mi < C::MI; ++mi)
 #pragma unroll
-                        for (int q = 0; q < 4; ++q) {
+                        for (int q = 0; q < G; ++q) {
                             const V4 v = *reinterpret_cast<const V4*>(
-                                src + ((ni * C::MI + mi) * 4 + q) * 1024);
+                                src + ((ni * C::MI + mi) * G + q) * 1024);
 #pragma unroll
                             for (int e = 0; e < 4; ++e) acc[ni][mi][4 * q + e] += v[e];
                         }
@@ -718,20 +802,21 @@ template <class C>
 __device__ __forceinline__ void store_i32(const Acc<C, ElemI8>& acc, int32_t* __restrict__ out,
                                           int64_t M, int64_t N, int64_t m0, int64_t n0, int wm,
                                           int wn, int lane) {
-    const int ncol = wn * C::TN + 4 * (lane >> 5);
+    constexpr int G = C::ACC_N / 4, GS = C::MT / 4;
+    const int ncol = wn * C::TN + 4 * (int)((unsigned)lane / C::MT);
 #pragma unroll
     for (int mi = 0; mi < C::MI; ++mi) {
-        const int ml = wm * C::TM + mi * 32 + (lane & 31);
+        const int ml = wm * C::TM + mi * C::MT + (int)((unsigned)lane % C::MT);
         if (m0 + ml >= M) continue;
         int32_t* rowp = out + (m0 + ml) * N + n0 + ncol;
 #pragma unroll
         for (int ni = 0; ni < C::NI; ++ni)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                if (n0 + ncol + ni * 32 + 8 * g >= N) continue;
+            for (int g = 0; g < G; ++g) {
+                if (n0 + ncol + ni * C::MT + GS * g >= N) continue;
                 v4i v = {acc[ni][mi][4 * g], acc[ni][mi][4 * g + 1], acc[ni][mi][4 * g + 2],
                          acc[ni][mi][4 * g + 3]};
-                *reinterpret_cast<v4i*>(rowp + ni * 32 + 8 * g) = v;
+                *reinterpret_cast<v4i*>(rowp + ni * C::MT + GS * g) = v;
             }
     }
 }
@@ -871,7 +956,7 @@ void gemm_tiled(const void* __restrict__ a, const float* __restrict__ sa, int64_
 #pragma unroll
         for (int i = 0; i < C::NI; ++i)
 #pragma unroll
-            for (int j = 0; j < MI; ++j) acc[i][j] = (typename E::acc_t){};
+            for (int j = 0; j < MI; ++j) acc[i][j] = (AccT<C, E>){};
         Frags<C> cur;
         const FragBase fb0 = frag_base(c);
 #pragma unroll
@@ -961,25 +1046,15 @@ hipError_t launch_cfg(const void* a, const float* sa, int64_t M, const void* w, 
 
 // Tile choice.  Larger tiles move less data per MFMA, which is what sets the
 // clock under the power cap; smaller ones only pay off when the large ones
-// leave most CUs idle.  xl (1.5x the work of a large tile) is taken when it
-// needs no more rounds of persistent tiles than large does (rounds x 1.5 <=
-// large's rounds) and either K >= 8192 or there are at least 4 xl tiles per
-// CU: measured 2-3% faster on the FFN up (24576 x 16384 x 4096, 16 tiles per
-// CU) and down (K = 16384) projections and 3.5% faster on 24576 x 4096 x 4096
-// and 12288 x 8192 x 4096 (4 tiles per CU); with 1 tile per CU it is not taken.
+// leave most CUs idle.
 template <class E, int OUT_I32, int ACT, bool VEC_OUT>
 hipError_t launch_tiles(const void* a, const float* sa, int64_t M, const void* w, const float* sw,
                         int64_t N, int64_t K, const uint16_t* bias, void* out,
                         hipStream_t stream) {
     const int cus = cu_count();
     if (cus <= 0) return hipErrorInvalidDevice;
-    if constexpr (E::BYTES == 1 && ACT == 0) {
-        const int64_t txl = tile_count<CfgXL>(M, N), tl = tile_count<CfgLarge>(M, N);
-        const int64_t rounds_xl = (txl + cus - 1) / cus, rounds_l = (tl + cus - 1) / cus;
-        if (2 * txl >= cus && 3 * rounds_xl <= 2 * rounds_l && (K >= 8192 || txl >= 4 * (int64_t)cus))
-            return launch_cfg<CfgXL, E, OUT_I32, ACT, VEC_OUT>(a, sa, M, w, sw, N, K, bias, out,
-                                                              cus, stream);
-    }
+    typedef typename Tiers<E>::Large CfgLarge;
+    typedef typename Tiers<E>::Mid CfgMid;
     if (2 * tile_count<CfgLarge>(M, N) >= cus) {
         // mid when its rounds x 3/4 of a large tile's work, with 7% for its
         // lower efficiency per MFMA, come to less than large's rounds
@@ -991,9 +1066,9 @@ hipError_t launch_tiles(const void* a, const float* sa, int64_t M, const void* w
         return launch_cfg<CfgLarge, E, OUT_I32, ACT, VEC_OUT>(a, sa, M, w, sw, N, K, bias, out, cus,
                                                              stream);
     }
-    typedef CfgSmall CSmall;
-    typedef CfgSmallDeep CDeep;
-    typedef CfgTiny CTiny;
+    typedef typename Tiers<E>::Small CSmall;
+    typedef typename Tiers<E>::Deep CDeep;
+    typedef typename Tiers<E>::Tiny CTiny;
     if (2 * tile_count<CSmall>(M, N) >= cus) {
         // A 3-deep ring keeps two stages of loads in flight: with one wave per
         // SIMD and 512 cycles of MFMAs per stage, the 2-deep ring's per-stage
@@ -1019,7 +1094,10 @@ hipError_t launch_tiles(const void* a, const float* sa, int64_t M, const void* w
 // splitk_reduce adds the slices in order s = 0 .. S-1 (exact in INT32: the
 // scales come only after the whole accumulation) and applies the same
 // epilogue as the tiled kernel, so the result is w8a8_gemm's bit for bit.
-typedef Cfg<128, 128, 2, 2, 128, 2, GROUP_ROWS, 2, true> CfgSplit;
+#ifndef W8A8_I8_SPLIT_MT
+#define W8A8_I8_SPLIT_MT 32
+#endif
+typedef Cfg<128, 128, 2, 2, 128, 2, GROUP_ROWS, 2, true, W8A8_I8_SPLIT_MT> CfgSplit;
 
 // Four consecutive outputs of one row per thread (N is a multiple of 64), in a
 // grid-stride loop: acc = sum of the S partials, then exactly store_bf16's
@@ -1070,7 +1148,8 @@ int splitk_slices(int64_t M, int64_t N, int64_t K) {
     constexpr int64_t kCUs = 256;
     if (M <= 0 || N <= 0) return 1;
     // only shapes the large tiles and the 128 x 128 tiles leave mostly idle
-    if (2 * tile_count<CfgLarge>(M, N) >= kCUs || 2 * tile_count<CfgSplit>(M, N) >= kCUs) return 1;
+    if (2 * tile_count<Tiers<ElemI8>::Large>(M, N) >= kCUs || 2 * tile_count<CfgSplit>(M, N) >= kCUs)
+        return 1;
     const int64_t tiles = tile_count<CfgSplit>(M, N), stages = K / CfgSplit::BK;
     int64_t S = kCUs / tiles;
     if (S > 8) S = 8;

@@ -438,15 +438,16 @@ def test_quantize_blocks_guard_bands():
 # On a 256-CU MI355X the launcher takes 256 x 256 tiles when there are at
 # least 128 of them, else 128 x 128 tiles when there are at least 128 of those,
 # else 64 x 64 tiles; instead of 256 x 256 it takes 192 x 256 tiles where their
-# rounds of tiles per CU cost less, and 384 x 256 (INT8 without GELU, long K
-# loops or many tiles).  A persistent workgroup takes several tiles when there
+# rounds of tiles per CU cost less (256 x 256 and 192 x 256 tiles run 16 x 16
+# x 64 MFMAs, the smaller ones 32 x 32 x 32).  A persistent workgroup takes several tiles when there
 # are more than 256.  Covered here: 64 x 64 tiles (the first seven shapes),
 # 128 x 128 tiles (2048^3 and 2000 x 1984, ragged; 1000 x 2048 x 8192 with the
 # 3-deep K ring of long K loops), 192 x 256 tiles with ragged
 # M, with ragged N (4100 x 4096, 4096 x 4160, both with workgroups taking two
 # tiles) and on a text-projection row count (2378 x 4096), 256 x 256 tiles
-# with ragged M and N (3900 x 3776, 3900 x 4032).  The 384 x 256 tiles are
-# covered by test_gemm_xl_tiles_ragged_sampled and by the full-size FFN tests.
+# with ragged M and N (3900 x 3776, 3900 x 4032).  Larger ragged shapes:
+# test_gemm_mid_tiles_ragged_sampled, test_gemm_large_tiles_short_k_ragged_sampled
+# and the full-size FFN tests.
 GEMM_SHAPES = [(1, 64, 128), (64, 128, 256), (129, 192, 384), (300, 320, 1024), (257, 64, 4096),
                (1000, 448, 2048), (33, 256, 16384), (2048, 2048, 2048), (2000, 1984, 512),
                (1000, 2048, 8192), (4100, 4096, 256), (4096, 4160, 128), (2378, 4096, 512), (3900, 3776, 128),
@@ -467,7 +468,7 @@ def test_gemm_int32_bit_exact(M, N, K):
 def _random_gemm_shapes(n, seed):
     """Seeded shapes the guard accepts: M any (1 .. 3000), N a multiple of 64
     (64 .. 4096), K a multiple of 128 (128 .. 8192), so that every tile
-    configuration below the 384 x 256 one, full and ragged, is met."""
+    configuration, full and ragged, is met."""
     rng = np.random.default_rng(seed)
     out = []
     for _ in range(n):
@@ -576,13 +577,14 @@ def test_gemm_int32_extremes_and_max_k():
     assert np.all(acc[0::2] == 16129 * K) and np.all(acc[1::2] == -16129 * K)
 
 
-def test_gemm_xl_tiles_max_k_closed_form():
+def test_gemm_max_k_closed_form():
     """K = 131072 (the largest the guard admits: |acc| <= 127^2 K < 2^31) on the
-    384 x 256 tiles (4600 x 4096: 192 such tiles, one round, against two rounds
-    of 256 x 256 tiles; ragged M).  Codes are +-127 by row, so every accumulator
-    is +-16129 K: a closed form, checked on all outputs."""
+    192 x 256 tiles with 16 x 16 x 64 MFMAs (4600 x 4096: 384 such tiles, two
+    rounds, as many as 288 tiles of 256 x 256 take; ragged M).  Codes are +-127
+    by row, so every accumulator is +-16129 K: a closed form, checked on all
+    outputs."""
     M, N, K = 4600, 4096, 131072
-    say(f"gemm xl tiles max K M={M} N={N} K={K}")
+    say(f"gemm max K M={M} N={N} K={K}")
     sa = torch.where(torch.arange(M, device=DEV) % 3 == 0, -1, 1).to(torch.int8)
     sw = torch.where(torch.arange(N, device=DEV) % 5 == 0, -1, 1).to(torch.int8)
     qa = (sa[:, None] * 127).expand(M, K).contiguous()
@@ -618,27 +620,29 @@ def test_gemm_epilogue_matches_oracle(M, N, K, act, with_bias):
         assert np.array_equal(got, ref)  # same binary32 sequence on both sides
 
 
-def _tile_edge_rows(M, tile, rng, extra=120):
-    """Rows on both sides of every tile boundary, the ragged last tile and a
-    seeded random sample."""
-    edges = [r for b in range(tile, M, tile) for r in (b - 1, b)]
+def _tile_edge_rows(M, tiles, rng, extra=120):
+    """Rows on both sides of every boundary of tiles of each height in `tiles`,
+    the ragged last tile and a seeded random sample."""
+    tiles = (tiles,) if isinstance(tiles, int) else tiles
+    edges = [r for tile in tiles for b in range(tile, M, tile) for r in (b - 1, b)]
     tail = list(range(max(0, M - 70), M))
     rnd = list(rng.choice(M, extra, replace=False))
     return np.unique(np.array([0, 1] + edges + tail + rnd, dtype=np.int64))
 
 
-def test_gemm_xl_tiles_ragged_sampled():
-    """6100 x 4032 x 8192: K >= 8192 with 256 tiles of 384 x 256 rows x columns,
-    so on a 256-CU MI355X the 384 x 256 tile path runs (ragged in M and in N).
-    INT32 accumulators and the bf16 epilogue (with bias) compared on sampled
-    rows that include both sides of every 384-row tile boundary and the
-    ragged last tile; all columns."""
+def test_gemm_mid_tiles_ragged_sampled():
+    """6100 x 4032 x 8192: 512 tiles of 192 x 256 take two rounds on a 256-CU
+    MI355X, as 384 of 256 x 256 would, so the 192 x 256 path (16 x 16 x 64
+    MFMAs) runs, ragged in M and in N, persistent with two tiles per
+    workgroup.  INT32 accumulators and the bf16 epilogue (with bias) compared
+    on sampled rows that include both sides of every 192-row tile boundary and
+    the ragged last tile; all columns."""
     M, N, K = 6100, 4032, 8192
-    say(f"gemm xl tiles M={M} N={N} K={K}")
+    say(f"gemm mid tiles M={M} N={N} K={K}")
     rng = np.random.default_rng(8192)
     qa = rng.integers(-127, 128, (M, K), dtype=np.int8)
     qw = rng.integers(-127, 128, (N, K), dtype=np.int8)
-    rows = _tile_edge_rows(M, 384, rng)
+    rows = _tile_edge_rows(M, 192, rng)
     qa_d, qw_d = d_i8(qa), d_i8(qw)
     acc = h(w8.gemm(qa_d, None, qw_d, None, out_kind=w8.OUT_I32))
     acc_ref = oracle.gemm_i32(np.ascontiguousarray(qa[rows]), qw)
@@ -654,18 +658,18 @@ def test_gemm_xl_tiles_ragged_sampled():
     assert np.array_equal(h_u16(y)[rows], ref)
 
 
-def test_gemm_xl_tiles_short_k_ragged_sampled():
-    """12000 x 8000 x 512: 1024 tiles of 384 x 256 (4 per CU on a 256-CU MI355X)
-    with a short K loop, ragged in M (96 rows in the last tile-row) and N (64
-    columns in the last tile-column): the 384 x 256 path by its tiles-per-CU
-    rule.  INT32 accumulators and the bf16 epilogue (with and without bias) on
-    sampled rows, both sides of every 384-row boundary included."""
+def test_gemm_large_tiles_short_k_ragged_sampled():
+    """12000 x 8000 x 512: 1504 tiles of 256 x 256 (16 x 16 x 64 MFMAs, about 6
+    per CU on a 256-CU MI355X) with a short K loop, ragged in M (224 rows in
+    the last tile-row) and N (64 columns in the last tile-column).  INT32
+    accumulators and the bf16 epilogue (with and without bias) on sampled
+    rows, both sides of every 256-row boundary included."""
     M, N, K = 12000, 8000, 512
-    say(f"gemm xl short K M={M} N={N} K={K}")
+    say(f"gemm large short K M={M} N={N} K={K}")
     rng = np.random.default_rng(512)
     qa = rng.integers(-127, 128, (M, K), dtype=np.int8)
     qw = rng.integers(-127, 128, (N, K), dtype=np.int8)
-    rows = _tile_edge_rows(M, 384, rng, extra=60)
+    rows = _tile_edge_rows(M, 256, rng, extra=60)
     qa_d, qw_d = d_i8(qa), d_i8(qw)
     acc_ref = oracle.gemm_i32(np.ascontiguousarray(qa[rows]), qw)
     assert np.array_equal(h(w8.gemm(qa_d, None, qw_d, None, out_kind=w8.OUT_I32))[rows], acc_ref)
@@ -684,8 +688,9 @@ def test_gemm_without_bias_keeps_the_sign_of_zero(M, N, K):
     """Without a bias the output is the rounded product alone.  With scales whose
     product underflows to +0 that product is +0 or -0 by the sign of the
     accumulator, so the bf16 output is 0x8000 exactly where acc < 0 and 0x0000
-    elsewhere (the last shape runs the 384 x 256 tiles, the others the smaller
-    ones).  Rows compared: every tile edge, the tail and a random sample."""
+    elsewhere (the last shape runs the 192 x 256 tiles with 16 x 16 x 64 MFMAs,
+    the others smaller ones with 32 x 32 x 32).  Rows compared: every tile
+    edge, the tail and a random sample."""
     say(f"gemm signed zero M={M} N={N} K={K}")
     rng = np.random.default_rng(M + 7)
     qa = rng.integers(-127, 128, (M, K), dtype=np.int8)
@@ -693,7 +698,7 @@ def test_gemm_without_bias_keeps_the_sign_of_zero(M, N, K):
     sa = np.full(M, 1e-30, dtype=np.float32)
     sw = np.full(N, 1e-30, dtype=np.float32)
     assert np.float32(sa[0]) * np.float32(sw[0]) == 0  # underflows in binary32
-    rows = _tile_edge_rows(M, 128, rng, extra=40)
+    rows = _tile_edge_rows(M, (128, 192), rng, extra=40)
     y = h_u16(w8.gemm(d_i8(qa), torch.from_numpy(sa).to(DEV), d_i8(qw), torch.from_numpy(sw).to(DEV),
                       None))[rows]
     acc = oracle.gemm_i32(np.ascontiguousarray(qa[rows]), qw)
