@@ -289,9 +289,16 @@ template <> struct Tiers<ElemI8> {
     typedef Cfg<W8A8_TINY_CFG, W8A8_I8_TINY_MT> Tiny;
 };
 
-template <int BK>
+// Physical chunk of logical chunk c in LDS row r.  LDS serves a ds_read_b128
+// 32 lanes at a time over 128 banks (four per 16-byte chunk): a 32 x 32 MFMA
+// fragment read has 32 lanes on 32 consecutive rows at one chunk, a 16 x 16 one
+// 16 consecutive rows at two chunks, and each swizzle spreads its pattern over
+// all 128 banks (SQ_LDS_BANK_CONFLICT: the 32 x 32 swizzle on 16 x 16 reads
+// conflicted on about half of the LDS cycles).  Both are XOR-separable over
+// blocks of 8 rows (the loads) and of MT rows (the fragment sub-tiles).
+template <int BK, int MT>
 __device__ __forceinline__ int swz(int r, int c) {
-    if (BK == 128) return c ^ ((r ^ (r >> 3)) & 7);
+    if (BK == 128) return MT == 16 ? c ^ ((r ^ (r >> 2)) & 7) : c ^ ((r ^ (r >> 3)) & 7);
     return c ^ ((r >> 2) & 3);
 }
 
@@ -383,9 +390,12 @@ template <class C>
 __device__ __forceinline__ void lane_ctx(Ctx<C>& c, int lane) {
     const int rsub = (int)((unsigned)lane / C::CPR), pc = (int)((unsigned)lane % C::CPR);
     c.lrow = (uint32_t)rsub * c.kb;
-    // 128-byte rows: swz(r0 + rsub, pc) = pc ^ rsub ^ ((r0 >> 3) & 7) for r0 % 8 == 0;
+    // 128-byte rows: swz(r0 + rsub, pc) = pc ^ rsub ^ ((r0 >> 3) & 7) for r0 % 8 == 0
+    // (MT = 32), pc ^ rsub ^ (rsub >> 2) ^ ((r0 >> 2) & 7) (MT = 16);
     // 64-byte rows: swz(r0 + rsub, pc) = pc ^ ((rsub >> 2) & 3) for r0 % 16 == 0
-    c.lx = C::BK == 128 ? 16u * (uint32_t)(pc ^ rsub) : 16u * (uint32_t)(pc ^ ((rsub >> 2) & 3));
+    c.lx = C::BK != 128 ? 16u * (uint32_t)(pc ^ ((rsub >> 2) & 3))
+           : C::MT == 16  ? 16u * (uint32_t)(pc ^ rsub ^ (rsub >> 2))
+                          : 16u * (uint32_t)(pc ^ rsub);
     // lane l reads row l % MT of a sub-tile at K-chunk l / MT of the sub-step
     const int hi = (int)((unsigned)lane / C::MT);
     const int lr = (int)((unsigned)lane % C::MT);
@@ -395,8 +405,8 @@ __device__ __forceinline__ void lane_ctx(Ctx<C>& c, int lane) {
     // a K group's sub-steps are kg, kg + KS, ...: KSUB * kg shares no bit with
     // KSUB * KS * (the wave's own sub-step) or with 16 * hi, so it joins the
     // per-lane XOR term
-    c.ga = (16u * (uint32_t)swz<C::BK>(ra, hi)) ^ ((uint32_t)C::KSUB * (uint32_t)c.kg);
-    c.gw = (16u * (uint32_t)swz<C::BK>(rw, hi)) ^ ((uint32_t)C::KSUB * (uint32_t)c.kg);
+    c.ga = (16u * (uint32_t)swz<C::BK, C::MT>(ra, hi)) ^ ((uint32_t)C::KSUB * (uint32_t)c.kg);
+    c.gw = (16u * (uint32_t)swz<C::BK, C::MT>(rw, hi)) ^ ((uint32_t)C::KSUB * (uint32_t)c.kg);
 }
 
 template <class C>
@@ -416,7 +426,8 @@ __device__ __forceinline__ void make_ctx(Ctx<C>& c, int64_t KB, int wave, int la
 // wave-uniform, a multiple of RPI); lane l takes row r0 + l / CPR, logical
 // chunk l % CPR, which lands at LDS byte 16*l of the load's 1 KB, the physical
 // chunk of the swizzle.  Its lane offset is row * KB + 16 * swz(row, chunk) =
-// lrow + r0 * KB + (lx ^ 16 * ((r0 >> 3) & 7)) for 128-byte rows (the XOR term
+// lrow + r0 * KB + (lx ^ 16 * ((r0 >> 3) & 7)) for 128-byte rows (r0 >> 2 for
+// the MT = 16 swizzle; the XOR term
 // is 0 for 64-byte rows): two VALU operations per load instead of a register
 // per load held across the K loop.  lrow and lx are passed by the caller
 // through an empty asm statement so that the compiler forms each offset here.
@@ -427,7 +438,7 @@ __device__ __forceinline__ void stage_load_one(const Ctx<C>& c, uint32_t lrow, u
     const bool is_a = j < C::LPW_A;
     const int i = is_a ? j : j - C::LPW_A;
     const uint32_t r0 = (uint32_t)(c.wave * ((is_a ? C::BM : C::BN) / C::WAVES) + i * C::RPI);
-    const uint32_t xr = C::BK == 128 ? 16u * ((r0 >> 3) & 7u) : 0u;
+    const uint32_t xr = C::BK != 128 ? 0u : 16u * ((r0 >> (C::MT == 16 ? 2 : 3)) & 7u);
     const uint32_t voff = lrow + r0 * c.kb + (lx ^ xr);
     char* dst = lds_stage + (is_a ? 0 : C::BM * C::BK) + r0 * C::BK;
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -462,11 +473,11 @@ using Acc = AccT<C, E>[C::NI][C::MI];
 // Fragment q of sub-step ks: q < MI -> activation sub-tile q, else weight
 // sub-tile q - MI.  Lane l reads row l % MT of the sub-tile at K-chunk
 // ch = (KSUB/16)*ks + l/MT, stored at physical chunk ch ^ f(row).  Sub-tile i
-// starts MT*i rows further on, where f changes by ((MT/8)*i) & 7 for 128-byte
-// rows (4*(i & 1) for MT = 32, 2*(i & 3) for MT = 16) and not at all for
-// 64-byte rows; so 16 * (ch ^ f(row)) = g ^ (KSUB*ks) ^ 16*(((MT/8)*i) & 7)
-// (128-byte rows) with g = 16 * ((l/MT) ^ f(first row)) from the context:
-// one XOR-add per read.  ga, gw are that g for the two operands.
+// starts MT*i rows further on, where f changes by 4*(i & 1) for 128-byte rows
+// (both swizzles) and not at all for 64-byte rows; so 16 * (ch ^ f(row)) =
+// g ^ (KSUB*ks) ^ (64*(i & 1)) (128-byte rows) with g = 16 * ((l/MT) ^
+// f(first row)) from the context: one XOR-add per read.  ga, gw are that g for
+// the two operands.
 // The four per-lane fragment-read values of the context.
 struct FragBase {
     uint32_t fa, fw, ga, gw;
@@ -483,8 +494,7 @@ __device__ __forceinline__ void read_frag(const char* lds_stage, const FragBase&
                                           Frags<C>& f) {
     const bool is_a = q < C::MI;
     const int i = is_a ? q : q - C::MI;
-    const uint32_t k = (uint32_t)(C::KSUB * ks) ^
-                       (C::BK == 128 ? 16u * (uint32_t)(((C::MT / 8) * i) & 7) : 0u);
+    const uint32_t k = (uint32_t)(C::KSUB * ks) ^ (C::BK == 128 ? 64u * (uint32_t)(i & 1) : 0u);
     const uint32_t off = ((is_a ? fb.ga : fb.gw) ^ k) + (is_a ? fb.fa : fb.fw);
     const v4i v = *reinterpret_cast<const v4i*>(lds_stage + off + i * C::MT * C::BK);
     if (is_a) f.a[i] = v;
