@@ -541,7 +541,9 @@ def small_from(trace_dir, pmc_dir):
         if cs and "SQ_INSTS_MFMA" in cs[0]:
             c = cs[len(cs) // 2]
             n, busy = c["SQ_INSTS_MFMA"], c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0)
-            ops = n * (65536 if "ElemI8" in k else 32768)  # 32x32x32 int8 / 32x32x16 bf16
+            mt = re.search(r"Cfg<[^>]*, (16|32)>", k)  # the MFMA tile edge
+            # int8: 32x32x32 or 16x16x64; bf16: 32x32x16 or 16x16x32 (ops = 2 x MACs)
+            ops = n * (65536 if "ElemI8" in k else 32768) // (2 if mt and mt.group(1) == "16" else 1)
             r.update({"mfma": int(n), "mfma_busy_cycles": int(busy),
                       "issued_TOPS": round(ops / t / 1e12, 1),
                       "mfma_busy_frac_at_2.4GHz": round(busy / (1024 * t * 2.4e9), 4)})
