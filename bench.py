@@ -988,9 +988,13 @@ def cpu_baseline(ffn, rows, np, log):
         return time.perf_counter() - t0
 
     if rows <= 0:
-        probe = max(threads, 16)
-        tp = run(probe)
-        rows = int(min(ffn.x.shape[0], max(probe, probe * 15.0 / max(tp, 1e-3))))
+        # size the sample to ~15 s from the marginal time per row of two probes (a
+        # single small probe is dominated by its fixed cost and sized it too small)
+        p1 = max(threads, 16)
+        p2 = 4 * p1
+        t1, t2 = run(p1), run(p2)
+        per_row = max((t2 - t1) / (p2 - p1), t2 / p2 / 4, 1e-6)
+        rows = int(min(ffn.x.shape[0], max(p2, 15.0 / per_row)))
         rows = max(threads, rows - rows % threads)
     log(f"cpu baseline: oracle on {rows} rows with {threads} threads")
     t = run(rows)
