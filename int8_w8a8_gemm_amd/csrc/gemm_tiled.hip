@@ -52,11 +52,12 @@ namespace {
 //          operand bytes per MFMA, 32 x 32 MFMAs: with 16 x 16 its accumulators
 //          and fragments outgrow the 256 registers of a wave at two per SIMD)
 //          ran 1280 us, 8192^3 7.7% and 4096^3 8.5% slower than this tile.
-//   mid:   192 x 256 tile, 2 x 4 waves of 96 x 64, 16 x 16 MFMAs for INT8:
-//          three quarters of a large tile's work, for row counts where large
-//          tiles leave many CUs idle in their last round (the ~2300-row text
-//          projection: 160 large tiles or 208 mid ones on 256 CUs; 16 x 16
-//          MFMAs took it from 41.1 to 39.6 us).
+//   mid:   192 x 256 tile, 2 x 4 waves of 96 x 64, 16 x 16 MFMAs (INT8 and
+//          BF16): three quarters of a large tile's work, for row counts where
+//          large tiles leave many CUs idle in their last round (the ~2300-row
+//          text projection: 160 large tiles or 208 mid ones on 256 CUs; 16 x 16
+//          MFMAs took it from 41.1 to 39.6 us, and the BF16 fallback on the
+//          same rows, 2378 x 4096 x 4096, from 76.5 to 70.6 us).
 //   small: 128 x 128 tile, 2 x 2 waves of 64 x 64, K split between two groups
 //          of waves (a 3-deep K ring for long K loops); 32 x 32 MFMAs (16 x 16
 //          ran 2048^3 and 512 x 4096 x 4096 12-15% slower).
@@ -274,7 +275,7 @@ struct Cfg {
 #define W8A8_BF16_LARGE_MT 16
 #endif
 #ifndef W8A8_BF16_MID_MT
-#define W8A8_BF16_MID_MT 32
+#define W8A8_BF16_MID_MT 16
 #endif
 #ifndef W8A8_BF16_SMALL_MT
 #define W8A8_BF16_SMALL_MT 32
@@ -673,8 +674,8 @@ __device__ __forceinline__ void for_each_pass(F& f, std::integer_sequence<int, P
 // free of bank conflicts.  `stage` must not overlap the K buffer that the next
 // tile's first stage is being loaded into.  VEC_OUT: y rows are 16-byte
 // aligned and N % 8 == 0, so every 16-byte chunk is stored whole; otherwise
-// chunks are stored element by element.  b_l holds the bias, -0.0 where
-// there is none.
+// chunks are stored in 8-, 4- or 2-byte parts, as N and y's alignment allow.
+// b_l holds the bias, -0.0 where there is none.
 template <class C, class E, int ACT, bool VEC_OUT>
 __device__ __forceinline__ void store_bf16(const Acc<C, E>& acc, uint16_t* __restrict__ y, int64_t M,
                                            int64_t N, int64_t m0, int64_t n0, int wave, int wm,
@@ -763,14 +764,33 @@ __device__ __forceinline__ void store_bf16(const Acc<C, E>& acc, uint16_t* __res
                 if (row + i * C::RPINS < M && n0 + 8 * cc < N)
                     *reinterpret_cast<v4i*>(gbase + i * C::RPINS * N) = d[i];
         } else {
+            // rows not 16-byte aligned: the widest stores that N and y allow.
+            // n0 and 8 * cc are multiples of 8, so with N % 4 == 0 (N % 2 == 0)
+            // each 4-column (2-column) part of a chunk lies wholly inside or
+            // wholly past column N, and its address is 8- (4-) byte aligned.
+            const uintptr_t ya = reinterpret_cast<uintptr_t>(y);
+            const bool w8 = N % 4 == 0 && ya % 8 == 0, w4 = N % 2 == 0 && ya % 4 == 0;
+            const int64_t c0 = n0 + 8 * cc;
 #pragma unroll
             for (int i = 0; i < NI_OUT; ++i) {
                 if (row + i * C::RPINS >= M) continue;
                 uint16_t* pr = gbase + i * C::RPINS * N;
+                if (w8) {
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    if (n0 + 8 * cc + e < N)
-                        pr[e] = (uint16_t)(((uint32_t)d[i][e >> 1] >> (16 * (e & 1))) & 0xffffu);
+                    for (int h = 0; h < 2; ++h)
+                        if (c0 + 4 * h < N)
+                            *reinterpret_cast<uint2*>(pr + 4 * h) =
+                                make_uint2((uint32_t)d[i][2 * h], (uint32_t)d[i][2 * h + 1]);
+                } else if (w4) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        if (c0 + 2 * j < N) *reinterpret_cast<uint32_t*>(pr + 2 * j) = (uint32_t)d[i][j];
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        if (c0 + e < N)
+                            pr[e] = (uint16_t)(((uint32_t)d[i][e >> 1] >> (16 * (e & 1))) & 0xffffu);
+                }
             }
         }
         lds_barrier();  // the staging area is free again

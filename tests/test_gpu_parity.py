@@ -1180,11 +1180,14 @@ def test_fallback_on_conforming_shapes_and_gelu():
 
 
 # The tiled BF16 path (K % 64 == 0, 16-byte aligned operands) on each tile
-# configuration: 64 x 64 (first two), 128 x 128, 192 x 256 (4100 x 4100 and
-# 4352 x 4104, with workgroups taking two tiles), 256 x 256 (3900 x 3900);
-# N % 8 != 0 stores element by element, K = 64 is a single stage.
-@pytest.mark.parametrize("M,N,K", [(300, 100, 64), (97, 256, 1024), (2000, 1992, 256),
-                                   (4100, 4100, 64), (4352, 4104, 192), (3900, 3900, 64)])
+# configuration: 64 x 64 (first four), 128 x 128, 192 x 256 (4100 x 4100 and
+# 4352 x 4104, with workgroups taking two tiles; 2378 x 4098 in one round),
+# 256 x 256 (3900 x 3900); with N % 8 != 0 rows are stored in 8-byte parts
+# (N % 4 == 0), 4-byte parts (N = 258, 4098) or element by element (N = 255),
+# K = 64 is a single stage.
+@pytest.mark.parametrize("M,N,K", [(300, 100, 64), (97, 256, 1024), (300, 258, 64), (97, 255, 128),
+                                   (2000, 1992, 256), (4100, 4100, 64), (4352, 4104, 192),
+                                   (2378, 4098, 128), (3900, 3900, 64)])
 @pytest.mark.parametrize("act", [w8.ACT_NONE, w8.ACT_GELU_TANH])
 def test_fallback_tiled_path(M, N, K, act):
     say(f"fallback tiled M={M} N={N} K={K} act={act}")
@@ -1215,6 +1218,28 @@ def test_fallback_tiled_k_tail(M, N, K, act):
     b = wl.to_bf16_bits(rng.standard_normal(N).astype(np.float32) * np.float32(0.01))
     y = h_u16(w8.linear_bf16(d_bf16(x), d_bf16(w), d_bf16(b), act=act))
     _check_fallback(y, x, w, b, act=act)
+
+
+@pytest.mark.parametrize("off", [1, 2, 4])
+def test_fallback_tiled_store_alignment(off):
+    """The 192 x 256 BF16 tiles into an output view offset by `off` elements
+    from a 256-byte aligned buffer (N = 4100: rows 8-byte aligned at offset 4,
+    4-byte at 2, 2-byte at 1, so each store width is taken); every element of
+    the view is checked and the guard elements around it stay untouched."""
+    M, N, K = 2378, 4100, 64
+    say(f"fallback tiled store alignment off={off}")
+    rng = np.random.default_rng(40 + off)
+    x = wl.to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+    w = wl.to_bf16_bits(rng.standard_normal((N, K)).astype(np.float32) * np.float32(0.05))
+    b = wl.to_bf16_bits(rng.standard_normal(N).astype(np.float32) * np.float32(0.01))
+    buf = torch.full((M * N + off + 8,), 1234.0, dtype=torch.bfloat16, device=DEV)
+    y = buf[off:off + M * N].view(M, N)
+    w8.linear_bf16(d_bf16(x), d_bf16(w), d_bf16(b), y=y)
+    torch.cuda.synchronize()
+    hb = h_u16(buf)
+    _check_fallback(hb[off:off + M * N].reshape(M, N), x, w, b)
+    guard = np.concatenate([hb[:off], hb[off + M * N:]])
+    assert np.all(guard == h_u16(torch.tensor([1234.0], dtype=torch.bfloat16))[0])
 
 
 def test_fallback_tiled_and_generic_agree_on_offsets():
