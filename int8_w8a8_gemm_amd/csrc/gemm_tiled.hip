@@ -223,7 +223,17 @@ struct Cfg {
     static constexpr int SCALE_BYTES = (BM + 2 * BN) * 4;
     static constexpr bool SCALES_IN_RING = RING + SCALE_BYTES > 160 * 1024;
     static constexpr int SCALE_OFF = SCALES_IN_RING ? STAGE + EPI_BYTES : RING;
-    static constexpr int SMEM = SCALES_IN_RING ? RING : RING + SCALE_BYTES;
+    // Epilogue straight from registers (store_direct): 16 x 16 MFMA tiles in
+    // pairs, no K groups, and not the register-tight tiles (on the 256 x 256
+    // tile it measured level on FFN up and 0.7-1.1% slower on FFN down, whose
+    // 64-byte non-temporal row pieces drain slower than the staged full rows;
+    // the 192 x 256 tile gained 2.3% on the 2378-row text projection).  With no
+    // barrier at its end, the next tile's scales go to the other of two scale
+    // buffers while slower waves still read these.
+    static constexpr bool DIRECT_OK = MT == 16 && NI % 2 == 0 && KS == 1 && !RECYCLE &&
+                                      !SCALES_IN_RING && RING + 2 * SCALE_BYTES <= 160 * 1024;
+    static constexpr int SCALE_BUFS = DIRECT_OK ? 2 : 1;
+    static constexpr int SMEM = SCALES_IN_RING ? RING : RING + SCALE_BUFS * SCALE_BYTES;
     static_assert(SMEM <= 160 * 1024 && SCALE_OFF + SCALE_BYTES <= SMEM, "LDS budget");
     static_assert(BM % (WAVES * RPI) == 0 && BN % (WAVES * RPI) == 0, "load split");
     static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile");
@@ -698,46 +708,63 @@ __device__ __forceinline__ void store_bf16(const Acc<C, E>& acc, uint16_t* __res
     // where the GELU body made the loop too large to unroll)
     auto pass = [&](auto pc) {
         constexpr int p = decltype(pc)::value;
+        // row scales of the pass's PM sub-tile rows
+        float sam[C::PM];
 #pragma unroll
-        for (int q = 0; q < C::PM; ++q) {
-            const int mi = p * C::PM + q;
-            float sam = 0.f;
-            if constexpr (E::BYTES == 1) sam = sa_l[wm * C::TM + mi * C::MT + lr];
-            // with K groups only group 0 holds the sums; every wave copies out
+        for (int q = 0; q < C::PM; ++q)
+            sam[q] = E::BYTES == 1 ? sa_l[wm * C::TM + (p * C::PM + q) * C::MT + lr] : 0.f;
+        // column groups outermost: a group's column scales and bias are read
+        // once for all PM rows, and the next group's are read while this one
+        // is computed (read and used back to back, each group waited out the
+        // LDS latency: 16 times per pass on the 256 x 256 tile)
+        // (register-tight tiles: no prefetch, the reads go just before their use)
+        constexpr bool PREF = !C::RECYCLE;
+        v4f swv[2][G], bv[2][G];
+        auto read_cols = [&](int ni, int buf) {
 #pragma unroll
-            for (int ni = 0; ni < (kg == 0 ? C::NI : 0); ++ni) {
-                v4f swv[G], bv[G];
+            for (int g = 0; g < G; ++g) {
+                const int cl = ncol + ni * C::MT + GS * g;
+                if constexpr (E::BYTES == 1) swv[buf][g] = *reinterpret_cast<const v4f*>(sw_l + cl);
+                bv[buf][g] = *reinterpret_cast<const v4f*>(b_l + cl);
+            }
+        };
+        // with K groups only group 0 holds the sums; every wave copies out
+        if (kg == 0) {
+            if (PREF) read_cols(0, 0);
 #pragma unroll
-                for (int g = 0; g < G; ++g) {
-                    const int cl = ncol + ni * C::MT + GS * g;
-                    if constexpr (E::BYTES == 1) swv[g] = *reinterpret_cast<const v4f*>(sw_l + cl);
-                    bv[g] = *reinterpret_cast<const v4f*>(b_l + cl);
-                }
+            for (int ni = 0; ni < C::NI; ++ni) {
+                const int cb = PREF ? ni & 1 : 0;
+                if (!PREF) read_cols(ni, 0);
+                else if (ni + 1 < C::NI) read_cols(ni + 1, cb ^ 1);
 #pragma unroll
-                for (int g = 0; g < G; ++g) {
-                    float v[4];
+                for (int q = 0; q < C::PM; ++q) {
+                    const int mi = p * C::PM + q;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        if constexpr (E::BYTES == 1) {
-                            const float t = (float)acc[ni][mi][4 * g + e];  // nearest even
-                            const float u = __fmul_rn(sam, swv[g][e]);
-                            v[e] = __builtin_fmaf(t, u, bv[g][e]);
-                        } else {
-                            const float t = acc[ni][mi][4 * g + e];
-                            v[e] = __fadd_rn(t, bv[g][e]);
+                    for (int g = 0; g < G; ++g) {
+                        float v[4];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            if constexpr (E::BYTES == 1) {
+                                const float t = (float)acc[ni][mi][4 * g + e];  // nearest even
+                                const float u = __fmul_rn(sam[q], swv[cb][g][e]);
+                                v[e] = __builtin_fmaf(t, u, bv[cb][g][e]);
+                            } else {
+                                const float t = acc[ni][mi][4 * g + e];
+                                v[e] = __fadd_rn(t, bv[cb][g][e]);
+                            }
                         }
+                        uint2 o = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+                        if (ACT == 1) {
+                            // GELU-tanh of the bf16-rounded value, rounded to bf16 (gelu_bf16_rn)
+                            o = make_uint2(gelu_bf16_rn(o.x & 0xffffu) | (gelu_bf16_rn(o.x >> 16) << 16),
+                                           gelu_bf16_rn(o.y & 0xffffu) | (gelu_bf16_rn(o.y >> 16) << 16));
+                        }
+                        *reinterpret_cast<uint2*>(wbase + q * C::MT * C::OUT_ROW +
+                                                  (ni * C::MT + GS * g) * 2) = o;
                     }
-                    uint2 o = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-                    if (ACT == 1) {
-                        // GELU-tanh of the bf16-rounded value, rounded to bf16 (gelu_bf16_rn)
-                        o = make_uint2(gelu_bf16_rn(o.x & 0xffffu) | (gelu_bf16_rn(o.x >> 16) << 16),
-                                       gelu_bf16_rn(o.y & 0xffffu) | (gelu_bf16_rn(o.y >> 16) << 16));
-                    }
-                    *reinterpret_cast<uint2*>(wbase + q * C::MT * C::OUT_ROW +
-                                              (ni * C::MT + GS * g) * 2) = o;
                 }
-                // register-tight tiles: keep the next column group's scale reads
-                // from being hoisted next to this one's (they would spill)
+                // register-tight tiles: keep the reads of later column groups
+                // from being hoisted next to these (they would spill)
                 if constexpr (C::RECYCLE) __builtin_amdgcn_sched_barrier(0);
             }
         }
@@ -796,6 +823,93 @@ __device__ __forceinline__ void store_bf16(const Acc<C, E>& acc, uint16_t* __res
         lds_barrier();  // the staging area is free again
     };
     for_each_pass(pass, std::make_integer_sequence<int, C::NPASS>{});
+}
+
+// Epilogue without LDS staging, for 16 x 16 MFMA tiles and 16-byte aligned
+// output rows.  After the scale and bias arithmetic a lane holds, for each
+// pair of adjacent MFMA tiles (ni, ni + 1) of one row tile mi, 4 columns of
+// row lane % 16 in each: columns 4 * (lane / 16) .. + 3.  One
+// v_permlane16_swap exchanges lanes 16-31 of the first tile's values with
+// lanes 0-15 of the second's (and 48-63 with 32-47), after which lane l holds
+// 8 consecutive columns (16 bytes) of row l % 16: tile ni + ((l / 16) & 1),
+// columns 8 * (l / 32) .. + 7.  A store instruction then writes 64 contiguous
+// bytes of each of 16 rows; there is no staging area, so no barrier.
+template <class C, class E, int ACT>
+__device__ __forceinline__ void store_direct(const Acc<C, E>& acc, uint16_t* __restrict__ y, int64_t M,
+                                             int64_t N, int64_t m0, int64_t n0, int wm, int wn,
+                                             int lane, const float* sa_l, const float* sw_l,
+                                             const float* b_l) {
+    static_assert(C::DIRECT_OK, "direct epilogue: 16 x 16 tiles in pairs");
+    const int lr = (int)((unsigned)lane % 16), hi = (int)((unsigned)lane / 16);
+    const bool interior = (m0 + C::BM <= M) && (n0 + C::BN <= N);
+    float sam[C::MI];
+#pragma unroll
+    for (int mi = 0; mi < C::MI; ++mi)
+        sam[mi] = E::BYTES == 1 ? sa_l[wm * C::TM + mi * 16 + lr] : 0.f;
+    // this lane's store: tile 2 * pp + (hi & 1), columns 8 * (hi >> 1) .. + 7,
+    // at base + mi * 16 rows + 32 * pp columns
+    const int64_t col0 = n0 + wn * C::TN + 16 * (hi & 1) + 8 * (hi >> 1);
+    const int64_t row0 = m0 + wm * C::TM + lr;
+    uint16_t* base = y + row0 * N + col0;
+    const int64_t rows_left = M - row0, cols_left = N - col0;
+#pragma unroll
+    for (int pp = 0; pp < C::NI / 2; ++pp) {
+        // the pair's column scales and bias, shared by every row tile
+        v4f swv[2], bv[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int cl = wn * C::TN + (2 * pp + j) * 16 + 4 * hi;
+            if constexpr (E::BYTES == 1) swv[j] = *reinterpret_cast<const v4f*>(sw_l + cl);
+            bv[j] = *reinterpret_cast<const v4f*>(b_l + cl);
+        }
+#pragma unroll
+        for (int mi = 0; mi < C::MI; ++mi) {
+            uint32_t d[2][2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    if constexpr (E::BYTES == 1) {
+                        const float t = (float)acc[2 * pp + j][mi][e];  // nearest even
+                        const float u = __fmul_rn(sam[mi], swv[j][e]);
+                        v[e] = __builtin_fmaf(t, u, bv[j][e]);
+                    } else {
+                        v[e] = __fadd_rn(acc[2 * pp + j][mi][e], bv[j][e]);
+                    }
+                }
+                uint32_t lo = pack_bf16x2(v[0], v[1]), hi2 = pack_bf16x2(v[2], v[3]);
+                if (ACT == 1) {
+                    // GELU-tanh of the bf16-rounded value, rounded to bf16 (gelu_bf16_rn)
+                    lo = gelu_bf16_rn(lo & 0xffffu) | (gelu_bf16_rn(lo >> 16) << 16);
+                    hi2 = gelu_bf16_rn(hi2 & 0xffffu) | (gelu_bf16_rn(hi2 >> 16) << 16);
+                }
+                d[j][0] = lo;
+                d[j][1] = hi2;
+            }
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const auto r = __builtin_amdgcn_permlane16_swap(d[0][k], d[1][k], false, false);
+                d[0][k] = r[0];
+                d[1][k] = r[1];
+            }
+            v4i o;
+            o[0] = (int)d[0][0];
+            o[1] = (int)d[0][1];
+            o[2] = (int)d[1][0];
+            o[3] = (int)d[1][1];
+            v4i* dst = reinterpret_cast<v4i*>(base + (int64_t)(mi * 16) * N + 32 * pp);
+            if (interior || (mi * 16 < rows_left && 32 * pp < cols_left)) {
+#if W8A8_STORE_NT
+                __builtin_nontemporal_store(o, dst);
+#else
+                *dst = o;
+#endif
+            }
+        }
+        // register-tight tiles: keep the next pair's reads from being hoisted
+        if constexpr (C::RECYCLE) __builtin_amdgcn_sched_barrier(0);
+    }
 }
 
 // K groups g > 0 hand their accumulators to group 0 through LDS (the ring,
@@ -892,6 +1006,9 @@ void gemm_tiled(const void* __restrict__ a, const float* __restrict__ sa, int64_
     // fragment reads from the in-flight direct-to-LDS loads and waits for
     // every load.
     __shared__ __attribute__((aligned(1024))) char smem[C::SMEM];
+    // the epilogue straight from registers (INT8, 16-byte aligned output rows;
+    // the BF16 192 x 256 kernel measured 1.5% slower with it)
+    constexpr bool DIRECT = C::DIRECT_OK && VEC_OUT && !OUT_I32 && E::BYTES == 1;
     float* sa_l = reinterpret_cast<float*>(smem + C::SCALE_OFF);
     float* sw_l = sa_l + BM;
     float* b_l = sw_l + BN;
@@ -1038,6 +1155,11 @@ void gemm_tiled(const void* __restrict__ a, const float* __restrict__ sa, int64_
             set_tile<C>(c, ab, wb, M, N, KB, m0n, n0n);
             if constexpr (C::SPLIT) c.kofs = slice * kt_split * BK;
             stage_load<C>(c, 0, smem);  // next tile's stage 0 -> buffer 0
+            // without a staging area the later stages can go now too
+            if constexpr (DIRECT) {
+                for (int s = 1; s < NST; ++s)
+                    if (s < KT) stage_load<C>(c, s * BK, smem + s * C::STAGE);
+            }
         }
         // The epilogue's lane addresses depend only on the lane, and hoisted out
         // of the tile loop they would stay live across the K loop; an opaque
@@ -1048,19 +1170,33 @@ void gemm_tiled(const void* __restrict__ a, const float* __restrict__ sa, int64_
             if (kg == 0)
                 store_i32<C>(acc, reinterpret_cast<int32_t*>(out) + (int64_t)slice_now * M * N, M, N,
                              m0, n0, wm, wn, elane);
+        } else if constexpr (DIRECT) {
+            store_direct<C, E, ACT>(acc, reinterpret_cast<uint16_t*>(out), M, N, m0, n0, wm, wn,
+                                    elane, sa_l, sw_l, b_l);
         } else {
             store_bf16<C, E, ACT, VEC_OUT>(acc, reinterpret_cast<uint16_t*>(out), M, N, m0, n0,
                                            wave, wm, wn, elane, sa_l, sw_l, b_l, smem + C::STAGE,
                                            kg);
         }
         if (!has_next) break;
-        // this tile's epilogue is done with the old values
+        if constexpr (C::SCALE_BUFS == 2) {
+            // the next tile's scales go to the other buffer: slower waves may
+            // still be reading these
+            const int flip = sa_l == reinterpret_cast<float*>(smem + C::SCALE_OFF) ? 1 : 0;
+            sa_l = reinterpret_cast<float*>(smem + C::SCALE_OFF + flip * C::SCALE_BYTES);
+            sw_l = sa_l + BM;
+            b_l = sw_l + BN;
+        }
+        // this tile's epilogue is done with the old values (store_bf16 ends
+        // with a barrier; store_direct's reads are in the other buffer)
         if constexpr (!C::SCALES_IN_RING) put_scales();
         wait_vm_lgkm0<0>();  // the next tile's stage 0 (and this tile's stores) are done ...
         __syncthreads();     // ... for every wave, and the staging area is free
         lane_ctx<C>(c, elane);
-        for (int s = 1; s < NST; ++s)
-            if (s < KT) stage_load<C>(c, s * BK, smem + s * C::STAGE);
+        if constexpr (!DIRECT) {
+            for (int s = 1; s < NST; ++s)
+                if (s < KT) stage_load<C>(c, s * BK, smem + s * C::STAGE);
+        }
         t = t_next;
         m0 = m0n;
         n0 = n0n;
