@@ -75,12 +75,12 @@ namespace {
 //   position is a scalar offset; each load's lane offset is formed from two
 //   per-lane values and wave-uniform terms as it is issued (stage_load_one).
 // * An LDS row r (BK bytes = BK/16 chunks) stores logical K-chunk c at physical
-//   chunk c ^ f(r).  A fragment read has lane l on row l % MT at logical chunk
-//   l / MT of the sub-step (each 16 lanes read 16 consecutive rows at one
-//   chunk); with f(r) = (r ^ (r >> 3)) & 7 for 128-byte rows and (r >> 2) & 3
-//   for 64-byte rows these reads are free of LDS bank conflicts on gfx950
-//   (measured with the SQ_LDS_BANK_CONFLICT counter; LDS serves 256 bytes per
-//   clock, so a conflict-free ds_read_b128 takes 4 clocks).
+//   chunk c ^ f(r) (swz below).  A fragment read has lane l on row l % MT at
+//   logical chunk l / MT of the sub-step; LDS serves a ds_read_b128 32 lanes at
+//   a time over 128 four-byte banks, and f(r) = (r ^ (r >> 3)) & 7 (32 x 32
+//   MFMAs) or (r ^ (r >> 2)) & 7 (16 x 16) for 128-byte rows, (r >> 2) & 3 for
+//   64-byte rows, makes those reads free of bank conflicts (SQ_LDS_BANK_CONFLICT
+//   counts only the epilogue's).
 // * MFMA roles are transposed (A-operand = weight rows, B-operand = activation
 //   rows) so the accumulator holds D[n][m]: each lane ends with 4 consecutive
 //   output columns of one row.
@@ -91,6 +91,10 @@ namespace {
 // * Tile order is XCD-aware: workgroup b runs on XCD b % 8, so each XCD is
 //   given a contiguous range of tiles, walked in groups of GROUP_M tile-rows
 //   (1024 rows: the 32 large tiles an XCD runs at once form a 4 x 8 block).
+// * Epilogue once per tile, after the whole K loop: the scale product, fma
+//   with the bias and bf16 packing per output, then 16-byte stores of whole
+//   rows through an LDS staging area (store_bf16), or, on the INT8 192 x 256
+//   tier, straight from registers after a lane exchange (store_direct).
 // ---------------------------------------------------------------------------
 constexpr int NUM_XCD = 8;
 // The W8A8_* macros below are the tuned defaults; each can be overridden on
