@@ -231,7 +231,8 @@ struct Cfg {
     // pairs, no K groups, and not the register-tight tiles (on the 256 x 256
     // tile it measured level on FFN up and 0.7-1.1% slower on FFN down, whose
     // 64-byte non-temporal row pieces drain slower than the staged full rows;
-    // the 192 x 256 tile gained 2.3% on the 2378-row text projection).  With no
+    // the INT8 192 x 256 tile gained 0.8-2.3% on the ~2300-row text projection,
+    // in three runs).  With no
     // barrier at its end, the next tile's scales go to the other of two scale
     // buffers while slower waves still read these.
     static constexpr bool DIRECT_OK = MT == 16 && NI % 2 == 0 && KS == 1 && !RECYCLE &&
