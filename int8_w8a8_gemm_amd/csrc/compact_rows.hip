@@ -8,10 +8,11 @@
 // in *count.
 //
 // Up to kSinglePassRows rows: one launch.  Block i owns source rows
-// [i*RPB, (i+1)*RPB).  It first counts the valid mask bytes before its first
-// row (a block-wide reduction over fewer than kSinglePassRows bytes, four mask
-// bytes per load when the mask is 4-byte aligned, served from L2), ranks its
-// own rows with a ballot, then copies its valid rows.  The (valid row, 16-byte
+// [i*RPB, (i+1)*RPB).  It ranks its own rows with a ballot, issues the loads
+// of its valid rows, and while they are in flight counts the valid mask bytes
+// before its first row (a block-wide reduction over fewer than
+// kSinglePassRows bytes, four mask bytes per load when the mask is 4-byte
+// aligned, served from L2), which places its rows in the output.  The (valid row, 16-byte
 // chunk) pairs of the block form one index space that the threads walk in
 // batches of kBatch loads issued before any store, so a block waits about one
 // memory latency per batch rather than one per row.  The last block writes
@@ -54,19 +55,28 @@ __device__ __forceinline__ int nonzero_bytes(uint32_t w) {
     return __builtin_popcount(hi & 0x80808080u);
 }
 
-// Copies nvalid rows x + rowsrc[j] * D (j < nvalid) to dst + j * D, the
-// block's (row, 16-byte chunk) pairs walked in batches of kBatch loads per
-// thread (VEC16: D % 8 == 0 and 16-byte aligned rows), else element by element.
-template <bool VEC16>
+// Copies nvalid rows x + rowsrc[j] * D (j < nvalid) to out + (base + j) * D,
+// the block's (row, 16-byte chunk) pairs walked in batches of kBatch loads per
+// thread (VEC16: D % 8 == 0 and 16-byte aligned rows), else element by
+// element.  base = get_base(), which every thread of the block calls once (it
+// may hold a barrier): with LATE (and VEC16) after the first batch's loads are
+// issued, so that the rows are in flight while the block works out where they
+// go, else before any load.
+template <bool VEC16, bool LATE, class GetBase>
 __device__ __forceinline__ void copy_rows(const uint16_t* __restrict__ x, int64_t D,
                                           const int64_t* rowsrc, int nvalid,
-                                          uint16_t* __restrict__ dst) {
+                                          uint16_t* __restrict__ out, GetBase get_base) {
     const int tid = threadIdx.x;
     if (VEC16) {
         const int64_t nch = D / 8;
         const int64_t step_j = kBlock / nch, step_c = kBlock % nch;
         int64_t j = tid / nch, c = tid % nch;
-        while (j < nvalid) {
+        uint16_t* dst = LATE ? nullptr : out + get_base() * D;
+        bool first = LATE;
+        for (;;) {
+            // every thread takes the first batch (loads guarded), so that all
+            // of them reach get_base
+            if (!first && j >= nvalid) break;
             u32x4 v[kBatch];
             int64_t jj = j, cc = c;
 #pragma unroll
@@ -78,6 +88,10 @@ __device__ __forceinline__ void copy_rows(const uint16_t* __restrict__ x, int64_
                 cc += step_c;
                 if (cc >= nch) { cc -= nch; ++jj; }
             }
+            if (LATE && first) {
+                dst = out + get_base() * D;
+                first = false;
+            }
 #pragma unroll
             for (int k = 0; k < kBatch; ++k) {
                 if (j < nvalid)
@@ -88,6 +102,7 @@ __device__ __forceinline__ void copy_rows(const uint16_t* __restrict__ x, int64_
             }
         }
     } else {
+        uint16_t* dst = out + get_base() * D;
         for (int j = 0; j < nvalid; ++j) {
             const uint16_t* src = x + rowsrc[j] * D;
             uint16_t* d = dst + j * D;
@@ -107,17 +122,7 @@ __global__ __launch_bounds__(kBlock) void compact_rows_kernel(
     const int64_t r0 = (int64_t)blockIdx.x * kRowsPerBlock;
     const int tid = threadIdx.x;
 
-    // 1. valid rows before r0 (r0 is a multiple of 8, so whole words)
-    int local = 0;
-    if (mask_words) {
-        const uint32_t* mw = reinterpret_cast<const uint32_t*>(mask);
-        for (int64_t i = tid; i < r0 / 4; i += kBlock) local += nonzero_bytes(mw[i]);
-    } else {
-        for (int64_t i = tid; i < r0; i += kBlock) local += (mask[i] != 0);
-    }
-    const int base = block_sum(local, red);
-
-    // 2. rank of this block's rows: a ballot over the first kRowsPerBlock lanes
+    // 1. rank of this block's rows: a ballot over the first kRowsPerBlock lanes
     if (tid < 64) {
         const int64_t r = r0 + tid;
         const bool valid = tid < kRowsPerBlock && r < R && mask[r] != 0;
@@ -127,11 +132,24 @@ __global__ __launch_bounds__(kBlock) void compact_rows_kernel(
     }
     __syncthreads();
     const int nvalid = nvalid_s;
-    if (blockIdx.x == gridDim.x - 1 && tid == 0) *count = base + nvalid;
-    if (tid < nvalid) src_row[base + tid] = (int32_t)rowsrc[tid];
 
-    // 3. copy: item i is chunk i % nch of valid row i / nch
-    copy_rows<VEC16>(x, D, rowsrc, nvalid, out + base * D);
+    // 2. copy (item i is chunk i % nch of valid row i / nch); the valid rows
+    // before r0 (r0 is a multiple of 8, so whole words) are counted while the
+    // first loads are in flight
+    auto get_base = [&]() -> int64_t {
+        int local = 0;
+        if (mask_words) {
+            const uint32_t* mw = reinterpret_cast<const uint32_t*>(mask);
+            for (int64_t i = tid; i < r0 / 4; i += kBlock) local += nonzero_bytes(mw[i]);
+        } else {
+            for (int64_t i = tid; i < r0; i += kBlock) local += (mask[i] != 0);
+        }
+        const int base = block_sum(local, red);
+        if (blockIdx.x == gridDim.x - 1 && tid == 0) *count = base + nvalid;
+        if (tid < nvalid) src_row[base + tid] = (int32_t)rowsrc[tid];
+        return base;
+    };
+    copy_rows<VEC16, true>(x, D, rowsrc, nvalid, out, get_base);
 }
 
 // ---- the linear-time path ----
@@ -239,7 +257,7 @@ __global__ __launch_bounds__(kBlock) void compact_gather_rows(
         __syncthreads();  // the previous rows' copies are done with rowsrc
         if ((int)threadIdx.x < nvalid) rowsrc[threadIdx.x] = src_row[m0 + threadIdx.x];
         __syncthreads();
-        copy_rows<VEC16>(x, D, rowsrc, nvalid, out + m0 * D);
+        copy_rows<VEC16, false>(x, D, rowsrc, nvalid, out, [&]() -> int64_t { return m0; });
     }
 }
 

@@ -395,21 +395,28 @@ __device__ __forceinline__ void cq_rank(const uint8_t* __restrict__ mask, int64_
 }
 
 // One wave quantises source row r of x [* x D] into output row m of q and
-// scale (the row held in registers, CPL 16-byte chunks per lane).
+// scale (the row held in registers, CPL 16-byte chunks per lane): cq_load_row
+// issues the row's loads, cq_store_row quantises and stores it.
 template <int CPL>
-__device__ __forceinline__ void cq_quantize_row_vec(const uint16_t* __restrict__ x, int64_t D,
-                                                    int64_t r, int64_t m, int8_t* __restrict__ q,
-                                                    float* __restrict__ scale, int lane) {
+__device__ __forceinline__ void cq_load_row(const uint16_t* __restrict__ x, int64_t D, int64_t r,
+                                            int lane, u32x4 (&v)[CPL]) {
     const int64_t nchunk = D >> 3;
     const u32x4* xr = reinterpret_cast<const u32x4*>(x + r * D);
-    u32x4 v[CPL];
-    uint32_t amax = 0;
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
         const int64_t ch = (int64_t)c * 64 + lane;
         v[c] = ch < nchunk ? __builtin_nontemporal_load(xr + ch) : (u32x4){0u, 0u, 0u, 0u};
-        amax = max(amax, absmax_bits(v[c]));
     }
+}
+
+template <int CPL>
+__device__ __forceinline__ void cq_store_row(const u32x4 (&v)[CPL], int64_t D, int64_t m,
+                                             int8_t* __restrict__ q, float* __restrict__ scale,
+                                             int lane) {
+    const int64_t nchunk = D >> 3;
+    uint32_t amax = 0;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) amax = max(amax, absmax_bits(v[c]));
     amax = wave_max_u32(amax);
     const float a = __uint_as_float(amax << 16);
     const bool zero = !(a >= 0x1p-100f);
@@ -428,6 +435,15 @@ __device__ __forceinline__ void cq_quantize_row_vec(const uint16_t* __restrict__
 }
 
 template <int CPL>
+__device__ __forceinline__ void cq_quantize_row_vec(const uint16_t* __restrict__ x, int64_t D,
+                                                    int64_t r, int64_t m, int8_t* __restrict__ q,
+                                                    float* __restrict__ scale, int lane) {
+    u32x4 v[CPL];
+    cq_load_row<CPL>(x, D, r, lane, v);
+    cq_store_row<CPL>(v, D, m, q, scale, lane);
+}
+
+template <int CPL>
 __global__ __launch_bounds__(kCqBlock) void compact_quantize_rows_vec(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ mask, int64_t R, int64_t D,
     int8_t* __restrict__ q, float* __restrict__ scale, int32_t* __restrict__ src_row,
@@ -435,14 +451,19 @@ __global__ __launch_bounds__(kCqBlock) void compact_quantize_rows_vec(
     __shared__ int red[kCqRows];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int64_t r0 = (int64_t)blockIdx.x * kCqRows;
+    const int64_t r = r0 + wave;
+    // the wave's row is loaded first: it is in flight while the block counts
+    // the valid rows before r0, which only its output position needs
+    u32x4 v[CPL];
+    if (r < R && mask[r] != 0) cq_load_row<CPL>(x, D, r, lane, v);
     int base, rank, nvalid;
     bool valid;
     cq_rank(mask, R, r0, mask_words, red, base, rank, nvalid, valid);
     if (blockIdx.x == gridDim.x - 1 && threadIdx.x == 0) *count = base + nvalid;
     if (!valid) return;
-    const int64_t r = r0 + wave, m = base + rank;
+    const int64_t m = base + rank;
     if (lane == 0) src_row[m] = (int32_t)r;
-    cq_quantize_row_vec<CPL>(x, D, r, m, q, scale, lane);
+    cq_store_row<CPL>(v, D, m, q, scale, lane);
 }
 
 // The linear-time path's last step: output rows m < *count quantised from
