@@ -99,9 +99,12 @@ namespace {
 constexpr int NUM_XCD = 8;
 // The W8A8_* macros below are the tuned defaults; each can be overridden on
 // the compiler command line to measure an alternative.
+// rows of output per raster group of the tile order (see tile_of)
 #ifndef W8A8_GROUP_ROWS
 #define W8A8_GROUP_ROWS 1024
 #endif
+// 1: weight sub-tiles innermost in a sub-step's MFMA order where a wave has
+// more of them than activation sub-tiles (Cfg::N_INNER); 0: always activation
 #ifndef W8A8_ORDER_N_INNER
 #define W8A8_ORDER_N_INNER 1
 #endif
