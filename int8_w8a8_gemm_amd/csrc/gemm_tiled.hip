@@ -165,7 +165,7 @@ template <> struct ElemBF16::Mfma<16> {
 };
 
 template <int BM_, int BN_, int WM_, int WN_, int BK_, int NST_, int GROUP_ROWS_ = GROUP_ROWS,
-          int KS_ = 1, bool SPLIT_ = false, int MT_ = 32, bool NIN_ = true>
+          int KS_ = 1, bool SPLIT_ = false, int MT_ = 32, bool NIN_ = true, bool EPW_ = false>
 struct Cfg {
     static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_, NST = NST_;
     static constexpr int GROUP_M = GROUP_ROWS_ / BM;  // tile-rows per group of the raster
@@ -225,11 +225,19 @@ struct Cfg {
     // bytes the groups g > 0 pass their accumulators through (KS > 1)
     static constexpr int RED_WAVE = NI * MI * ACC_N * 64 * 4;
     static constexpr int RED_BYTES = (KS - 1) * WG * RED_WAVE;
-    static constexpr int RING0 = NST * STAGE > STAGE + EPI_BYTES ? NST * STAGE : STAGE + EPI_BYTES;
+    // EPW: the epilogue stages each wave's outputs in a 2 KB area of its own
+    // past the ring (store_perwave), so the ring holds no staging area
+    static constexpr bool EPW = EPW_;
+    static constexpr int PW_BYTES = 16 * 128;  // 16 rows x 64 bf16 columns
+    static constexpr int RING0 = EPW                              ? NST * STAGE
+                                 : NST * STAGE > STAGE + EPI_BYTES ? NST * STAGE
+                                                                   : STAGE + EPI_BYTES;
     static constexpr int RING = RING0 > RED_BYTES ? RING0 : RED_BYTES;
+    static constexpr int PW_OFF = RING;
+    static constexpr int RING_PW = EPW ? RING + WAVES * PW_BYTES : RING;
     static constexpr int SCALE_BYTES = (BM + 2 * BN) * 4;
-    static constexpr bool SCALES_IN_RING = RING + SCALE_BYTES > 160 * 1024;
-    static constexpr int SCALE_OFF = SCALES_IN_RING ? STAGE + EPI_BYTES : RING;
+    static constexpr bool SCALES_IN_RING = RING_PW + SCALE_BYTES > 160 * 1024;
+    static constexpr int SCALE_OFF = SCALES_IN_RING ? STAGE + EPI_BYTES : RING_PW;
     // Epilogue straight from registers (store_direct): 16 x 16 MFMA tiles in
     // pairs, no K groups, and not the register-tight tiles (on the 256 x 256
     // tile it measured level on FFN up and 0.7-1.1% slower on FFN down, whose
@@ -238,10 +246,12 @@ struct Cfg {
     // in three runs).  With no
     // barrier at its end, the next tile's scales go to the other of two scale
     // buffers while slower waves still read these.
-    static constexpr bool DIRECT_OK = MT == 16 && NI % 2 == 0 && KS == 1 && !RECYCLE &&
+    static constexpr bool DIRECT_OK = MT == 16 && NI % 2 == 0 && KS == 1 && !RECYCLE && !EPW &&
                                       !SCALES_IN_RING && RING + 2 * SCALE_BYTES <= 160 * 1024;
-    static constexpr int SCALE_BUFS = DIRECT_OK ? 2 : 1;
-    static constexpr int SMEM = SCALES_IN_RING ? RING : RING + SCALE_BUFS * SCALE_BYTES;
+    static constexpr int SCALE_BUFS = DIRECT_OK || EPW ? 2 : 1;
+    static constexpr int SMEM = SCALES_IN_RING ? RING : RING_PW + SCALE_BUFS * SCALE_BYTES;
+    static_assert(!EPW || (MT == 16 && NI % 4 == 0 && KS == 1 && !SCALES_IN_RING),
+                  "per-wave epilogue: 16 x 16 tiles in groups of four, no K groups");
     static_assert(SMEM <= 160 * 1024 && SCALE_OFF + SCALE_BYTES <= SMEM, "LDS budget");
     static_assert(BM % (WAVES * RPI) == 0 && BN % (WAVES * RPI) == 0, "load split");
     static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile");
@@ -289,6 +299,10 @@ struct Cfg {
 #ifndef W8A8_I8_TINY_MT
 #define W8A8_I8_TINY_MT 32
 #endif
+// the INT8 256 x 256 tier stages its epilogue per wave (store_perwave)
+#ifndef W8A8_I8_LARGE_EPW
+#define W8A8_I8_LARGE_EPW 1
+#endif
 #ifndef W8A8_BF16_LARGE_MT
 #define W8A8_BF16_LARGE_MT 16
 #endif
@@ -309,7 +323,7 @@ template <class E> struct Tiers {  // BF16
     typedef Cfg<W8A8_TINY_CFG, W8A8_BF16_TINY_MT> Tiny;
 };
 template <> struct Tiers<ElemI8> {
-    typedef Cfg<W8A8_LARGE_CFG, W8A8_I8_LARGE_MT> Large;
+    typedef Cfg<W8A8_LARGE_CFG, W8A8_I8_LARGE_MT, true, W8A8_I8_LARGE_EPW> Large;
     typedef Cfg<W8A8_MID_CFG, W8A8_I8_MID_MT> Mid;
     typedef Cfg<W8A8_SMALL_CFG, W8A8_I8_SMALL_MT> Small;
     typedef Cfg<W8A8_SMALL_DEEP_CFG, W8A8_I8_SMALL_MT> Deep;
@@ -920,6 +934,87 @@ __device__ __forceinline__ void store_direct(const Acc<C, E>& acc, uint16_t* __r
     }
 }
 
+// Epilogue with a staging area per wave (C::EPW), 2 KB past the ring: a wave
+// stages a piece of 16 rows x 64 columns of its own outputs (MFMA row tile mi,
+// four column tiles), reads it back as 2 x 8 rows of 128 bytes and stores
+// whole 128-byte row segments.  A wave reads only what it wrote itself and
+// LDS executes a wave's instructions in order, so there is no barrier.  Row r
+// of a piece (128 bytes) keeps 16-byte chunk c at c ^ 2*((r >> 2) & 3): the
+// 8-byte writes (64 lanes, rows lane % 16) and the 16-byte reads (rows
+// lane / 8 and lane / 8 + 8) are then free of bank conflicts.
+template <class C, class E, int ACT>
+__device__ __forceinline__ void store_perwave(const Acc<C, E>& acc, uint16_t* __restrict__ y,
+                                              int64_t M, int64_t N, int64_t m0, int64_t n0, int wm,
+                                              int wn, int lane, const float* sa_l, const float* sw_l,
+                                              const float* b_l, char* pw) {
+    static_assert(C::EPW, "per-wave epilogue");
+    const int lr = (int)((unsigned)lane % 16), hi = (int)((unsigned)lane / 16);
+    // writes: row lr, byte 32 * nl + 16 * (hi >> 1) + 8 * (hi & 1), chunk XOR g
+    const uint32_t wofs = (uint32_t)(lr * 128 + 16 * (hi >> 1) + 8 * (hi & 1));
+    const uint32_t g = 32u * (uint32_t)((lr >> 2) & 3);
+    // reads: rows rr and rr + 8, chunk rc
+    const int rr = (int)((unsigned)lane / 8), rc = (int)((unsigned)lane % 8);
+    const uint32_t rofs0 = (uint32_t)(rr * 128 + 16 * (rc ^ (2 * ((rr >> 2) & 3))));
+    const uint32_t rofs1 = (uint32_t)((rr + 8) * 128 + 16 * (rc ^ (2 * (((rr + 8) >> 2) & 3))));
+    const bool interior = (m0 + C::BM <= M) && (n0 + C::BN <= N);
+    const int64_t row0 = m0 + wm * C::TM + rr, col0 = n0 + wn * C::TN + 8 * rc;
+    uint16_t* base = y + row0 * N + col0;
+    const int64_t rows_left = M - row0, cols_left = N - col0;
+#pragma unroll
+    for (int mi = 0; mi < C::MI; ++mi) {
+        const float sam = E::BYTES == 1 ? sa_l[wm * C::TM + mi * 16 + lr] : 0.f;
+#pragma unroll
+        for (int h = 0; h < C::NI / 4; ++h) {
+#pragma unroll
+            for (int nl = 0; nl < 4; ++nl) {
+                const int ni = 4 * h + nl;
+                const int cl = wn * C::TN + ni * 16 + 4 * hi;
+                v4f swv = {}, bv;
+                if constexpr (E::BYTES == 1) swv = *reinterpret_cast<const v4f*>(sw_l + cl);
+                bv = *reinterpret_cast<const v4f*>(b_l + cl);
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    if constexpr (E::BYTES == 1) {
+                        const float t = (float)acc[ni][mi][e];  // nearest even
+                        const float u = __fmul_rn(sam, swv[e]);
+                        v[e] = __builtin_fmaf(t, u, bv[e]);
+                    } else {
+                        v[e] = __fadd_rn(acc[ni][mi][e], bv[e]);
+                    }
+                }
+                uint2 o = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+                if (ACT == 1) {
+                    // GELU-tanh of the bf16-rounded value, rounded to bf16 (gelu_bf16_rn)
+                    o = make_uint2(gelu_bf16_rn(o.x & 0xffffu) | (gelu_bf16_rn(o.x >> 16) << 16),
+                                   gelu_bf16_rn(o.y & 0xffffu) | (gelu_bf16_rn(o.y >> 16) << 16));
+                }
+                *reinterpret_cast<uint2*>(pw + (wofs + ((32u * (uint32_t)nl) ^ g))) = o;
+            }
+            const v4i d0 = *reinterpret_cast<const v4i*>(pw + rofs0);
+            const v4i d1 = *reinterpret_cast<const v4i*>(pw + rofs1);
+            uint16_t* dst = base + (int64_t)(mi * 16) * N + 64 * h;
+            const bool cols_in = interior || 64 * h < cols_left;
+            if (cols_in && (interior || mi * 16 < rows_left)) {
+#if W8A8_STORE_NT
+                __builtin_nontemporal_store(d0, reinterpret_cast<v4i*>(dst));
+#else
+                *reinterpret_cast<v4i*>(dst) = d0;
+#endif
+            }
+            if (cols_in && (interior || mi * 16 + 8 < rows_left)) {
+#if W8A8_STORE_NT
+                __builtin_nontemporal_store(d1, reinterpret_cast<v4i*>(dst + 8 * N));
+#else
+                *reinterpret_cast<v4i*>(dst + 8 * N) = d1;
+#endif
+            }
+            // register-tight tiles: keep the next piece's scale reads here
+            if constexpr (C::RECYCLE) __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+}
+
 // K groups g > 0 hand their accumulators to group 0 through LDS (the ring,
 // which the K loop is done with), and group 0 adds them in order g = 1, 2, ...:
 // exact for INT32, a fixed order for fp32.  Lane l's values of accumulator
@@ -1015,8 +1110,11 @@ void gemm_tiled(const void* __restrict__ a, const float* __restrict__ sa, int64_
     // every load.
     __shared__ __attribute__((aligned(1024))) char smem[C::SMEM];
     // the epilogue straight from registers (INT8, 16-byte aligned output rows;
-    // the BF16 192 x 256 kernel measured 1.5% slower with it)
+    // the BF16 192 x 256 kernel measured 1.5% slower with it), or staged per wave
     constexpr bool DIRECT = C::DIRECT_OK && VEC_OUT && !OUT_I32 && E::BYTES == 1;
+    constexpr bool PERWAVE = C::EPW && !OUT_I32;
+    static_assert(!PERWAVE || VEC_OUT, "the per-wave epilogue stores whole 16-byte chunks");
+    constexpr bool NO_STAGE = DIRECT || PERWAVE;  // the ring holds no staging area
     float* sa_l = reinterpret_cast<float*>(smem + C::SCALE_OFF);
     float* sw_l = sa_l + BM;
     float* b_l = sw_l + BN;
@@ -1159,12 +1257,14 @@ void gemm_tiled(const void* __restrict__ a, const float* __restrict__ sa, int64_
             item(t_next);
             m0n = tile_m * BM;
             n0n = tile_n * BN;
-            if constexpr (!C::SCALES_IN_RING) load_scales(m0n, n0n);
+            // (the per-wave epilogue leaves no register for them: they are
+            // loaded after it, from L2)
+            if constexpr (!C::SCALES_IN_RING && !PERWAVE) load_scales(m0n, n0n);
             set_tile<C>(c, ab, wb, M, N, KB, m0n, n0n);
             if constexpr (C::SPLIT) c.kofs = slice * kt_split * BK;
             stage_load<C>(c, 0, smem);  // next tile's stage 0 -> buffer 0
-            // without a staging area the later stages can go now too
-            if constexpr (DIRECT) {
+            // without a staging area in the ring the later stages can go now too
+            if constexpr (NO_STAGE) {
                 for (int s = 1; s < NST; ++s)
                     if (s < KT) stage_load<C>(c, s * BK, smem + s * C::STAGE);
             }
@@ -1181,12 +1281,16 @@ void gemm_tiled(const void* __restrict__ a, const float* __restrict__ sa, int64_
         } else if constexpr (DIRECT) {
             store_direct<C, E, ACT>(acc, reinterpret_cast<uint16_t*>(out), M, N, m0, n0, wm, wn,
                                     elane, sa_l, sw_l, b_l);
+        } else if constexpr (PERWAVE) {
+            store_perwave<C, E, ACT>(acc, reinterpret_cast<uint16_t*>(out), M, N, m0, n0, wm, wn,
+                                     elane, sa_l, sw_l, b_l, smem + C::PW_OFF + wave * C::PW_BYTES);
         } else {
             store_bf16<C, E, ACT, VEC_OUT>(acc, reinterpret_cast<uint16_t*>(out), M, N, m0, n0,
                                            wave, wm, wn, elane, sa_l, sw_l, b_l, smem + C::STAGE,
                                            kg);
         }
         if (!has_next) break;
+        if constexpr (PERWAVE) load_scales(m0n, n0n);
         if constexpr (C::SCALE_BUFS == 2) {
             // the next tile's scales go to the other buffer: slower waves may
             // still be reading these
@@ -1196,12 +1300,13 @@ void gemm_tiled(const void* __restrict__ a, const float* __restrict__ sa, int64_
             b_l = sw_l + BN;
         }
         // this tile's epilogue is done with the old values (store_bf16 ends
-        // with a barrier; store_direct's reads are in the other buffer)
+        // with a barrier; store_direct's and store_perwave's reads are in the
+        // other buffer)
         if constexpr (!C::SCALES_IN_RING) put_scales();
         wait_vm_lgkm0<0>();  // the next tile's stage 0 (and this tile's stores) are done ...
         __syncthreads();     // ... for every wave, and the staging area is free
         lane_ctx<C>(c, elane);
-        if constexpr (!DIRECT) {
+        if constexpr (!NO_STAGE) {
             for (int s = 1; s < NST; ++s)
                 if (s < KT) stage_load<C>(c, s * BK, smem + s * C::STAGE);
         }
