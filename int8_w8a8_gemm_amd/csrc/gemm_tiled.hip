@@ -92,9 +92,11 @@ namespace {
 //   given a contiguous range of tiles, walked in groups of GROUP_M tile-rows
 //   (1024 rows: the 32 large tiles an XCD runs at once form a 4 x 8 block).
 // * Epilogue once per tile, after the whole K loop: the scale product, fma
-//   with the bias and bf16 packing per output, then 16-byte stores of whole
-//   rows through an LDS staging area (store_bf16), or, on the INT8 192 x 256
-//   tier, straight from registers after a lane exchange (store_direct).
+//   with the bias and bf16 packing per output, then 16-byte stores: through a
+//   staging area per wave on the INT8 256 x 256 tier (store_perwave), straight
+//   from registers after a lane exchange on the INT8 192 x 256 tier
+//   (store_direct), through an LDS staging area of whole tile rows otherwise
+//   (store_bf16).
 // ---------------------------------------------------------------------------
 constexpr int NUM_XCD = 8;
 // The W8A8_* macros below are the tuned defaults; each can be overridden on
@@ -241,7 +243,7 @@ struct Cfg {
     // Epilogue straight from registers (store_direct): 16 x 16 MFMA tiles in
     // pairs, no K groups, and not the register-tight tiles (on the 256 x 256
     // tile it measured level on FFN up and 0.7-1.1% slower on FFN down, whose
-    // 64-byte non-temporal row pieces drain slower than the staged full rows;
+    // 64-byte non-temporal row pieces drain slower than full 128-byte rows;
     // the INT8 192 x 256 tile gained 0.8-2.3% on the ~2300-row text projection,
     // in three runs).  With no
     // barrier at its end, the next tile's scales go to the other of two scale
