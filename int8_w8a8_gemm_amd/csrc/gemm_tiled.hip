@@ -332,17 +332,19 @@ template <> struct Tiers<ElemI8> {
     typedef Cfg<W8A8_TINY_CFG, W8A8_I8_TINY_MT> Tiny;
 };
 
-// Physical chunk of logical chunk c in LDS row r.  LDS serves a ds_read_b128
-// 32 lanes at a time over 128 banks (four per 16-byte chunk): a 32 x 32 MFMA
-// fragment read has 32 lanes on 32 consecutive rows at one chunk, a 16 x 16 one
-// 16 consecutive rows at two chunks, and each swizzle spreads its pattern over
-// all 128 banks (SQ_LDS_BANK_CONFLICT: the 32 x 32 swizzle on 16 x 16 reads
-// conflicted on about half of the LDS cycles).  Both are XOR-separable over
-// blocks of 8 rows (the loads) and of MT rows (the fragment sub-tiles).
+// Physical chunk of logical chunk c in LDS row r.  A ds_read_b128 takes four
+// LDS cycles of 16 lanes when free of bank conflicts; a 32 x 32 MFMA fragment
+// read has 32 lanes on 32 consecutive rows at one chunk, a 16 x 16 one 16
+// consecutive rows at four chunks.  Each swizzle here was measured free of
+// conflicts with SQ_LDS_BANK_CONFLICT, on the fragment reads of the kernel and
+// on the same lane pattern alone: the 32 x 32 swizzle on 16 x 16 reads and
+// c ^ ((r >> 2) & 3) on 64-byte rows conflicted two ways, 64-byte rows with no
+// swizzle two ways and 128-byte rows with none four.  All are XOR-separable
+// over blocks of 8 rows (the loads) and of MT rows (the fragment sub-tiles).
 template <int BK, int MT>
 __device__ __forceinline__ int swz(int r, int c) {
     if (BK == 128) return MT == 16 ? c ^ ((r ^ (r >> 2)) & 7) : c ^ ((r ^ (r >> 3)) & 7);
-    return c ^ ((r >> 2) & 3);
+    return c ^ ((r >> 1) & 3);
 }
 
 // Workgroup barrier for the wave's own LDS reads and writes (ds_*) only.
@@ -435,8 +437,8 @@ __device__ __forceinline__ void lane_ctx(Ctx<C>& c, int lane) {
     c.lrow = (uint32_t)rsub * c.kb;
     // 128-byte rows: swz(r0 + rsub, pc) = pc ^ rsub ^ ((r0 >> 3) & 7) for r0 % 8 == 0
     // (MT = 32), pc ^ rsub ^ (rsub >> 2) ^ ((r0 >> 2) & 7) (MT = 16);
-    // 64-byte rows: swz(r0 + rsub, pc) = pc ^ ((rsub >> 2) & 3) for r0 % 16 == 0
-    c.lx = C::BK != 128 ? 16u * (uint32_t)(pc ^ ((rsub >> 2) & 3))
+    // 64-byte rows: swz(r0 + rsub, pc) = pc ^ ((rsub >> 1) & 3) for r0 % 8 == 0
+    c.lx = C::BK != 128 ? 16u * (uint32_t)(pc ^ ((rsub >> 1) & 3))
            : C::MT == 16  ? 16u * (uint32_t)(pc ^ rsub ^ (rsub >> 2))
                           : 16u * (uint32_t)(pc ^ rsub);
     // lane l reads row l % MT of a sub-tile at K-chunk l / MT of the sub-step
