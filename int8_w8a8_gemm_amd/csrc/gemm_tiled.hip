@@ -76,9 +76,8 @@ namespace {
 //   per-lane values and wave-uniform terms as it is issued (stage_load_one).
 // * An LDS row r (BK bytes = BK/16 chunks) stores logical K-chunk c at physical
 //   chunk c ^ f(r) (swz below).  A fragment read has lane l on row l % MT at
-//   logical chunk l / MT of the sub-step; LDS serves a ds_read_b128 32 lanes at
-//   a time over 128 four-byte banks, and f(r) = (r ^ (r >> 3)) & 7 (32 x 32
-//   MFMAs) or (r ^ (r >> 2)) & 7 (16 x 16) for 128-byte rows, (r >> 2) & 3 for
+//   logical chunk l / MT of the sub-step; f(r) = (r ^ (r >> 3)) & 7 (32 x 32
+//   MFMAs) or (r ^ (r >> 2)) & 7 (16 x 16) for 128-byte rows, (r >> 1) & 3 for
 //   64-byte rows, makes those reads free of bank conflicts (SQ_LDS_BANK_CONFLICT
 //   counts only the epilogue's).
 // * MFMA roles are transposed (A-operand = weight rows, B-operand = activation
