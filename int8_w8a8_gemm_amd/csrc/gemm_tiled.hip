@@ -718,6 +718,10 @@ __device__ __forceinline__ void store_bf16(const Acc<C, E>& acc, uint16_t* __res
                                            const float* b_l, char* stage, int kg) {
     constexpr int G = C::ACC_N / 4;  // groups of 4 consecutive columns per MFMA tile
     constexpr int GS = C::MT / 4;    // column step between them
+    // the column tiles this wave finalises: all, or with two K groups the
+    // group's half, whose sums reduce_k_groups left in acc[0 .. NI/2)
+    constexpr int NIS = C::KS == 2 ? C::NI / 2 : C::NI;
+    const int cofs = C::KS == 2 ? kg * NIS * C::MT : 0;
     const int lr = (int)((unsigned)lane % C::MT);
     const int ncol = wn * C::TN + 4 * (int)((unsigned)lane / C::MT);  // this lane's first column
     char* wbase = stage + (wm * 32 + lr) * C::OUT_ROW + ncol * 2;
@@ -748,19 +752,20 @@ __device__ __forceinline__ void store_bf16(const Acc<C, E>& acc, uint16_t* __res
         auto read_cols = [&](int ni, int buf) {
 #pragma unroll
             for (int g = 0; g < G; ++g) {
-                const int cl = ncol + ni * C::MT + GS * g;
+                const int cl = ncol + cofs + ni * C::MT + GS * g;
                 if constexpr (E::BYTES == 1) swv[buf][g] = *reinterpret_cast<const v4f*>(sw_l + cl);
                 bv[buf][g] = *reinterpret_cast<const v4f*>(b_l + cl);
             }
         };
-        // with K groups only group 0 holds the sums; every wave copies out
-        if (kg == 0) {
+        // with more than two K groups only group 0 holds the sums; every wave
+        // copies out
+        if (C::KS <= 2 || kg == 0) {
             if (PREF) read_cols(0, 0);
 #pragma unroll
-            for (int ni = 0; ni < C::NI; ++ni) {
+            for (int ni = 0; ni < NIS; ++ni) {
                 const int cb = PREF ? ni & 1 : 0;
                 if (!PREF) read_cols(ni, 0);
-                else if (ni + 1 < C::NI) read_cols(ni + 1, cb ^ 1);
+                else if (ni + 1 < NIS) read_cols(ni + 1, cb ^ 1);
 #pragma unroll
                 for (int q = 0; q < C::PM; ++q) {
                     const int mi = p * C::PM + q;
@@ -785,7 +790,7 @@ __device__ __forceinline__ void store_bf16(const Acc<C, E>& acc, uint16_t* __res
                                            gelu_bf16_rn(o.y & 0xffffu) | (gelu_bf16_rn(o.y >> 16) << 16));
                         }
                         *reinterpret_cast<uint2*>(wbase + q * C::MT * C::OUT_ROW +
-                                                  (ni * C::MT + GS * g) * 2) = o;
+                                                  (cofs + ni * C::MT + GS * g) * 2) = o;
                     }
                 }
                 // register-tight tiles: keep the reads of later column groups
@@ -1021,16 +1026,58 @@ __device__ __forceinline__ void store_perwave(const Acc<C, E>& acc, uint16_t* __
     }
 }
 
-// K groups g > 0 hand their accumulators to group 0 through LDS (the ring,
-// which the K loop is done with), and group 0 adds them in order g = 1, 2, ...:
-// exact for INT32, a fixed order for fp32.  Lane l's values of accumulator
-// register group q of MFMA tile (ni, mi) sit at ((ni*MI + mi)*G + q)*1 KB +
-// 16*l of the wave's area, so each 16-byte access of a wave is contiguous.
-// Every wave calls it (it holds two barriers).
+// The K groups' partial sums are added through LDS (the ring, which the K loop
+// is done with).  With two groups each finalises half of the wave's column
+// tiles, group g the tiles [g*NI/2, (g+1)*NI/2): it hands the other half to its
+// partner wave (same slot in the other group), adds the partner's half of its
+// own, and leaves the sums in acc[0 .. NI/2) (so that no accumulator index
+// depends on the group, which would put the accumulators in scratch memory).
+// Both groups then share the adds and the epilogue.  The sums are the same
+// either way: exact for INT32, and for fp32 a + b, which is b + a.  With more
+// groups, groups g > 0 hand everything to group 0, which adds them in order
+// g = 1, 2, ....  Lane l's values of accumulator register group q of MFMA tile
+// j of the handed range sit at ((j*MI + mi)*G + q)*1 KB + 16*l of the wave's
+// area, so each 16-byte access of a wave is contiguous.  Every wave calls it
+// (it holds two barriers).
 template <class C, class E>
 __device__ __forceinline__ void reduce_k_groups(Acc<C, E>& acc, char* smem, int kg, int slot,
                                                 int lane) {
-    if constexpr (C::KS > 1) {
+    if constexpr (C::KS == 2) {
+        typedef std::conditional_t<E::BYTES == 1, v4i, v4f> V4;
+        constexpr int G = C::ACC_N / 4, H = C::NI / 2;
+        constexpr int HALF = H * C::MI * G * 1024;  // bytes one wave hands over
+        static_assert(C::NI % 2 == 0 && 2 * C::WG * HALF <= C::RING, "K-group halves");
+        const bool g1 = kg != 0;
+        char* dst = smem + (kg * C::WG + slot) * HALF + 16 * lane;
+#pragma unroll
+        for (int j = 0; j < H; ++j)
+#pragma unroll
+            for (int mi = 0; mi < C::MI; ++mi)
+#pragma unroll
+                for (int q = 0; q < G; ++q) {
+                    V4 v;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        v[e] = g1 ? acc[j][mi][4 * q + e] : acc[H + j][mi][4 * q + e];
+                    *reinterpret_cast<V4*>(dst + ((j * C::MI + mi) * G + q) * 1024) = v;
+                }
+        lds_barrier();
+        const char* src = smem + ((1 - kg) * C::WG + slot) * HALF + 16 * lane;
+#pragma unroll
+        for (int j = 0; j < H; ++j)
+#pragma unroll
+            for (int mi = 0; mi < C::MI; ++mi)
+#pragma unroll
+                for (int q = 0; q < G; ++q) {
+                    const V4 v = *reinterpret_cast<const V4*>(src + ((j * C::MI + mi) * G + q) * 1024);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const auto own = g1 ? acc[H + j][mi][4 * q + e] : acc[j][mi][4 * q + e];
+                        acc[j][mi][4 * q + e] = own + v[e];
+                    }
+                }
+        lds_barrier();  // the ring is free again
+    } else if constexpr (C::KS > 2) {
         typedef AccT<C, E> A;
         typedef std::conditional_t<E::BYTES == 1, v4i, v4f> V4;
         constexpr int G = C::ACC_N / 4;
@@ -1069,19 +1116,23 @@ __device__ __forceinline__ void reduce_k_groups(Acc<C, E>& acc, char* smem, int 
     }
 }
 
+// (with two K groups a wave stores its group's half of its column tiles, kg
+// the group: their sums are in acc[0 .. NI/2), see reduce_k_groups)
 template <class C>
 __device__ __forceinline__ void store_i32(const Acc<C, ElemI8>& acc, int32_t* __restrict__ out,
                                           int64_t M, int64_t N, int64_t m0, int64_t n0, int wm,
-                                          int wn, int lane) {
+                                          int wn, int lane, int kg) {
     constexpr int G = C::ACC_N / 4, GS = C::MT / 4;
-    const int ncol = wn * C::TN + 4 * (int)((unsigned)lane / C::MT);
+    constexpr int NIS = C::KS == 2 ? C::NI / 2 : C::NI;
+    const int ncol = wn * C::TN + (C::KS == 2 ? kg * NIS * C::MT : 0) +
+                     4 * (int)((unsigned)lane / C::MT);
 #pragma unroll
     for (int mi = 0; mi < C::MI; ++mi) {
         const int ml = wm * C::TM + mi * C::MT + (int)((unsigned)lane % C::MT);
         if (m0 + ml >= M) continue;
         int32_t* rowp = out + (m0 + ml) * N + n0 + ncol;
 #pragma unroll
-        for (int ni = 0; ni < C::NI; ++ni)
+        for (int ni = 0; ni < NIS; ++ni)
 #pragma unroll
             for (int g = 0; g < G; ++g) {
                 if (n0 + ncol + ni * C::MT + GS * g >= N) continue;
@@ -1281,9 +1332,9 @@ void gemm_tiled(const void* __restrict__ a, const float* __restrict__ sa, int64_
         int elane = lane;
         asm volatile("" : "+v"(elane));
         if constexpr (OUT_I32 != 0) {
-            if (kg == 0)
+            if (C::KS <= 2 || kg == 0)
                 store_i32<C>(acc, reinterpret_cast<int32_t*>(out) + (int64_t)slice_now * M * N, M, N,
-                             m0, n0, wm, wn, elane);
+                             m0, n0, wm, wn, elane, kg);
         } else if constexpr (DIRECT) {
             store_direct<C, E, ACT>(acc, reinterpret_cast<uint16_t*>(out), M, N, m0, n0, wm, wn,
                                     elane, sa_l, sw_l, b_l);
