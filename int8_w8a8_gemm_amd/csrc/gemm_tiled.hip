@@ -947,11 +947,15 @@ __device__ __forceinline__ void store_direct(const Acc<C, E>& acc, uint16_t* __r
 // four column tiles), reads it back as 2 x 8 rows of 128 bytes and stores
 // whole 128-byte row segments.  A wave reads only what it wrote itself and
 // LDS executes a wave's instructions in order, so there is no barrier.  Row r
-// of a piece (128 bytes) keeps 16-byte chunk c at c ^ ((r >> 1) & 7): the
-// 8-byte writes (rows lane % 16) and the 16-byte reads (rows lane / 8 and
-// lane / 8 + 8) are then free of bank conflicts whether LDS takes 32 lanes of
-// 8 bytes over 64 banks or 64 lanes over 128 (c ^ 2*((r >> 2) & 3), free
-// only in the second case, measured 10.9% bank-conflict cycles on FFN up).
+// of a piece (128 bytes) keeps its 8-byte slot s at s ^ f(r), f(r) =
+// 2 * (r & 7) + (r >> 3), a permutation of 0 .. 15.  An 8-byte write
+// instruction takes 16 lanes per LDS cycle, here 16 rows at the same logical
+// slot, which the XOR spreads over all 16 slots of a row: free of bank
+// conflicts (SQ_LDS_BANK_CONFLICT; with any swizzle of 16-byte chunks instead,
+// each such group hits only the low halves of the chunks and takes two cycles).
+// A 16-byte read of logical bytes 16c .. 16c + 15 of row r then finds them in
+// chunk c ^ (r & 7), with the two halves exchanged in rows 8 .. 15 (f odd):
+// the second read of each piece, so the exchange is a fixed register order.
 template <class C, class E, int ACT>
 __device__ __forceinline__ void store_perwave(const Acc<C, E>& acc, uint16_t* __restrict__ y,
                                               int64_t M, int64_t N, int64_t m0, int64_t n0, int wm,
@@ -959,14 +963,13 @@ __device__ __forceinline__ void store_perwave(const Acc<C, E>& acc, uint16_t* __
                                               const float* b_l, char* pw) {
     static_assert(C::EPW, "per-wave epilogue");
     const int lr = (int)((unsigned)lane % 16), hi = (int)((unsigned)lane / 16);
-    // writes: row lr, logical byte 32 * nl + 16 * (hi >> 1) + 8 * (hi & 1), at
-    // wofs + ((32 * nl) ^ g) with the row's chunk XOR folded into g
-    const uint32_t wofs = (uint32_t)(lr * 128 + 8 * (hi & 1));
-    const uint32_t g = (16u * (uint32_t)(hi >> 1)) ^ (16u * (uint32_t)((lr >> 1) & 7));
-    // reads: rows rr and rr + 8, chunk rc
+    // writes: row lr, logical slot 4 * nl + hi, at wofs + ((32 * nl) ^ g)
+    const uint32_t wofs = (uint32_t)(lr * 128);
+    const uint32_t g = 8u * (uint32_t)(hi ^ (2 * (lr & 7) + (lr >> 3)));
+    // reads: rows rr and rr + 8, logical chunk rc, at physical chunk rc ^ rr
     const int rr = (int)((unsigned)lane / 8), rc = (int)((unsigned)lane % 8);
-    const uint32_t rofs0 = (uint32_t)(rr * 128 + 16 * (rc ^ ((rr >> 1) & 7)));
-    const uint32_t rofs1 = (uint32_t)((rr + 8) * 128 + 16 * (rc ^ (((rr + 8) >> 1) & 7)));
+    const uint32_t rofs0 = (uint32_t)(rr * 128 + 16 * (rc ^ rr));
+    const uint32_t rofs1 = rofs0 + 8u * 128u;
     const bool interior = (m0 + C::BM <= M) && (n0 + C::BN <= N);
     const int64_t row0 = m0 + wm * C::TM + rr, col0 = n0 + wn * C::TN + 8 * rc;
     uint16_t* base = y + row0 * N + col0;
@@ -1003,7 +1006,8 @@ __device__ __forceinline__ void store_perwave(const Acc<C, E>& acc, uint16_t* __
                 *reinterpret_cast<uint2*>(pw + (wofs + ((32u * (uint32_t)nl) ^ g))) = o;
             }
             const v4i d0 = *reinterpret_cast<const v4i*>(pw + rofs0);
-            const v4i d1 = *reinterpret_cast<const v4i*>(pw + rofs1);
+            const v4i e1 = *reinterpret_cast<const v4i*>(pw + rofs1);
+            const v4i d1 = {e1[2], e1[3], e1[0], e1[1]};  // rows 8 .. 15: halves exchanged
             uint16_t* dst = base + (int64_t)(mi * 16) * N + 64 * h;
             const bool cols_in = interior || 64 * h < cols_left;
             if (cols_in && (interior || mi * 16 < rows_left)) {
