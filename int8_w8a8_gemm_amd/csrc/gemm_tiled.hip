@@ -974,60 +974,74 @@ __device__ __forceinline__ void store_perwave(const Acc<C, E>& acc, uint16_t* __
     const int64_t row0 = m0 + wm * C::TM + rr, col0 = n0 + wn * C::TN + 8 * rc;
     uint16_t* base = y + row0 * N + col0;
     const int64_t rows_left = M - row0, cols_left = N - col0;
-#pragma unroll
-    for (int mi = 0; mi < C::MI; ++mi) {
+    // the bf16 values of piece (mi, h) for column groups nl = 0 .. 3, packed
+    auto piece = [&](auto mic, auto hc, uint2 (&o)[4]) __attribute__((always_inline)) {
+        constexpr int mi = decltype(mic)::value, h = decltype(hc)::value;
         const float sam = E::BYTES == 1 ? sa_l[wm * C::TM + mi * 16 + lr] : 0.f;
 #pragma unroll
-        for (int h = 0; h < C::NI / 4; ++h) {
+        for (int nl = 0; nl < 4; ++nl) {
+            const int ni = 4 * h + nl;
+            const int cl = wn * C::TN + ni * 16 + 4 * hi;
+            v4f swv = {}, bv;
+            if constexpr (E::BYTES == 1) swv = *reinterpret_cast<const v4f*>(sw_l + cl);
+            bv = *reinterpret_cast<const v4f*>(b_l + cl);
+            float v[4];
 #pragma unroll
-            for (int nl = 0; nl < 4; ++nl) {
-                const int ni = 4 * h + nl;
-                const int cl = wn * C::TN + ni * 16 + 4 * hi;
-                v4f swv = {}, bv;
-                if constexpr (E::BYTES == 1) swv = *reinterpret_cast<const v4f*>(sw_l + cl);
-                bv = *reinterpret_cast<const v4f*>(b_l + cl);
-                float v[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    if constexpr (E::BYTES == 1) {
-                        const float t = (float)acc[ni][mi][e];  // nearest even
-                        const float u = __fmul_rn(sam, swv[e]);
-                        v[e] = __builtin_fmaf(t, u, bv[e]);
-                    } else {
-                        v[e] = __fadd_rn(acc[ni][mi][e], bv[e]);
-                    }
+            for (int e = 0; e < 4; ++e) {
+                if constexpr (E::BYTES == 1) {
+                    const float t = (float)acc[ni][mi][e];  // nearest even
+                    const float u = __fmul_rn(sam, swv[e]);
+                    v[e] = __builtin_fmaf(t, u, bv[e]);
+                } else {
+                    v[e] = __fadd_rn(acc[ni][mi][e], bv[e]);
                 }
-                uint2 o = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-                if (ACT == 1) {
-                    // GELU-tanh of the bf16-rounded value, rounded to bf16 (gelu_bf16_rn)
-                    o = make_uint2(gelu_bf16_rn(o.x & 0xffffu) | (gelu_bf16_rn(o.x >> 16) << 16),
-                                   gelu_bf16_rn(o.y & 0xffffu) | (gelu_bf16_rn(o.y >> 16) << 16));
-                }
-                *reinterpret_cast<uint2*>(pw + (wofs + ((32u * (uint32_t)nl) ^ g))) = o;
             }
-            const v4i d0 = *reinterpret_cast<const v4i*>(pw + rofs0);
-            const v4i e1 = *reinterpret_cast<const v4i*>(pw + rofs1);
-            const v4i d1 = {e1[2], e1[3], e1[0], e1[1]};  // rows 8 .. 15: halves exchanged
-            uint16_t* dst = base + (int64_t)(mi * 16) * N + 64 * h;
-            const bool cols_in = interior || 64 * h < cols_left;
-            if (cols_in && (interior || mi * 16 < rows_left)) {
-#if W8A8_STORE_NT
-                __builtin_nontemporal_store(d0, reinterpret_cast<v4i*>(dst));
-#else
-                *reinterpret_cast<v4i*>(dst) = d0;
-#endif
+            o[nl] = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+            if (ACT == 1) {
+                // GELU-tanh of the bf16-rounded value, rounded to bf16 (gelu_bf16_rn)
+                o[nl] = make_uint2(gelu_bf16_rn(o[nl].x & 0xffffu) | (gelu_bf16_rn(o[nl].x >> 16) << 16),
+                                   gelu_bf16_rn(o[nl].y & 0xffffu) | (gelu_bf16_rn(o[nl].y >> 16) << 16));
             }
-            if (cols_in && (interior || mi * 16 + 8 < rows_left)) {
-#if W8A8_STORE_NT
-                __builtin_nontemporal_store(d1, reinterpret_cast<v4i*>(dst + 8 * N));
-#else
-                *reinterpret_cast<v4i*>(dst + 8 * N) = d1;
-#endif
-            }
-            // register-tight tiles: keep the next piece's scale reads here
-            if constexpr (C::RECYCLE) __builtin_amdgcn_sched_barrier(0);
         }
-    }
+    };
+    // Pieces in order mi, h, software-pipelined: a piece is staged and its
+    // reads issued, then the next piece's values are computed while those
+    // reads are in flight, and only then are they waited for and stored (the
+    // next piece's writes come after this piece's reads, which LDS executes
+    // first).
+    constexpr int H = C::NI / 4, P = C::MI * H;
+    uint2 o[4];
+    piece(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, o);
+    auto step = [&](auto pc) __attribute__((always_inline)) {
+        constexpr int p = decltype(pc)::value, mi = p / H, h = p % H;
+#pragma unroll
+        for (int nl = 0; nl < 4; ++nl)
+            *reinterpret_cast<uint2*>(pw + (wofs + ((32u * (uint32_t)nl) ^ g))) = o[nl];
+        const v4i d0 = *reinterpret_cast<const v4i*>(pw + rofs0);
+        const v4i e1 = *reinterpret_cast<const v4i*>(pw + rofs1);
+        if constexpr (p + 1 < P)
+            piece(std::integral_constant<int, (p + 1) / H>{}, std::integral_constant<int, (p + 1) % H>{}, o);
+        const v4i d1 = {e1[2], e1[3], e1[0], e1[1]};  // rows 8 .. 15: halves exchanged
+        uint16_t* dst = base + (int64_t)(mi * 16) * N + 64 * h;
+        const bool cols_in = interior || 64 * h < cols_left;
+        if (cols_in && (interior || mi * 16 < rows_left)) {
+#if W8A8_STORE_NT
+            __builtin_nontemporal_store(d0, reinterpret_cast<v4i*>(dst));
+#else
+            *reinterpret_cast<v4i*>(dst) = d0;
+#endif
+        }
+        if (cols_in && (interior || mi * 16 + 8 < rows_left)) {
+#if W8A8_STORE_NT
+            __builtin_nontemporal_store(d1, reinterpret_cast<v4i*>(dst + 8 * N));
+#else
+            *reinterpret_cast<v4i*>(dst + 8 * N) = d1;
+#endif
+        }
+        // register-tight tiles: keep the piece after next from being hoisted here
+        if constexpr (C::RECYCLE) __builtin_amdgcn_sched_barrier(0);
+    };
+    for_each_pass(step, std::make_integer_sequence<int, P>{});
 }
 
 // The K groups' partial sums are added through LDS (the ring, which the K loop
