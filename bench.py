@@ -498,9 +498,12 @@ def hbm_from(trace_dir, fetch_dir, write_dir):
 
 def small_from(trace_dir, pmc_dir):
     """Per-kernel duration (kernel trace, median of each kernel's last SMALL_PROBE_REPS
-    launches) and MFMA counters (SQ_INSTS_MFMA, SQ_VALU_MFMA_BUSY_CYCLES, median launch)
-    of --probe-small: the rate the matrix cores were issued at, and their busy share of
-    the 1024 SIMDs at 2.4 GHz over the kernel's duration."""
+    launches) and counters (median launch) of a rocprofv3 run of --probe-small (or of
+    any other probe: a directory without a kernel trace gives counters only).  With
+    SQ_INSTS_MFMA and SQ_VALU_MFMA_BUSY_CYCLES: the rate the matrix cores were issued
+    at, and their busy share of the 1024 SIMDs at 2.4 GHz over the kernel's duration;
+    with the per-CU texture-path counters (TA, TD, TCP) and GRBM_GUI_ACTIVE: their busy
+    or stalled share of the active cycles."""
     import csv
     import glob
     import re
@@ -533,12 +536,24 @@ def small_from(trace_dir, pmc_dir):
     for (kn, _), v in per.items():
         cnt.setdefault(kn, []).append(v)
     out = {}
-    for k, ds in dur.items():
-        ds = ds[-SMALL_PROBE_REPS:]
-        t = sorted(ds)[len(ds) // 2]
-        r = {"launches": len(ds), "median_us": round(t * 1e6, 2)}
+    for k in sorted(set(dur) | set(cnt)):
+        ds = dur.get(k, [])[-SMALL_PROBE_REPS:]
+        t = sorted(ds)[len(ds) // 2] if ds else None
+        r = {"launches": len(ds), "median_us": round(t * 1e6, 2)} if ds else {}
         cs = cnt.get(k, [])
-        if cs and "SQ_INSTS_MFMA" in cs[0]:
+        if cs:
+            # every counter of the median launch; per-CU blocks (TA, TD, TCP: one per CU,
+            # 256) as a share of the active cycles of one XCC (GRBM_GUI_ACTIVE is summed
+            # over the 8 XCCs)
+            c = cs[len(cs) // 2]
+            r["counters"] = {n: v for n, v in sorted(c.items())}
+            act = c.get("GRBM_GUI_ACTIVE", 0.0) / 8
+            for n in ("TA_TA_BUSY_sum", "TA_ADDR_STALLED_BY_TC_CYCLES_sum",
+                      "TA_DATA_STALLED_BY_TC_CYCLES_sum", "TD_TD_BUSY_sum", "TD_TC_STALL_sum",
+                      "TCP_PENDING_STALL_CYCLES_sum", "TCP_TCP_TA_DATA_STALL_CYCLES_sum"):
+                if n in c and act > 0:
+                    r[n.replace("_sum", "") + "_per_cu_frac"] = round(c[n] / (256 * act), 4)
+        if cs and t and "SQ_INSTS_MFMA" in cs[0]:
             c = cs[len(cs) // 2]
             n, busy = c["SQ_INSTS_MFMA"], c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0)
             mt = re.search(r"Cfg<[^>]*, (16|32)>", k)  # the MFMA tile edge

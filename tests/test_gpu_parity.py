@@ -776,11 +776,12 @@ def _sampled_linear(x_u16, w_u16, b_u16, rows, act=w8.ACT_NONE, label=""):
     return got, ref
 
 
-def _video_rows(M, n=512, tile=384, seed=1):
-    """n seeded rows of [0, M): both rows at every boundary of the 384-row tiles
-    the video GEMMs run on, the first and the last row, and seeded random rows
-    to make up n (M = 24576: 128 edge rows and 384 random ones)."""
-    edges = {0, M - 1} | {r for b in range(tile, M, tile) for r in (b - 1, b)}
+def _video_rows(M, n=512, tiles=(256, 384), seed=1):
+    """n seeded rows of [0, M): both rows at every boundary of the 256-row tiles
+    the video GEMMs run on (and of 384-row tiles), the first and the last row,
+    and seeded random rows to make up n (M = 24576: 256 edge rows and 256
+    random ones)."""
+    edges = {0, M - 1} | {r for t in tiles for b in range(t, M, t) for r in (b - 1, b)}
     rng = np.random.Generator(np.random.PCG64(seed))
     rest = [int(r) for r in rng.permutation(M) if int(r) not in edges][:max(0, n - len(edges))]
     return np.array(sorted(edges | set(rest)), dtype=np.int64)
