@@ -556,7 +556,8 @@ def small_from(trace_dir, pmc_dir):
         if cs and t and "SQ_INSTS_MFMA" in cs[0]:
             c = cs[len(cs) // 2]
             n, busy = c["SQ_INSTS_MFMA"], c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0)
-            mt = re.search(r"Cfg<[^>]*, (16|32)>", k)  # the MFMA tile edge
+            # the MFMA tile edge: Cfg's tenth template argument
+            mt = re.search(r"Cfg<(?:[^,<>]*, ){9}(16|32)\b", k)
             # int8: 32x32x32 or 16x16x64; bf16: 32x32x16 or 16x16x32 (ops = 2 x MACs)
             ops = n * (65536 if "ElemI8" in k else 32768) // (2 if mt and mt.group(1) == "16" else 1)
             r.update({"mfma": int(n), "mfma_busy_cycles": int(busy),
